@@ -1,0 +1,366 @@
+"""Seeded synthetic decode workloads shaped like the pages' examples.
+
+This module only builds inputs: sequence lengths, block tables (through a
+small reference-counted block allocator) and N(0,1) tensors.  It holds none of
+the arithmetic of the paged write or of attention, so both the HIP path and
+the CPU oracle may be fed from it.
+
+Five workloads are defined (sizes in the docstring of each builder):
+
+* ``tiny_f32``         - 4 sequences of lengths 1/7/16/33, fp32, 4/2 heads, D 64
+* ``qwen1p5b_bf16``    - 64 sequences, lognormal lengths (mean ~480), 12/2, D 128
+* ``llama_gqa4k_bf16`` - 256 sequences x 4096 tokens, 32/8, D 128
+* ``opt13b_mha_f16``   - 200 sequences, prompt U[100,2000] + output U[20,1500], 40/40
+* ``shared_prefix_bf16`` - 64 prompts x 6 forked samples, 450 tokens, 32/8
+
+Block tables are built by allocating blocks in a plain sequence of logical
+ids and then relabelling every id through a seeded permutation of the whole
+pool, so a table's physical ids are scattered and unrelated to each other.
+"""
+
+from __future__ import annotations
+
+import math
+import random
+from collections import deque
+from dataclasses import dataclass, field
+
+import numpy as np
+
+DTYPES = ("f32", "f16", "bf16")
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+
+# --------------------------------------------------------------------------
+# Block allocation (input construction only)
+# --------------------------------------------------------------------------
+
+
+class BlockPool:
+    """Fixed set of physical blocks: FIFO free queue plus reference counts.
+
+    Behaves like the handbook's BlockPool: ``allocate(n)`` takes n blocks from
+    the head of the free queue or returns None when short, ``free`` drops one
+    reference per block and re-queues a block at the tail when its count
+    reaches zero.  ``retain`` adds a reference (a fork sharing the block).
+    """
+
+    def __init__(self, num_blocks: int, order=None):
+        self.num_blocks = int(num_blocks)
+        self.ref_cnt = [0] * self.num_blocks
+        ids = range(self.num_blocks) if order is None else [int(x) for x in order]
+        self.free_queue = deque(ids)
+
+    def num_free(self) -> int:
+        return len(self.free_queue)
+
+    def allocate(self, n: int):
+        if n > len(self.free_queue):
+            return None
+        blocks = [self.free_queue.popleft() for _ in range(n)]
+        for b in blocks:
+            self.ref_cnt[b] = 1
+        return blocks
+
+    def retain(self, blocks) -> None:
+        for b in blocks:
+            self.ref_cnt[b] += 1
+
+    def free(self, blocks) -> None:
+        for b in blocks:
+            self.ref_cnt[b] -= 1
+            if self.ref_cnt[b] == 0:
+                self.free_queue.append(b)
+
+
+@dataclass
+class SeqBlocks:
+    """One sequence's block list and token count, grown token-run by run."""
+
+    block_size: int
+    blocks: list = field(default_factory=list)
+    length: int = 0
+
+    def fork(self, pool: BlockPool) -> "SeqBlocks":
+        """A second sequence sharing every block (parallel sampling)."""
+        pool.retain(self.blocks)
+        return SeqBlocks(self.block_size, list(self.blocks), self.length)
+
+    def append(self, n: int, pool: BlockPool, copies: list) -> None:
+        """Append n tokens: open a new block when the last one is full, and
+        copy a shared, partly filled last block before writing into it
+        (copy-on-write).  Each copy is recorded as (src, dst, rows)."""
+        while n > 0:
+            used = self.length % self.block_size
+            if used == 0:
+                got = pool.allocate(1)
+                if got is None:
+                    raise MemoryError("block pool exhausted")
+                self.blocks.append(got[0])
+            elif pool.ref_cnt[self.blocks[-1]] > 1:
+                got = pool.allocate(1)
+                if got is None:
+                    raise MemoryError("block pool exhausted")
+                old = self.blocks[-1]
+                copies.append((old, got[0], used))
+                pool.free([old])
+                self.blocks[-1] = got[0]
+            take = min(n, self.block_size - used)
+            self.length += take
+            n -= take
+
+
+# --------------------------------------------------------------------------
+# Workload structure (integers only)
+# --------------------------------------------------------------------------
+
+
+@dataclass
+class Workload:
+    name: str
+    dtype: str
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    context_lens: np.ndarray  # int32 [B], includes this step's token
+    block_tables: np.ndarray  # int32 [B, max_blocks_per_seq]
+    scale: float  # float32 value 1/sqrt(head_dim)
+    pad_block: int  # an unowned block id filling unused table entries
+    unowned_blocks: np.ndarray  # int64 ids no sequence references
+    cow_copies: list  # (src, dst, rows) prefix copies made by copy-on-write
+    description: str = ""
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max())
+
+    @property
+    def elem_bytes(self) -> int:
+        return ELEM_BYTES[self.dtype]
+
+    def kv_read_bytes(self) -> int:
+        """K and V bytes of every valid context token (each read once)."""
+        return int(self.context_lens.astype(np.int64).sum()) * self.num_kv_heads * self.head_dim * self.elem_bytes * 2
+
+
+def _scale(head_dim: int) -> float:
+    return float(np.float32(1.0 / math.sqrt(head_dim)))
+
+
+def _finish(name, dtype, heads, kv_heads, head_dim, bs, seqs, used, num_blocks, perm_ids,
+            lens, copies, extra_cols, description):
+    """Relabel logical ids 0..used-1 to physical ids perm_ids[k]; pad tables."""
+    perm_ids = np.asarray(perm_ids, dtype=np.int64)
+    assert len(set(perm_ids[:used].tolist())) == used
+    owned = set(int(x) for x in perm_ids[:used])
+    unowned = np.array(sorted(set(range(num_blocks)) - owned), dtype=np.int64)
+    assert unowned.size > 0, "pool needs at least one unowned block"
+    pad = int(unowned[0])
+    width = max(len(s.blocks) for s in seqs) + int(extra_cols)
+    tables = np.full((len(seqs), width), pad, dtype=np.int32)
+    for i, s in enumerate(seqs):
+        tables[i, : len(s.blocks)] = perm_ids[np.asarray(s.blocks, dtype=np.int64)]
+    cow = [(int(perm_ids[a]), int(perm_ids[b]), int(r)) for a, b, r in copies]
+    return Workload(name, dtype, heads, kv_heads, head_dim, bs, int(num_blocks),
+                    np.asarray(lens, dtype=np.int32), tables, _scale(head_dim), pad, unowned,
+                    cow, description)
+
+
+def _alloc_plain(lens, bs):
+    """Allocate each sequence's full context in sequence order (logical ids)."""
+    pool = BlockPool(sum(int(n) for n in lens) + 1)  # ample: a block holds >= 1 token
+    seqs, copies = [], []
+    for n in lens:
+        s = SeqBlocks(bs)
+        s.append(int(n), pool, copies)
+        seqs.append(s)
+    used = pool.num_blocks - pool.num_free()
+    return seqs, used, copies
+
+
+def tiny_f32(seed: int = 0, extra_cols: int = 0) -> Workload:
+    """4 sequences with contexts 1, 7, 16, 33; block 16; 64-block pool whose
+    free order is a seeded permutation; 4 query / 2 KV heads; D 64; fp32;
+    scale 1/8.  New tokens land at positions 0, 6, 15 (last slot of a block)
+    and 32 (first slot of a new block)."""
+    lens = [1, 7, 16, 33]
+    bs, nb = 16, 64
+    perm = np.random.default_rng(seed).permutation(nb)
+    seqs, used, copies = _alloc_plain(lens, bs)
+    return _finish("tiny_f32", "f32", 4, 2, 64, bs, seqs, used, nb, perm, lens, copies,
+                   extra_cols, "4 seqs L={1,7,16,33}, H 4 / Hkv 2, D 64, fp32, NB 64")
+
+
+def lognormal_lengths(n: int, mean: float, sigma: float, lo: int, hi: int, seed: int):
+    """Lengths ~ lognormal with the given mean, rounded and clipped."""
+    mu = math.log(mean) - sigma * sigma / 2.0
+    raw = np.random.default_rng(seed).lognormal(mu, sigma, n)
+    return np.clip(np.rint(raw), lo, hi).astype(np.int64)
+
+
+def qwen1p5b_bf16(seed: int = 0, extra_cols: int = 0) -> Workload:
+    """Qwen2.5-1.5B-shaped layer: 64 sequences, lengths lognormal (sigma 0.8,
+    mean 480) clipped to [16, 2048]; 12 query / 2 KV heads; D 128; bf16; pool =
+    used blocks + 10%, physical ids shuffled."""
+    lens = lognormal_lengths(64, 480.0, 0.8, 16, 2048, seed)
+    bs = 16
+    seqs, used, copies = _alloc_plain(lens, bs)
+    nb = math.ceil(1.1 * used)
+    perm = np.random.default_rng(seed + 1).permutation(nb)
+    return _finish("qwen1p5b_bf16", "bf16", 12, 2, 128, bs, seqs, used, nb, perm, lens, copies,
+                   extra_cols, "64 seqs lognormal(mean 480, sigma 0.8) in [16,2048], H 12 / Hkv 2, D 128, bf16")
+
+
+def llama_gqa4k_bf16(seed: int = 0, extra_cols: int = 0, num_seqs: int = 256,
+                     context: int = 4096) -> Workload:
+    """Llama-style GQA layer: 256 sequences of exactly 4096 tokens (256
+    blocks each); 32 query / 8 KV heads; D 128; bf16; the 65536 used blocks
+    are a random sample of a 72090-block pool, in random order."""
+    lens = [context] * num_seqs
+    bs = 16
+    seqs, used, copies = _alloc_plain(lens, bs)
+    nb = max(math.ceil(1.1 * used), used + 1)
+    perm = np.random.default_rng(seed).permutation(nb)
+    return _finish("llama_gqa4k_bf16", "bf16", 32, 8, 128, bs, seqs, used, nb, perm, lens, copies,
+                   extra_cols, f"{num_seqs} seqs x {context} tokens, H 32 / Hkv 8, D 128, bf16, NB {nb}")
+
+
+def opt13b_lengths(seed: int = 0):
+    """Prompt U[100,2000] + output U[20,1500] for 200 requests, drawn with
+    Python's random module exactly as the handbook's utilisation estimate."""
+    rnd = random.Random(seed)
+    reqs = [(rnd.randint(100, 2000), rnd.randint(20, 1500)) for _ in range(200)]
+    return [p + o for p, o in reqs]
+
+
+def opt13b_mha_f16(seed: int = 0, extra_cols: int = 0) -> Workload:
+    """OPT-13B-shaped MHA layer: 200 sequences of prompt+output length from
+    the handbook's seed-0 generator; 40 query / 40 KV heads; D 128; fp16; pool =
+    used blocks + 10%, physical ids shuffled."""
+    lens = opt13b_lengths(seed)
+    bs = 16
+    seqs, used, copies = _alloc_plain(lens, bs)
+    nb = math.ceil(1.1 * used)
+    perm = np.random.default_rng(seed + 1).permutation(nb)
+    return _finish("opt13b_mha_f16", "f16", 40, 40, 128, bs, seqs, used, nb, perm, lens, copies,
+                   extra_cols, "200 seqs prompt U[100,2000] + output U[20,1500], H 40 / Hkv 40, D 128, fp16")
+
+
+def shared_prefix_bf16(seed: int = 0, extra_cols: int = 0, prompts: int = 64, samples: int = 6,
+                       prompt_len: int = 300, gen_len: int = 150) -> Workload:
+    """Parallel sampling: 64 prompts of 300 tokens, each forked into 6
+    samples that generate 150 tokens; the prompt's blocks are shared by
+    reference count and a sample copies the shared, partly filled last prompt
+    block before its first write (copy-on-write).  One decode step at length
+    450 over the 384 sequences (sample-major within each prompt); 32/8 heads,
+    D 128, bf16; pool = used blocks + 10%, physical ids shuffled.
+
+    Engine-like order: prefill every prompt, fork, then generate round-robin
+    over all sequences; the decode step's token is the last generated one."""
+    bs = 16
+    total = prompt_len + gen_len
+    pool = BlockPool(prompts * samples * total + 1)  # ample: a block holds >= 1 token
+    copies = []
+    roots = []
+    for _ in range(prompts):
+        s = SeqBlocks(bs)
+        s.append(prompt_len, pool, copies)
+        roots.append(s)
+    seqs = []
+    for r in roots:
+        group = [r] + [r.fork(pool) for _ in range(samples - 1)]
+        # the root becomes the last sample: the others copy before it writes
+        seqs.extend(group[1:] + [group[0]])
+    for _ in range(gen_len):
+        for s in seqs:
+            s.append(1, pool, copies)
+    used = len(set(b for s in seqs for b in s.blocks))
+    nb = math.ceil(1.1 * used)
+    perm = np.random.default_rng(seed).permutation(nb)
+    # make the referenced logical ids dense before relabelling
+    live = sorted(set(b for s in seqs for b in s.blocks))
+    relabel = {b: i for i, b in enumerate(live)}
+    for s in seqs:
+        s.blocks = [relabel[b] for b in s.blocks]
+    copies = [(relabel[a], relabel[b], r) for a, b, r in copies if a in relabel and b in relabel]
+    lens = [total] * len(seqs)
+    return _finish("shared_prefix_bf16", "bf16", 32, 8, 128, bs, seqs, len(live), nb, perm, lens,
+                   copies, extra_cols,
+                   f"{prompts} prompts x {samples} samples, {prompt_len}+{gen_len} tokens, H 32 / Hkv 8, D 128, bf16")
+
+
+BUILDERS = {
+    "tiny_f32": tiny_f32,
+    "qwen1p5b_bf16": qwen1p5b_bf16,
+    "llama_gqa4k_bf16": llama_gqa4k_bf16,
+    "opt13b_mha_f16": opt13b_mha_f16,
+    "shared_prefix_bf16": shared_prefix_bf16,
+}
+
+
+def make_workload(name: str, seed: int = 0, **kw) -> Workload:
+    return BUILDERS[name](seed=seed, **kw)
+
+
+# --------------------------------------------------------------------------
+# Tensors (torch, on any device)
+# --------------------------------------------------------------------------
+
+def torch_dtype(dtype: str):
+    import torch
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+
+
+def _randn(shape, dtype, gen, device, chunk=1 << 27):
+    """N(0,1) drawn in float32 from ``gen`` and rounded to ``dtype``,
+    generated in chunks so large pools need no float32 copy of the whole."""
+    import torch
+    td = torch_dtype(dtype)
+    out = torch.empty(shape, dtype=td, device=device)
+    flat = out.view(-1)
+    n = flat.numel()
+    for start in range(0, n, chunk):
+        stop = min(n, start + chunk)
+        flat[start:stop] = torch.randn(stop - start, generator=gen, device=device,
+                                       dtype=torch.float32).to(td)
+    return out
+
+
+def make_tensors(w: Workload, seed: int = 0, device="cpu"):
+    """q [B,H,D], new key/value rows [B,H_kv,D] and the K/V pools
+    [NB,BS,H_kv,D], all N(0,1) in the workload dtype from one seeded
+    generator on ``device``.  Copy-on-write copies are replayed on the pools,
+    so a copied block starts with the rows of the block it was copied from."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    b, h, hkv, d = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim
+    q = _randn((b, h, d), w.dtype, gen, device)
+    key = _randn((b, hkv, d), w.dtype, gen, device)
+    value = _randn((b, hkv, d), w.dtype, gen, device)
+    pshape = (w.num_blocks, w.block_size, hkv, d)
+    k_pool = _randn(pshape, w.dtype, gen, device)
+    v_pool = _randn(pshape, w.dtype, gen, device)
+    for src, dst, rows in w.cow_copies:
+        k_pool[dst, :rows] = k_pool[src, :rows]
+        v_pool[dst, :rows] = v_pool[src, :rows]
+    return {"query": q, "key": key, "value": value, "k_pool": k_pool, "v_pool": v_pool}
+
+
+def raw_numpy(t):
+    """A torch tensor's storage as numpy: float32/float16 as such, bfloat16 as
+    uint16 bit patterns."""
+    import torch
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()

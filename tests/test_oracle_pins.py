@@ -1,0 +1,380 @@
+"""Pins of the CPU oracle against facts the pages fix and mathematics.
+
+Each test checks the oracle against something other than itself: values
+printed on the pages (fixtures under tests/golden/, each citing its page and
+section), an independent library routine (PyTorch's float64 scaled dot-product
+attention), a scalar brute-force implementation with exact sums, closed forms
+and invariants.
+"""
+
+import json
+import math
+from pathlib import Path
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle as O
+from paged_kv_cache_size_amd.workloads import BlockPool, SeqBlocks, opt13b_lengths
+
+GOLDEN = Path(__file__).parent / "golden"
+
+
+def load(name):
+    return json.loads((GOLDEN / name).read_text())
+
+
+# ---------------------------------------------------------------- slots / counts
+
+def test_slot_examples_from_pages():
+    for case in load("slot_examples.json")["cases"]:
+        got = [O.slot_for(case["block_table"], p, case["block_size"]) for p in case["positions"]]
+        assert got == case["slots"], case["source"]
+
+
+def test_slot_mapping_places_new_tokens_at_end_of_context():
+    # [7,3], block 4: a 6-token context; the decode token is position 5 -> 13.
+    assert O.slot_mapping([[7, 3]], [6], 4).tolist() == [13]
+    # all six tokens as new tokens of one request -> the page's full list
+    assert O.slot_mapping([[7, 3]], [6], 4, query_lens=[6]).tolist() == [28, 29, 30, 31, 12, 13]
+    # two requests concatenated in order
+    got = O.slot_mapping([[7, 3], [5, 6, 7, 0]], [5, 14], 4, query_lens=[2, 3]).tolist()
+    assert got == [31, 12, 31, 0, 1]  # positions 3,4 of [7,3]; 11,12,13 of [5,6,7,0]
+
+
+def test_block_counts_from_pages():
+    data = load("block_counts.json")
+    for case in data["cases"]:
+        assert O.num_blocks(case["tokens"], case["block_size"]) == case["blocks"], case["source"]
+        if "allocated_slots" in case:
+            assert O.num_blocks(case["tokens"], case["block_size"]) * case["block_size"] == case["allocated_slots"]
+            assert O.tail_slots(case["tokens"], case["block_size"]) == case["empty_slots"]
+    ex = data["bytes_example"]
+    per_tok = O.kv_bytes_per_token(32, 8, 128, 2)
+    assert per_tok == ex["bytes_per_token"]
+    assert 4100 * per_tok / 2**20 == ex["valid_MiB"]
+    assert O.num_blocks(4100, 16) * 16 * per_tok / 2**20 == ex["allocated_MiB"]
+    assert O.tail_slots(4100, 16) * per_tok / 2**20 == ex["empty_MiB"]
+
+
+def test_tail_waste_bound():
+    # at most B-1 slots wasted, zero exactly at multiples of B
+    for bs in (1, 4, 16, 64):
+        for t in range(1, 300):
+            w = O.tail_slots(t, bs)
+            assert 0 <= w <= bs - 1
+            assert (w == 0) == (t % bs == 0)
+
+
+# ---------------------------------------------------------------- allocator (input builder)
+
+def test_fifo_pool_doctest():
+    d = load("allocator_examples.json")["fifo_doctest"]
+    pool = BlockPool(d["num_blocks"])
+    table = pool.allocate(d["first_allocate"])
+    assert (table, pool.num_free()) == (d["first_table"], d["free_after_first"])
+    pool.allocate(d["second_allocate"])
+    pool.free(table)
+    assert pool.allocate(d["third_allocate"]) == d["third_table"]
+    assert pool.allocate(100) is None
+
+
+def round_robin_tables(num_blocks, block_size, seq_lens):
+    pool = BlockPool(num_blocks)
+    tables = [[] for _ in seq_lens]
+    while any(len(t) * block_size < s for t, s in zip(tables, seq_lens)):
+        for t, s in zip(tables, seq_lens):
+            if len(t) * block_size < s:
+                t += pool.allocate(1)
+    return tables
+
+
+def test_round_robin_tables_from_page():
+    d = load("allocator_examples.json")["round_robin_tables"]
+    assert round_robin_tables(d["num_blocks"], d["block_size"], d["seq_lens"]) == d["tables"]
+
+
+def _refs(pool):
+    return {str(i): c for i, c in enumerate(pool.ref_cnt) if c > 0}
+
+
+def test_fork_copy_on_write_snapshots():
+    d = load("allocator_examples.json")["fork_cow_snapshots"]
+    pool = BlockPool(16)
+    copies = []
+    a = SeqBlocks(d["block_size"])
+    a.append(d["a_tokens"], pool, copies)
+    b = a.fork(pool)
+    s = d["after_fork"]
+    assert (a.blocks, b.blocks, _refs(pool)) == (s["a"], s["b"], s["refs"])
+    assert len(_refs(pool)) == s["physical_blocks"]
+    b.append(1, pool, copies)
+    s = d["after_b_appends_one"]
+    assert (a.blocks, b.blocks, _refs(pool)) == (s["a"], s["b"], s["refs"])
+    assert len(_refs(pool)) == s["physical_blocks"]
+    assert copies == [(1, 2, 2)]  # B copied A's half-full second block (2 rows)
+    pool.free(a.blocks)
+    assert _refs(pool) == d["after_release_a"]["refs"]
+    pool.free(b.blocks)
+    assert len(_refs(pool)) == d["after_release_b"]["physical_blocks"]
+
+
+def test_parallel_sampling_block_table():
+    d = load("allocator_examples.json")["parallel_sampling"]
+    bs = d["block_size"]
+    for row in d["rows"]:
+        n = row["samples"]
+        pool = BlockPool(1000)
+        copies = []
+        root = SeqBlocks(bs)
+        root.append(d["prompt_len"], pool, copies)
+        seqs = [root.fork(pool) for _ in range(n - 1)] + [root]
+        for _ in range(d["gen_len"]):
+            for s in seqs:
+                s.append(1, pool, copies)
+        shared = len({b for s in seqs for b in s.blocks})
+        unshared = n * O.num_blocks(d["prompt_len"] + d["gen_len"], bs)
+        assert (unshared, shared) == (row["unshared_blocks"], row["shared_blocks"])
+        assert round(100 * (1 - shared / unshared), 1) == row["saving_pct"]
+
+
+# ---------------------------------------------------------------- utilisation / capacity
+
+def test_seed0_utilisation_from_page():
+    d = load("utilisation.json")["seed0_workload"]
+    lens = opt13b_lengths(0)
+    assert round(100 * O.capacity.reserved_utilisation(lens, d["max_len"]), 1) == d["reserved_pct"]
+    for bs, pct in d["paged_pct"].items():
+        assert round(100 * O.paged_utilisation(lens, int(bs)), 1) == pct
+
+
+def test_mini_vllm_utilisation():
+    d = load("utilisation.json")["mini_vllm"]
+    used = d["requests"] * d["used"]
+    assert round(100 * used / (d["requests"] * d["reserve"])) == d["contiguous_pct"]
+    assert round(100 * O.paged_utilisation([d["used"]] * d["requests"], d["block_size"])) == d["paged_pct"]
+
+
+def test_capacity_examples():
+    c = load("capacity.json")
+    e = c["qwen25_7b_exercise"]
+    per_tok = O.kv_bytes_per_token(e["layers"], e["kv_heads"], e["head_dim"], e["elem_bytes"])
+    assert per_tok == e["bytes_per_token"]
+    budget = e["budget_GiB"] * 1024**3
+    assert budget // (O.num_blocks(e["avg_context"], e["block_size"]) * e["block_size"] * per_tok) == e["paged_concurrency"]
+    assert budget // (e["reserve_len"] * per_tok) == e["reserved_concurrency"]
+    g = c["gqa_example"]
+    assert O.kv_bytes_per_token(g["layers"], g["kv_heads"], g["head_dim"], g["elem_bytes"]) == g["bytes_per_token"]
+    for h, mib in g["by_kv_heads_MiB"].items():
+        assert O.kv_bytes(g["layers"], int(h), g["head_dim"], g["tokens"], g["elem_bytes"]) // 2**20 == mib
+    assert O.kv_bytes(g["layers"], g["kv_heads"], g["head_dim"], g["tokens"], g["elem_bytes"], 8) / 2**30 == g["eight_requests_GiB"]
+    b = c["budget_example"]
+    per_req = O.kv_bytes(32, 8, 128, b["tokens"], 2) // 2**20
+    assert b["budget_MiB"] // per_req == b["requests"]
+    per_req2 = O.kv_bytes(32, 8, 128, b["tokens_with_output"], 2) // 2**20
+    assert per_req2 == b["request_MiB_with_output"]
+    assert b["budget_MiB"] // per_req2 == b["requests_with_output"]
+    o = c["opt13b"]  # 5120 hidden = 40 heads x 128, MHA
+    assert O.kv_bytes_per_token(o["layers"], 40, 128, o["elem_bytes"]) == o["bytes_per_token"] == 2 * o["hidden"] * o["layers"] * o["elem_bytes"]
+    q = c["qwen25_15b"]
+    per_tok = O.kv_bytes_per_token(q["layers"], q["kv_heads"], q["head_dim"], q["elem_bytes"])
+    assert per_tok == q["bytes_per_token"]
+    assert per_tok * q["tokens"] / 2**20 == q["MiB"]
+
+
+def test_kv_bytes_rejects_bad_sizes():
+    for bad in (0, -1, 1.5, True):
+        with pytest.raises(ValueError):
+            O.kv_bytes(32, 8, 128, bad, 2)
+
+
+# ---------------------------------------------------------------- storage decode
+
+def test_bf16_widen_known_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x7F80, 0xFF80, 0x0001, 0x3E00, 0x4049], dtype=np.uint16)
+    got = O.widen(bits, "bf16")
+    want = [1.0, -2.0, 0.0, -0.0, math.inf, -math.inf, 2.0**-133, 0.125, 3.140625]
+    assert got.tolist() == want
+    assert math.copysign(1.0, got[3]) == -1.0
+    assert np.isnan(O.widen(np.array([0x7FC0], dtype=np.uint16), "bf16")[0])
+
+
+# ---------------------------------------------------------------- write / gather
+
+def _pool(rng, nb, bs, hkv, d, dtype=np.float32):
+    return rng.standard_normal((nb, bs, hkv, d)).astype(dtype)
+
+
+def test_reshape_and_cache_writes_only_listed_slots_bit_exact():
+    rng = np.random.default_rng(3)
+    nb, bs, hkv, d = 9, 4, 2, 8
+    pool = rng.integers(0, 2**16, size=(nb, bs, hkv, d), dtype=np.uint16)  # arbitrary bf16 bits, NaNs included
+    before = pool.copy()
+    slots = np.array([35, 0, 17, 4, 22], dtype=np.int64)
+    rows = rng.integers(0, 2**16, size=(len(slots), hkv, d), dtype=np.uint16)
+    O.reshape_and_cache(pool, rows, slots)
+    flat, flat0 = pool.reshape(nb * bs, hkv, d), before.reshape(nb * bs, hkv, d)
+    for i, s in enumerate(slots):
+        assert np.array_equal(flat[s], rows[i])
+    untouched = np.setdiff1d(np.arange(nb * bs), slots)
+    assert np.array_equal(flat[untouched], flat0[untouched])
+
+
+def test_write_then_gather_round_trip():
+    rng = np.random.default_rng(4)
+    nb, bs, hkv, d = 32, 4, 2, 6
+    pool = np.zeros((nb, bs, hkv, d), np.float32)
+    seq_lens = [37, 5, 20]
+    tables = round_robin_tables(nb, bs, seq_lens)
+    seqs = [rng.standard_normal((s, hkv, d)).astype(np.float32) for s in seq_lens]
+    for t, k, s in zip(tables, seqs, seq_lens):
+        O.reshape_and_cache(pool, k, O.slot_mapping([t], [s], bs, query_lens=[s]))
+    for t, k, s in zip(tables, seqs, seq_lens):
+        assert np.array_equal(O.gather(pool, t, s), k)
+
+
+# ---------------------------------------------------------------- attention
+
+def _fill_paged(rng, seq_lens, hkv, d, bs, nb, dtype="f32", tables=None):
+    """Build per-request contiguous K/V and write them into fresh pools."""
+    if tables is None:
+        tables = round_robin_tables(nb, bs, seq_lens)
+    mk = {"f32": lambda a: a.astype(np.float32), "f16": lambda a: a.astype(np.float16),
+          "bf16": lambda a: (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)}[dtype]
+    store = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[dtype]
+    kp = np.zeros((nb, bs, hkv, d), store)
+    vp = np.zeros((nb, bs, hkv, d), store)
+    ks = [mk(rng.standard_normal((s, hkv, d))) for s in seq_lens]
+    vs = [mk(rng.standard_normal((s, hkv, d))) for s in seq_lens]
+    for t, k, v, s in zip(tables, ks, vs, seq_lens):
+        sl = O.slot_mapping([t], [s], bs, query_lens=[s])
+        O.reshape_and_cache(kp, k, sl)
+        O.reshape_and_cache(vp, v, sl)
+    return tables, kp, vp, ks, vs, mk
+
+
+def test_paged_equals_contiguous_and_torch_sdpa_on_handbook_setup():
+    p = load("paged_vs_contiguous.json")
+    rng = np.random.default_rng(0)
+    h, hkv, d, bs = p["num_heads"], p["num_kv_heads"], p["head_dim"], p["block_size"]
+    tables, kp, vp, ks, vs, mk = _fill_paged(rng, p["seq_lens"], hkv, d, bs, p["num_blocks"])
+    assert tables == load("allocator_examples.json")["round_robin_tables"]["tables"]
+    qs = [mk(rng.standard_normal((n, h, d))) for n in p["query_lens"]]
+    qsl = np.concatenate([[0], np.cumsum(p["query_lens"])])
+    out = O.paged_attention(np.concatenate(qs), kp, vp, tables, p["seq_lens"], qsl, p["scale"], "f32")
+    rep = h // hkv
+    for i, (q, k, v, s, n) in enumerate(zip(qs, ks, vs, p["seq_lens"], p["query_lens"])):
+        mine = out[qsl[i]:qsl[i + 1]]
+        # second formulation on the unpaged arrays
+        assert np.max(np.abs(mine - O.contiguous_attention(q, k, v, p["scale"], "f32"))) < 1e-12
+        # library routine: PyTorch SDPA in float64, KV heads repeated group-wise, causal mask
+        mask = torch.ones(n, s, dtype=torch.bool).tril(diagonal=s - n)
+        qt = torch.from_numpy(q.astype(np.float64)).transpose(0, 1)
+        kt = torch.from_numpy(k.astype(np.float64)).repeat_interleave(rep, 1).transpose(0, 1)
+        vt = torch.from_numpy(v.astype(np.float64)).repeat_interleave(rep, 1).transpose(0, 1)
+        ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask).transpose(0, 1).numpy()
+        err = np.max(np.abs(mine - ref))
+        assert err < 1e-12 and err < p["asserted_bound"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("h,hkv", [(4, 2), (3, 3), (6, 1), (8, 2)])
+def test_decode_matches_brute_force(dtype, h, hkv):
+    rng = np.random.default_rng(7)
+    d, bs = 8, 4
+    seq_lens = [1, 3, 4, 5, 9]
+    tables, kp, vp, ks, vs, mk = _fill_paged(rng, seq_lens, hkv, d, bs, 16, dtype)
+    q = mk(rng.standard_normal((len(seq_lens), h, d)))
+    scale = float(np.float32(1 / math.sqrt(d)))
+    out = O.decode_attention(q, kp, vp, tables, seq_lens, scale, dtype)
+    for b in range(len(seq_lens)):
+        bf = O.brute_force_decode(q[b], ks[b], vs[b], scale, dtype)
+        assert np.max(np.abs(out[b] - bf)) < 1e-13
+
+
+@pytest.mark.parametrize("h,hkv", [(8, 8), (8, 1), (12, 2)])
+def test_decode_matches_torch_sdpa_mha_mqa_gqa(h, hkv):
+    rng = np.random.default_rng(11)
+    d, bs = 16, 4
+    seq_lens = [2, 13, 16, 17]
+    tables, kp, vp, ks, vs, mk = _fill_paged(rng, seq_lens, hkv, d, bs, 40)
+    q = mk(rng.standard_normal((len(seq_lens), h, d)))
+    scale = 0.3
+    out = O.decode_attention(q, kp, vp, tables, seq_lens, scale, "f32")
+    rep = h // hkv
+    for b, (k, v) in enumerate(zip(ks, vs)):
+        qt = torch.from_numpy(q[b:b + 1].astype(np.float64)).transpose(0, 1)
+        kt = torch.from_numpy(k.astype(np.float64)).repeat_interleave(rep, 1).transpose(0, 1)
+        vt = torch.from_numpy(v.astype(np.float64)).repeat_interleave(rep, 1).transpose(0, 1)
+        ref = F.scaled_dot_product_attention(qt, kt, vt, scale=float(np.float32(scale))).transpose(0, 1).numpy()[0]
+        assert np.max(np.abs(out[b] - ref)) < 1e-12
+
+
+def test_single_token_context_returns_its_value_exactly():
+    rng = np.random.default_rng(5)
+    tables, kp, vp, ks, vs, mk = _fill_paged(rng, [1, 1], 2, 8, 4, 8, "bf16")
+    q = mk(rng.standard_normal((2, 4, 8)))
+    out = O.decode_attention(q, kp, vp, tables, [1, 1], 0.5, "bf16")
+    for b in range(2):
+        for hh in range(4):
+            assert np.array_equal(out[b, hh], O.widen(vs[b][0, hh // 2], "bf16"))
+
+
+def test_uniform_weights_give_mean_of_values():
+    rng = np.random.default_rng(6)
+    seq_lens = [5, 23]
+    tables, kp, vp, ks, vs, mk = _fill_paged(rng, seq_lens, 2, 8, 4, 16)
+    q0 = np.zeros((2, 4, 8), np.float32)
+    out = O.decode_attention(q0, kp, vp, tables, seq_lens, 0.35, "f32")
+    for b in range(2):
+        mean = vs[b].astype(np.float64).mean(axis=0)  # [hkv, d]
+        assert np.allclose(out[b], np.repeat(mean, 2, axis=0), rtol=0, atol=1e-14)
+    # equal keys: any q gives the mean as well
+    kp_eq = np.ones_like(kp)
+    q = rng.standard_normal((2, 4, 8)).astype(np.float32)
+    out = O.decode_attention(q, kp_eq, vp, tables, seq_lens, 0.35, "f32")
+    for b in range(2):
+        assert np.allclose(out[b], np.repeat(vs[b].astype(np.float64).mean(axis=0), 2, axis=0), atol=1e-14)
+
+
+def test_one_dominant_key_selects_its_value():
+    rng = np.random.default_rng(8)
+    seq_lens = [12]
+    tables, kp, vp, ks, vs, mk = _fill_paged(rng, seq_lens, 1, 8, 4, 8)
+    q = np.zeros((1, 1, 8), np.float32)
+    q[0, 0, 0] = 1.0
+    t_star = 7
+    slot = O.slot_for(tables[0], t_star, 4)
+    kp.reshape(-1, 1, 8)[slot, 0, 0] = 1e4  # score 1e4 * scale dwarfs the others
+    out = O.decode_attention(q, kp, vp, tables, seq_lens, 1.0, "f32")
+    assert np.array_equal(out[0, 0], vs[0][t_star, 0].astype(np.float64))
+
+
+def test_key_shift_invariance():
+    rng = np.random.default_rng(9)
+    seq_lens = [9, 30]
+    tables, kp, vp, ks, vs, mk = _fill_paged(rng, seq_lens, 2, 8, 4, 20)
+    q = rng.standard_normal((2, 4, 8)).astype(np.float32)
+    base = O.decode_attention(q, kp.astype(np.float64).astype(np.float32), vp, tables, seq_lens, 0.4, "f32")
+    c = rng.standard_normal((2, 8))  # per-KV-head constant added to every key
+    kp2 = (kp.astype(np.float64) + c[None, None]).astype(np.float32)
+    # exact in float64 only if the shifted keys are representable; compare loosely
+    shifted = O.decode_attention(q, kp2, vp, tables, seq_lens, 0.4, "f32")
+    assert np.max(np.abs(shifted - base)) < 1e-5
+
+
+def test_physical_block_permutation_invariance():
+    rng = np.random.default_rng(10)
+    seq_lens = [3, 16, 17, 40]
+    nb, bs = 30, 4
+    tables, kp, vp, ks, vs, mk = _fill_paged(rng, seq_lens, 2, 8, bs, nb)
+    q = mk(rng.standard_normal((4, 6, 8)))
+    base = O.decode_attention(q, kp, vp, tables, seq_lens, 0.25, "f32")
+    perm = rng.permutation(nb)  # block b moves to perm[b]
+    kp2, vp2 = np.empty_like(kp), np.empty_like(vp)
+    kp2[perm], vp2[perm] = kp, vp
+    tables2 = [[int(perm[b]) for b in t] for t in tables]
+    again = O.decode_attention(q, kp2, vp2, tables2, seq_lens, 0.25, "f32")
+    assert np.array_equal(base, again)
