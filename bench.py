@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-decode hot path on one MI355X.
+
+One step = the whole decode hot path over one batch: slot mapping of the new
+tokens, their K/V written into the paged pools, paged attention over every
+sequence's context (partition kernel + merge kernel).  Default workload: the
+Llama-style GQA layer, 256 sequences x 4096 tokens, 32 query / 8 KV heads,
+head_dim 128, bf16, block 16 (4 GiB of K/V read per step).
+
+Prints ONE JSON line.  ``value`` = decode tokens/s (one new token per
+sequence per step) with every input resident in HBM; ``roofline`` = KV bytes
+the partition kernel must read per launch / its average launch time, timed
+live with HIP events on the stream the kernels run on; ``cpu_baseline`` = the
+float64 CPU oracle on a bounded sample of the same batch.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_size_amd", "csrc", "pa_kernels.hip")
+METRIC = "paged decode attention tokens/s and KV-read GB/s (% of MI355X HBM peak)"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="llama_gqa4k_bf16")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--partition-size", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle CPU time")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain 1 GiB device copy (counter calibration) and exit")
+    return p.parse_args()
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per partition-kernel launch from committed counter runs, or
+    None when the kernel source changed since they were taken."""
+    path = os.path.join(PROFILES, f"decode_partition_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+
+
+def cpu_baseline(w, t, seconds):
+    """The oracle as it stands, timed on the host on whole sequences of the
+    same batch: slot mapping, pool write and decode attention."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from paged_kv_cache_size_amd import workloads as W
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+
+    def run(seqs):
+        blocks = sorted({int(x) for b in seqs
+                         for x in w.block_tables[b, :O.num_blocks(int(w.context_lens[b]), w.block_size)]})
+        remap = {x: i for i, x in enumerate(blocks)}
+        idx = torch.tensor(blocks, device="cuda")
+        kp, vp = W.raw_numpy(t["k_pool"][idx]), W.raw_numpy(t["v_pool"][idx])
+        tables = [[remap[int(x)] for x in w.block_tables[b, :O.num_blocks(int(w.context_lens[b]), w.block_size)]]
+                  for b in seqs]
+        lens = [int(w.context_lens[b]) for b in seqs]
+        sel = torch.tensor(seqs, device="cuda")
+        q, key, val = (W.raw_numpy(t[k][sel]) for k in ("query", "key", "value"))
+        t0 = time.perf_counter()
+        slots = O.slot_mapping(tables, lens, w.block_size)
+        O.reshape_and_cache(kp, key, slots)
+        O.reshape_and_cache(vp, val, slots)
+        O.decode_attention(q, kp, vp, tables, lens, w.scale, w.dtype)
+        return time.perf_counter() - t0
+
+    one = run([0])
+    n = int(max(1, min(w.num_seqs, seconds / max(one, 1e-6))))
+    seqs = list(range(n))
+    dt = run(seqs)
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} of {w.num_seqs} sequences (whole contexts) of {w.name}; "
+                      f"slot mapping + pool write + float64 attention, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the hot path has no multi-GPU form in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    from paged_kv_cache_size_amd import binding as PB
+    from paged_kv_cache_size_amd import workloads as W
+
+    PB.lib()  # fail loudly before any work if the HIP library is missing
+    w = W.make_workload(args.workload, seed=args.seed)
+    t = W.make_tensors(w, seed=args.seed, device="cuda")
+    dev = "cuda"
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    lens = torch.from_numpy(w.context_lens).to(dev)
+    B, H, D = t["query"].shape
+    ps = args.partition_size or PB.pa_decode_partition_size(B, H, w.num_kv_heads, w.max_context_len, w.block_size)
+    ws_bytes = PB.pa_decode_workspace_bytes(B, H, D, w.max_context_len, w.block_size, ps)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(t["query"])
+    slots = torch.empty(B, dtype=torch.int64, device=dev)
+
+    base = None
+    if not args.no_cpu_baseline:
+        base = cpu_baseline(w, t, args.cpu_seconds)
+
+    def k_slot():
+        PB.pa_slot_mapping(bt, lens, w.block_size, out=slots)
+
+    def k_write():
+        PB.pa_reshape_and_cache(t["key"], t["value"], t["k_pool"], t["v_pool"], slots)
+
+    def k_part():
+        PB.pa_decode_partitions(t["query"], t["k_pool"], t["v_pool"], bt, lens, w.scale, w.max_context_len, ps,
+                                workspace=ws, out=out)
+
+    def k_comb():
+        PB.pa_decode_combine(out, lens, w.max_context_len, ps, workspace=ws)
+
+    stages = [k_slot, k_write, k_part, k_comb]
+
+    def step():
+        for f in stages:
+            f()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-step throughput
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel launch times, events between the launches
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        evs[i][0].record()
+        for j, f in enumerate(stages):
+            f()
+            evs[i][j + 1].record()
+    torch.cuda.synchronize()
+    per_kernel_ms = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
+                     for j in range(len(stages))]
+
+    kv_bytes = w.kv_read_bytes()
+    part_ms = per_kernel_ms[2]
+    achieved = kv_bytes / (part_ms * 1e-3) / 1e9
+    tokens_per_s = B / (ms_per_step * 1e-3)
+    rec = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "accumulate": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": B, "context_lens_sum": int(w.context_lens.sum()),
+                   "max_context_len": w.max_context_len, "num_heads": H, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": D, "block_size": w.block_size, "num_blocks": w.num_blocks,
+                   "partition_size": ps, "description": w.description},
+        "kv_read_bytes_per_step": kv_bytes,
+        "kv_GBps_step": kv_bytes / (ms_per_step * 1e-3) / 1e9,
+        "context_tokens_per_s": float(w.context_lens.sum()) / (ms_per_step * 1e-3),
+        "kernel_us": {"slot_mapping": per_kernel_ms[0] * 1e3, "reshape_and_cache": per_kernel_ms[1] * 1e3,
+                      "decode_partition": per_kernel_ms[2] * 1e3, "combine": per_kernel_ms[3] * 1e3},
+        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": load_traffic(w.name)},
+        "cpu_baseline": base,
+        "wall_s_timed": wall,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

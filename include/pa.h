@@ -1,0 +1,227 @@
+/*
+ * pa.h - C ABI of libpa: the paged KV-cache write and paged decode attention
+ * for AMD MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   HB - inference-systems handbook, chapter "分页 KV Cache" (Paged KV Cache)
+ *   MV - mini-vllm tutorial step 12, "PagedAttention：分页内存管理"
+ *   KC - "KV cache：容量推导、分页与回收" (capacity, paging and reclamation)
+ *   AQ - aiqz.cc article "paged-attention"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument except `stream` is a DEVICE pointer on the current
+ *    HIP device, allocated and owned by the caller.  The library allocates
+ *    nothing, keeps no state beyond a per-device cache of the compute-unit
+ *    count, and may be called from several threads.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work on it and returns; nothing synchronises the device.  Two
+ *    calls on one stream run in call order, which is how a pool write is
+ *    ordered before the attention that reads it.
+ *  - The return value is a pa_status.  Arguments are checked on the host
+ *    before any HIP call: a failed check returns PA_ERR_INVALID_ARG /
+ *    PA_ERR_UNSUPPORTED / PA_ERR_WORKSPACE and enqueues nothing.  A launch
+ *    failure returns PA_ERR_HIP.  Device-side CONTENTS (block ids, context
+ *    lengths, slots) are not checked by the host; what each kernel does with
+ *    out-of-range contents is stated per entry point.
+ *  - Layouts are dense, row-major, with no padding:
+ *      KV pool   [num_blocks, block_size, num_kv_heads, head_dim]  (HB, "实现":
+ *                one K tensor and one V tensor of this shape per layer; the
+ *                token at slot s = block * block_size + offset is row s of the
+ *                pool viewed as [num_blocks*block_size, num_kv_heads, head_dim])
+ *      key/value [num_tokens, num_kv_heads, head_dim]
+ *      query/out [num_seqs, num_heads, head_dim]
+ *      block_tables [num_seqs, max_blocks_per_seq] int32, entry j = physical
+ *                block of logical block j (HB, "块表与 slot mapping"; AQ,
+ *                "块表管理机制"); entries past a sequence's last block are
+ *                never read
+ *      context_lens [num_seqs] int32 = tokens of the context AFTER this step,
+ *                the new token included (HB, "分页注意力", the seq_lens input)
+ *  - Element types: query, key, value, pools and out share one pa_dtype.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, inconsistent shape */
+  PA_ERR_UNSUPPORTED = 2, /* dtype / head_dim / block_size outside the compiled set */
+  PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  PA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,  /* IEEE binary32 */
+  PA_F16 = 1,  /* IEEE binary16 */
+  PA_BF16 = 2  /* bfloat16 (upper 16 bits of a binary32) */
+} pa_dtype;
+
+/*
+ * pa_slot_mapping - physical slot of every new token of one step.
+ *
+ * Position p of a sequence lives in logical block p / block_size at offset
+ * p % block_size; its slot is block_tables[seq][p / block_size] * block_size
+ * + p % block_size (HB, "块表与 slot mapping"; MV, "block_table：逻辑位置到物理
+ * 槽位的翻译").  Sequence b's new tokens are the LAST n_b positions of its
+ * context, context_lens[b] - n_b .. context_lens[b] - 1 (HB, "分页注意力").
+ *
+ *   slot_mapping     out, int64 [num_tokens]; tokens of sequence b occupy
+ *                    query_start_loc[b] .. query_start_loc[b+1]-1
+ *   block_tables     int32 [num_seqs, max_blocks_per_seq]
+ *   context_lens     int32 [num_seqs]
+ *   query_start_loc  int32 [num_seqs+1] prefix sums of n_b, or NULL for a
+ *                    decode step (n_b = 1, token b of sequence b)
+ *   num_tokens       = query_start_loc[num_seqs] (num_seqs when NULL)
+ *
+ * Device contents: a token whose position is negative or whose logical block
+ * is >= max_blocks_per_seq gets slot -1 (pa_reshape_and_cache skips it).
+ * Errors: INVALID_ARG for null pointers, num_seqs/num_tokens/block_size/
+ * max_blocks_per_seq <= 0, or num_tokens != num_seqs when query_start_loc is
+ * NULL.
+ */
+int pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
+                    const int32_t* context_lens, const int32_t* query_start_loc,
+                    int32_t num_seqs, int32_t max_blocks_per_seq, int32_t block_size,
+                    int64_t num_tokens, void* stream);
+
+/*
+ * pa_reshape_and_cache - write each new token's K and V rows into its slot.
+ *
+ * k_pool viewed as [num_blocks*block_size, num_kv_heads, head_dim] gets
+ * row slot_mapping[i] = key[i], and v_pool likewise gets value[i]; a raw bit
+ * copy (HB, "实现", PagedKVCache.write).  Slots must be distinct.
+ *
+ *   key, value        [num_tokens, num_kv_heads, head_dim], dtype
+ *   k_pool, v_pool    [num_blocks, block_size, num_kv_heads, head_dim], dtype
+ *   slot_mapping      int64 [num_tokens]
+ *
+ * Device contents: a slot outside [0, num_blocks*block_size) - e.g. -1 for
+ * padding - is skipped and nothing is written for that token.  Duplicate
+ * slots race (which row lands is unspecified).
+ * Errors: INVALID_ARG for null pointers or non-positive sizes; UNSUPPORTED
+ * for an unknown dtype.  num_tokens == 0 is allowed and enqueues nothing.
+ */
+int pa_reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
+                         const int64_t* slot_mapping, int64_t num_tokens,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int64_t num_blocks, pa_dtype dtype, void* stream);
+
+/*
+ * Workspace for pa_decode_attention: float32 partial results of the split
+ * (partitioned) context, bytes >= what any partition size the library
+ * chooses needs for these sizes.  0 if the sizes are invalid.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t block_size);
+
+/* Workspace bytes for an explicit partition_size (see _ex below). */
+size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                    int32_t max_context_len, int32_t block_size,
+                                    int32_t partition_size);
+
+/*
+ * pa_decode_attention - one decode step of paged attention.
+ *
+ * For every sequence b and query head h, with g = h / (num_heads /
+ * num_kv_heads) the KV head serving h (grouped-query attention, HB "实现"
+ * paged_attention), and t over the context_lens[b] positions read through
+ * block_tables[b]:
+ *     out[b,h,:] = sum_t softmax_t(scale * <query[b,h,:], K[t,g,:]>) V[t,g,:]
+ * (HB, "分页注意力"; AQ, "工程实现要点": blocks are processed one by one and
+ * merged with the online-softmax rescaling).  Scores, softmax and the value
+ * sum are accumulated in float32; out is rounded to dtype (nearest-even).
+ * The context may be split into partitions whose partial results are merged
+ * by a second kernel through the workspace.
+ *
+ *   out            [num_seqs, num_heads, head_dim], dtype
+ *   query          [num_seqs, num_heads, head_dim], dtype
+ *   k_pool, v_pool [*, block_size, num_kv_heads, head_dim], dtype
+ *   block_tables   int32 [num_seqs, max_blocks_per_seq]
+ *   context_lens   int32 [num_seqs], each in [1, max_context_len]
+ *   scale          softmax scale, usually head_dim^-1/2 (HB, "分页注意力")
+ *   workspace      device buffer of workspace_bytes >=
+ *                  pa_decode_workspace_bytes(...), or NULL/0 when
+ *                  max_context_len needs a single partition
+ *
+ * Supported: dtype F32/F16/BF16, head_dim 64 or 128, block_size 16,
+ * num_heads a multiple of num_kv_heads.
+ * Device contents: block ids must address blocks of the pools and
+ * context_lens must lie in [0, max_context_len]; anything else is undefined
+ * (reads outside the pools).  A context length of 0 yields zeros.
+ * Errors: INVALID_ARG for null pointers, non-positive sizes,
+ * num_heads % num_kv_heads != 0, max_context_len > max_blocks_per_seq *
+ * block_size, or a non-finite scale; UNSUPPORTED for other dtype /
+ * head_dim / block_size; WORKSPACE if the workspace is too small.
+ */
+int pa_decode_attention(void* out, const void* query, const void* k_pool, const void* v_pool,
+                        const int32_t* block_tables, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                        int32_t max_context_len, float scale, pa_dtype dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * As pa_decode_attention with an explicit partition size in tokens: a
+ * multiple of block_size in [block_size, 64*block_size], or 0 to let the
+ * library choose.  INVALID_ARG for other values.
+ */
+int pa_decode_attention_ex(void* out, const void* query, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                           int32_t max_context_len, float scale, pa_dtype dtype,
+                           void* workspace, size_t workspace_bytes, int32_t partition_size,
+                           void* stream);
+
+/*
+ * The two stages of pa_decode_attention_ex, for callers that time or
+ * schedule them separately.  `partition_size` must be explicit here (a value
+ * pa_decode_partition_size returned, or any valid size) and identical in both
+ * calls.
+ *
+ * pa_decode_partitions: attention over every (sequence, partition, KV head)
+ * tile.  A sequence whose context fits one partition gets its final output
+ * directly; the others leave per-partition (max, denominator, weighted value
+ * sum) partials in the workspace.
+ *
+ * pa_decode_combine: merges the partials of every sequence that spans more
+ * than one partition into out (softmax rescaling by exp(m_s - max_s m_s));
+ * enqueues nothing when max_context_len fits one partition.
+ * Errors: as pa_decode_attention_ex.
+ */
+int pa_decode_partitions(void* out, const void* query, const void* k_pool, const void* v_pool,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                         int32_t max_context_len, float scale, pa_dtype dtype,
+                         void* workspace, size_t workspace_bytes, int32_t partition_size,
+                         void* stream);
+
+int pa_decode_combine(void* out, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_heads, int32_t head_dim, int32_t max_context_len,
+                      int32_t partition_size, pa_dtype dtype, const void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * Partition size (tokens) the library would choose for these sizes on the
+ * current device, or a negative pa_status on invalid sizes.  Makes one HIP
+ * query (the compute-unit count) the first time per device.
+ */
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t max_context_len, int32_t block_size);
+
+/* Static, human-readable name of a pa_status value. */
+const char* pa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

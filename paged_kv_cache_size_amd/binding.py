@@ -1,0 +1,256 @@
+"""Thin ctypes binding of libpa (include/pa.h).
+
+Argument marshalling only: every step runs in the HIP library.  Device memory
+and the stream come from PyTorch (``tensor.data_ptr()``,
+``torch.cuda.current_stream().cuda_stream``).  A missing library raises; there
+is no fallback implementation.
+
+Names follow the C entry points.  ``lib()`` exposes the raw C functions with
+their ctypes signatures; the ``pa_*`` functions below take tensors.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("PA_LIBRARY", os.path.join(HERE, "libpa.so"))
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+
+# Every symbol pa.h declares, with (restype, argtypes).
+_P = ctypes.c_void_p
+_I32, _I64, _F32, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "pa_slot_mapping": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I64, _P]),
+    "pa_reshape_and_cache": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I64, ctypes.c_int, _P]),
+    "pa_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "pa_decode_workspace_bytes_ex": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "pa_decode_attention": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                           _F32, ctypes.c_int, _P, _SZ, _P]),
+    "pa_decode_attention_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                              _F32, ctypes.c_int, _P, _SZ, _I32, _P]),
+    "pa_decode_partitions": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                            _F32, ctypes.c_int, _P, _SZ, _I32, _P]),
+    "pa_decode_combine": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _SZ, _P]),
+    "pa_decode_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32]),
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+_LIB = None
+
+
+def lib():
+    """Load libpa.so (once) and attach the C signatures."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libpa not built: {LIB_PATH} is missing "
+                               "(run `python -m paged_kv_cache_size_amd.build`)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def pa_status_string(status: int) -> str:
+    return lib().pa_status_string(int(status)).decode()
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {pa_status_string(status)}")
+        self.status = status
+
+
+def _check(rc: int, where: str):
+    if rc != PA_OK:
+        raise PAError(rc, where)
+
+
+# --------------------------------------------------------------------- tensors
+
+def _torch():
+    import torch
+    return torch
+
+
+def pa_dtype(t) -> int:
+    torch = _torch()
+    m = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def pa_slot_mapping(block_tables, context_lens, block_size: int, query_start_loc=None,
+                    num_tokens: int | None = None, out=None):
+    """int64 slot of every new token (see pa.h).  Decode when
+    ``query_start_loc`` is None; otherwise ``num_tokens`` (host int) is
+    required."""
+    torch = _torch()
+    B, mb = block_tables.shape
+    if query_start_loc is None:
+        num_tokens = B
+    elif num_tokens is None:
+        raise ValueError("num_tokens is required with query_start_loc")
+    if out is None:
+        out = torch.empty(num_tokens, dtype=torch.int64, device=block_tables.device)
+    rc = lib().pa_slot_mapping(
+        _dev(out, "out", torch.int64, 1), _dev(block_tables, "block_tables", torch.int32, 2),
+        _dev(context_lens, "context_lens", torch.int32, 1),
+        None if query_start_loc is None else _dev(query_start_loc, "query_start_loc", torch.int32, 1),
+        B, mb, int(block_size), int(num_tokens), _stream(block_tables))
+    _check(rc, "pa_slot_mapping")
+    return out
+
+
+def pa_reshape_and_cache(key, value, k_pool, v_pool, slot_mapping):
+    """Write key/value rows [N, H_kv, D] into the pools at slot_mapping."""
+    torch = _torch()
+    if key.shape != value.shape or k_pool.shape != v_pool.shape:
+        raise ValueError("key/value and k_pool/v_pool shapes must match")
+    if not (key.dtype == value.dtype == k_pool.dtype == v_pool.dtype):
+        raise TypeError("key, value and pools must share a dtype")
+    nb, bs, hkv, d = k_pool.shape
+    if tuple(key.shape[1:]) != (hkv, d):
+        raise ValueError(f"key rows {tuple(key.shape[1:])} do not match pool rows {(hkv, d)}")
+    n = key.shape[0]
+    if slot_mapping.shape != (n,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    rc = lib().pa_reshape_and_cache(
+        _dev(key, "key", ndim=3), _dev(value, "value", ndim=3), _dev(k_pool, "k_pool", ndim=4),
+        _dev(v_pool, "v_pool", ndim=4), _dev(slot_mapping, "slot_mapping", torch.int64, 1),
+        n, hkv, d, bs, nb, pa_dtype(key), _stream(key))
+    _check(rc, "pa_reshape_and_cache")
+
+
+def pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, block_size,
+                              partition_size: int = 0) -> int:
+    return int(lib().pa_decode_workspace_bytes_ex(num_seqs, num_heads, head_dim, max_context_len,
+                                                  block_size, partition_size))
+
+
+def pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, max_context_len, block_size) -> int:
+    ps = int(lib().pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, max_context_len, block_size))
+    if ps < 0:
+        raise PAError(-ps, "pa_decode_partition_size")
+    return ps
+
+
+def pa_decode_attention(query, k_pool, v_pool, block_tables, context_lens, scale: float,
+                        max_context_len: int | None = None, out=None, workspace=None,
+                        partition_size: int = 0):
+    """One decode step of paged attention; returns ``out`` [B, H, D].
+
+    ``max_context_len`` is a host int bounding context_lens (reading it from
+    the device would synchronise; pass it when known).  The workspace is
+    allocated with PyTorch when not given."""
+    torch = _torch()
+    B, H, D = query.shape
+    nb, bs, hkv, d2 = k_pool.shape
+    if d2 != D or k_pool.shape != v_pool.shape:
+        raise ValueError("pool shape does not match query")
+    if not (query.dtype == k_pool.dtype == v_pool.dtype):
+        raise TypeError("query and pools must share a dtype")
+    if block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables / context_lens batch mismatch")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item())
+    mb = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(query)
+    need = pa_decode_workspace_bytes(B, H, D, max_context_len, bs, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = None if workspace is None else _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().pa_decode_attention_ex(
+        _dev(out, "out", query.dtype, 3), _dev(query, "query", ndim=3), _dev(k_pool, "k_pool", ndim=4),
+        _dev(v_pool, "v_pool", ndim=4), _dev(block_tables, "block_tables", torch.int32, 2),
+        _dev(context_lens, "context_lens", torch.int32, 1), B, H, hkv, D, bs, mb, int(max_context_len),
+        float(scale), pa_dtype(query), ws_ptr, ws_bytes, int(partition_size), _stream(query))
+    _check(rc, "pa_decode_attention")
+    return out
+
+
+def _decode_common(query, k_pool, v_pool, block_tables, context_lens, out):
+    torch = _torch()
+    B, H, D = query.shape
+    nb, bs, hkv, d2 = k_pool.shape
+    if d2 != D or k_pool.shape != v_pool.shape:
+        raise ValueError("pool shape does not match query")
+    if not (query.dtype == k_pool.dtype == v_pool.dtype):
+        raise TypeError("query and pools must share a dtype")
+    if block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables / context_lens batch mismatch")
+    if out is None:
+        out = torch.empty_like(query)
+    return B, H, D, bs, hkv, out
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
+def pa_decode_partitions(query, k_pool, v_pool, block_tables, context_lens, scale: float,
+                         max_context_len: int, partition_size: int, workspace=None, out=None):
+    """Stage 1 of decode attention (see pa.h); ``partition_size`` explicit."""
+    torch = _torch()
+    B, H, D, bs, hkv, out = _decode_common(query, k_pool, v_pool, block_tables, context_lens, out)
+    ws_ptr, ws_bytes = _ws(workspace)
+    rc = lib().pa_decode_partitions(
+        _dev(out, "out", query.dtype, 3), _dev(query, "query", ndim=3), _dev(k_pool, "k_pool", ndim=4),
+        _dev(v_pool, "v_pool", ndim=4), _dev(block_tables, "block_tables", torch.int32, 2),
+        _dev(context_lens, "context_lens", torch.int32, 1), B, H, hkv, D, bs, block_tables.shape[1],
+        int(max_context_len), float(scale), pa_dtype(query), ws_ptr, ws_bytes, int(partition_size),
+        _stream(query))
+    _check(rc, "pa_decode_partitions")
+    return out
+
+
+def pa_decode_combine(out, context_lens, max_context_len: int, partition_size: int, workspace=None):
+    """Stage 2 of decode attention: merge partition partials into ``out``."""
+    torch = _torch()
+    B, H, D = out.shape
+    ws_ptr, ws_bytes = _ws(workspace)
+    rc = lib().pa_decode_combine(
+        _dev(out, "out", ndim=3), _dev(context_lens, "context_lens", torch.int32, 1), B, H, D,
+        int(max_context_len), int(partition_size), pa_dtype(out), ws_ptr, ws_bytes, _stream(out))
+    _check(rc, "pa_decode_combine")
+    return out
+
+
+def decode_step(query, key, value, k_pool, v_pool, block_tables, context_lens, scale: float,
+                max_context_len: int, out=None, workspace=None, slot_out=None, partition_size: int = 0):
+    """The whole decode hot path on one stream: slots of the new tokens,
+    their K/V written into the pools, then paged attention."""
+    bs = k_pool.shape[1]
+    slots = pa_slot_mapping(block_tables, context_lens, bs, out=slot_out)
+    pa_reshape_and_cache(key, value, k_pool, v_pool, slots)
+    return pa_decode_attention(query, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
+                               out=out, workspace=workspace, partition_size=partition_size)

@@ -1,0 +1,714 @@
+// libpa kernels for gfx950 (CDNA4) and the extern "C" entry points of pa.h.
+//
+//  * slot mapping      - slot of each new token from its block table
+//                        (handbook "分页 KV Cache", section "块表与 slot mapping")
+//  * reshape_and_cache - bit copy of each new token's K/V row into its slot
+//                        (same page, section "实现", PagedKVCache.write)
+//  * decode_partition  - paged decode attention over one partition of a
+//                        sequence's context for one KV head and its group of
+//                        query heads: block-table lookups on chip, 16-byte
+//                        coalesced row loads, QK with DPP lane reductions,
+//                        online softmax and the P.V accumulation in float32
+//                        (same page, section "分页注意力"; aiqz.cc
+//                        "paged-attention", section "工程实现要点": per-block
+//                        pieces merged by the online-softmax rescaling)
+//  * combine           - merge of the partitions' (max, sum, acc) partials
+//
+// Wave64 throughout.  A token row of one KV head is head_dim * elem bytes
+// (256 B for D=128 16-bit); LPR lanes cover it with one 16-byte load each,
+// so one load instruction of a wave reads RPI = 64 / LPR whole rows.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+#include "pa_host.h"
+
+namespace {
+
+constexpr int DT_F32 = PA_F32, DT_F16 = PA_F16, DT_BF16 = PA_BF16;
+
+template <int DT>
+struct ElemBytes { static constexpr int value = (DT == DT_F32) ? 4 : 2; };
+
+// ------------------------------------------------------------------ numerics
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float f16_bits_to_float(uint32_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+
+// 16 bytes of storage -> 16 / elem floats
+template <int DT>
+__device__ __forceinline__ void unpack16(const uint4 v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (DT == DT_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+  } else if constexpr (DT == DT_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(w[i]);
+      f[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = f16_bits_to_float(w[i] & 0xffffu);
+      f[2 * i + 1] = f16_bits_to_float(w[i] >> 16);
+    }
+  }
+}
+
+// float -> storage bits, round to nearest even
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t float_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+template <int DT, int N>
+__device__ __forceinline__ void store_row(uint8_t* dst, const float* f) {
+  // N floats -> N elements of storage, written as 16-byte vectors
+  if constexpr (DT == DT_F32) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4)
+      *reinterpret_cast<uint4*>(dst + 4 * i) =
+          make_uint4(__float_as_uint(f[i]), __float_as_uint(f[i + 1]), __float_as_uint(f[i + 2]),
+                     __float_as_uint(f[i + 3]));
+  } else {
+    uint32_t w[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const uint32_t lo = DT == DT_BF16 ? float_to_bf16_bits(f[2 * i]) : float_to_f16_bits(f[2 * i]);
+      const uint32_t hi = DT == DT_BF16 ? float_to_bf16_bits(f[2 * i + 1]) : float_to_f16_bits(f[2 * i + 1]);
+      w[i] = lo | (hi << 16);
+    }
+#pragma unroll
+    for (int i = 0; i < N / 2; i += 4)
+      *reinterpret_cast<uint4*>(dst + 4 * i) = make_uint4(w[i], w[i + 1], w[i + 2], w[i + 3]);
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------------------ lane exchange
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of G lanes (G = 8, 16 or 32); every lane of a group
+// ends with the same bits (each step adds a pair in both orders).
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm(1,0,3,2): partner lane ^ 1
+  x += dpp<0x4E>(x);   // quad_perm(2,3,0,1): partner lane ^ 2
+  x += dpp<0x141>(x);  // row_half_mirror: lane i <-> 7 - i within 8 lanes
+  if constexpr (G >= 16) x += dpp<0x140>(x);  // row_mirror: lane i <-> 15 - i within 16
+  if constexpr (G >= 32) x += __shfl_xor(x, 16);
+  static_assert(G == 8 || G == 16 || G == 32, "group size");
+  return x;
+}
+
+// Reduce over the lanes that differ only in bits >= log2(G) (the row groups).
+template <int G>
+__device__ __forceinline__ float across_groups_max(float x) {
+#pragma unroll
+  for (int m = G; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+template <int G>
+__device__ __forceinline__ float across_groups_sum(float x) {
+#pragma unroll
+  for (int m = G; m < 64; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// Workgroup id -> logical id such that each XCD (workgroups are dealt to the
+// 8 XCDs round-robin) receives one contiguous range of logical ids; a bijection
+// whatever the hardware order.
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+  const int xcd = i & 7, k = i >> 3, per = n >> 3, rem = n & 7;
+  return xcd * per + (xcd < rem ? xcd : rem) + k;
+}
+
+// ------------------------------------------------------------------ slot mapping
+
+__device__ __forceinline__ int64_t slot_of(const int32_t* table, int max_blocks, int block_size, int pos) {
+  if (pos < 0) return -1;
+  const int lb = pos / block_size;
+  if (lb >= max_blocks) return -1;
+  return (int64_t)table[lb] * block_size + pos % block_size;
+}
+
+__global__ void slot_mapping_decode_kernel(int64_t* __restrict__ slots, const int32_t* __restrict__ tables,
+                                           const int32_t* __restrict__ lens, int num_seqs, int max_blocks,
+                                           int block_size) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= num_seqs) return;
+  slots[b] = slot_of(tables + (size_t)b * max_blocks, max_blocks, block_size, lens[b] - 1);
+}
+
+__global__ void slot_mapping_varlen_kernel(int64_t* __restrict__ slots, const int32_t* __restrict__ tables,
+                                           const int32_t* __restrict__ lens, const int32_t* __restrict__ qsl,
+                                           int max_blocks, int block_size, int64_t num_tokens) {
+  const int b = blockIdx.x;
+  const int s0 = qsl[b], s1 = qsl[b + 1];
+  const int n = s1 - s0;
+  const int L = lens[b];
+  const int32_t* table = tables + (size_t)b * max_blocks;
+  for (int t = threadIdx.x; t < n; t += blockDim.x) {
+    const int64_t dst = (int64_t)s0 + t;
+    if (dst < 0 || dst >= num_tokens) continue;
+    slots[dst] = slot_of(table, max_blocks, block_size, L - n + t);
+  }
+}
+
+// ------------------------------------------------------------------ pool write
+
+template <typename V>
+__global__ void reshape_and_cache_kernel(const V* __restrict__ key, const V* __restrict__ value,
+                                         V* __restrict__ k_pool, V* __restrict__ v_pool,
+                                         const int64_t* __restrict__ slots, int row_vecs, int64_t num_slots) {
+  const int64_t i = blockIdx.x;
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= num_slots) return;
+  const V* src = (blockIdx.y == 0 ? key : value) + i * row_vecs;
+  V* dst = (blockIdx.y == 0 ? k_pool : v_pool) + slot * row_vecs;
+  for (int t = threadIdx.x; t < row_vecs; t += blockDim.x) dst[t] = src[t];
+}
+
+// ------------------------------------------------------------------ decode attention
+
+struct DecodeArgs {
+  void* out;
+  const void* query;
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_acc;   // [B, H, P, D]
+  float2* ws_ml;   // [B, H, P] (running max in log2 units, softmax denominator)
+  int num_heads, num_kv_heads, rep, chunks, max_blocks_per_seq;
+  int part_tokens, num_parts, groups;  // groups = head-group workgroups per (sequence, partition)
+  float qscale;    // scale * log2(e): scores come out in log2 units for exp2
+};
+
+template <int DT, int D, int REPC>
+struct DecodeTile {
+  static constexpr int BS = pa::kBlockSize;
+  static constexpr int EB = ElemBytes<DT>::value;
+  static constexpr int ROWB = D * EB;    // one KV head's row of one token
+  static constexpr int LPR = ROWB / 16;  // lanes per row
+  static constexpr int RPI = 64 / LPR;   // rows per load instruction
+  static constexpr int NLD = BS / RPI;   // load instructions per block (K or V)
+  static constexpr int EPL = 16 / EB;    // elements per lane and row
+  static_assert(LPR >= 8 && LPR <= 32 && BS % RPI == 0, "tile shape");
+};
+
+// One wave = one (sequence b, partition s, KV head g, chunk of REPC query heads).
+// Lane l reads, for every block, rows i*RPI + l/LPR (i < NLD), bytes
+// (l % LPR)*16 .. +16 of the row.  Each lane runs its own online softmax over
+// the tokens it holds (all LPR lanes of a row group hold the same tokens and
+// compute identical values); the RPI row-group streams merge at the end.
+template <int DT, int D, int REPC>
+__global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs a) {
+  using T = DecodeTile<DT, D, REPC>;
+  constexpr int BS = T::BS, ROWB = T::ROWB, LPR = T::LPR, RPI = T::RPI, NLD = T::NLD, EPL = T::EPL;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wpw = blockDim.x >> 6;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = logical % a.groups;
+  const int seq_part = logical / a.groups;
+  const int s = seq_part % a.num_parts;
+  const int b = seq_part / a.num_parts;
+  const int unit = grp * wpw + wave;
+  const int g = unit / a.chunks;
+  const int h0 = g * a.rep + (unit % a.chunks) * REPC;
+  const int r = lane / LPR, c = lane % LPR;
+
+  const int L = a.context_lens[b];
+  const int start = s * a.part_tokens;
+  if (start >= L) {
+    if (s == 0 && r == 0) {  // empty context: zeros
+      float z[EPL] = {};
+      for (int h = 0; h < REPC; ++h)
+        store_row<DT, EPL>((uint8_t*)a.out + ((size_t)b * a.num_heads + h0 + h) * ROWB + c * 16, z);
+    }
+    return;
+  }
+  const int end = min(L, start + a.part_tokens);
+  const int seq_parts = (L + a.part_tokens - 1) / a.part_tokens;
+  const int blk0 = start / BS;
+  const int nblk = (end - start + BS - 1) / BS;  // <= 64
+
+  // This partition's block-table slice: entry j in lane j, fetched by readlane.
+  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk0;
+  const int tab = lane < nblk ? bt[lane] : 0;
+
+  // Query rows of the REPC heads, scaled into log2 units.
+  float q[REPC][EPL];
+  {
+    const uint8_t* qp = (const uint8_t*)a.query + ((size_t)b * a.num_heads + h0) * ROWB + c * 16;
+#pragma unroll
+    for (int h = 0; h < REPC; ++h) {
+      unpack16<DT>(*reinterpret_cast<const uint4*>(qp + h * ROWB), q[h]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) q[h][e] *= a.qscale;
+    }
+  }
+
+  const size_t row_stride = (size_t)a.num_kv_heads * ROWB;
+  const size_t block_stride = (size_t)BS * row_stride;
+  const size_t lane_off = (size_t)r * row_stride + (size_t)g * ROWB + (size_t)c * 16;
+  const uint8_t* kbase = a.k_pool + lane_off;
+  const uint8_t* vbase = a.v_pool + lane_off;
+
+  float m[REPC], l[REPC], acc[REPC][EPL];
+#pragma unroll
+  for (int h = 0; h < REPC; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+
+  auto load_block = [&](int j, uint4* kr, uint4* vr) {
+    const int pb = __builtin_amdgcn_readlane(tab, j);
+    const size_t off = (size_t)(uint32_t)pb * block_stride;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      kr[i] = *reinterpret_cast<const uint4*>(kbase + off + (size_t)i * RPI * row_stride);
+      vr[i] = *reinterpret_cast<const uint4*>(vbase + off + (size_t)i * RPI * row_stride);
+    }
+  };
+
+  auto process = [&](const uint4* kr, const uint4* vr, int valid) {
+    float sc[NLD][REPC];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      float kf[EPL];
+      unpack16<DT>(kr[i], kf);
+#pragma unroll
+      for (int h = 0; h < REPC; ++h) {
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) part = fmaf(q[h][e], kf[e], part);
+        sc[i][h] = group_sum<LPR>(part);
+      }
+    }
+    const bool partial = valid < BS;
+    if (partial) {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i)
+        if (i * RPI + r >= valid)
+#pragma unroll
+          for (int h = 0; h < REPC; ++h) sc[i][h] = -INFINITY;
+    }
+#pragma unroll
+    for (int h = 0; h < REPC; ++h) {
+      float bm = sc[0][h];
+#pragma unroll
+      for (int i = 1; i < NLD; ++i) bm = fmaxf(bm, sc[i][h]);
+      const float mn = fmaxf(m[h], bm);
+      if (mn > m[h]) {
+        const float alpha = fast_exp2(m[h] - mn);
+        l[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+        m[h] = mn;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const bool ok = !partial || (i * RPI + r < valid);
+      float vf[EPL];
+      unpack16<DT>(vr[i], vf);
+      if (!ok) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[e] = 0.f;
+      }
+#pragma unroll
+      for (int h = 0; h < REPC; ++h) {
+        const float p = ok ? fast_exp2(sc[i][h] - m[h]) : 0.f;
+        l[h] += p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+      }
+    }
+  };
+
+  // Two register buffers: the next block's loads are in flight while the
+  // current block is computed.
+  uint4 ka[NLD], va[NLD], kb[NLD], vb[NLD];
+  const int first_tok = blk0 * BS;
+  load_block(0, ka, va);
+  for (int j = 0; j < nblk; j += 2) {
+    if (j + 1 < nblk) load_block(j + 1, kb, vb);
+    process(ka, va, min(BS, end - (first_tok + j * BS)));
+    if (j + 1 >= nblk) break;
+    if (j + 2 < nblk) load_block(j + 2, ka, va);
+    process(kb, vb, min(BS, end - (first_tok + (j + 1) * BS)));
+  }
+
+  // Merge the RPI row-group streams.
+#pragma unroll
+  for (int h = 0; h < REPC; ++h) {
+    const float M = across_groups_max<LPR>(m[h]);
+    const float f = (m[h] == -INFINITY) ? 0.f : fast_exp2(m[h] - M);
+    l[h] = across_groups_sum<LPR>(l[h] * f);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = across_groups_sum<LPR>(acc[h][e] * f);
+    m[h] = M;
+  }
+  if (r != 0) return;
+
+  if (seq_parts == 1) {
+#pragma unroll
+    for (int h = 0; h < REPC; ++h) {
+      const float inv = l[h] > 0.f ? 1.f / l[h] : 0.f;
+      float o[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = acc[h][e] * inv;
+      store_row<DT, EPL>((uint8_t*)a.out + ((size_t)b * a.num_heads + h0 + h) * ROWB + c * 16, o);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < REPC; ++h) {
+      const size_t idx = ((size_t)b * a.num_heads + h0 + h) * a.num_parts + s;
+      float* dst = a.ws_acc + idx * D + c * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4)
+        *reinterpret_cast<float4*>(dst + e) = make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
+      if (c == 0) a.ws_ml[idx] = make_float2(m[h], l[h]);
+    }
+  }
+}
+
+// One wave per (sequence, query head): out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void combine_kernel(void* __restrict__ out, const float* __restrict__ ws_acc,
+                                                      const float2* __restrict__ ws_ml,
+                                                      const int32_t* __restrict__ context_lens, int num_seqs,
+                                                      int num_heads, int part_tokens, int num_parts) {
+  constexpr int EB = ElemBytes<DT>::value;
+  constexpr int DPL = D / 64;  // dims per lane
+  const int lane = threadIdx.x & 63;
+  const int idx = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (idx >= num_seqs * num_heads) return;
+  const int b = idx / num_heads;
+  const int L = context_lens[b];
+  const int np = L > 0 ? (L + part_tokens - 1) / part_tokens : 0;
+  if (np <= 1) return;  // written by the partition kernel
+  const float2* ml = ws_ml + (size_t)idx * num_parts;
+  const float* acc = ws_acc + (size_t)idx * num_parts * D;
+
+  float M = -INFINITY;
+  for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[p].x);
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
+  float den = 0.f;
+  for (int p = lane; p < np; p += 64) den += ml[p].y * fast_exp2(ml[p].x - M);
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) den += __shfl_xor(den, x);
+
+  float o[DPL] = {};
+  for (int p = 0; p < np; ++p) {
+    const float f = fast_exp2(ml[p].x - M);
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) o[d] = fmaf(f, acc[(size_t)p * D + lane * DPL + d], o[d]);
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  uint8_t* dst = (uint8_t*)out + (size_t)idx * D * EB + lane * DPL * EB;
+#pragma unroll
+  for (int d = 0; d < DPL; ++d) {
+    const float v = o[d] * inv;
+    if constexpr (DT == DT_F32) reinterpret_cast<float*>(dst)[d] = v;
+    else if constexpr (DT == DT_BF16) reinterpret_cast<uint16_t*>(dst)[d] = (uint16_t)float_to_bf16_bits(v);
+    else reinterpret_cast<uint16_t*>(dst)[d] = (uint16_t)float_to_f16_bits(v);
+  }
+}
+
+// ------------------------------------------------------------------ dispatch
+
+using DecodeFn = void (*)(const DecodeArgs);
+
+template <int DT, int D>
+DecodeFn pick_rep(int repc) {
+  switch (repc) {
+    case 1: return decode_partition_kernel<DT, D, 1>;
+    case 2: return decode_partition_kernel<DT, D, 2>;
+    case 3: return decode_partition_kernel<DT, D, 3>;
+    case 4: return decode_partition_kernel<DT, D, 4>;
+    case 5: return decode_partition_kernel<DT, D, 5>;
+    case 6: return decode_partition_kernel<DT, D, 6>;
+    case 7: return decode_partition_kernel<DT, D, 7>;
+    case 8: return decode_partition_kernel<DT, D, 8>;
+    default: return nullptr;
+  }
+}
+
+template <int DT>
+DecodeFn pick_dim(int d, int repc) {
+  return d == 64 ? pick_rep<DT, 64>(repc) : pick_rep<DT, 128>(repc);
+}
+
+DecodeFn pick_decode(int dtype, int d, int repc) {
+  switch (dtype) {
+    case PA_F32: return pick_dim<DT_F32>(d, repc);
+    case PA_F16: return pick_dim<DT_F16>(d, repc);
+    case PA_BF16: return pick_dim<DT_BF16>(d, repc);
+    default: return nullptr;
+  }
+}
+
+using CombineFn = void (*)(void*, const float*, const float2*, const int32_t*, int, int, int, int);
+
+CombineFn pick_combine(int dtype, int d) {
+  const bool d64 = d == 64;
+  switch (dtype) {
+    case PA_F32: return d64 ? combine_kernel<DT_F32, 64> : combine_kernel<DT_F32, 128>;
+    case PA_F16: return d64 ? combine_kernel<DT_F16, 64> : combine_kernel<DT_F16, 128>;
+    case PA_BF16: return d64 ? combine_kernel<DT_BF16, 64> : combine_kernel<DT_BF16, 128>;
+    default: return nullptr;
+  }
+}
+
+int device_cu_count() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return -1;
+  if (dev < 64) cache[dev] = cus;
+  return cus;
+}
+
+int launch_status() { return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+struct DecodePlan {
+  int ps = 0, parts = 0;
+  size_t need = 0;
+};
+
+// Host checks and the partition count; no HIP call unless partition_req == 0.
+int plan_decode(const void* out, const void* query, const void* k_pool, const void* v_pool,
+                const int32_t* block_tables, const int32_t* context_lens, const pa::DecodeShape& shp,
+                float scale, void* workspace, size_t workspace_bytes, int32_t partition_req, DecodePlan* plan) {
+  int rc = pa::check_decode(out, query, k_pool, v_pool, block_tables, context_lens, shp, scale);
+  if (rc != PA_OK) return rc;
+  if (partition_req != 0 && pa::partition_size(shp, partition_req, 256) < 0) return PA_ERR_INVALID_ARG;
+  int cus = 256;
+  if (partition_req == 0) {
+    cus = device_cu_count();
+    if (cus <= 0) return PA_ERR_HIP;
+  }
+  const int ps = pa::partition_size(shp, partition_req, cus);
+  if (ps <= 0) return -ps;
+  plan->ps = ps;
+  plan->parts = pa::num_partitions(shp.max_context_len, ps);
+  plan->need = pa::workspace_bytes(shp.num_seqs, shp.num_heads, shp.head_dim, plan->parts);
+  if (plan->need > 0 && (workspace == nullptr || workspace_bytes < plan->need)) return PA_ERR_WORKSPACE;
+  return PA_OK;
+}
+
+float2* ml_region(void* workspace, const pa::DecodeShape& shp, int parts) {
+  if (parts <= 1) return nullptr;
+  return reinterpret_cast<float2*>(static_cast<float*>(workspace) +
+                                   (size_t)shp.num_seqs * shp.num_heads * parts * shp.head_dim);
+}
+
+int launch_partitions(void* out, const void* query, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* context_lens, const pa::DecodeShape& shp,
+                      float scale, void* workspace, const DecodePlan& plan, void* stream) {
+  const int rep = shp.num_heads / shp.num_kv_heads;
+  const int repc = pa::rep_per_wave(rep);
+  const int chunks = rep / repc;
+  const int units = shp.num_kv_heads * chunks;  // waves per (sequence, partition)
+  const int wpw = units % 4 == 0 ? 4 : (units % 2 == 0 ? 2 : 1);
+  const int groups = units / wpw;
+  const int64_t grid = (int64_t)shp.num_seqs * plan.parts * groups;
+  if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
+  DecodeFn fn = pick_decode(shp.dtype, shp.head_dim, repc);
+  if (!fn) return PA_ERR_UNSUPPORTED;
+
+  DecodeArgs a;
+  a.out = out;
+  a.query = query;
+  a.k_pool = static_cast<const uint8_t*>(k_pool);
+  a.v_pool = static_cast<const uint8_t*>(v_pool);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.ws_acc = static_cast<float*>(workspace);
+  a.ws_ml = ml_region(workspace, shp, plan.parts);
+  a.num_heads = shp.num_heads;
+  a.num_kv_heads = shp.num_kv_heads;
+  a.rep = rep;
+  a.chunks = chunks;
+  a.max_blocks_per_seq = shp.max_blocks_per_seq;
+  a.part_tokens = plan.ps;
+  a.num_parts = plan.parts;
+  a.groups = groups;
+  a.qscale = scale * 1.44269504088896340736f;  // log2(e)
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * wpw), 0, static_cast<hipStream_t>(stream), a);
+  return launch_status();
+}
+
+int launch_combine(void* out, const int32_t* context_lens, const pa::DecodeShape& shp, void* workspace,
+                   const DecodePlan& plan, void* stream) {
+  if (plan.parts <= 1) return PA_OK;
+  CombineFn cf = pick_combine(shp.dtype, shp.head_dim);
+  if (!cf) return PA_ERR_UNSUPPORTED;
+  const int64_t waves = (int64_t)shp.num_seqs * shp.num_heads;
+  hipLaunchKernelGGL(cf, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, static_cast<hipStream_t>(stream), out,
+                     static_cast<const float*>(workspace), ml_region(workspace, shp, plan.parts), context_lens,
+                     shp.num_seqs, shp.num_heads, plan.ps, plan.parts);
+  return launch_status();
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ C ABI
+
+extern "C" int pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens,
+                               const int32_t* query_start_loc, int32_t num_seqs, int32_t max_blocks_per_seq,
+                               int32_t block_size, int64_t num_tokens, void* stream) {
+  int rc = pa::check_slot_mapping(slot_mapping, block_tables, context_lens, query_start_loc, num_seqs,
+                                  max_blocks_per_seq, block_size, num_tokens);
+  if (rc != PA_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!query_start_loc) {
+    hipLaunchKernelGGL(slot_mapping_decode_kernel, dim3((num_seqs + 255) / 256), dim3(256), 0, st, slot_mapping,
+                       block_tables, context_lens, num_seqs, max_blocks_per_seq, block_size);
+  } else {
+    hipLaunchKernelGGL(slot_mapping_varlen_kernel, dim3(num_seqs), dim3(64), 0, st, slot_mapping, block_tables,
+                       context_lens, query_start_loc, max_blocks_per_seq, block_size, num_tokens);
+  }
+  return launch_status();
+}
+
+extern "C" int pa_reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
+                                    const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                                    void* stream) {
+  int rc = pa::check_reshape(key, value, k_pool, v_pool, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                             block_size, num_blocks, dtype);
+  if (rc != PA_OK) return rc;
+  if (num_tokens == 0) return PA_OK;
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * pa::elem_bytes(dtype);
+  const int64_t num_slots = num_blocks * block_size;
+  const uintptr_t align = (uintptr_t)key | (uintptr_t)value | (uintptr_t)k_pool | (uintptr_t)v_pool;
+  int vec = 16;
+  while (vec > 1 && ((row_bytes % vec) != 0 || (align % vec) != 0)) vec >>= 1;
+  const int row_vecs = (int)(row_bytes / vec);
+  const int threads = row_vecs >= 256 ? 256 : (row_vecs > 64 ? 128 : 64);
+  const dim3 grid((unsigned)num_tokens, 2);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (vec) {
+    case 16:
+      hipLaunchKernelGGL(reshape_and_cache_kernel<uint4>, grid, dim3(threads), 0, st, (const uint4*)key,
+                         (const uint4*)value, (uint4*)k_pool, (uint4*)v_pool, slot_mapping, row_vecs, num_slots);
+      break;
+    case 8:
+      hipLaunchKernelGGL(reshape_and_cache_kernel<uint2>, grid, dim3(threads), 0, st, (const uint2*)key,
+                         (const uint2*)value, (uint2*)k_pool, (uint2*)v_pool, slot_mapping, row_vecs, num_slots);
+      break;
+    case 4:
+      hipLaunchKernelGGL(reshape_and_cache_kernel<uint32_t>, grid, dim3(threads), 0, st, (const uint32_t*)key,
+                         (const uint32_t*)value, (uint32_t*)k_pool, (uint32_t*)v_pool, slot_mapping, row_vecs,
+                         num_slots);
+      break;
+    case 2:
+      hipLaunchKernelGGL(reshape_and_cache_kernel<uint16_t>, grid, dim3(threads), 0, st, (const uint16_t*)key,
+                         (const uint16_t*)value, (uint16_t*)k_pool, (uint16_t*)v_pool, slot_mapping, row_vecs,
+                         num_slots);
+      break;
+    default:
+      hipLaunchKernelGGL(reshape_and_cache_kernel<uint8_t>, grid, dim3(threads), 0, st, (const uint8_t*)key,
+                         (const uint8_t*)value, (uint8_t*)k_pool, (uint8_t*)v_pool, slot_mapping, row_vecs,
+                         num_slots);
+      break;
+  }
+  return launch_status();
+}
+
+extern "C" int pa_decode_attention_ex(void* out, const void* query, const void* k_pool, const void* v_pool,
+                                      const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                                      int32_t partition_size, void* stream) {
+  const pa::DecodeShape shp{num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                            max_context_len, (int)dtype};
+  DecodePlan plan;
+  int rc = plan_decode(out, query, k_pool, v_pool, block_tables, context_lens, shp, scale, workspace,
+                       workspace_bytes, partition_size, &plan);
+  if (rc != PA_OK) return rc;
+  rc = launch_partitions(out, query, k_pool, v_pool, block_tables, context_lens, shp, scale, workspace, plan,
+                         stream);
+  if (rc != PA_OK) return rc;
+  return launch_combine(out, context_lens, shp, workspace, plan, stream);
+}
+
+extern "C" int pa_decode_attention(void* out, const void* query, const void* k_pool, const void* v_pool,
+                                   const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                   pa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return pa_decode_attention_ex(out, query, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
+                                num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_context_len, scale,
+                                dtype, workspace, workspace_bytes, 0, stream);
+}
+
+extern "C" int pa_decode_partitions(void* out, const void* query, const void* k_pool, const void* v_pool,
+                                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                    pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                                    int32_t partition_size, void* stream) {
+  if (partition_size == 0) return PA_ERR_INVALID_ARG;
+  const pa::DecodeShape shp{num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                            max_context_len, (int)dtype};
+  DecodePlan plan;
+  int rc = plan_decode(out, query, k_pool, v_pool, block_tables, context_lens, shp, scale, workspace,
+                       workspace_bytes, partition_size, &plan);
+  if (rc != PA_OK) return rc;
+  return launch_partitions(out, query, k_pool, v_pool, block_tables, context_lens, shp, scale, workspace, plan,
+                           stream);
+}
+
+extern "C" int pa_decode_combine(void* out, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                 int32_t head_dim, int32_t max_context_len, int32_t partition_size, pa_dtype dtype,
+                                 const void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = pa::check_combine(out, context_lens, num_seqs, num_heads, head_dim, max_context_len, partition_size,
+                             (int)dtype);
+  if (rc != PA_OK) return rc;
+  const pa::DecodeShape shp{num_seqs, num_heads, 1, head_dim, pa::kBlockSize, 1, max_context_len, (int)dtype};
+  DecodePlan plan;
+  plan.ps = partition_size;
+  plan.parts = pa::num_partitions(max_context_len, partition_size);
+  plan.need = pa::workspace_bytes(num_seqs, num_heads, head_dim, plan.parts);
+  if (plan.need > 0 && (workspace == nullptr || workspace_bytes < plan.need)) return PA_ERR_WORKSPACE;
+  return launch_combine(out, context_lens, shp, const_cast<void*>(workspace), plan, stream);
+}
+
+extern "C" int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                            int32_t max_context_len, int32_t block_size) {
+  pa::DecodeShape shp{num_seqs, num_heads, num_kv_heads, 128, block_size, 1 << 30, max_context_len, PA_F32};
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || max_context_len <= 0 || block_size <= 0 ||
+      num_heads % num_kv_heads != 0)
+    return -PA_ERR_INVALID_ARG;
+  const int cus = device_cu_count();
+  if (cus <= 0) return -PA_ERR_HIP;
+  return pa::partition_size(shp, 0, cus);
+}

@@ -298,6 +298,17 @@ def shared_prefix_bf16(seed: int = 0, extra_cols: int = 0, prompts: int = 64, sa
                    f"{prompts} prompts x {samples} samples, {prompt_len}+{gen_len} tokens, H 32 / Hkv 8, D 128, bf16")
 
 
+def custom(lens, num_heads: int, num_kv_heads: int, head_dim: int, dtype: str, seed: int = 0,
+           extra_cols: int = 0, slack: float = 0.1, name: str = "custom") -> Workload:
+    """Any batch of context lengths with shuffled physical ids (edge cases)."""
+    bs = 16
+    seqs, used, copies = _alloc_plain(lens, bs)
+    nb = max(math.ceil((1.0 + slack) * used), used + 1)
+    perm = np.random.default_rng(seed).permutation(nb)
+    return _finish(name, dtype, num_heads, num_kv_heads, head_dim, bs, seqs, used, nb, perm, lens, copies,
+                   extra_cols, f"custom {len(lens)} seqs, H {num_heads} / Hkv {num_kv_heads}, D {head_dim}, {dtype}")
+
+
 BUILDERS = {
     "tiny_f32": tiny_f32,
     "qwen1p5b_bf16": qwen1p5b_bf16,

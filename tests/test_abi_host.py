@@ -1,0 +1,124 @@
+"""The C ABI without a GPU: symbols, argument checks, workspace sizing.
+
+Every call here fails host-side validation (or is a pure size query), so no
+HIP call is reached.
+"""
+
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from paged_kv_cache_size_amd import binding as B
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "pa.h"
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(B.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for s, key in [(0, "PA_OK"), (1, "INVALID_ARG"), (2, "UNSUPPORTED"), (3, "WORKSPACE"), (4, "HIP")]:
+        assert key in B.pa_status_string(s)
+    assert "unknown" in B.pa_status_string(99)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def decode(**kw):
+    args = dict(out=FAKE, query=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, B=4, H=8, Hkv=2, D=128, bs=16,
+                mb=8, maxlen=128, scale=0.088, dtype=B.PA_BF16, ws=None, wsb=0, ps=16)
+    args.update(kw)
+    a = args
+    return B.lib().pa_decode_attention_ex(a["out"], a["query"], a["k"], a["v"], a["bt"], a["lens"], a["B"], a["H"],
+                                          a["Hkv"], a["D"], a["bs"], a["mb"], a["maxlen"], a["scale"], a["dtype"],
+                                          a["ws"], a["wsb"], a["ps"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), B.PA_ERR_INVALID_ARG),
+    (dict(query=None), B.PA_ERR_INVALID_ARG),
+    (dict(k=None), B.PA_ERR_INVALID_ARG),
+    (dict(bt=None), B.PA_ERR_INVALID_ARG),
+    (dict(lens=None), B.PA_ERR_INVALID_ARG),
+    (dict(B=0), B.PA_ERR_INVALID_ARG),
+    (dict(H=-1), B.PA_ERR_INVALID_ARG),
+    (dict(H=6, Hkv=4), B.PA_ERR_INVALID_ARG),
+    (dict(maxlen=129), B.PA_ERR_INVALID_ARG),     # > mb * bs
+    (dict(maxlen=0), B.PA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), B.PA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), B.PA_ERR_INVALID_ARG),
+    (dict(dtype=7), B.PA_ERR_UNSUPPORTED),
+    (dict(D=96), B.PA_ERR_UNSUPPORTED),
+    (dict(bs=32, mb=4), B.PA_ERR_UNSUPPORTED),
+    (dict(ps=24), B.PA_ERR_INVALID_ARG),          # not a multiple of the block size
+    (dict(ps=2048), B.PA_ERR_INVALID_ARG),        # above 64 blocks
+    (dict(ps=-16), B.PA_ERR_INVALID_ARG),
+    (dict(ps=16), B.PA_ERR_WORKSPACE),            # 8 partitions need a workspace
+    (dict(ps=16, ws=FAKE, wsb=100), B.PA_ERR_WORKSPACE),
+])
+def test_decode_argument_checks(kw, status):
+    assert decode(**kw) == status
+
+
+def test_workspace_sizes():
+    lib = B.lib()
+    # explicit partition: B*H*P*(D+2)*4 bytes, none for a single partition
+    assert lib.pa_decode_workspace_bytes_ex(4, 8, 128, 128, 16, 16) == 4 * 8 * 8 * 130 * 4
+    assert lib.pa_decode_workspace_bytes_ex(4, 8, 128, 128, 16, 128) == 0
+    assert lib.pa_decode_workspace_bytes_ex(4, 8, 128, 128, 16, 24) == 0  # invalid
+    # automatic: sized for partitions of at least 128 tokens
+    assert lib.pa_decode_workspace_bytes(256, 32, 128, 4096, 16) == 256 * 32 * 32 * 130 * 4
+    assert lib.pa_decode_workspace_bytes(4, 4, 64, 33, 16) == 0
+    assert lib.pa_decode_workspace_bytes(0, 4, 64, 33, 16) == 0
+    assert lib.pa_decode_workspace_bytes_ex(4, 8, 128, 128, 16, 16) == B.pa_decode_workspace_bytes(4, 8, 128, 128, 16, 16)
+    assert decode(ps=16, ws=FAKE, wsb=4 * 8 * 8 * 130 * 4 - 1) == B.PA_ERR_WORKSPACE
+
+
+def test_reshape_argument_checks():
+    lib = B.lib()
+    f = lib.pa_reshape_and_cache
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 64, 16, 10, B.PA_F32, None)
+    def call(**kw):
+        a = list(ok)
+        names = ["key", "value", "kp", "vp", "slots", "n", "hkv", "d", "bs", "nb", "dtype", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+    assert call(key=None) == B.PA_ERR_INVALID_ARG
+    assert call(slots=None) == B.PA_ERR_INVALID_ARG
+    assert call(kp=None) == B.PA_ERR_INVALID_ARG
+    assert call(n=-1) == B.PA_ERR_INVALID_ARG
+    assert call(hkv=0) == B.PA_ERR_INVALID_ARG
+    assert call(nb=0) == B.PA_ERR_INVALID_ARG
+    assert call(dtype=9) == B.PA_ERR_UNSUPPORTED
+    assert call(n=0, key=None, value=None, slots=None) == B.PA_OK  # nothing to write
+
+
+def test_slot_mapping_argument_checks():
+    f = B.lib().pa_slot_mapping
+    assert f(None, FAKE, FAKE, None, 4, 8, 16, 4, None) == B.PA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, None, 4, 8, 16, 5, None) == B.PA_ERR_INVALID_ARG  # decode needs num_tokens == num_seqs
+    assert f(FAKE, FAKE, FAKE, None, 0, 8, 16, 0, None) == B.PA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 8, 0, 9, None) == B.PA_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_LIB", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        B.lib()

@@ -1,0 +1,281 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Every case runs the whole decode hot path on the device - slot mapping, the
+pool write, paged attention (and the split-context merge when the context is
+partitioned) - and compares with the oracle on the same seeded inputs:
+
+  * slots and the written pools: bit-exact, over the whole pool;
+  * attention: max-abs error <= 1e-5 (fp32) / 2e-2 (bf16, fp16) against the
+    unrounded float64 oracle.
+
+Full-size batches of the two large workloads are checked on sampled
+sequences (the oracle recomputes those one by one) plus a whole-pool
+integrity check on the device.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from paged_kv_cache_size_amd import binding as PB
+from paged_kv_cache_size_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}
+DEV = "cuda"
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    PB.lib()
+
+
+def bits(t):
+    return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+
+
+def poison(w, t):
+    """NaN into every slot no context position before this step owns: unowned
+    blocks (the table padding included) and the last block's slots from the
+    new token's position on."""
+    ids = torch.from_numpy(w.unowned_blocks).to(DEV)
+    for key in ("k_pool", "v_pool"):
+        t[key][ids] = float("nan")
+    slots = []
+    for b in range(w.num_seqs):
+        L = int(w.context_lens[b])
+        for p in range(max(L - 1, 0), O.num_blocks(L, w.block_size) * w.block_size):
+            slots.append(O.slot_for(w.block_tables[b], p, w.block_size))
+    if slots:
+        s = torch.tensor(slots, device=DEV)
+        for key in ("k_pool", "v_pool"):
+            t[key].view(-1, w.num_kv_heads, w.head_dim)[s] = float("nan")
+
+
+def gpu_step(w, t, partition_size=0):
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    lens = torch.from_numpy(w.context_lens).to(DEV)
+    slots = PB.pa_slot_mapping(bt, lens, w.block_size)
+    PB.pa_reshape_and_cache(t["key"], t["value"], t["k_pool"], t["v_pool"], slots)
+    out = PB.pa_decode_attention(t["query"], t["k_pool"], t["v_pool"], bt, lens, w.scale,
+                                 max(w.max_context_len, 1), partition_size=partition_size)
+    torch.cuda.synchronize()
+    return slots, out
+
+
+def check_whole(w, seed=0, partition_size=0, poisoned=False):
+    """Whole-batch parity; returns the GPU output."""
+    say(f"{w.name} seed={seed} ps={partition_size} poison={poisoned} B={w.num_seqs} "
+        f"H={w.num_heads}/{w.num_kv_heads} D={w.head_dim} {w.dtype}")
+    t = W.make_tensors(w, seed, DEV)
+    if poisoned:
+        poison(w, t)
+    kp, vp = W.raw_numpy(t["k_pool"]), W.raw_numpy(t["v_pool"])
+    q, key, val = W.raw_numpy(t["query"]), W.raw_numpy(t["key"]), W.raw_numpy(t["value"])
+    slots, out = gpu_step(w, t, partition_size)
+
+    ref_slots = O.slot_mapping(w.block_tables, w.context_lens, w.block_size)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    O.reshape_and_cache(kp, key, ref_slots)
+    O.reshape_and_cache(vp, val, ref_slots)
+    assert np.array_equal(W.raw_numpy(t["k_pool"]).view(np.uint8), kp.view(np.uint8))
+    assert np.array_equal(W.raw_numpy(t["v_pool"]).view(np.uint8), vp.view(np.uint8))
+
+    ref = O.decode_attention(q, kp, vp, w.block_tables, w.context_lens, w.scale, w.dtype)
+    got = O.widen(W.raw_numpy(out), w.dtype)
+    assert np.isfinite(got).all()
+    err = float(np.max(np.abs(got - ref)))
+    say(f"  max abs err {err:.3e} (tol {TOL[w.dtype]})")
+    assert err <= TOL[w.dtype], err
+    return out, t
+
+
+# ------------------------------------------------------------------ the five workloads
+
+def test_tiny_fp32_full():
+    w = W.make_workload("tiny_f32")
+    out, t = check_whole(w)
+    # context of one token: the output is that token's value row, exactly
+    rep = w.num_heads // w.num_kv_heads
+    for h in range(w.num_heads):
+        assert torch.equal(out[0, h], t["value"][0, h // rep])
+
+
+def test_qwen1p5b_bf16_full():
+    check_whole(W.make_workload("qwen1p5b_bf16"))
+
+
+def test_shared_prefix_bf16_full():
+    check_whole(W.make_workload("shared_prefix_bf16"))
+
+
+def sampled(w, n_sample=6, seed=0, partition_size=0):
+    """Full-size batch; oracle on sampled sequences, pool integrity on device."""
+    say(f"{w.name} full size, sampled oracle, ps={partition_size}")
+    t = W.make_tensors(w, seed, DEV)
+    rng = np.random.default_rng(123)
+    pick = sorted(set([0, w.num_seqs - 1] + rng.choice(w.num_seqs, n_sample - 2, replace=False).tolist()))
+    # snapshot the sampled sequences' blocks before the write, renumbered 0..n-1
+    blocks = []
+    for b in pick:
+        blocks += w.block_tables[b, :O.num_blocks(int(w.context_lens[b]), w.block_size)].tolist()
+    blocks = sorted(set(blocks))
+    new_id = {x: i for i, x in enumerate(blocks)}
+    idx = torch.tensor(blocks, device=DEV)
+    kp_s, vp_s = W.raw_numpy(t["k_pool"][idx]), W.raw_numpy(t["v_pool"][idx])
+    tables_s = [[new_id[x] for x in w.block_tables[b, :O.num_blocks(int(w.context_lens[b]), w.block_size)]]
+                for b in pick]
+    lens_s = [int(w.context_lens[b]) for b in pick]
+    sel = torch.tensor(pick, device=DEV)
+    q_s = W.raw_numpy(t["query"][sel])
+    key_s, val_s = W.raw_numpy(t["key"][sel]), W.raw_numpy(t["value"][sel])
+    k_before, v_before = t["k_pool"].clone(), t["v_pool"].clone()
+
+    slots, out = gpu_step(w, t, partition_size)
+
+    ref_slots = O.slot_mapping(w.block_tables, w.context_lens, w.block_size)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    rs = torch.from_numpy(ref_slots).to(DEV)
+    for after, before, rows in ((t["k_pool"], k_before, t["key"]), (t["v_pool"], v_before, t["value"])):
+        fa = after.view(-1, w.num_kv_heads, w.head_dim)
+        fb = before.view(-1, w.num_kv_heads, w.head_dim)
+        assert torch.equal(bits(fa[rs]), bits(rows))  # written rows, bit for bit
+        fb[rs] = fa[rs]
+        assert torch.equal(bits(before), bits(after))  # nothing else changed
+    del k_before, v_before
+
+    O.reshape_and_cache(kp_s, key_s, O.slot_mapping(tables_s, lens_s, w.block_size))
+    O.reshape_and_cache(vp_s, val_s, O.slot_mapping(tables_s, lens_s, w.block_size))
+    ref = O.decode_attention(q_s, kp_s, vp_s, tables_s, lens_s, w.scale, w.dtype)
+    got = O.widen(W.raw_numpy(out[sel]), w.dtype)
+    assert np.isfinite(O.widen(W.raw_numpy(out), w.dtype)).all()
+    err = float(np.max(np.abs(got - ref)))
+    say(f"  sampled seqs {pick}: max abs err {err:.3e}")
+    assert err <= TOL[w.dtype], err
+
+
+def test_llama_gqa4k_bf16_full_size_sampled():
+    sampled(W.make_workload("llama_gqa4k_bf16"))
+
+
+def test_opt13b_mha_f16_full_size_sampled():
+    sampled(W.make_workload("opt13b_mha_f16"))
+
+
+# ------------------------------------------------------------------ splits, poison, edges
+
+@pytest.mark.parametrize("ps", [16, 48, 128, 1024])
+def test_partition_sizes_tiny(ps):
+    check_whole(W.make_workload("tiny_f32", extra_cols=2), partition_size=ps)
+
+
+@pytest.mark.parametrize("ps", [16, 64, 256, 1024])
+def test_partition_sizes_qwen(ps):
+    check_whole(W.make_workload("qwen1p5b_bf16"), partition_size=ps)
+
+
+@pytest.mark.parametrize("ps", [128, 512, 1024, 0])
+def test_partition_sizes_llama_subset(ps):
+    check_whole(W.make_workload("llama_gqa4k_bf16", num_seqs=8), partition_size=ps)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "qwen1p5b_bf16", "shared_prefix_bf16"])
+def test_poisoned_unowned_and_tail_slots(name):
+    check_whole(W.make_workload(name, extra_cols=3), poisoned=True)
+
+
+EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 127, 128, 129, 255, 256, 257, 1023, 1024, 1025, 1500]
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("f16", 64), ("f16", 128), ("bf16", 64),
+                                     ("bf16", 128)])
+@pytest.mark.parametrize("ps", [0, 16, 256])
+def test_edge_lengths_all_dtypes(dtype, d, ps):
+    w = W.custom(EDGE_LENS, 8, 2, d, dtype, seed=5, extra_cols=1)
+    check_whole(w, seed=5, partition_size=ps, poisoned=True)
+
+
+@pytest.mark.parametrize("h,hkv", [(4, 4), (8, 4), (12, 4), (16, 4), (10, 2), (12, 2), (14, 2), (16, 2),
+                                   (32, 2), (32, 1), (9, 1), (22, 2)])
+def test_head_groupings(h, hkv):
+    w = W.custom([1, 40, 300, 777], h, hkv, 128, "bf16", seed=h * 100 + hkv)
+    check_whole(w, seed=3, partition_size=128)
+    check_whole(w, seed=3, partition_size=0)
+
+
+def test_zero_length_context_gives_zeros():
+    w = W.custom([0, 5, 0, 20], 4, 2, 64, "f32", seed=2)
+    t = W.make_tensors(w, 0, DEV)
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    lens = torch.from_numpy(w.context_lens).to(DEV)
+    for ps in (16, 0):
+        out = PB.pa_decode_attention(t["query"], t["k_pool"], t["v_pool"], bt, lens, w.scale, 20,
+                                     partition_size=ps)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(out[0]) == 0 and torch.count_nonzero(out[2]) == 0
+        ref = O.decode_attention(W.raw_numpy(t["query"])[[1, 3]], W.raw_numpy(t["k_pool"]),
+                                 W.raw_numpy(t["v_pool"]), w.block_tables[[1, 3]], [5, 20], w.scale, "f32")
+        assert np.max(np.abs(out[[1, 3]].cpu().numpy() - ref)) <= 1e-5
+
+
+# ------------------------------------------------------------------ properties
+
+def test_block_permutation_gives_bitwise_identical_output():
+    w = W.make_workload("qwen1p5b_bf16")
+    t = W.make_tensors(w, 0, DEV)
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    lens = torch.from_numpy(w.context_lens).to(DEV)
+    base = PB.pa_decode_attention(t["query"], t["k_pool"], t["v_pool"], bt, lens, w.scale, w.max_context_len)
+    perm = torch.from_numpy(np.random.default_rng(9).permutation(w.num_blocks)).to(DEV)
+    kp2, vp2 = torch.empty_like(t["k_pool"]), torch.empty_like(t["v_pool"])
+    kp2[perm], vp2[perm] = t["k_pool"], t["v_pool"]
+    bt2 = perm[bt.long()].to(torch.int32)
+    again = PB.pa_decode_attention(t["query"], kp2, vp2, bt2, lens, w.scale, w.max_context_len)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(base), bits(again))
+
+
+def test_run_to_run_bitwise_determinism():
+    w = W.make_workload("llama_gqa4k_bf16", num_seqs=16)
+    t = W.make_tensors(w, 0, DEV)
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    lens = torch.from_numpy(w.context_lens).to(DEV)
+    outs = [PB.pa_decode_attention(t["query"], t["k_pool"], t["v_pool"], bt, lens, w.scale, 4096,
+                                   partition_size=ps) for ps in (256, 256, 0, 0)]
+    torch.cuda.synchronize()
+    assert torch.equal(bits(outs[0]), bits(outs[1])) and torch.equal(bits(outs[2]), bits(outs[3]))
+    # different splits agree to float32 rounding
+    assert (outs[0].float() - outs[2].float()).abs().max().item() < 1e-2
+
+
+def test_varlen_slot_mapping_matches_oracle():
+    w = W.custom([5, 37, 20, 64, 1], 8, 2, 64, "f32", seed=4)
+    qlens = [2, 7, 20, 16, 1]
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    lens = torch.from_numpy(w.context_lens).to(DEV)
+    got = PB.pa_slot_mapping(bt, lens, w.block_size, query_start_loc=torch.from_numpy(qsl).to(DEV),
+                             num_tokens=int(qsl[-1]))
+    ref = O.slot_mapping(w.block_tables, w.context_lens, w.block_size, query_lens=qlens)
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+def test_reshape_skips_out_of_range_slots():
+    w = W.custom([3, 9], 4, 2, 64, "bf16", seed=6)
+    t = W.make_tensors(w, 0, DEV)
+    before = t["k_pool"].clone()
+    nslots = w.num_blocks * w.block_size
+    slots = torch.tensor([-1, nslots], dtype=torch.int64, device=DEV)
+    PB.pa_reshape_and_cache(t["key"], t["value"], t["k_pool"], t["v_pool"], slots)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(before), bits(t["k_pool"]))
