@@ -140,7 +140,8 @@ def main():
     bt = torch.from_numpy(w.block_tables).to(dev)
     lens = torch.from_numpy(w.context_lens).to(dev)
     B, H, D = t["query"].shape
-    ps = args.partition_size or PB.pa_decode_partition_size(B, H, w.num_kv_heads, w.max_context_len, w.block_size)
+    ps = args.partition_size or PB.pa_decode_partition_size(B, H, w.num_kv_heads, D, w.max_context_len,
+                                                            w.block_size, t["query"].dtype)
     ws_bytes = PB.pa_decode_workspace_bytes(B, H, D, w.max_context_len, w.block_size, ps)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(t["query"])
@@ -224,7 +225,9 @@ def main():
         "context_tokens_per_s": float(w.context_lens.sum()) / (ms_per_step * 1e-3),
         "kernel_us": {"slot_mapping": per_kernel_ms[0] * 1e3, "reshape_and_cache": per_kernel_ms[1] * 1e3,
                       "decode_partition": per_kernel_ms[2] * 1e3, "combine": per_kernel_ms[3] * 1e3},
-        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": achieved,
+        "roofline": {"bound": "hbm",
+                     "kernel": "decode_partition_kernel" if w.dtype == "f32" else "decode_mfma_kernel",
+                     "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": load_traffic(w.name)},
         "cpu_baseline": base,

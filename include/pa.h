@@ -12,8 +12,10 @@
  * ---------------------------------------
  *  - Every pointer argument except `stream` is a DEVICE pointer on the current
  *    HIP device, allocated and owned by the caller.  The library allocates
- *    nothing, keeps no state beyond a per-device cache of the compute-unit
- *    count, and may be called from several threads.
+ *    nothing, keeps no state beyond per-device caches of the compute-unit
+ *    count and of how many workgroups of each decode kernel fit one compute
+ *    unit (both filled on first use, guarded for concurrent callers), and may
+ *    be called from several threads.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
  *    enqueues work on it and returns; nothing synchronises the device.  Two
  *    calls on one stream run in call order, which is how a pool write is
@@ -210,12 +212,15 @@ int pa_decode_combine(void* out, const int32_t* context_lens, int32_t num_seqs,
                       size_t workspace_bytes, void* stream);
 
 /*
- * Partition size (tokens) the library would choose for these sizes on the
- * current device, or a negative pa_status on invalid sizes.  Makes one HIP
- * query (the compute-unit count) the first time per device.
+ * Partition size (tokens) pa_decode_attention would choose for these sizes on
+ * the current device, or a negative pa_status (INVALID_ARG / UNSUPPORTED as
+ * pa_decode_attention; HIP if the device cannot be queried).  The choice
+ * depends on the compute-unit count and on how many workgroups of the decode
+ * kernel fit one compute unit (two HIP queries, cached per device).
  */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                 int32_t max_context_len, int32_t block_size);
+                                 int32_t head_dim, int32_t max_context_len, int32_t block_size,
+                                 pa_dtype dtype);
 
 /* Static, human-readable name of a pa_status value. */
 const char* pa_status_string(int status);

@@ -35,7 +35,7 @@ SIGNATURES = {
     "pa_decode_partitions": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                             _F32, ctypes.c_int, _P, _SZ, _I32, _P]),
     "pa_decode_combine": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _SZ, _P]),
-    "pa_decode_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32]),
+    "pa_decode_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_int]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -153,8 +153,12 @@ def pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, bl
                                                   block_size, partition_size))
 
 
-def pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, max_context_len, block_size) -> int:
-    ps = int(lib().pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, max_context_len, block_size))
+def pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, block_size,
+                             dtype) -> int:
+    """``dtype``: a torch dtype or a PA_* code."""
+    code = dtype if isinstance(dtype, int) else pa_dtype(_torch().empty(0, dtype=dtype))
+    ps = int(lib().pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+                                            block_size, code))
     if ps < 0:
         raise PAError(-ps, "pa_decode_partition_size")
     return ps

@@ -21,7 +21,9 @@ ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 # Packed-FP32 instructions are kept out of the device code (the compiler would
 # otherwise form v_pk_* f32 operations from plain float code).
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # MFMA accumulators in ordinary VGPRs: the softmax rescale multiplies them in place
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _hipcc():

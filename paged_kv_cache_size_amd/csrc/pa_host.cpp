@@ -14,11 +14,13 @@ int elem_bytes(int dtype) {
   }
 }
 
-int rep_per_wave(int rep) {
-  for (int c = kMaxRepPerWave; c >= 1; --c)
+int rep_per_wave(int rep, int cap) {
+  for (int c = cap; c >= 1; --c)
     if (rep % c == 0) return c;
   return 1;
 }
+
+int max_rep_per_wave(int dtype) { return dtype == PA_F32 ? kMaxRepPerWaveValu : kMaxRepPerWaveMfma; }
 
 int check_decode(const void* out, const void* query, const void* k_pool, const void* v_pool,
                  const int32_t* block_tables, const int32_t* context_lens, const DecodeShape& s,
@@ -42,28 +44,51 @@ int num_partitions(int max_context_len, int partition) {
   return (max_context_len + partition - 1) / partition;
 }
 
-int partition_size(const DecodeShape& s, int requested, int num_cus) {
+DecodeGrid decode_grid(const DecodeShape& s) {
+  DecodeGrid g;
+  g.rep = s.num_heads / s.num_kv_heads;
+  g.repc = rep_per_wave(g.rep, max_rep_per_wave(s.dtype));
+  g.chunks = g.rep / g.repc;
+  g.units = s.num_kv_heads * g.chunks;
+  g.wpw = g.units % 4 == 0 ? 4 : (g.units % 2 == 0 ? 2 : 1);
+  g.groups = g.units / g.wpw;
+  return g;
+}
+
+int partition_size(const DecodeShape& s, int requested, int num_cus, int wg_per_cu) {
   const int bs = s.block_size;
   const int max_ps = kMaxPartitionBlocks * bs;
   if (requested != 0) {
     if (requested < bs || requested > max_ps || requested % bs != 0) return -PA_ERR_INVALID_ARG;
     return requested;
   }
-  // Aim for ~64 waves per compute unit so every SIMD keeps several waves in
-  // flight, without splitting below kMinPartition tokens.
-  const int rep = s.num_heads / s.num_kv_heads;
-  const int64_t waves_per_seq = (int64_t)s.num_kv_heads * (rep / rep_per_wave(rep));
-  const int64_t target = 64LL * (num_cus > 0 ? num_cus : 256);
-  const int64_t base = (int64_t)s.num_seqs * waves_per_seq;
-  int64_t parts = (target + base - 1) / base;
+  // Cost model in "block steps" (every resident workgroup processing one
+  // 16-token block): the batch is assumed to be at max_context_len.
+  const DecodeGrid g = decode_grid(s);
+  const int64_t slots = (int64_t)(num_cus > 0 ? num_cus : 256) * (wg_per_cu > 0 ? wg_per_cu : 1);
+  const int64_t nb = (s.max_context_len + bs - 1) / bs;
   const int64_t bound = auto_partition_bound(s.max_context_len, bs);
-  if (parts > bound) parts = bound;
-  if (parts < 1) parts = 1;
-  int64_t ps = (s.max_context_len + parts - 1) / parts;
-  ps = (ps + bs - 1) / bs * bs;
-  if (ps > max_ps) ps = max_ps;
-  if (ps < bs) ps = bs;
-  return (int)ps;
+  const double wg_block_bytes = (double)g.wpw * 2.0 * bs * s.head_dim * elem_bytes(s.dtype);
+  const double setup = 1.0, merge_launch = 1.5;
+  int best_pb = 0;
+  double best = 0.0;
+  for (int64_t parts = 1; parts <= bound; ++parts) {
+    const int64_t pb = (nb + parts - 1) / parts;  // blocks per partition
+    if (pb > kMaxPartitionBlocks) continue;
+    const int64_t p = (nb + pb - 1) / pb;
+    const int64_t wgs = (int64_t)s.num_seqs * p * g.groups;
+    const int64_t rounds = (wgs + slots - 1) / slots;
+    double cost = (double)rounds * ((double)pb + setup);
+    if (p > 1)
+      cost += merge_launch + 2.0 * (double)s.num_seqs * s.num_heads * p * (s.head_dim + 2) * 4.0 /
+                                 ((double)slots * wg_block_bytes);
+    if (best_pb == 0 || cost < best - 1e-9) {
+      best = cost;
+      best_pb = (int)pb;
+    }
+  }
+  if (best_pb == 0) best_pb = kMaxPartitionBlocks;
+  return best_pb * bs;
 }
 
 int auto_partition_bound(int max_context_len, int block_size) {

@@ -10,15 +10,17 @@
 namespace pa {
 
 constexpr int kBlockSize = 16;           // compiled block size (tokens per block)
-constexpr int kMaxRepPerWave = 8;        // query heads one wave serves from one K/V read
+constexpr int kMaxRepPerWaveValu = 8;    // query heads a VALU (fp32) wave serves from one K/V read
+constexpr int kMaxRepPerWaveMfma = 16;   // query heads an MFMA (16-bit) wave serves: the 16 MFMA columns
 constexpr int kMinPartition = 128;       // smallest partition the library picks itself
 constexpr int kMaxPartitionBlocks = 64;  // a partition's table slice fits one wave (one entry per lane)
 
 int elem_bytes(int dtype);  // 0 for an unknown dtype
 
-// Query heads served per wave (largest divisor of rep that is <= kMaxRepPerWave)
-// and the number of such chunks per KV head.
-int rep_per_wave(int rep);
+// Query heads served per wave: the largest divisor of rep that is <= cap.
+int rep_per_wave(int rep, int cap);
+// The cap for a dtype's decode kernel (fp32: VALU kernel; fp16/bf16: MFMA kernel).
+int max_rep_per_wave(int dtype);
 
 struct DecodeShape {
   int num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_context_len;
@@ -30,10 +32,20 @@ int check_decode(const void* out, const void* query, const void* k_pool, const v
                  const int32_t* block_tables, const int32_t* context_lens, const DecodeShape& s,
                  float scale);
 
-// Partition size in tokens for the decode kernels.  `requested` = 0 picks one
-// from the shape and the compute-unit count; otherwise it is validated.
+// Launch geometry of the decode partition kernel: one wave per (sequence,
+// partition, KV head, chunk of `repc` query heads); `wpw` waves per workgroup
+// share (sequence, partition); `groups` workgroups per (sequence, partition).
+struct DecodeGrid {
+  int rep, repc, chunks, units, wpw, groups;
+};
+DecodeGrid decode_grid(const DecodeShape& s);
+
+// Partition size in tokens for the decode kernels.  `requested` = 0 picks one:
+// with `wg_per_cu` workgroups resident per compute unit, the candidate that
+// minimises (rounds of resident workgroups) x (blocks per partition + setup)
+// plus the cost of merging partitions; otherwise `requested` is validated.
 // Returns the size (> 0) or a negated pa_status.
-int partition_size(const DecodeShape& s, int requested, int num_cus);
+int partition_size(const DecodeShape& s, int requested, int num_cus, int wg_per_cu);
 
 int num_partitions(int max_context_len, int partition);
 

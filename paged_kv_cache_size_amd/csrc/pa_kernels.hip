@@ -20,6 +20,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+#include <type_traits>
+
 #include "pa.h"
 #include "pa_host.h"
 
@@ -393,6 +397,328 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
   }
 }
 
+// ------------------------------------------------------------------ MFMA decode (16-bit K/V)
+//
+// The query-head group of one KV head against a 16-token block is a small
+// dense contraction, done on the matrix cores:
+//   QK:  S[token][head]  = K[16 x D] . Q^T[D x 16]     mfma_f32_16x16x32 (D/32 of them)
+//   PV:  O^T[dim][head] += V^T[16dims x 16] . P^T      mfma_f32_16x16x16 (D/16 of them)
+// Heads occupy the 16 MFMA columns (a group of up to 16 query heads; unused
+// columns hold zeros).  Lane l = 16*gq + col.
+//  * K is loaded straight into the QK A-operand layout: lane l holds 16 bytes
+//    (dims 32c + 8gq ..+8) of MFMA row col, and row col is token
+//    4*(col%4) + col/4.  With that row order the score tile comes back as
+//    lane (gq, head col) holding tokens 4i + gq in register i, which is the
+//    PV B operand in place (k = 4gq + i <-> token 4i + gq, n = head col).
+//  * V is loaded row-coalesced: load i gives lane l token 4i + gq, dims
+//    (D/16)*col .. +D/16.  Element t of the four loads, paired by v_perm, is
+//    the PV A operand of tile t (row col <-> dim (D/16)*col + t).
+//  * Accumulator tile t: lane (gq, col) register r = O[head col][dim
+//    (D/16)*(4gq + r) + t]; a lane owns dims 4*(D/16)*gq .. +4*(D/16) of its
+//    head, so the softmax rescale factor of a head is lane-local.
+// The running max of a head is kept uniform over the four row groups (a
+// permlane max per block); denominators are per-lane partial sums.
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+#ifndef PA_K_CPOL
+#define PA_K_CPOL 2
+#endif
+#ifndef PA_V_CPOL
+#define PA_V_CPOL 0
+#endif
+// Cache-policy bits of the K and V stream loads (gfx950: 1 = sc0, 2 = nt, 16 = sc1).
+// Measured on MI355X: marking one of the two streams non-temporal is fastest
+// (~10% over neither, ~4% over both), and keeps shared prompt blocks of
+// forked sequences cacheable through the other stream.
+constexpr int kKCpol = PA_K_CPOL, kVCpol = PA_V_CPOL;
+
+// Raw buffer descriptor over `bytes` bytes from `base` (gfx9 data format word).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_block_rsrc(const uint8_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, 0x00020000);
+}
+template <typename VT>
+__device__ __forceinline__ VT buffer_load_v(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (sizeof(VT) == 16)
+    return __builtin_bit_cast(VT, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kVCpol));
+  else
+    return __builtin_bit_cast(VT, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kVCpol));
+}
+
+// XOR swizzle of a K row's 16-byte chunks in LDS: token t's chunk k sits at
+// position k ^ kswz(t), so the 16 rows read by one 16-lane group at a fixed
+// chunk land in 16 distinct bank groups.  (Rows of 16 chunks: kswz = t;
+// rows of 8 chunks: two rows share 16 positions, kswz = t / 2.)
+template <int CPR>
+__device__ __forceinline__ int kswz_t(int t) {
+  return CPR == 16 ? t : (t >> 1) & (CPR - 1);
+}
+
+template <int DT>
+struct MfmaOps;
+
+template <>
+struct MfmaOps<DT_BF16> {
+  static __device__ __forceinline__ f32x4 qk(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(uint2 a, uint2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                     0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};  // v_cvt_pk_bf16_f32, nearest even
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+template <>
+struct MfmaOps<DT_F16> {
+  static __device__ __forceinline__ f32x4 qk(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(uint2 a, uint2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0,
+                                                 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    return float_to_f16_bits(lo) | (float_to_f16_bits(hi) << 16);
+  }
+};
+
+// Max over the four 16-lane rows (lanes l, l^16, l^32, l^48), every lane ends equal.
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+
+template <int VPL>
+struct VRow;  // V elements per lane and row
+template <>
+struct VRow<8> { using T = uint4; };
+template <>
+struct VRow<4> { using T = uint2; };
+
+template <int VPL>
+__device__ __forceinline__ uint32_t vword(const typename VRow<VPL>::T& v, int w) {
+  if constexpr (VPL == 8) return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+  else return w == 0 ? v.x : v.y;
+}
+
+template <int DT, int D, int NBUF, int WPW>
+__global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs a) {
+  using Ops = MfmaOps<DT>;
+  constexpr int BS = pa::kBlockSize;
+  constexpr int ROWB = D * 2;
+  constexpr int NKC = D / 32;  // QK k-chunks
+  constexpr int VPL = D / 16;  // V elements per lane and row = PV output tiles
+  constexpr int DPL = 4 * VPL; // output dims owned by a lane
+  constexpr int CPR = ROWB / 16;  // 16-byte chunks per K row
+  constexpr int NLI = BS * CPR / 64;  // K load instructions per block
+  constexpr int KBYTES = BS * ROWB;   // one K block of one head
+  using VT = typename VRow<VPL>::T;
+  auto kswz = [](int t) { return kswz_t<CPR>(t); };
+  static_assert(BS == 16, "the MFMA tiling assumes 16-token blocks");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = logical % a.groups;
+  const int seq_part = logical / a.groups;
+  const int s = seq_part % a.num_parts;
+  const int b = seq_part / a.num_parts;
+  const int unit = grp * WPW + wave;
+  const int g = unit / a.chunks;
+  const int repc = a.rep / a.chunks;
+  const int h0 = g * a.rep + (unit % a.chunks) * repc;
+  const int gq = lane >> 4, col = lane & 15;
+  const bool live = col < repc;  // this lane's column is a real query head
+  uint8_t* const out_row = (uint8_t*)a.out + ((size_t)b * a.num_heads + h0 + (live ? col : 0)) * ROWB + gq * DPL * 2;
+
+  const int L = a.context_lens[b];
+  const int start = s * a.part_tokens;
+  if (start >= L) {
+    if (s == 0 && live) {  // empty context: zeros
+      float z[DPL] = {};
+      store_row<DT, DPL>(out_row, z);
+    }
+    return;
+  }
+  const int end = min(L, start + a.part_tokens);
+  const int seq_parts = (L + a.part_tokens - 1) / a.part_tokens;
+  const int blk0 = start / BS;
+  const int nblk = (end - start + BS - 1) / BS;  // 1..64
+  const int last = nblk - 1;
+
+  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk0;
+  const int tab = lane < nblk ? bt[lane] : 0;
+
+  // Q^T as the QK B operand: column col = head h0 + col, k-chunk c = dims 32c + 8gq .. +8.
+  uint4 qop[NKC];
+  {
+    const uint8_t* qp = (const uint8_t*)a.query + ((size_t)b * a.num_heads + h0 + (live ? col : 0)) * ROWB + gq * 16;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qp + c * 64);
+      qop[c] = live ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // Byte offsets inside one block (< 2^32).
+  //  K: direct-to-LDS loads, NLI instructions of whole rows; load n, lane l fills
+  //     LDS slot 64n + l = (token t, position q) with the row's 16-byte chunk
+  //     q ^ f(t), so the row-order MFMA reads below hit 16 distinct bank groups.
+  //  V: row-coalesced into registers, row gq (+4i).
+  const uint32_t row_stride = (uint32_t)a.num_kv_heads * ROWB;
+  const size_t block_stride = (size_t)BS * row_stride;
+  uint32_t kdma[NLI];
+#pragma unroll
+  for (int n = 0; n < NLI; ++n) {
+    const int slot = 64 * n + lane, t = slot / CPR, q = slot % CPR;
+    kdma[n] = (uint32_t)t * row_stride + (uint32_t)g * ROWB + (uint32_t)((q ^ kswz(t)) * 16);
+  }
+  uint32_t kread[NKC];  // QK A operand: token 4*(col%4) + col/4, chunk 4c + gq
+  {
+    const int t = 4 * (col & 3) + (col >> 2);
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) kread[c] = (uint32_t)(t * CPR + ((4 * c + gq) ^ kswz(t))) * 16;
+  }
+  const uint32_t voff = (uint32_t)gq * row_stride + (uint32_t)g * ROWB + col * VPL * 2;
+  // One LDS object per ring slot, so that the compiler's wait counting can
+  // tell a slot being read from the slots whose loads are still in flight.
+  __shared__ __attribute__((aligned(1024))) uint8_t kslot0[NBUF > 0 ? WPW : 1][KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kslot1[NBUF > 1 ? WPW : 1][KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kslot2[NBUF > 2 ? WPW : 1][KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kslot3[NBUF > 3 ? WPW : 1][KBYTES];
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
+  auto slot_base = [&](int slot) -> uint8_t* {
+    return slot == 0 ? &kslot0[wave][0] : slot == 1 ? &kslot1[wave][0] : slot == 2 ? &kslot2[wave][0] : &kslot3[wave][0];
+  };
+
+  f32x4 acc[VPL];
+#pragma unroll
+  for (int t = 0; t < VPL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;  // running max (log2 units) and partial denominator of head col
+
+  // One block: K rows into ring slot `slot` of this wave's LDS, V rows into
+  // registers; scalar buffer descriptors over the block (an offset past the
+  // block would read zeros).
+  auto load_block = [&](int j, int slot, VT* vr) {
+    const size_t off = (size_t)(uint32_t)__builtin_amdgcn_readlane(tab, j) * block_stride;
+    const __amdgpu_buffer_rsrc_t rk = make_block_rsrc(a.k_pool + off, (uint32_t)block_stride);
+    const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, (uint32_t)block_stride);
+#pragma unroll
+    for (int n = 0; n < NLI; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (__attribute__((address_space(3))) void*)(slot_base(slot) + n * 1024), 16, (int)kdma[n], 0, 0,
+          kKCpol);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vr[i] = buffer_load_v<VT>(rv, voff + (uint32_t)(4 * i) * row_stride);
+  };
+
+  // One block; `valid` = context tokens in it (16 for inner blocks, fewer for
+  // the sequence's last, 0 for the ring's overrun).  Branch free.
+  // The QK A operand of ring slot `slot`, from LDS.
+  auto read_k = [&](int slot, uint4* kr) {
+    const uint8_t* kb = slot_base(slot);
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) kr[c] = *reinterpret_cast<const uint4*>(kb + kread[c]);
+  };
+
+  auto process = [&](const uint4* kr, const VT* vr, int valid) {
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) sacc = Ops::qk(kr[c], qop[c], sacc);
+    float sc[4];
+    VT vm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = 4 * i + gq < valid;
+      sc[i] = ok ? sacc[i] * a.qscale : -INFINITY;
+      vm[i] = ok ? vr[i] : VT{};  // garbage (even NaN) past the context must not reach the MFMA
+    }
+    const float mn = fmaxf(m, rows_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]))));
+    const float alpha = fast_exp2(m - mn);  // 0 on the first block (m = -inf), 1 while the max stays
+    m = mn;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - mn);
+    l = fmaf(l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+    const uint2 pb = make_uint2(Ops::pack(p[0], p[1]), Ops::pack(p[2], p[3]));
+#pragma unroll
+    for (int t = 0; t < VPL; ++t) {
+      const int w = t >> 1;
+      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;  // high or low 16-bit halves
+      const uint2 va = make_uint2(__builtin_amdgcn_perm(vword<VPL>(vm[1], w), vword<VPL>(vm[0], w), sel),
+                                  __builtin_amdgcn_perm(vword<VPL>(vm[3], w), vword<VPL>(vm[2], w), sel));
+      acc[t] *= alpha;
+      acc[t] = Ops::pv(va, pb, acc[t]);
+    }
+  };
+
+  // Ring of NBUF buffers (LDS for K, registers for V): NBUF-1 blocks are in
+  // flight while one is computed.  Every step issues its loads
+  // unconditionally (past the last block the index is clamped to it: those
+  // loads hit the caches, and the steps past the end run fully masked), so
+  // each wait is an exact count.
+  VT vr[NBUF][4];
+  const int tok0 = start;
+#pragma unroll
+  for (int u = 0; u < NBUF - 1; ++u) load_block(min(u, last), u, vr[u]);
+  for (int j = 0; j < nblk; j += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      const int jj = j + u;
+      uint4 kr[NKC];
+      read_k(u, kr);  // this block's K, before its slot's neighbour is refilled
+      load_block(min(jj + NBUF - 1, last), (u + NBUF - 1) % NBUF, vr[(u + NBUF - 1) % NBUF]);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch issued ahead of this block's math
+      process(kr, vr[u], max(0, min(BS, end - (tok0 + jj * BS))));
+    }
+  }
+
+  const float lt = rows_sum(l);  // denominator of head col
+  if (!live) return;
+  if (seq_parts == 1) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float o[DPL];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int t = 0; t < VPL; ++t) o[VPL * r + t] = acc[t][r] * inv;
+    store_row<DT, DPL>(out_row, o);
+  } else {
+    const size_t idx = ((size_t)b * a.num_heads + h0 + col) * a.num_parts + s;
+    float* dst = a.ws_acc + idx * D + gq * DPL;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int t = 0; t < VPL; t += 4)
+        *reinterpret_cast<float4*>(dst + VPL * r + t) =
+            make_float4(acc[t][r], acc[t + 1][r], acc[t + 2][r], acc[t + 3][r]);
+    if (gq == 0) a.ws_ml[idx] = make_float2(m, lt);
+  }
+}
+
 // One wave per (sequence, query head): out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void combine_kernel(void* __restrict__ out, const float* __restrict__ ws_acc,
@@ -441,6 +767,11 @@ __global__ __launch_bounds__(256) void combine_kernel(void* __restrict__ out, co
 
 using DecodeFn = void (*)(const DecodeArgs);
 
+#ifndef PA_MFMA_RING
+#define PA_MFMA_RING 4
+#endif
+constexpr int kRing = PA_MFMA_RING;  // ring depth (blocks) of the MFMA decode kernel
+
 template <int DT, int D>
 DecodeFn pick_rep(int repc) {
   switch (repc) {
@@ -456,16 +787,23 @@ DecodeFn pick_rep(int repc) {
   }
 }
 
-template <int DT>
-DecodeFn pick_dim(int d, int repc) {
-  return d == 64 ? pick_rep<DT, 64>(repc) : pick_rep<DT, 128>(repc);
+template <int DT, int D>
+DecodeFn pick_mfma(int wpw) {
+  switch (wpw) {
+    case 1: return decode_mfma_kernel<DT, D, kRing, 1>;
+    case 2: return decode_mfma_kernel<DT, D, kRing, 2>;
+    case 4: return decode_mfma_kernel<DT, D, kRing, 4>;
+    default: return nullptr;
+  }
 }
 
-DecodeFn pick_decode(int dtype, int d, int repc) {
+// fp32: VALU kernel (one instantiation per heads-per-wave); fp16/bf16: MFMA
+// kernel (one per waves-per-workgroup).
+DecodeFn pick_decode(int dtype, int d, const pa::DecodeGrid& g) {
   switch (dtype) {
-    case PA_F32: return pick_dim<DT_F32>(d, repc);
-    case PA_F16: return pick_dim<DT_F16>(d, repc);
-    case PA_BF16: return pick_dim<DT_BF16>(d, repc);
+    case PA_F32: return d == 64 ? pick_rep<DT_F32, 64>(g.repc) : pick_rep<DT_F32, 128>(g.repc);
+    case PA_F16: return d == 64 ? pick_mfma<DT_F16, 64>(g.wpw) : pick_mfma<DT_F16, 128>(g.wpw);
+    case PA_BF16: return d == 64 ? pick_mfma<DT_BF16, 64>(g.wpw) : pick_mfma<DT_BF16, 128>(g.wpw);
     default: return nullptr;
   }
 }
@@ -483,18 +821,43 @@ CombineFn pick_combine(int dtype, int d) {
 }
 
 int device_cu_count() {
-  static int cache[64] = {};
+  static std::atomic<int> cache[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return -1;
-  if (dev < 64) cache[dev] = cus;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
 int launch_status() { return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// Workgroups of `fn` (with `threads` threads) resident per compute unit, cached
+// per (device, kernel).  0 on failure.
+int resident_per_cu(DecodeFn fn, int threads) {
+  struct Entry { int dev; const void* fn; int n; };
+  static Entry cache[256];
+  static int used = 0;
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+      if (cache[i].dev == dev && cache[i].fn == (const void*)fn) return cache[i].n;
+  }
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(fn), threads, 0) != hipSuccess)
+    return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (used < 256) cache[used++] = Entry{dev, (const void*)fn, n};
+  return n;
+}
 
 struct DecodePlan {
   int ps = 0, parts = 0;
@@ -507,13 +870,17 @@ int plan_decode(const void* out, const void* query, const void* k_pool, const vo
                 float scale, void* workspace, size_t workspace_bytes, int32_t partition_req, DecodePlan* plan) {
   int rc = pa::check_decode(out, query, k_pool, v_pool, block_tables, context_lens, shp, scale);
   if (rc != PA_OK) return rc;
-  if (partition_req != 0 && pa::partition_size(shp, partition_req, 256) < 0) return PA_ERR_INVALID_ARG;
-  int cus = 256;
+  if (partition_req != 0 && pa::partition_size(shp, partition_req, 256, 1) < 0) return PA_ERR_INVALID_ARG;
+  int cus = 256, per_cu = 1;
   if (partition_req == 0) {
     cus = device_cu_count();
-    if (cus <= 0) return PA_ERR_HIP;
+    const pa::DecodeGrid g = pa::decode_grid(shp);
+    DecodeFn fn = pick_decode(shp.dtype, shp.head_dim, g);
+    if (!fn) return PA_ERR_UNSUPPORTED;
+    per_cu = resident_per_cu(fn, 64 * g.wpw);
+    if (cus <= 0 || per_cu <= 0) return PA_ERR_HIP;
   }
-  const int ps = pa::partition_size(shp, partition_req, cus);
+  const int ps = pa::partition_size(shp, partition_req, cus, per_cu);
   if (ps <= 0) return -ps;
   plan->ps = ps;
   plan->parts = pa::num_partitions(shp.max_context_len, ps);
@@ -531,15 +898,10 @@ float2* ml_region(void* workspace, const pa::DecodeShape& shp, int parts) {
 int launch_partitions(void* out, const void* query, const void* k_pool, const void* v_pool,
                       const int32_t* block_tables, const int32_t* context_lens, const pa::DecodeShape& shp,
                       float scale, void* workspace, const DecodePlan& plan, void* stream) {
-  const int rep = shp.num_heads / shp.num_kv_heads;
-  const int repc = pa::rep_per_wave(rep);
-  const int chunks = rep / repc;
-  const int units = shp.num_kv_heads * chunks;  // waves per (sequence, partition)
-  const int wpw = units % 4 == 0 ? 4 : (units % 2 == 0 ? 2 : 1);
-  const int groups = units / wpw;
-  const int64_t grid = (int64_t)shp.num_seqs * plan.parts * groups;
+  const pa::DecodeGrid gd = pa::decode_grid(shp);
+  const int64_t grid = (int64_t)shp.num_seqs * plan.parts * gd.groups;
   if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-  DecodeFn fn = pick_decode(shp.dtype, shp.head_dim, repc);
+  DecodeFn fn = pick_decode(shp.dtype, shp.head_dim, gd);
   if (!fn) return PA_ERR_UNSUPPORTED;
 
   DecodeArgs a;
@@ -553,14 +915,14 @@ int launch_partitions(void* out, const void* query, const void* k_pool, const vo
   a.ws_ml = ml_region(workspace, shp, plan.parts);
   a.num_heads = shp.num_heads;
   a.num_kv_heads = shp.num_kv_heads;
-  a.rep = rep;
-  a.chunks = chunks;
+  a.rep = gd.rep;
+  a.chunks = gd.chunks;
   a.max_blocks_per_seq = shp.max_blocks_per_seq;
   a.part_tokens = plan.ps;
   a.num_parts = plan.parts;
-  a.groups = groups;
+  a.groups = gd.groups;
   a.qscale = scale * 1.44269504088896340736f;  // log2(e)
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * wpw), 0, static_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * gd.wpw), 0, static_cast<hipStream_t>(stream), a);
   return launch_status();
 }
 
@@ -703,12 +1065,18 @@ extern "C" int pa_decode_combine(void* out, const int32_t* context_lens, int32_t
 }
 
 extern "C" int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                            int32_t max_context_len, int32_t block_size) {
-  pa::DecodeShape shp{num_seqs, num_heads, num_kv_heads, 128, block_size, 1 << 30, max_context_len, PA_F32};
-  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || max_context_len <= 0 || block_size <= 0 ||
-      num_heads % num_kv_heads != 0)
-    return -PA_ERR_INVALID_ARG;
+                                            int32_t head_dim, int32_t max_context_len, int32_t block_size,
+                                            pa_dtype dtype) {
+  const pa::DecodeShape shp{num_seqs, num_heads, num_kv_heads, head_dim, block_size, 1 << 30, max_context_len,
+                            (int)dtype};
+  static const int kFake = 0;
+  const int rc = pa::check_decode(&kFake, &kFake, &kFake, &kFake, &kFake, &kFake, shp, 1.0f);
+  if (rc != PA_OK) return -rc;
+  const pa::DecodeGrid g = pa::decode_grid(shp);
+  DecodeFn fn = pick_decode(shp.dtype, shp.head_dim, g);
+  if (!fn) return -PA_ERR_UNSUPPORTED;
   const int cus = device_cu_count();
-  if (cus <= 0) return -PA_ERR_HIP;
-  return pa::partition_size(shp, 0, cus);
+  const int per_cu = resident_per_cu(fn, 64 * g.wpw);
+  if (cus <= 0 || per_cu <= 0) return -PA_ERR_HIP;
+  return pa::partition_size(shp, 0, cus, per_cu);
 }
