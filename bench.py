@@ -140,8 +140,10 @@ def main():
     bt = torch.from_numpy(w.block_tables).to(dev)
     lens = torch.from_numpy(w.context_lens).to(dev)
     B, H, D = t["query"].shape
+    # the partition size a scheduler would ask for: it holds the lengths on the host
     ps = args.partition_size or PB.pa_decode_partition_size(B, H, w.num_kv_heads, D, w.max_context_len,
-                                                            w.block_size, t["query"].dtype)
+                                                            w.block_size, t["query"].dtype,
+                                                            context_lens=w.context_lens)
     ws_bytes = PB.pa_decode_workspace_bytes(B, H, D, w.max_context_len, w.block_size, ps)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(t["query"])

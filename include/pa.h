@@ -171,7 +171,7 @@ int pa_decode_attention(void* out, const void* query, const void* k_pool, const 
 
 /*
  * As pa_decode_attention with an explicit partition size in tokens: a
- * multiple of block_size in [block_size, 64*block_size], or 0 to let the
+ * multiple of block_size in [block_size, 256*block_size], or 0 to let the
  * library choose.  INVALID_ARG for other values.
  */
 int pa_decode_attention_ex(void* out, const void* query, const void* k_pool, const void* v_pool,
@@ -212,15 +212,36 @@ int pa_decode_combine(void* out, const int32_t* context_lens, int32_t num_seqs,
                       size_t workspace_bytes, void* stream);
 
 /*
- * Partition size (tokens) pa_decode_attention would choose for these sizes on
- * the current device, or a negative pa_status (INVALID_ARG / UNSUPPORTED as
- * pa_decode_attention; HIP if the device cannot be queried).  The choice
- * depends on the compute-unit count and on how many workgroups of the decode
- * kernel fit one compute unit (two HIP queries, cached per device).
+ * Partition size (tokens) for the decode kernels on the current device, or a
+ * negative pa_status (INVALID_ARG / UNSUPPORTED as pa_decode_attention; HIP if
+ * the device cannot be queried).
+ *
+ * host_context_lens: NULL, or the num_seqs context lengths in HOST memory (a
+ * serving scheduler holds them there; they are only read during the call).
+ * NULL gives the size pa_decode_attention picks by itself: every sequence is
+ * taken to be at max_context_len and partitions stay at most 64 blocks long,
+ * so that a ragged batch still balances.  With the lengths the library
+ * simulates the launch (its workgroups dealt to the XCDs and list-scheduled
+ * onto the resident slots, each costing its blocks plus a fixed setup) for
+ * every candidate size up to 256 blocks and returns the fastest, merge
+ * included; the host work is O(num_seqs x partitions) per candidate.
+ *
+ * The choice depends on the compute-unit count and on how many workgroups of
+ * the decode kernel fit one compute unit (two HIP queries, cached per device).
  */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len, int32_t block_size,
-                                 pa_dtype dtype);
+                                 pa_dtype dtype, const int32_t* host_context_lens);
+
+/*
+ * The same choice without a device: `num_cus` compute units holding
+ * `workgroups_per_cu` decode workgroups each (both > 0, else INVALID_ARG).
+ * For planning on a host, and to test the policy.
+ */
+int32_t pa_decode_plan_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t max_context_len, int32_t block_size,
+                                      pa_dtype dtype, const int32_t* host_context_lens,
+                                      int32_t num_cus, int32_t workgroups_per_cu);
 
 /* Static, human-readable name of a pa_status value. */
 const char* pa_status_string(int status);

@@ -35,7 +35,8 @@ SIGNATURES = {
     "pa_decode_partitions": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                             _F32, ctypes.c_int, _P, _SZ, _I32, _P]),
     "pa_decode_combine": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _SZ, _P]),
-    "pa_decode_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_int]),
+    "pa_decode_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_int, _P]),
+    "pa_decode_plan_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _I32, _I32]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -153,14 +154,45 @@ def pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, bl
                                                   block_size, partition_size))
 
 
+def _host_lens(context_lens, num_seqs):
+    """Host int32 copy of the context lengths (kept alive by the caller) and
+    its pointer, or (None, None)."""
+    if context_lens is None:
+        return None, None
+    import numpy as np
+    arr = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32).reshape(-1))
+    if arr.shape[0] != num_seqs:
+        raise ValueError(f"context_lens has {arr.shape[0]} entries, num_seqs is {num_seqs}")
+    return arr, ctypes.c_void_p(arr.ctypes.data)
+
+
+def _dtype_code(dtype) -> int:
+    return dtype if isinstance(dtype, int) else pa_dtype(_torch().empty(0, dtype=dtype))
+
+
 def pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, block_size,
-                             dtype) -> int:
-    """``dtype``: a torch dtype or a PA_* code."""
-    code = dtype if isinstance(dtype, int) else pa_dtype(_torch().empty(0, dtype=dtype))
+                             dtype, context_lens=None) -> int:
+    """``dtype``: a torch dtype or a PA_* code; ``context_lens``: None or the
+    host-side lengths (a sequence of ints / numpy array)."""
+    arr, ptr = _host_lens(context_lens, num_seqs)
     ps = int(lib().pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
-                                            block_size, code))
+                                            block_size, _dtype_code(dtype), ptr))
+    del arr
     if ps < 0:
         raise PAError(-ps, "pa_decode_partition_size")
+    return ps
+
+
+def pa_decode_plan_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, block_size,
+                                  dtype, context_lens, num_cus, workgroups_per_cu) -> int:
+    """Device-free form of pa_decode_partition_size for a given geometry."""
+    arr, ptr = _host_lens(context_lens, num_seqs)
+    ps = int(lib().pa_decode_plan_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+                                                 block_size, _dtype_code(dtype), ptr, num_cus,
+                                                 workgroups_per_cu))
+    del arr
+    if ps < 0:
+        raise PAError(-ps, "pa_decode_plan_partition_size")
     return ps
 
 

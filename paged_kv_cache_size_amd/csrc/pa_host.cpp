@@ -1,7 +1,10 @@
 // Host-side argument checks and partition policy of libpa (no HIP calls).
 #include "pa_host.h"
 
+#include <algorithm>
 #include <cmath>
+#include <functional>
+#include <vector>
 
 namespace pa {
 
@@ -55,40 +58,200 @@ DecodeGrid decode_grid(const DecodeShape& s) {
   return g;
 }
 
-int partition_size(const DecodeShape& s, int requested, int num_cus, int wg_per_cu) {
+namespace {
+
+// Cost-model constants, in block steps (the time a workgroup takes for one
+// 16-token block while every resident workgroup streams, i.e. at the HBM
+// bound): a workgroup's fixed cost (table and query loads, ring fill, final
+// stores), a partition past its sequence's end (exits at once), the merge
+// launch, and how much faster a workgroup runs once so few remain that HBM is
+// no longer saturated (its own loads in flight then bound it).  Fitted to
+// launches on MI355X over partition sizes 128..4096 on uniform (256 x 4096
+// tokens), ragged (200 sequences, 120..3400 tokens) and small (64 sequences)
+// batches: the chosen size is within 2.5% of the best measured on each.
+constexpr int kItemSetupQ = 16;  // quarter steps: every cost is a whole number of them
+constexpr int kEmptyItemQ = 1;
+constexpr double kItemSetup = kItemSetupQ / 4.0;
+constexpr double kEmptyItem = kEmptyItemQ / 4.0;
+constexpr double kMergeLaunch = 1.5;
+constexpr double kMaxSpeedup = 2.0;
+
+// Duration of the partition kernel in block steps.  Workgroups are dealt to
+// the 8 XCDs round-robin and the kernel remaps them so that each XCD takes one
+// contiguous range of (sequence, partition, head group) items, in order, as its
+// slots free up.  All running workgroups share HBM equally: with `active` of
+// the `slots` running each advances at min(kMaxSpeedup, slots / active) blocks
+// per step.  Since they all advance at the same rate, the items finish in the
+// order of (work done when they started + their work), a whole number of
+// quarter steps: a bucket queue over that key replays the launch in
+// O(items + makespan).
+double simulate_partitions(const DecodeShape& s, const DecodeGrid& g, const int32_t* lens, int64_t pb,
+                           int64_t parts, int64_t slots) {
+  const int bs = s.block_size;
+  const int64_t items = (int64_t)s.num_seqs * parts * g.groups;
+  const int64_t xcd_slots = std::max<int64_t>(1, slots / 8);
+  const int64_t per = items / 8, rem = items % 8;
+  std::vector<int64_t> seq_blocks((size_t)s.num_seqs);
+  for (int b = 0; b < s.num_seqs; ++b) {
+    const int64_t len = lens ? std::max<int64_t>(0, lens[b]) : s.max_context_len;
+    seq_blocks[(size_t)b] = (len + bs - 1) / bs;
+  }
+  // Per-XCD cursors over (sequence, partition, head group), advanced without
+  // divisions.
+  struct Cursor {
+    int64_t left, b, part, grp;
+  };
+  Cursor cur[8];
+  auto take = [&](Cursor& c) -> int64_t {  // quarter steps of the cursor's item; advance it
+    const int64_t nblk = std::min<int64_t>(pb, seq_blocks[(size_t)c.b] - c.part * pb);
+    --c.left;
+    if (++c.grp == g.groups) {
+      c.grp = 0;
+      if (++c.part == parts) {
+        c.part = 0;
+        ++c.b;
+      }
+    }
+    return nblk > 0 ? 4 * nblk + kItemSetupQ : kEmptyItemQ;
+  };
+  // One node per slot, reused by the slot's next item; head[key] lists the
+  // nodes whose item ends when every running item has done `key` quarters.
+  std::vector<int32_t> head, link, node_xcd;
+  auto push = [&](int64_t key, int32_t node) {
+    if (key >= (int64_t)head.size()) head.resize((size_t)std::max<int64_t>(key + 1, 2 * (int64_t)head.size()), -1);
+    link[(size_t)node] = head[(size_t)key];
+    head[(size_t)key] = node;
+  };
+  int64_t active = 0;
+  for (int x = 0; x < 8; ++x) {
+    const int64_t first = x * per + (x < rem ? x : rem);
+    const int64_t seq_part = first / g.groups;
+    cur[x] = {per + (x < rem ? 1 : 0), seq_part / parts, seq_part % parts, first % g.groups};
+    for (int64_t k = 0; k < xcd_slots && cur[x].left > 0; ++k) {
+      const int32_t node = (int32_t)node_xcd.size();
+      node_xcd.push_back(x);
+      link.push_back(-1);
+      push(take(cur[x]), node);
+      ++active;
+    }
+  }
+  const double total = (double)(8 * xcd_slots);
+  double t = 0.0;
+  int64_t done = 0;
+  for (int64_t key = 0; active > 0; ++key) {
+    while (head[(size_t)key] >= 0) {
+      const int32_t node = head[(size_t)key];
+      head[(size_t)key] = link[(size_t)node];
+      t += (double)(key - done) / 4.0 / std::min(kMaxSpeedup, total / (double)active);
+      done = key;
+      Cursor& c = cur[node_xcd[(size_t)node]];
+      if (c.left > 0)
+        push(key + take(c), node);  // at least one quarter later: never this bucket
+      else
+        --active;
+    }
+  }
+  return t;
+}
+
+}  // namespace
+
+namespace {
+
+double merge_cost(const DecodeShape& s, const DecodeGrid& g, int64_t parts, int64_t slots) {
+  if (parts <= 1) return 0.0;  // merge: read every partial once, write the output
+  const double wg_block_bytes = (double)g.wpw * 2.0 * s.block_size * s.head_dim * elem_bytes(s.dtype);
+  return kMergeLaunch + 2.0 * (double)s.num_seqs * s.num_heads * parts * (s.head_dim + 2) * 4.0 /
+                            ((double)slots * wg_block_bytes);
+}
+
+int64_t total_slots(int num_cus, int wg_per_cu) {
+  return (int64_t)(num_cus > 0 ? num_cus : 256) * (wg_per_cu > 0 ? wg_per_cu : 1);
+}
+
+// A lower bound of decode_cost: the whole work spread evenly over the slots,
+// and no less than the longest item.
+double cost_lower_bound(const DecodeShape& s, const DecodeGrid& g, const int32_t* lens, int64_t pb,
+                        int64_t parts, int64_t slots) {
+  double work = 0.0;
+  int64_t longest = 0;
+  for (int b = 0; b < s.num_seqs; ++b) {
+    const int64_t nblk = (std::max<int64_t>(0, lens[b]) + s.block_size - 1) / s.block_size;
+    const int64_t used = std::min<int64_t>(parts, (nblk + pb - 1) / pb);
+    work += (double)nblk + kItemSetup * used + kEmptyItem * (parts - used);
+    longest = std::max(longest, std::min(nblk, pb));
+  }
+  const double spread = work * g.groups / slots;
+  const double item = longest > 0 ? ((double)longest + kItemSetup) / kMaxSpeedup : 0.0;
+  return std::max(spread, item) + merge_cost(s, g, parts, slots);
+}
+
+}  // namespace
+
+double decode_cost(const DecodeShape& s, int64_t pb, const int32_t* lens, int num_cus, int wg_per_cu) {
+  const DecodeGrid g = decode_grid(s);
+  const int64_t slots = total_slots(num_cus, wg_per_cu);
+  const int64_t nb = (s.max_context_len + s.block_size - 1) / s.block_size;
+  const int64_t parts = (nb + pb - 1) / pb;
+  double cost;
+  if (lens) {
+    cost = simulate_partitions(s, g, lens, pb, parts, slots);
+  } else {  // every sequence at max_context_len: identical items in waves of `slots`
+    const int64_t items = (int64_t)s.num_seqs * parts * g.groups;
+    const double item = (double)pb + kItemSetup;
+    const int64_t tail = items % slots;
+    cost = (double)(items / slots) * item;
+    if (tail > 0) cost += item / std::min(kMaxSpeedup, (double)slots / (double)tail);
+  }
+  return cost + merge_cost(s, g, parts, slots);
+}
+
+int partition_size(const DecodeShape& s, int requested, int num_cus, int wg_per_cu, const int32_t* lens) {
   const int bs = s.block_size;
   const int max_ps = kMaxPartitionBlocks * bs;
   if (requested != 0) {
     if (requested < bs || requested > max_ps || requested % bs != 0) return -PA_ERR_INVALID_ARG;
     return requested;
   }
-  // Cost model in "block steps" (every resident workgroup processing one
-  // 16-token block): the batch is assumed to be at max_context_len.
-  const DecodeGrid g = decode_grid(s);
-  const int64_t slots = (int64_t)(num_cus > 0 ? num_cus : 256) * (wg_per_cu > 0 ? wg_per_cu : 1);
+  // Without the lengths the batch is taken to be at max_context_len and the
+  // partitions are kept short enough to balance a ragged one; with them the
+  // launch is simulated and any size up to the table-slice limit may win.
+  const int64_t cap = lens ? kMaxPartitionBlocks : kMaxAutoPartitionBlocks;
   const int64_t nb = (s.max_context_len + bs - 1) / bs;
   const int64_t bound = auto_partition_bound(s.max_context_len, bs);
-  const double wg_block_bytes = (double)g.wpw * 2.0 * bs * s.head_dim * elem_bytes(s.dtype);
-  const double setup = 1.0, merge_launch = 1.5;
-  int best_pb = 0;
-  double best = 0.0;
+  struct Cand {
+    int64_t pb;
+    double lb;
+  };
+  std::vector<Cand> cands;
+  const DecodeGrid g = decode_grid(s);
+  const int64_t slots = total_slots(num_cus, wg_per_cu);
   for (int64_t parts = 1; parts <= bound; ++parts) {
     const int64_t pb = (nb + parts - 1) / parts;  // blocks per partition
-    if (pb > kMaxPartitionBlocks) continue;
+    if (pb > cap || (!cands.empty() && cands.back().pb == pb)) continue;
     const int64_t p = (nb + pb - 1) / pb;
-    const int64_t wgs = (int64_t)s.num_seqs * p * g.groups;
-    const int64_t rounds = (wgs + slots - 1) / slots;
-    double cost = (double)rounds * ((double)pb + setup);
-    if (p > 1)
-      cost += merge_launch + 2.0 * (double)s.num_seqs * s.num_heads * p * (s.head_dim + 2) * 4.0 /
-                                 ((double)slots * wg_block_bytes);
-    if (best_pb == 0 || cost < best - 1e-9) {
+    cands.push_back({pb, lens ? cost_lower_bound(s, g, lens, pb, p, slots) : 0.0});
+  }
+  if (cands.empty()) return (int)(std::min<int64_t>(cap, nb > 0 ? nb : 1) * bs);
+  // Simulate in order of the lower bound; stop once no bound can win.  Near
+  // ties go to the longer partition (fewer partials to write and merge).
+  std::stable_sort(cands.begin(), cands.end(), [](const Cand& x, const Cand& y) { return x.lb < y.lb; });
+  int64_t best_pb = 0;
+  double best = 0.0;
+  for (const Cand& c : cands) {
+    if (best_pb != 0 && c.lb >= best - 1e-9) break;
+    const double cost = decode_cost(s, c.pb, lens, num_cus, wg_per_cu);
+    if (best_pb == 0 || cost < best - 1e-9 || (cost < best + 1e-9 && c.pb > best_pb)) {
       best = cost;
-      best_pb = (int)pb;
+      best_pb = c.pb;
     }
   }
-  if (best_pb == 0) best_pb = kMaxPartitionBlocks;
-  return best_pb * bs;
+  return (int)(best_pb * bs);
+}
+
+int check_partition_query(const DecodeShape& s) {
+  static const int kFake = 0;
+  return check_decode(&kFake, &kFake, &kFake, &kFake, &kFake, &kFake, s, 1.0f);
 }
 
 int auto_partition_bound(int max_context_len, int block_size) {
@@ -169,4 +332,16 @@ extern "C" size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_hea
     return 0;
   return pa::workspace_bytes(num_seqs, num_heads, head_dim,
                              pa::num_partitions(max_context_len, partition_size));
+}
+
+extern "C" int32_t pa_decode_plan_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                                 int32_t head_dim, int32_t max_context_len, int32_t block_size,
+                                                 pa_dtype dtype, const int32_t* host_context_lens,
+                                                 int32_t num_cus, int32_t workgroups_per_cu) {
+  const pa::DecodeShape shp{num_seqs, num_heads, num_kv_heads, head_dim, block_size, 1 << 30, max_context_len,
+                            (int)dtype};
+  const int rc = pa::check_partition_query(shp);
+  if (rc != PA_OK) return -rc;
+  if (num_cus <= 0 || workgroups_per_cu <= 0) return -PA_ERR_INVALID_ARG;
+  return pa::partition_size(shp, 0, num_cus, workgroups_per_cu, host_context_lens);
 }

@@ -13,7 +13,9 @@ constexpr int kBlockSize = 16;           // compiled block size (tokens per bloc
 constexpr int kMaxRepPerWaveValu = 8;    // query heads a VALU (fp32) wave serves from one K/V read
 constexpr int kMaxRepPerWaveMfma = 16;   // query heads an MFMA (16-bit) wave serves: the 16 MFMA columns
 constexpr int kMinPartition = 128;       // smallest partition the library picks itself
-constexpr int kMaxPartitionBlocks = 64;  // a partition's table slice fits one wave (one entry per lane)
+constexpr int kMaxPartitionBlocks = 256;  // a partition's table slice: 4 VGPRs of a wave, one entry per lane
+constexpr int kMaxAutoPartitionBlocks = 64;  // automatic choice without the context lengths: short
+                                             // enough partitions to balance a ragged batch
 
 int elem_bytes(int dtype);  // 0 for an unknown dtype
 
@@ -40,14 +42,23 @@ struct DecodeGrid {
 };
 DecodeGrid decode_grid(const DecodeShape& s);
 
-// Partition size in tokens for the decode kernels.  `requested` = 0 picks one:
-// with `wg_per_cu` workgroups resident per compute unit, the candidate that
-// minimises (rounds of resident workgroups) x (blocks per partition + setup)
-// plus the cost of merging partitions; otherwise `requested` is validated.
-// Returns the size (> 0) or a negated pa_status.
-int partition_size(const DecodeShape& s, int requested, int num_cus, int wg_per_cu);
+// Predicted duration, in block steps (one 16-token block per resident
+// workgroup with every workgroup busy), of the partition and merge launches
+// for partitions of `pb` blocks.  `lens`: the num_seqs context lengths in host
+// memory, or NULL to take every sequence at max_context_len.
+double decode_cost(const DecodeShape& s, int64_t pb, const int32_t* lens, int num_cus, int wg_per_cu);
+
+// Partition size in tokens for the decode kernels.  `requested` = 0 picks the
+// candidate of least decode_cost (partitions of at most kMaxAutoPartitionBlocks
+// blocks without `lens`, kMaxPartitionBlocks with them); otherwise `requested`
+// is validated.  Returns the size (> 0) or a negated pa_status.
+int partition_size(const DecodeShape& s, int requested, int num_cus, int wg_per_cu,
+                   const int32_t* lens = nullptr);
 
 int num_partitions(int max_context_len, int partition);
+
+// check_decode for a partition-size query (sizes only, no pointers).
+int check_partition_query(const DecodeShape& s);
 
 // Workspace bytes for `parts` partitions (0 when parts <= 1).
 size_t workspace_bytes(int num_seqs, int num_heads, int head_dim, int parts);

@@ -134,6 +134,29 @@ __device__ __forceinline__ float across_groups_sum(float x) {
   return x;
 }
 
+// A partition's block-table slice, staged on chip: entry j sits in lane j % 64
+// of register j / 64, so one wave holds up to 64 * kTabRegs entries.
+constexpr int kTabRegs = pa::kMaxPartitionBlocks / 64;
+struct TableSlice {
+  int r[kTabRegs];
+  __device__ __forceinline__ void load(const int32_t* bt, int n, int lane) {
+#pragma unroll
+    for (int k = 0; k < kTabRegs; ++k) r[k] = (64 * k + lane < n) ? bt[64 * k + lane] : 0;
+  }
+  // entry j (wave-uniform j < 64 * kTabRegs), as a scalar: one readlane per
+  // register and scalar selects (no dynamic register indexing)
+  __device__ __forceinline__ int get(int j) const {
+    const int lane = j & 63, k = j >> 6;
+    int v = __builtin_amdgcn_readlane(r[0], lane);
+#pragma unroll
+    for (int i = 1; i < kTabRegs; ++i) {
+      const int e = __builtin_amdgcn_readlane(r[i], lane);
+      v = (k == i) ? e : v;
+    }
+    return v;
+  }
+};
+
 // Workgroup id -> logical id such that each XCD (workgroups are dealt to the
 // 8 XCDs round-robin) receives one contiguous range of logical ids; a bijection
 // whatever the hardware order.
@@ -252,11 +275,12 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
   const int end = min(L, start + a.part_tokens);
   const int seq_parts = (L + a.part_tokens - 1) / a.part_tokens;
   const int blk0 = start / BS;
-  const int nblk = (end - start + BS - 1) / BS;  // <= 64
+  const int nblk = (end - start + BS - 1) / BS;  // <= kMaxPartitionBlocks
 
-  // This partition's block-table slice: entry j in lane j, fetched by readlane.
+  // This partition's block-table slice, fetched per block by readlane.
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk0;
-  const int tab = lane < nblk ? bt[lane] : 0;
+  TableSlice tab;
+  tab.load(bt, nblk, lane);
 
   // Query rows of the REPC heads, scaled into log2 units.
   float q[REPC][EPL];
@@ -286,7 +310,7 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
   }
 
   auto load_block = [&](int j, uint4* kr, uint4* vr) {
-    const int pb = __builtin_amdgcn_readlane(tab, j);
+    const int pb = tab.get(j);
     const size_t off = (size_t)(uint32_t)pb * block_stride;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
@@ -566,11 +590,12 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
   const int end = min(L, start + a.part_tokens);
   const int seq_parts = (L + a.part_tokens - 1) / a.part_tokens;
   const int blk0 = start / BS;
-  const int nblk = (end - start + BS - 1) / BS;  // 1..64
+  const int nblk = (end - start + BS - 1) / BS;  // 1..kMaxPartitionBlocks
   const int last = nblk - 1;
 
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk0;
-  const int tab = lane < nblk ? bt[lane] : 0;
+  TableSlice tab;
+  tab.load(bt, nblk, lane);
 
   // Q^T as the QK B operand: column col = head h0 + col, k-chunk c = dims 32c + 8gq .. +8.
   uint4 qop[NKC];
@@ -609,9 +634,14 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
   __shared__ __attribute__((aligned(1024))) uint8_t kslot1[NBUF > 1 ? WPW : 1][KBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t kslot2[NBUF > 2 ? WPW : 1][KBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t kslot3[NBUF > 3 ? WPW : 1][KBYTES];
-  static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
+  __shared__ __attribute__((aligned(1024))) uint8_t kslot4[NBUF > 4 ? WPW : 1][KBYTES];
+  static_assert(NBUF >= 2 && NBUF <= 5, "ring depth");
   auto slot_base = [&](int slot) -> uint8_t* {
-    return slot == 0 ? &kslot0[wave][0] : slot == 1 ? &kslot1[wave][0] : slot == 2 ? &kslot2[wave][0] : &kslot3[wave][0];
+    return slot == 0   ? &kslot0[wave][0]
+           : slot == 1 ? &kslot1[wave][0]
+           : slot == 2 ? &kslot2[wave][0]
+           : slot == 3 ? &kslot3[wave][0]
+                       : &kslot4[wave][0];
   };
 
   f32x4 acc[VPL];
@@ -622,10 +652,15 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
   // One block: K rows into ring slot `slot` of this wave's LDS, V rows into
   // registers; scalar buffer descriptors over the block (an offset past the
   // block would read zeros).
+  // Past the partition's last block the loads are still issued (so every
+  // wait stays an exact count) but through an empty descriptor: they return
+  // zeros without touching memory.
   auto load_block = [&](int j, int slot, VT* vr) {
-    const size_t off = (size_t)(uint32_t)__builtin_amdgcn_readlane(tab, j) * block_stride;
-    const __amdgpu_buffer_rsrc_t rk = make_block_rsrc(a.k_pool + off, (uint32_t)block_stride);
-    const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, (uint32_t)block_stride);
+    const bool real = j <= last;
+    const size_t off = (size_t)(uint32_t)tab.get(real ? j : last) * block_stride;
+    const uint32_t span = real ? (uint32_t)block_stride : 0u;
+    const __amdgpu_buffer_rsrc_t rk = make_block_rsrc(a.k_pool + off, span);
+    const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, span);
 #pragma unroll
     for (int n = 0; n < NLI; ++n)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -677,20 +712,19 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
 
   // Ring of NBUF buffers (LDS for K, registers for V): NBUF-1 blocks are in
   // flight while one is computed.  Every step issues its loads
-  // unconditionally (past the last block the index is clamped to it: those
-  // loads hit the caches, and the steps past the end run fully masked), so
-  // each wait is an exact count.
+  // unconditionally (past the last block through an empty descriptor, and
+  // the steps past the end run fully masked), so each wait is an exact count.
   VT vr[NBUF][4];
   const int tok0 = start;
 #pragma unroll
-  for (int u = 0; u < NBUF - 1; ++u) load_block(min(u, last), u, vr[u]);
+  for (int u = 0; u < NBUF - 1; ++u) load_block(u, u, vr[u]);
   for (int j = 0; j < nblk; j += NBUF) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
       const int jj = j + u;
       uint4 kr[NKC];
       read_k(u, kr);  // this block's K, before its slot's neighbour is refilled
-      load_block(min(jj + NBUF - 1, last), (u + NBUF - 1) % NBUF, vr[(u + NBUF - 1) % NBUF]);
+      load_block(jj + NBUF - 1, (u + NBUF - 1) % NBUF, vr[(u + NBUF - 1) % NBUF]);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch issued ahead of this block's math
       process(kr, vr[u], max(0, min(BS, end - (tok0 + jj * BS))));
     }
@@ -712,9 +746,10 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int t = 0; t < VPL; t += 4)
+      for (int t = 0; t < VPL; t += 4) {
         *reinterpret_cast<float4*>(dst + VPL * r + t) =
             make_float4(acc[t][r], acc[t + 1][r], acc[t + 2][r], acc[t + 3][r]);
+      }
     if (gq == 0) a.ws_ml[idx] = make_float2(m, lt);
   }
 }
@@ -1066,11 +1101,10 @@ extern "C" int pa_decode_combine(void* out, const int32_t* context_lens, int32_t
 
 extern "C" int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                             int32_t head_dim, int32_t max_context_len, int32_t block_size,
-                                            pa_dtype dtype) {
+                                            pa_dtype dtype, const int32_t* host_context_lens) {
   const pa::DecodeShape shp{num_seqs, num_heads, num_kv_heads, head_dim, block_size, 1 << 30, max_context_len,
                             (int)dtype};
-  static const int kFake = 0;
-  const int rc = pa::check_decode(&kFake, &kFake, &kFake, &kFake, &kFake, &kFake, shp, 1.0f);
+  const int rc = pa::check_partition_query(shp);
   if (rc != PA_OK) return -rc;
   const pa::DecodeGrid g = pa::decode_grid(shp);
   DecodeFn fn = pick_decode(shp.dtype, shp.head_dim, g);
@@ -1078,5 +1112,5 @@ extern "C" int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads,
   const int cus = device_cu_count();
   const int per_cu = resident_per_cu(fn, 64 * g.wpw);
   if (cus <= 0 || per_cu <= 0) return -PA_ERR_HIP;
-  return pa::partition_size(shp, 0, cus, per_cu);
+  return pa::partition_size(shp, 0, cus, per_cu, host_context_lens);
 }

@@ -66,7 +66,7 @@ def decode(**kw):
     (dict(D=96), B.PA_ERR_UNSUPPORTED),
     (dict(bs=32, mb=4), B.PA_ERR_UNSUPPORTED),
     (dict(ps=24), B.PA_ERR_INVALID_ARG),          # not a multiple of the block size
-    (dict(ps=2048), B.PA_ERR_INVALID_ARG),        # above 64 blocks
+    (dict(ps=4112, maxlen=128), B.PA_ERR_INVALID_ARG),  # above 256 blocks
     (dict(ps=-16), B.PA_ERR_INVALID_ARG),
     (dict(ps=16), B.PA_ERR_WORKSPACE),            # 8 partitions need a workspace
     (dict(ps=16, ws=FAKE, wsb=100), B.PA_ERR_WORKSPACE),

@@ -164,12 +164,26 @@ def sampled(w, n_sample=6, seed=0, partition_size=0):
     assert err <= TOL[w.dtype], err
 
 
+def bench_partition_size(w):
+    """The size bench.py launches with: the policy given the host-side lengths."""
+    ps = PB.pa_decode_partition_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.max_context_len,
+                                     w.block_size, W.torch_dtype(w.dtype), context_lens=w.context_lens)
+    assert ps % w.block_size == 0 and w.block_size <= ps <= 256 * w.block_size
+    return ps
+
+
 def test_llama_gqa4k_bf16_full_size_sampled():
-    sampled(W.make_workload("llama_gqa4k_bf16"))
+    w = W.make_workload("llama_gqa4k_bf16")
+    sampled(w, partition_size=bench_partition_size(w))
+
+
+def test_llama_gqa4k_bf16_full_size_sampled_blind_policy():
+    sampled(W.make_workload("llama_gqa4k_bf16"), partition_size=0)
 
 
 def test_opt13b_mha_f16_full_size_sampled():
-    sampled(W.make_workload("opt13b_mha_f16"))
+    w = W.make_workload("opt13b_mha_f16")
+    sampled(w, partition_size=bench_partition_size(w))
 
 
 # ------------------------------------------------------------------ splits, poison, edges
@@ -184,7 +198,7 @@ def test_partition_sizes_qwen(ps):
     check_whole(W.make_workload("qwen1p5b_bf16"), partition_size=ps)
 
 
-@pytest.mark.parametrize("ps", [128, 512, 1024, 0])
+@pytest.mark.parametrize("ps", [128, 512, 1024, 2048, 4096, 0])
 def test_partition_sizes_llama_subset(ps):
     check_whole(W.make_workload("llama_gqa4k_bf16", num_seqs=8), partition_size=ps)
 

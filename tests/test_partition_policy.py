@@ -1,0 +1,99 @@
+"""The partition-size policy of libpa, device-free (pa_decode_plan_partition_size).
+
+The policy only decides how a batch is split into (sequence, partition)
+pieces; every valid size gives the same attention (checked on the GPU).  These
+tests pin what the choice must satisfy on the MI355X geometry (256 compute
+units, two decode workgroups resident per unit for the 16-bit kernel).
+"""
+
+import numpy as np
+import pytest
+
+from paged_kv_cache_size_amd import binding as B
+from paged_kv_cache_size_amd import workloads as W
+
+CUS, PER_CU = 256, 2
+DT = {"f32": B.PA_F32, "f16": B.PA_F16, "bf16": B.PA_BF16}
+
+
+def plan(w_or_args, lens=None, cus=CUS, per_cu=PER_CU):
+    return B.pa_decode_plan_partition_size(*w_or_args, lens, cus, per_cu)
+
+
+def args_of(w):
+    return (w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.max_context_len, w.block_size, DT[w.dtype])
+
+
+def valid(ps, w_args):
+    num_seqs, H, _, D, maxlen, bs, _ = w_args
+    assert ps % bs == 0 and bs <= ps <= 256 * bs
+    parts = -(-maxlen // ps)
+    # the automatic workspace size covers whatever the policy picks
+    assert B.pa_decode_workspace_bytes(num_seqs, H, D, maxlen, bs) >= \
+        B.pa_decode_workspace_bytes(num_seqs, H, D, maxlen, bs, ps)
+    return parts
+
+
+@pytest.mark.parametrize("name", ["llama_gqa4k_bf16", "opt13b_mha_f16", "qwen1p5b_bf16",
+                                  "shared_prefix_bf16", "tiny_f32"])
+def test_choice_is_valid_with_and_without_lengths(name):
+    w = W.make_workload(name, seed=0)
+    a = args_of(w)
+    for lens in (None, w.context_lens):
+        valid(plan(a, lens), a)
+    assert plan(a) <= 64 * w.block_size  # without lengths: short enough for a ragged batch
+
+
+def test_uniform_long_batch_takes_one_partition_per_sequence():
+    # 256 x 4096 tokens, 32/8 heads: 512 workgroups fill the 512 slots exactly
+    # once; splitting only adds per-workgroup setup and a merge.
+    w = W.make_workload("llama_gqa4k_bf16", seed=0)
+    assert plan(args_of(w), w.context_lens) == 4096
+    assert plan(args_of(w)) == 1024  # blind to the lengths: capped at 64 blocks
+
+
+def test_small_batch_splits_to_fill_the_machine():
+    # 8 sequences x 4096 tokens: one partition each would use 16 of 512 slots.
+    a = (8, 32, 8, 128, 4096, 16, B.PA_BF16)
+    lens = np.full(8, 4096, np.int32)
+    ps = plan(a, lens)
+    assert 8 * -(-4096 // ps) * 2 >= 256  # at least half the slots busy
+    assert ps == plan(a)  # uniform at the maximum: the lengths add nothing
+
+
+def test_lengths_matter_for_a_ragged_batch():
+    # one long sequence among short ones: the long one must be split so that it
+    # does not run alone long after the rest
+    lens = np.full(256, 64, np.int32)
+    lens[0] = 4096
+    a = (256, 32, 8, 128, 4096, 16, B.PA_BF16)
+    assert plan(a, lens) <= 1024
+
+
+def test_more_slots_never_need_longer_partitions_for_a_uniform_batch():
+    a = (64, 32, 8, 128, 2048, 16, B.PA_BF16)
+    lens = np.full(64, 2048, np.int32)
+    sizes = [plan(a, lens, cus=c) for c in (32, 64, 128, 256)]
+    assert sizes == sorted(sizes, reverse=True)
+
+
+def test_empty_and_zero_lengths():
+    a = (4, 8, 8, 64, 300, 16, B.PA_F16)
+    valid(plan(a, np.zeros(4, np.int32)), a)
+    valid(plan(a, np.array([0, 300, 0, 17], np.int32)), a)
+
+
+def test_plan_argument_checks():
+    a = (4, 8, 8, 64, 300, 16, B.PA_F16)
+    for cus, per in ((0, 2), (256, 0), (-1, 1)):
+        with pytest.raises(B.PAError) as e:
+            plan(a, None, cus, per)
+        assert e.value.status == B.PA_ERR_INVALID_ARG
+    with pytest.raises(B.PAError) as e:
+        plan((4, 8, 3, 64, 300, 16, B.PA_F16))  # heads not a multiple of KV heads
+    assert e.value.status == B.PA_ERR_INVALID_ARG
+    with pytest.raises(B.PAError) as e:
+        plan((4, 8, 8, 96, 300, 16, B.PA_F16))
+    assert e.value.status == B.PA_ERR_UNSUPPORTED
+    with pytest.raises(ValueError):
+        plan(a, np.zeros(3, np.int32))  # one length per sequence
