@@ -243,6 +243,45 @@ int32_t pa_decode_plan_partition_size(int32_t num_seqs, int32_t num_heads, int32
                                       pa_dtype dtype, const int32_t* host_context_lens,
                                       int32_t num_cus, int32_t workgroups_per_cu);
 
+/*
+ * Paged attention for several new tokens per sequence: varlen prefill,
+ * chunked prefill, and batches mixing prefill chunks with decode steps
+ * (handbook "分页 KV Cache", section "分页注意力": context lengths after this
+ * step, query_start_loc delimiting each sequence's new tokens, causal mask).
+ *
+ *   query, out       [num_tokens, num_heads, head_dim]  (dtype; rows packed by sequence)
+ *   query_start_loc  int32 [num_seqs + 1], device: sequence b owns rows
+ *                    query_start_loc[b] .. query_start_loc[b+1]-1
+ *                    (non-decreasing, [0] = 0, [num_seqs] <= num_tokens)
+ *   context_lens     int32 [num_seqs], device: L_b, the context INCLUDING the
+ *                    n_b new tokens, whose K/V must already be in the pools
+ *                    (pa_slot_mapping with query_start_loc, then
+ *                    pa_reshape_and_cache); new token i sits at position
+ *                    L_b - n_b + i and attends to positions 0 .. L_b - n_b + i.
+ *   max_query_len    host bound of n_b; 1 <= max_query_len <= num_tokens.
+ *   other arguments  as pa_decode_attention (pools, tables, scale, dtype, stream).
+ * fp16 and bf16 only (the tile runs on the matrix cores): UNSUPPORTED for fp32.
+ * partition_size: 0 lets the library choose (it may split long contexts into
+ * partitions merged by a second kernel, keeping the partials within 256 MiB),
+ * or a multiple of block_size in [block_size, 256*block_size].  The workspace
+ * must hold pa_prefill_workspace_bytes(...) for the same partition_size (0 when
+ * the context fits one partition).  Rows past query_start_loc[num_seqs] are
+ * not written.  Device contents are the caller's contract (n_b <= L_b <=
+ * max_context_len, n_b <= max_query_len, valid block ids).
+ */
+int pa_prefill_attention(void* out, const void* query, const void* k_pool, const void* v_pool,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                         int32_t max_query_len, int32_t num_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                         int32_t max_context_len, float scale, pa_dtype dtype, void* workspace,
+                         size_t workspace_bytes, int32_t partition_size, void* stream);
+
+/* Workspace bytes pa_prefill_attention needs for this partition_size (0: the
+ * most the automatic choice can use); 0 for invalid sizes. */
+size_t pa_prefill_workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t block_size, int32_t partition_size);
+
 /* Static, human-readable name of a pa_status value. */
 const char* pa_status_string(int status);
 

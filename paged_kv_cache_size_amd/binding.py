@@ -37,6 +37,9 @@ SIGNATURES = {
     "pa_decode_combine": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _SZ, _P]),
     "pa_decode_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_int, _P]),
     "pa_decode_plan_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _I32, _I32]),
+    "pa_prefill_attention": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                            _I32, _I32, _F32, ctypes.c_int, _P, _SZ, _I32, _P]),
+    "pa_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -229,6 +232,48 @@ def pa_decode_attention(query, k_pool, v_pool, block_tables, context_lens, scale
         _dev(context_lens, "context_lens", torch.int32, 1), B, H, hkv, D, bs, mb, int(max_context_len),
         float(scale), pa_dtype(query), ws_ptr, ws_bytes, int(partition_size), _stream(query))
     _check(rc, "pa_decode_attention")
+    return out
+
+
+def pa_prefill_workspace_bytes(num_tokens, num_heads, head_dim, max_context_len, block_size,
+                               partition_size: int = 0) -> int:
+    return int(lib().pa_prefill_workspace_bytes(num_tokens, num_heads, head_dim, max_context_len, block_size,
+                                                partition_size))
+
+
+def pa_prefill_attention(query, k_pool, v_pool, block_tables, context_lens, query_start_loc, scale: float,
+                         max_query_len: int, max_context_len: int, out=None, workspace=None,
+                         partition_size: int = 0):
+    """Paged attention of several new tokens per sequence; returns ``out`` [T, H, D].
+
+    ``query_start_loc`` (int32 [B+1], device) delimits each sequence's rows of
+    ``query``; ``context_lens`` include the new tokens, whose K/V must already
+    be in the pools.  ``max_query_len`` / ``max_context_len`` are host bounds."""
+    torch = _torch()
+    T, H, D = query.shape
+    nb, bs, hkv, d2 = k_pool.shape
+    B = block_tables.shape[0]
+    if d2 != D or k_pool.shape != v_pool.shape:
+        raise ValueError("pool shape does not match query")
+    if not (query.dtype == k_pool.dtype == v_pool.dtype):
+        raise TypeError("query and pools must share a dtype")
+    if context_lens.shape != (B,) or query_start_loc.shape != (B + 1,):
+        raise ValueError("context_lens / query_start_loc do not match the block tables' batch")
+    if out is None:
+        out = torch.empty_like(query)
+    need = pa_prefill_workspace_bytes(T, H, D, int(max_context_len), bs, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = None if workspace is None else _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().pa_prefill_attention(
+        _dev(out, "out", query.dtype, 3), _dev(query, "query", ndim=3), _dev(k_pool, "k_pool", ndim=4),
+        _dev(v_pool, "v_pool", ndim=4), _dev(block_tables, "block_tables", torch.int32, 2),
+        _dev(context_lens, "context_lens", torch.int32, 1),
+        _dev(query_start_loc, "query_start_loc", torch.int32, 1), B, T, int(max_query_len), H, hkv, D, bs,
+        block_tables.shape[1], int(max_context_len), float(scale), pa_dtype(query), ws_ptr, ws_bytes,
+        int(partition_size), _stream(query))
+    _check(rc, "pa_prefill_attention")
     return out
 
 

@@ -260,6 +260,75 @@ int auto_partition_bound(int max_context_len, int block_size) {
   return b < 1 ? 1 : b;
 }
 
+int check_prefill(const void* out, const void* query, const void* k_pool, const void* v_pool,
+                  const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc,
+                  const PrefillShape& s, float scale) {
+  if (!query_start_loc) return PA_ERR_INVALID_ARG;
+  const int rc = check_decode(out, query, k_pool, v_pool, block_tables, context_lens, s.d, scale);
+  if (rc != PA_OK) return rc;
+  if (s.num_tokens <= 0 || s.max_query_len <= 0 || s.max_query_len > s.num_tokens) return PA_ERR_INVALID_ARG;
+  if (s.max_query_len > s.d.max_context_len) return PA_ERR_INVALID_ARG;
+  if (s.d.dtype == PA_F32) return PA_ERR_UNSUPPORTED;  // the prefill tile is an MFMA tile (16-bit inputs)
+  if ((int64_t)s.num_tokens * s.d.num_heads > (int64_t)1 << 30) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+int prefill_tiles(const PrefillShape& s, const DecodeGrid& g) {
+  return (int)(((int64_t)s.max_query_len * g.repc + 15) / 16);
+}
+
+int prefill_partition_bounds(const PrefillShape& s, int* min_parts, int* max_parts) {
+  const int bs = s.d.block_size;
+  const int64_t nb = (s.d.max_context_len + bs - 1) / bs;
+  const int64_t lo = (nb + kMaxPartitionBlocks - 1) / kMaxPartitionBlocks;
+  int64_t hi = auto_partition_bound(s.d.max_context_len, bs);
+  const size_t per_part = (size_t)s.num_tokens * s.d.num_heads * ((size_t)s.d.head_dim + 2) * sizeof(float);
+  const int64_t cap = per_part > 0 ? (int64_t)(kPrefillWorkspaceCap / per_part) : hi;
+  hi = std::min(hi, std::max<int64_t>(lo, cap));
+  *min_parts = (int)std::max<int64_t>(1, lo);
+  *max_parts = (int)std::max<int64_t>(*min_parts, hi);
+  return PA_OK;
+}
+
+int prefill_partition_size(const PrefillShape& s, int requested, int num_cus, int wg_per_cu) {
+  const int bs = s.d.block_size;
+  if (requested != 0) {
+    if (requested < bs || requested > kMaxPartitionBlocks * bs || requested % bs != 0) return -PA_ERR_INVALID_ARG;
+    return requested;
+  }
+  const DecodeGrid g = decode_grid(s.d);
+  const int64_t slots = total_slots(num_cus, wg_per_cu);
+  const int64_t nb = (s.d.max_context_len + bs - 1) / bs;
+  const int64_t tiles = prefill_tiles(s, g);
+  int lo = 1, hi = 1;
+  prefill_partition_bounds(s, &lo, &hi);
+  int64_t best_pb = 0, prev_pb = 0;
+  double best = 0.0;
+  for (int64_t parts = lo; parts <= hi; ++parts) {
+    const int64_t pb = (nb + parts - 1) / parts;
+    if (pb == prev_pb) continue;
+    prev_pb = pb;
+    const int64_t p = (nb + pb - 1) / pb;
+    if (p > hi) continue;
+    const int64_t items = (int64_t)s.d.num_seqs * tiles * p * g.groups;
+    const double item = (double)pb + kItemSetup;
+    const int64_t tail = items % slots;
+    double cost = (double)(items / slots) * item;
+    if (tail > 0) cost += item / std::min(kMaxSpeedup, (double)slots / (double)tail);
+    if (p > 1) {  // merge: every partial read once
+      const double wg_block_bytes = (double)g.wpw * 2.0 * bs * s.d.head_dim * elem_bytes(s.d.dtype);
+      cost += kMergeLaunch + 2.0 * (double)s.num_tokens * s.d.num_heads * p * (s.d.head_dim + 2) * 4.0 /
+                                 ((double)slots * wg_block_bytes);
+    }
+    if (best_pb == 0 || cost < best - 1e-9) {
+      best = cost;
+      best_pb = pb;
+    }
+  }
+  if (best_pb == 0) best_pb = std::min<int64_t>(kMaxPartitionBlocks, nb);
+  return (int)(best_pb * bs);
+}
+
 size_t workspace_bytes(int num_seqs, int num_heads, int head_dim, int parts) {
   if (parts <= 1) return 0;
   return (size_t)num_seqs * num_heads * parts * ((size_t)head_dim + 2) * sizeof(float);

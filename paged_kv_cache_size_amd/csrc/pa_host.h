@@ -66,6 +66,36 @@ size_t workspace_bytes(int num_seqs, int num_heads, int head_dim, int parts);
 // Upper bound of partition counts the automatic policy can pick.
 int auto_partition_bound(int max_context_len, int block_size);
 
+// ----------------------------------------------------------------- prefill
+//
+// Several new tokens per sequence (varlen prefill, chunked prefill, mixed
+// batches): the query rows of sequence b are query_start_loc[b] .. [b+1].
+struct PrefillShape {
+  DecodeShape d;      // num_seqs, heads, head_dim, block_size, table width, max_context_len, dtype
+  int num_tokens;     // rows of query / out
+  int max_query_len;  // bound of query_start_loc[b+1] - query_start_loc[b]
+};
+
+constexpr size_t kPrefillWorkspaceCap = size_t(256) << 20;  // automatic split: partials kept under 256 MiB
+
+// Argument checks of pa_prefill_attention that do not depend on the device.
+int check_prefill(const void* out, const void* query, const void* k_pool, const void* v_pool,
+                  const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc,
+                  const PrefillShape& s, float scale);
+
+// Column tiles (16 MFMA columns of (token, query head) pairs) per (sequence, wave unit).
+int prefill_tiles(const PrefillShape& s, const DecodeGrid& g);
+
+// Partitions the automatic prefill split may use: at least enough for the
+// 256-block table slice, at most one per 128 tokens, and partials within
+// kPrefillWorkspaceCap.
+int prefill_partition_bounds(const PrefillShape& s, int* min_parts, int* max_parts);
+
+// Partition size (tokens) for the prefill kernel: `requested` validated, or 0
+// to pick the candidate of least cost (every tile taken at max_context_len,
+// whole waves of `slots` workgroups, plus the merge).  Negated pa_status on error.
+int prefill_partition_size(const PrefillShape& s, int requested, int num_cus, int wg_per_cu);
+
 int check_combine(const void* out, const int32_t* context_lens, int num_seqs, int num_heads, int head_dim,
                   int max_context_len, int partition_size, int dtype);
 

@@ -25,145 +25,11 @@
 #include <type_traits>
 
 #include "pa.h"
+#include "pa_device.h"
 #include "pa_host.h"
+#include "pa_runtime.h"
 
 namespace {
-
-constexpr int DT_F32 = PA_F32, DT_F16 = PA_F16, DT_BF16 = PA_BF16;
-
-template <int DT>
-struct ElemBytes { static constexpr int value = (DT == DT_F32) ? 4 : 2; };
-
-// ------------------------------------------------------------------ numerics
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ float f16_bits_to_float(uint32_t h) {
-  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
-}
-
-// 16 bytes of storage -> 16 / elem floats
-template <int DT>
-__device__ __forceinline__ void unpack16(const uint4 v, float* f) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  if constexpr (DT == DT_F32) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
-  } else if constexpr (DT == DT_BF16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = bf16_lo(w[i]);
-      f[2 * i + 1] = bf16_hi(w[i]);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = f16_bits_to_float(w[i] & 0xffffu);
-      f[2 * i + 1] = f16_bits_to_float(w[i] >> 16);
-    }
-  }
-}
-
-// float -> storage bits, round to nearest even
-__device__ __forceinline__ uint32_t float_to_bf16_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ uint32_t float_to_f16_bits(float x) {
-  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
-}
-
-template <int DT, int N>
-__device__ __forceinline__ void store_row(uint8_t* dst, const float* f) {
-  // N floats -> N elements of storage, written as 16-byte vectors
-  if constexpr (DT == DT_F32) {
-#pragma unroll
-    for (int i = 0; i < N; i += 4)
-      *reinterpret_cast<uint4*>(dst + 4 * i) =
-          make_uint4(__float_as_uint(f[i]), __float_as_uint(f[i + 1]), __float_as_uint(f[i + 2]),
-                     __float_as_uint(f[i + 3]));
-  } else {
-    uint32_t w[N / 2];
-#pragma unroll
-    for (int i = 0; i < N / 2; ++i) {
-      const uint32_t lo = DT == DT_BF16 ? float_to_bf16_bits(f[2 * i]) : float_to_f16_bits(f[2 * i]);
-      const uint32_t hi = DT == DT_BF16 ? float_to_bf16_bits(f[2 * i + 1]) : float_to_f16_bits(f[2 * i + 1]);
-      w[i] = lo | (hi << 16);
-    }
-#pragma unroll
-    for (int i = 0; i < N / 2; i += 4)
-      *reinterpret_cast<uint4*>(dst + 4 * i) = make_uint4(w[i], w[i + 1], w[i + 2], w[i + 3]);
-  }
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// ------------------------------------------------------------------ lane exchange
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-
-// Sum over aligned groups of G lanes (G = 8, 16 or 32); every lane of a group
-// ends with the same bits (each step adds a pair in both orders).
-template <int G>
-__device__ __forceinline__ float group_sum(float x) {
-  x += dpp<0xB1>(x);   // quad_perm(1,0,3,2): partner lane ^ 1
-  x += dpp<0x4E>(x);   // quad_perm(2,3,0,1): partner lane ^ 2
-  x += dpp<0x141>(x);  // row_half_mirror: lane i <-> 7 - i within 8 lanes
-  if constexpr (G >= 16) x += dpp<0x140>(x);  // row_mirror: lane i <-> 15 - i within 16
-  if constexpr (G >= 32) x += __shfl_xor(x, 16);
-  static_assert(G == 8 || G == 16 || G == 32, "group size");
-  return x;
-}
-
-// Reduce over the lanes that differ only in bits >= log2(G) (the row groups).
-template <int G>
-__device__ __forceinline__ float across_groups_max(float x) {
-#pragma unroll
-  for (int m = G; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
-}
-template <int G>
-__device__ __forceinline__ float across_groups_sum(float x) {
-#pragma unroll
-  for (int m = G; m < 64; m <<= 1) x += __shfl_xor(x, m);
-  return x;
-}
-
-// A partition's block-table slice, staged on chip: entry j sits in lane j % 64
-// of register j / 64, so one wave holds up to 64 * kTabRegs entries.
-constexpr int kTabRegs = pa::kMaxPartitionBlocks / 64;
-struct TableSlice {
-  int r[kTabRegs];
-  __device__ __forceinline__ void load(const int32_t* bt, int n, int lane) {
-#pragma unroll
-    for (int k = 0; k < kTabRegs; ++k) r[k] = (64 * k + lane < n) ? bt[64 * k + lane] : 0;
-  }
-  // entry j (wave-uniform j < 64 * kTabRegs), as a scalar: one readlane per
-  // register and scalar selects (no dynamic register indexing)
-  __device__ __forceinline__ int get(int j) const {
-    const int lane = j & 63, k = j >> 6;
-    int v = __builtin_amdgcn_readlane(r[0], lane);
-#pragma unroll
-    for (int i = 1; i < kTabRegs; ++i) {
-      const int e = __builtin_amdgcn_readlane(r[i], lane);
-      v = (k == i) ? e : v;
-    }
-    return v;
-  }
-};
-
-// Workgroup id -> logical id such that each XCD (workgroups are dealt to the
-// 8 XCDs round-robin) receives one contiguous range of logical ids; a bijection
-// whatever the hardware order.
-__device__ __forceinline__ int xcd_remap(int i, int n) {
-  const int xcd = i & 7, k = i >> 3, per = n >> 3, rem = n & 7;
-  return xcd * per + (xcd < rem ? xcd : rem) + k;
-}
 
 // ------------------------------------------------------------------ slot mapping
 
@@ -443,111 +309,6 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
 // The running max of a head is kept uniform over the four row groups (a
 // permlane max per block); denominators are per-lane partial sums.
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-
-#ifndef PA_K_CPOL
-#define PA_K_CPOL 2
-#endif
-#ifndef PA_V_CPOL
-#define PA_V_CPOL 0
-#endif
-// Cache-policy bits of the K and V stream loads (gfx950: 1 = sc0, 2 = nt, 16 = sc1).
-// Measured on MI355X: marking one of the two streams non-temporal is fastest
-// (~10% over neither, ~4% over both), and keeps shared prompt blocks of
-// forked sequences cacheable through the other stream.
-constexpr int kKCpol = PA_K_CPOL, kVCpol = PA_V_CPOL;
-
-// Raw buffer descriptor over `bytes` bytes from `base` (gfx9 data format word).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_block_rsrc(const uint8_t* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, 0x00020000);
-}
-template <typename VT>
-__device__ __forceinline__ VT buffer_load_v(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  if constexpr (sizeof(VT) == 16)
-    return __builtin_bit_cast(VT, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kVCpol));
-  else
-    return __builtin_bit_cast(VT, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kVCpol));
-}
-
-// XOR swizzle of a K row's 16-byte chunks in LDS: token t's chunk k sits at
-// position k ^ kswz(t), so the 16 rows read by one 16-lane group at a fixed
-// chunk land in 16 distinct bank groups.  (Rows of 16 chunks: kswz = t;
-// rows of 8 chunks: two rows share 16 positions, kswz = t / 2.)
-template <int CPR>
-__device__ __forceinline__ int kswz_t(int t) {
-  return CPR == 16 ? t : (t >> 1) & (CPR - 1);
-}
-
-template <int DT>
-struct MfmaOps;
-
-template <>
-struct MfmaOps<DT_BF16> {
-  static __device__ __forceinline__ f32x4 qk(uint4 a, uint4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                   0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4 pv(uint2 a, uint2 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
-                                                     0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
-    const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};  // v_cvt_pk_bf16_f32, nearest even
-    return __builtin_bit_cast(uint32_t, v);
-  }
-};
-
-template <>
-struct MfmaOps<DT_F16> {
-  static __device__ __forceinline__ f32x4 qk(uint4 a, uint4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
-                                                  0, 0);
-  }
-  static __device__ __forceinline__ f32x4 pv(uint2 a, uint2 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0,
-                                                 0);
-  }
-  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
-    return float_to_f16_bits(lo) | (float_to_f16_bits(hi) << 16);
-  }
-};
-
-// Max over the four 16-lane rows (lanes l, l^16, l^32, l^48), every lane ends equal.
-__device__ __forceinline__ float rows_max(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float rows_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-
-template <int VPL>
-struct VRow;  // V elements per lane and row
-template <>
-struct VRow<8> { using T = uint4; };
-template <>
-struct VRow<4> { using T = uint2; };
-
-template <int VPL>
-__device__ __forceinline__ uint32_t vword(const typename VRow<VPL>::T& v, int w) {
-  if constexpr (VPL == 8) return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
-  else return w == 0 ? v.x : v.y;
-}
-
 template <int DT, int D, int NBUF, int WPW>
 __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs a) {
   using Ops = MfmaOps<DT>;
@@ -754,14 +515,13 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
   }
 }
 
-// One wave per (sequence, query head): out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+// One wave per (sequence, query head): merges the partials of a sequence that
+// spans more than one partition.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void combine_kernel(void* __restrict__ out, const float* __restrict__ ws_acc,
                                                       const float2* __restrict__ ws_ml,
                                                       const int32_t* __restrict__ context_lens, int num_seqs,
                                                       int num_heads, int part_tokens, int num_parts) {
-  constexpr int EB = ElemBytes<DT>::value;
-  constexpr int DPL = D / 64;  // dims per lane
   const int lane = threadIdx.x & 63;
   const int idx = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (idx >= num_seqs * num_heads) return;
@@ -769,33 +529,8 @@ __global__ __launch_bounds__(256) void combine_kernel(void* __restrict__ out, co
   const int L = context_lens[b];
   const int np = L > 0 ? (L + part_tokens - 1) / part_tokens : 0;
   if (np <= 1) return;  // written by the partition kernel
-  const float2* ml = ws_ml + (size_t)idx * num_parts;
-  const float* acc = ws_acc + (size_t)idx * num_parts * D;
-
-  float M = -INFINITY;
-  for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[p].x);
-#pragma unroll
-  for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
-  float den = 0.f;
-  for (int p = lane; p < np; p += 64) den += ml[p].y * fast_exp2(ml[p].x - M);
-#pragma unroll
-  for (int x = 1; x < 64; x <<= 1) den += __shfl_xor(den, x);
-
-  float o[DPL] = {};
-  for (int p = 0; p < np; ++p) {
-    const float f = fast_exp2(ml[p].x - M);
-#pragma unroll
-    for (int d = 0; d < DPL; ++d) o[d] = fmaf(f, acc[(size_t)p * D + lane * DPL + d], o[d]);
-  }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  uint8_t* dst = (uint8_t*)out + (size_t)idx * D * EB + lane * DPL * EB;
-#pragma unroll
-  for (int d = 0; d < DPL; ++d) {
-    const float v = o[d] * inv;
-    if constexpr (DT == DT_F32) reinterpret_cast<float*>(dst)[d] = v;
-    else if constexpr (DT == DT_BF16) reinterpret_cast<uint16_t*>(dst)[d] = (uint16_t)float_to_bf16_bits(v);
-    else reinterpret_cast<uint16_t*>(dst)[d] = (uint16_t)float_to_f16_bits(v);
-  }
+  merge_partials<DT, D>((uint8_t*)out + (size_t)idx * D * ElemBytes<DT>::value, ws_acc + (size_t)idx * num_parts * D,
+                        ws_ml + (size_t)idx * num_parts, np, lane);
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -855,45 +590,6 @@ CombineFn pick_combine(int dtype, int d) {
   }
 }
 
-int device_cu_count() {
-  static std::atomic<int> cache[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
-  if (dev < 64) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return -1;
-  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
-  return cus;
-}
-
-int launch_status() { return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP; }
-
-// Workgroups of `fn` (with `threads` threads) resident per compute unit, cached
-// per (device, kernel).  0 on failure.
-int resident_per_cu(DecodeFn fn, int threads) {
-  struct Entry { int dev; const void* fn; int n; };
-  static Entry cache[256];
-  static int used = 0;
-  static std::mutex mu;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  {
-    std::lock_guard<std::mutex> lock(mu);
-    for (int i = 0; i < used; ++i)
-      if (cache[i].dev == dev && cache[i].fn == (const void*)fn) return cache[i].n;
-  }
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(fn), threads, 0) != hipSuccess)
-    return 0;
-  std::lock_guard<std::mutex> lock(mu);
-  if (used < 256) cache[used++] = Entry{dev, (const void*)fn, n};
-  return n;
-}
-
 struct DecodePlan {
   int ps = 0, parts = 0;
   size_t need = 0;
@@ -908,11 +604,11 @@ int plan_decode(const void* out, const void* query, const void* k_pool, const vo
   if (partition_req != 0 && pa::partition_size(shp, partition_req, 256, 1) < 0) return PA_ERR_INVALID_ARG;
   int cus = 256, per_cu = 1;
   if (partition_req == 0) {
-    cus = device_cu_count();
+    cus = pa::device_cu_count();
     const pa::DecodeGrid g = pa::decode_grid(shp);
     DecodeFn fn = pick_decode(shp.dtype, shp.head_dim, g);
     if (!fn) return PA_ERR_UNSUPPORTED;
-    per_cu = resident_per_cu(fn, 64 * g.wpw);
+    per_cu = pa::resident_per_cu(reinterpret_cast<const void*>(fn), 64 * g.wpw);
     if (cus <= 0 || per_cu <= 0) return PA_ERR_HIP;
   }
   const int ps = pa::partition_size(shp, partition_req, cus, per_cu);
@@ -958,7 +654,7 @@ int launch_partitions(void* out, const void* query, const void* k_pool, const vo
   a.groups = gd.groups;
   a.qscale = scale * 1.44269504088896340736f;  // log2(e)
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * gd.wpw), 0, static_cast<hipStream_t>(stream), a);
-  return launch_status();
+  return pa::launch_status();
 }
 
 int launch_combine(void* out, const int32_t* context_lens, const pa::DecodeShape& shp, void* workspace,
@@ -970,10 +666,53 @@ int launch_combine(void* out, const int32_t* context_lens, const pa::DecodeShape
   hipLaunchKernelGGL(cf, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, static_cast<hipStream_t>(stream), out,
                      static_cast<const float*>(workspace), ml_region(workspace, shp, plan.parts), context_lens,
                      shp.num_seqs, shp.num_heads, plan.ps, plan.parts);
-  return launch_status();
+  return pa::launch_status();
 }
 
 }  // namespace
+
+namespace pa {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return -1;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+int launch_status() { return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// Workgroups of `fn` (with `threads` threads) resident per compute unit, cached
+// per (device, kernel).  0 on failure.
+int resident_per_cu(const void* fn, int threads) {
+  struct Entry { int dev; const void* fn; int n; };
+  static Entry cache[256];
+  static int used = 0;
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+      if (cache[i].dev == dev && cache[i].fn == fn) return cache[i].n;
+  }
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, 0) != hipSuccess)
+    return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (used < 256) cache[used++] = Entry{dev, fn, n};
+  return n;
+}
+
+}  // namespace pa
 
 // ------------------------------------------------------------------ C ABI
 
@@ -991,7 +730,7 @@ extern "C" int pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_table
     hipLaunchKernelGGL(slot_mapping_varlen_kernel, dim3(num_seqs), dim3(64), 0, st, slot_mapping, block_tables,
                        context_lens, query_start_loc, max_blocks_per_seq, block_size, num_tokens);
   }
-  return launch_status();
+  return pa::launch_status();
 }
 
 extern "C" int pa_reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
@@ -1036,7 +775,7 @@ extern "C" int pa_reshape_and_cache(const void* key, const void* value, void* k_
                          num_slots);
       break;
   }
-  return launch_status();
+  return pa::launch_status();
 }
 
 extern "C" int pa_decode_attention_ex(void* out, const void* query, const void* k_pool, const void* v_pool,
@@ -1109,8 +848,8 @@ extern "C" int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads,
   const pa::DecodeGrid g = pa::decode_grid(shp);
   DecodeFn fn = pick_decode(shp.dtype, shp.head_dim, g);
   if (!fn) return -PA_ERR_UNSUPPORTED;
-  const int cus = device_cu_count();
-  const int per_cu = resident_per_cu(fn, 64 * g.wpw);
+  const int cus = pa::device_cu_count();
+  const int per_cu = pa::resident_per_cu(reinterpret_cast<const void*>(fn), 64 * g.wpw);
   if (cus <= 0 || per_cu <= 0) return -PA_ERR_HIP;
   return pa::partition_size(shp, 0, cus, per_cu, host_context_lens);
 }

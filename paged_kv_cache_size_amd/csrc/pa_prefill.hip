@@ -1,0 +1,384 @@
+// Paged attention for several new tokens per sequence on gfx950: varlen
+// prefill, chunked prefill, and batches that mix prefill chunks with decode
+// steps.  Sequence b contributes the query rows query_start_loc[b] ..
+// query_start_loc[b+1]; they are the last n_b positions of its context of
+// length L_b, and the row at position p attends causally to positions 0..p
+// (handbook "分页 KV Cache", section "分页注意力": seq_lens is the context after
+// this step, query_start_loc delimits each sequence's new tokens, and the mask
+// keeps, for new token i, the positions up to L_b - n_b + i).
+//
+// The tile is the decode MFMA tile with its 16 columns re-purposed: a column
+// is a (new token, query head) pair of one KV head's group instead of one
+// query head of the single new token.  Per 16-token block of the context:
+//   QK:  S^T[key][column]  = K[16 x D] . Q^T[D x 16]   mfma_f32_16x16x32 (D/32)
+//   PV:  O^T[dim][column] += V^T[16 x 16] . P^T          mfma_f32_16x16x16 (D/16)
+// with the same operand layouts as the decode kernel (K through LDS in the
+// swizzled row order, V row-coalesced into registers and paired by v_perm).
+// Causality is a per-column key limit applied to the scores; V rows past the
+// partition's last key are zeroed, so stale slots never reach the MFMA.
+// Long contexts split into partitions like decode; the partials are merged per
+// (query row, head) by the combine kernel below.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+#include "pa_device.h"
+#include "pa_host.h"
+#include "pa_runtime.h"
+
+namespace {
+
+struct PrefillArgs {
+  void* out;                 // [T, H, D]
+  const void* query;         // [T, H, D]
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start_loc;  // [B + 1]
+  float* ws_acc;                   // [T, H, P, D]
+  float2* ws_ml;                   // [T, H, P] (running max in log2 units, denominator)
+  int num_heads, num_kv_heads, rep, repc, chunks, max_blocks_per_seq;
+  int part_tokens, num_parts, groups, tiles;  // tiles: 16-column tiles per (sequence, wave unit)
+  float qscale;                               // scale * log2(e)
+};
+
+// A finite floor for the running max: a column whose keys all lie beyond this
+// block (or partition) keeps m at the floor, so alpha = 2^0 and p = 2^-inf = 0
+// instead of the NaN that -inf - -inf would give.
+constexpr float kMaxFloor = -3.0e38f;
+
+template <int DT, int D, int NBUF, int WPW>
+__global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArgs a) {
+  using Ops = MfmaOps<DT>;
+  constexpr int BS = pa::kBlockSize;
+  constexpr int ROWB = D * 2;
+  constexpr int NKC = D / 32;      // QK k-chunks
+  constexpr int VPL = D / 16;      // V elements per lane and row = PV output tiles
+  constexpr int DPL = 4 * VPL;     // output dims owned by a lane
+  constexpr int CPR = ROWB / 16;   // 16-byte chunks per K row
+  constexpr int NLI = BS * CPR / 64;  // K load instructions per block
+  constexpr int KBYTES = BS * ROWB;
+  using VT = typename VRow<VPL>::T;
+  static_assert(BS == 16, "the MFMA tiling assumes 16-token blocks");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int rest = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = rest % a.groups;
+  rest /= a.groups;
+  const int s = rest % a.num_parts;
+  rest /= a.num_parts;
+  const int tile = rest % a.tiles;
+  const int b = rest / a.tiles;
+  const int unit = grp * WPW + wave;
+  const int g = unit / a.chunks;
+  const int gq = lane >> 4, col = lane & 15;
+
+  const int q0 = a.query_start_loc[b];
+  const int n = a.query_start_loc[b + 1] - q0;  // new tokens of this sequence
+  const int L = a.context_lens[b];
+  const int first_tok = (16 * tile) / a.repc;
+  if (first_tok >= n) return;  // the whole wave lies past this sequence's new tokens
+  const int last_tok = min(n - 1, (16 * tile + 15) / a.repc);
+
+  // This lane's column: new token ti, query head h, position pos.
+  const int cc = 16 * tile + col;
+  const int ti = cc / a.repc;
+  const bool live = ti < n;
+  const int h = g * a.rep + (unit % a.chunks) * a.repc + cc % a.repc;
+  const int pos = L - n + ti;
+
+  const int start = s * a.part_tokens;
+  const int pend = min(L, start + a.part_tokens);
+  const int end = min(pend, L - n + last_tok + 1);  // keys any column of the wave sees here
+  if (start >= end) return;  // no column's keys in this partition: the merge does not read it
+  const int lim = live ? min(pend, pos + 1) : 0;  // this column's keys are [start, lim)
+  const int col_parts = (pos + a.part_tokens) / a.part_tokens;  // partitions holding its keys
+  const int blk0 = start / BS;
+  const int nblk = (end - start + BS - 1) / BS;  // 1..kMaxPartitionBlocks
+  const int last = nblk - 1;
+
+  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk0;
+  TableSlice tab;
+  tab.load(bt, nblk, lane);
+
+  const size_t qrow = ((size_t)(q0 + (live ? ti : 0)) * a.num_heads + h);
+  uint4 qop[NKC];
+  {
+    const uint8_t* qp = (const uint8_t*)a.query + qrow * ROWB + gq * 16;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qp + c * 64);
+      qop[c] = live ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  const uint32_t row_stride = (uint32_t)a.num_kv_heads * ROWB;
+  const size_t block_stride = (size_t)BS * row_stride;
+  uint32_t kdma[NLI];
+#pragma unroll
+  for (int i = 0; i < NLI; ++i) {
+    const int slot = 64 * i + lane, t = slot / CPR, q = slot % CPR;
+    kdma[i] = (uint32_t)t * row_stride + (uint32_t)g * ROWB + (uint32_t)((q ^ kswz_t<CPR>(t)) * 16);
+  }
+  uint32_t kread[NKC];  // QK A operand: token 4*(col%4) + col/4, chunk 4c + gq
+  {
+    const int t = 4 * (col & 3) + (col >> 2);
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) kread[c] = (uint32_t)(t * CPR + ((4 * c + gq) ^ kswz_t<CPR>(t))) * 16;
+  }
+  const uint32_t voff = (uint32_t)gq * row_stride + (uint32_t)g * ROWB + col * VPL * 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t kslot0[WPW][KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kslot1[WPW][KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kslot2[NBUF > 2 ? WPW : 1][KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kslot3[NBUF > 3 ? WPW : 1][KBYTES];
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
+  auto slot_base = [&](int slot) -> uint8_t* {
+    return slot == 0 ? &kslot0[wave][0] : slot == 1 ? &kslot1[wave][0] : slot == 2 ? &kslot2[wave][0] : &kslot3[wave][0];
+  };
+
+  f32x4 acc[VPL];
+#pragma unroll
+  for (int t = 0; t < VPL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = kMaxFloor, l = 0.f;
+
+  // Loads past the partition's last block go through an empty descriptor
+  // (zeros, no memory access), so every wait stays an exact count.
+  auto load_block = [&](int j, int slot, VT* vr) {
+    const bool real = j <= last;
+    const size_t off = (size_t)(uint32_t)tab.get(real ? j : last) * block_stride;
+    const uint32_t span = real ? (uint32_t)block_stride : 0u;
+    const __amdgpu_buffer_rsrc_t rk = make_block_rsrc(a.k_pool + off, span);
+    const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, span);
+#pragma unroll
+    for (int i = 0; i < NLI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (__attribute__((address_space(3))) void*)(slot_base(slot) + i * 1024), 16, (int)kdma[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vr[i] = buffer_load_v<VT>(rv, voff + (uint32_t)(4 * i) * row_stride);
+  };
+  auto read_k = [&](int slot, uint4* kr) {
+    const uint8_t* kb = slot_base(slot);
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) kr[c] = *reinterpret_cast<const uint4*>(kb + kread[c]);
+  };
+  // One block whose first key is `key0`.  Lane (gq, col) register i holds key
+  // key0 + 4i + gq of column col.  Branch free.
+  auto process = [&](const uint4* kr, const VT* vr, int key0) {
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) sacc = Ops::qk(kr[c], qop[c], sacc);
+    float sc[4];
+    VT vm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = key0 + 4 * i + gq;
+      sc[i] = key < lim ? sacc[i] * a.qscale : -INFINITY;
+      vm[i] = key < end ? vr[i] : VT{};  // rows past the last key (stale, even NaN) must not reach the MFMA
+    }
+    const float mn = fmaxf(m, rows_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]))));
+    const float alpha = fast_exp2(m - mn);
+    m = mn;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - mn);
+    l = fmaf(l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+    const uint2 pb = make_uint2(Ops::pack(p[0], p[1]), Ops::pack(p[2], p[3]));
+#pragma unroll
+    for (int t = 0; t < VPL; ++t) {
+      const int w = t >> 1;
+      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+      const uint2 va = make_uint2(__builtin_amdgcn_perm(vword<VPL>(vm[1], w), vword<VPL>(vm[0], w), sel),
+                                  __builtin_amdgcn_perm(vword<VPL>(vm[3], w), vword<VPL>(vm[2], w), sel));
+      acc[t] *= alpha;
+      acc[t] = Ops::pv(va, pb, acc[t]);
+    }
+  };
+
+  VT vr[NBUF][4];
+#pragma unroll
+  for (int u = 0; u < NBUF - 1; ++u) load_block(u, u, vr[u]);
+  for (int j = 0; j < nblk; j += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      const int jj = j + u;
+      uint4 kr[NKC];
+      read_k(u, kr);
+      load_block(jj + NBUF - 1, (u + NBUF - 1) % NBUF, vr[(u + NBUF - 1) % NBUF]);
+      __builtin_amdgcn_sched_barrier(0);
+      process(kr, vr[u], start + jj * BS);
+    }
+  }
+
+  const float lt = rows_sum(l);
+  if (!live || s >= col_parts) return;  // no keys of this column here
+  if (col_parts == 1) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float o[DPL];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int t = 0; t < VPL; ++t) o[VPL * r + t] = acc[t][r] * inv;
+    store_row<DT, DPL>((uint8_t*)a.out + qrow * ROWB + gq * DPL * 2, o);
+  } else {
+    const size_t idx = qrow * a.num_parts + s;
+    float* dst = a.ws_acc + idx * D + gq * DPL;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int t = 0; t < VPL; t += 4)
+        *reinterpret_cast<float4*>(dst + VPL * r + t) =
+            make_float4(acc[t][r], acc[t + 1][r], acc[t + 2][r], acc[t + 3][r]);
+    if (gq == 0) a.ws_ml[idx] = make_float2(m, lt);
+  }
+}
+
+// One wave per (query row, head): the sequence of row t is found by binary
+// search over query_start_loc; rows whose keys fit one partition were written
+// by the partition kernel.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void prefill_combine_kernel(void* __restrict__ out, const float* __restrict__ ws_acc,
+                                                              const float2* __restrict__ ws_ml,
+                                                              const int32_t* __restrict__ context_lens,
+                                                              const int32_t* __restrict__ query_start_loc,
+                                                              int num_seqs, int num_tokens, int num_heads,
+                                                              int part_tokens, int num_parts) {
+  const int lane = threadIdx.x & 63;
+  const int idx = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (idx >= num_tokens * num_heads) return;
+  const int t = idx / num_heads;
+  int lo = 0, hi = num_seqs;  // largest b with query_start_loc[b] <= t
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (query_start_loc[mid] <= t) lo = mid;
+    else hi = mid;
+  }
+  const int q0 = query_start_loc[lo], n = query_start_loc[lo + 1] - q0;
+  if (t >= q0 + n) return;  // a row no sequence owns
+  const int pos = context_lens[lo] - n + (t - q0);
+  const int np = (pos + part_tokens) / part_tokens;
+  if (np <= 1) return;
+  merge_partials<DT, D>((uint8_t*)out + (size_t)idx * D * ElemBytes<DT>::value, ws_acc + (size_t)idx * num_parts * D,
+                        ws_ml + (size_t)idx * num_parts, np, lane);
+}
+
+using PrefillFn = void (*)(const PrefillArgs);
+using PrefillCombineFn = void (*)(void*, const float*, const float2*, const int32_t*, const int32_t*, int, int, int,
+                                  int, int);
+constexpr int kPrefillRing = 4;
+
+template <int DT, int D>
+PrefillFn pick_prefill_wpw(int wpw) {
+  switch (wpw) {
+    case 1: return prefill_mfma_kernel<DT, D, kPrefillRing, 1>;
+    case 2: return prefill_mfma_kernel<DT, D, kPrefillRing, 2>;
+    case 4: return prefill_mfma_kernel<DT, D, kPrefillRing, 4>;
+    default: return nullptr;
+  }
+}
+
+PrefillFn pick_prefill(int dtype, int d, int wpw) {
+  switch (dtype) {
+    case PA_F16: return d == 64 ? pick_prefill_wpw<DT_F16, 64>(wpw) : pick_prefill_wpw<DT_F16, 128>(wpw);
+    case PA_BF16: return d == 64 ? pick_prefill_wpw<DT_BF16, 64>(wpw) : pick_prefill_wpw<DT_BF16, 128>(wpw);
+    default: return nullptr;
+  }
+}
+
+PrefillCombineFn pick_prefill_combine(int dtype, int d) {
+  switch (dtype) {
+    case PA_F16: return d == 64 ? prefill_combine_kernel<DT_F16, 64> : prefill_combine_kernel<DT_F16, 128>;
+    case PA_BF16: return d == 64 ? prefill_combine_kernel<DT_BF16, 64> : prefill_combine_kernel<DT_BF16, 128>;
+    default: return nullptr;
+  }
+}
+
+size_t prefill_workspace(const pa::PrefillShape& s, int parts) {
+  return pa::workspace_bytes(s.num_tokens, s.d.num_heads, s.d.head_dim, parts);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ C ABI
+
+extern "C" size_t pa_prefill_workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t head_dim,
+                                             int32_t max_context_len, int32_t block_size, int32_t partition_size) {
+  if (num_tokens <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0 || block_size <= 0) return 0;
+  pa::PrefillShape s{{1, num_heads, 1, head_dim, block_size, 1 << 30, max_context_len, PA_BF16}, num_tokens, 1};
+  int parts;
+  if (partition_size == 0) {
+    int lo = 1;
+    pa::prefill_partition_bounds(s, &lo, &parts);
+  } else {
+    if (partition_size < block_size || partition_size % block_size != 0) return 0;
+    parts = pa::num_partitions(max_context_len, partition_size);
+  }
+  return prefill_workspace(s, parts);
+}
+
+extern "C" int pa_prefill_attention(void* out, const void* query, const void* k_pool, const void* v_pool,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                                    int32_t max_query_len, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                    int32_t max_context_len, float scale, pa_dtype dtype, void* workspace,
+                                    size_t workspace_bytes, int32_t partition_size, void* stream) {
+  const pa::PrefillShape shp{{num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                              max_context_len, (int)dtype},
+                             num_tokens,
+                             max_query_len};
+  int rc = pa::check_prefill(out, query, k_pool, v_pool, block_tables, context_lens, query_start_loc, shp, scale);
+  if (rc != PA_OK) return rc;
+  const pa::DecodeGrid gd = pa::decode_grid(shp.d);
+  PrefillFn fn = pick_prefill(shp.d.dtype, shp.d.head_dim, gd.wpw);
+  if (!fn) return PA_ERR_UNSUPPORTED;
+  int cus = 256, per_cu = 1;
+  if (partition_size == 0) {
+    cus = pa::device_cu_count();
+    per_cu = pa::resident_per_cu(reinterpret_cast<const void*>(fn), 64 * gd.wpw);
+    if (cus <= 0 || per_cu <= 0) return PA_ERR_HIP;
+  }
+  const int ps = pa::prefill_partition_size(shp, partition_size, cus, per_cu);
+  if (ps <= 0) return -ps;
+  const int parts = pa::num_partitions(max_context_len, ps);
+  const size_t need = prefill_workspace(shp, parts);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  const int tiles = pa::prefill_tiles(shp, gd);
+  const int64_t grid = (int64_t)num_seqs * tiles * parts * gd.groups;
+  if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
+
+  PrefillArgs a;
+  a.out = out;
+  a.query = query;
+  a.k_pool = static_cast<const uint8_t*>(k_pool);
+  a.v_pool = static_cast<const uint8_t*>(v_pool);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.ws_acc = parts > 1 ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = parts > 1 ? reinterpret_cast<float2*>(static_cast<float*>(workspace) +
+                                                  (size_t)num_tokens * num_heads * parts * head_dim)
+                      : nullptr;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.rep = gd.rep;
+  a.repc = gd.repc;
+  a.chunks = gd.chunks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.part_tokens = ps;
+  a.num_parts = parts;
+  a.groups = gd.groups;
+  a.tiles = tiles;
+  a.qscale = scale * 1.44269504088896340736f;  // log2(e)
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * gd.wpw), 0, st, a);
+  rc = pa::launch_status();
+  if (rc != PA_OK || parts <= 1) return rc;
+  PrefillCombineFn cf = pick_prefill_combine(shp.d.dtype, shp.d.head_dim);
+  if (!cf) return PA_ERR_UNSUPPORTED;
+  const int64_t waves = (int64_t)num_tokens * num_heads;
+  hipLaunchKernelGGL(cf, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, out, a.ws_acc, a.ws_ml, context_lens,
+                     query_start_loc, num_seqs, num_tokens, num_heads, ps, parts);
+  return pa::launch_status();
+}

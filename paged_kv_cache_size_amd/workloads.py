@@ -323,6 +323,90 @@ def make_workload(name: str, seed: int = 0, **kw) -> Workload:
 
 
 # --------------------------------------------------------------------------
+# Several new tokens per sequence (varlen prefill, chunked prefill)
+# --------------------------------------------------------------------------
+
+@dataclass
+class PrefillBatch:
+    """A batch whose sequence b brings query_lens[b] new tokens: the last
+    query_lens[b] positions of its context of workload.context_lens[b] tokens
+    (the context after this step, as in the decode workloads)."""
+    workload: Workload
+    query_lens: np.ndarray  # int32 [B], 1 <= n_b <= L_b
+    description: str = ""
+
+    @property
+    def name(self) -> str:
+        return self.workload.name
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query_lens.sum())
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.query_lens.max())
+
+    @property
+    def query_start_loc(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.query_lens.astype(np.int64))]).astype(np.int32)
+
+    def attention_flops(self) -> int:
+        """QK and PV multiply-adds of every visible (query row, key) pair,
+        2 flops each: new token i of sequence b sees L_b - n_b + i + 1 keys."""
+        w = self.workload
+        pairs = 0
+        for L, n in zip(w.context_lens.astype(np.int64), self.query_lens.astype(np.int64)):
+            pairs += n * (L - n) + n * (n + 1) // 2
+        return int(pairs) * w.num_heads * w.head_dim * 4
+
+    def kv_read_bytes(self) -> int:
+        return self.workload.kv_read_bytes()
+
+
+def prefill_batch(lens, query_lens, num_heads: int, num_kv_heads: int, head_dim: int, dtype: str,
+                  seed: int = 0, name: str = "prefill", extra_cols: int = 0) -> PrefillBatch:
+    q = np.asarray(query_lens, dtype=np.int32)
+    lens = np.asarray(lens, dtype=np.int32)
+    assert q.shape == lens.shape and (q >= 1).all() and (q <= lens).all()
+    w = custom(lens.tolist(), num_heads, num_kv_heads, head_dim, dtype, seed=seed, extra_cols=extra_cols,
+               name=name)
+    return PrefillBatch(w, q, f"{len(lens)} seqs, {int(q.sum())} new tokens, contexts {lens.min()}..{lens.max()}")
+
+
+def chunked_prefill_llama_bf16(seed: int = 0, num_seqs: int = 16, context: int = 4096,
+                               chunk: int = 512) -> PrefillBatch:
+    """Chunked prefill of the Llama-style GQA layer: 16 sequences each add a
+    512-token chunk on top of 3584 cached tokens (context 4096); 32 query /
+    8 KV heads; D 128; bf16; physical ids shuffled in a pool with 10% slack."""
+    pb = prefill_batch([context] * num_seqs, [chunk] * num_seqs, 32, 8, 128, "bf16", seed=seed,
+                       name="chunked_prefill_llama_bf16")
+    pb.description = (f"{num_seqs} seqs x {chunk}-token chunks on {context - chunk} cached tokens, "
+                      f"H 32 / Hkv 8, D 128, bf16")
+    return pb
+
+
+def mixed_varlen_bf16(seed: int = 0) -> PrefillBatch:
+    """A mixed batch: whole prompts (n = L), chunks on cached context, and
+    decode steps (n = 1), with ragged lengths over block boundaries; 12 query
+    / 2 KV heads (group of 6), D 128, bf16."""
+    rng = np.random.default_rng(seed)
+    lens = [1, 16, 17, 33, 200, 500, 1000, 1500, 64, 300, 2049, 7]
+    qls = [1, 16, 5, 33, 1, 129, 64, 1, 64, 300, 700, 7]
+    order = rng.permutation(len(lens))
+    pb = prefill_batch([lens[i] for i in order], [qls[i] for i in order], 12, 2, 128, "bf16", seed=seed,
+                       name="mixed_varlen_bf16")
+    pb.description = "12 seqs mixing whole prompts, chunks and decode steps, H 12 / Hkv 2, D 128, bf16"
+    return pb
+
+
+PREFILL_BUILDERS = {
+    "chunked_prefill_llama_bf16": chunked_prefill_llama_bf16,
+    "mixed_varlen_bf16": mixed_varlen_bf16,
+}
+
+
+# --------------------------------------------------------------------------
 # Tensors (torch, on any device)
 # --------------------------------------------------------------------------
 
@@ -365,6 +449,29 @@ def make_tensors(w: Workload, seed: int = 0, device="cpu"):
         k_pool[dst, :rows] = k_pool[src, :rows]
         v_pool[dst, :rows] = v_pool[src, :rows]
     return {"query": q, "key": key, "value": value, "k_pool": k_pool, "v_pool": v_pool}
+
+
+def make_prefill_tensors(pb: PrefillBatch, seed: int = 0, device="cpu"):
+    """q [T,H,D] and the new tokens' key/value rows [T,H_kv,D] (T = all new
+    tokens, packed by sequence), the K/V pools [NB,BS,H_kv,D] and
+    query_start_loc, all N(0,1) in the workload dtype from one seeded
+    generator on ``device``."""
+    import torch
+    w = pb.workload
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    t, h, hkv, d = pb.num_tokens, w.num_heads, w.num_kv_heads, w.head_dim
+    q = _randn((t, h, d), w.dtype, gen, device)
+    key = _randn((t, hkv, d), w.dtype, gen, device)
+    value = _randn((t, hkv, d), w.dtype, gen, device)
+    pshape = (w.num_blocks, w.block_size, hkv, d)
+    k_pool = _randn(pshape, w.dtype, gen, device)
+    v_pool = _randn(pshape, w.dtype, gen, device)
+    for src, dst, rows in w.cow_copies:
+        k_pool[dst, :rows] = k_pool[src, :rows]
+        v_pool[dst, :rows] = v_pool[src, :rows]
+    qsl = torch.from_numpy(pb.query_start_loc).to(device)
+    return {"query": q, "key": key, "value": value, "k_pool": k_pool, "v_pool": v_pool, "query_start_loc": qsl}
 
 
 def raw_numpy(t):

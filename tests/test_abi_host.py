@@ -89,6 +89,52 @@ def test_workspace_sizes():
     assert decode(ps=16, ws=FAKE, wsb=4 * 8 * 8 * 130 * 4 - 1) == B.PA_ERR_WORKSPACE
 
 
+def prefill(**kw):
+    args = dict(out=FAKE, query=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, qsl=FAKE, B=4, T=40, mq=16, H=8, Hkv=2,
+                D=128, bs=16, mb=8, maxlen=128, scale=0.088, dtype=B.PA_BF16, ws=None, wsb=0, ps=128)
+    args.update(kw)
+    a = args
+    return B.lib().pa_prefill_attention(a["out"], a["query"], a["k"], a["v"], a["bt"], a["lens"], a["qsl"], a["B"],
+                                        a["T"], a["mq"], a["H"], a["Hkv"], a["D"], a["bs"], a["mb"], a["maxlen"],
+                                        a["scale"], a["dtype"], a["ws"], a["wsb"], a["ps"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qsl=None), B.PA_ERR_INVALID_ARG),
+    (dict(out=None), B.PA_ERR_INVALID_ARG),
+    (dict(T=0), B.PA_ERR_INVALID_ARG),
+    (dict(mq=0), B.PA_ERR_INVALID_ARG),
+    (dict(mq=41), B.PA_ERR_INVALID_ARG),          # longer than all rows
+    (dict(mq=40, maxlen=32, mb=2), B.PA_ERR_INVALID_ARG),  # more new tokens than context
+    (dict(H=6, Hkv=4), B.PA_ERR_INVALID_ARG),
+    (dict(maxlen=129), B.PA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), B.PA_ERR_INVALID_ARG),
+    (dict(dtype=B.PA_F32), B.PA_ERR_UNSUPPORTED),  # the prefill tile runs on the matrix cores
+    (dict(D=96), B.PA_ERR_UNSUPPORTED),
+    (dict(bs=32, mb=4), B.PA_ERR_UNSUPPORTED),
+    (dict(ps=24), B.PA_ERR_INVALID_ARG),
+    (dict(ps=4112), B.PA_ERR_INVALID_ARG),
+    (dict(ps=16), B.PA_ERR_WORKSPACE),            # 8 partitions need a workspace
+    (dict(ps=16, ws=FAKE, wsb=40 * 8 * 8 * 130 * 4 - 1), B.PA_ERR_WORKSPACE),
+])
+def test_prefill_argument_checks(kw, status):
+    assert prefill(**kw) == status
+
+
+def test_prefill_workspace_sizes():
+    lib = B.lib()
+    # explicit partition: T*H*P*(D+2)*4 bytes, none for a single partition
+    assert lib.pa_prefill_workspace_bytes(40, 8, 128, 128, 16, 16) == 40 * 8 * 8 * 130 * 4
+    assert lib.pa_prefill_workspace_bytes(40, 8, 128, 128, 16, 128) == 0
+    assert lib.pa_prefill_workspace_bytes(40, 8, 128, 128, 16, 24) == 0
+    # automatic: at most one partition per 128 tokens, partials within 256 MiB
+    assert lib.pa_prefill_workspace_bytes(40, 8, 128, 4096, 16, 0) == 40 * 8 * 32 * 130 * 4
+    assert lib.pa_prefill_workspace_bytes(8192, 32, 128, 4096, 16, 0) == 0  # one split alone exceeds the cap
+    assert 0 < lib.pa_prefill_workspace_bytes(512, 32, 128, 4096, 16, 0) <= 256 << 20
+    # a context beyond one 256-block slice always needs partitions
+    assert lib.pa_prefill_workspace_bytes(1 << 20, 32, 128, 8192, 16, 0) == (1 << 20) * 32 * 2 * 130 * 4
+
+
 def test_reshape_argument_checks():
     lib = B.lib()
     f = lib.pa_reshape_and_cache

@@ -1,0 +1,208 @@
+"""GPU parity of the varlen / chunked-prefill path against the float64 oracle.
+
+Each case runs the whole path on the device - varlen slot mapping, the pool
+write of every new token, paged attention of all new tokens with the causal
+mask (and the merge when contexts are split) - and compares with the oracle
+(``paged_attention``, the plain definition) on the same seeded inputs:
+slots and pools bit-exact, attention max-abs error <= 2e-2 (bf16, fp16)
+against the unrounded float64 result.  The full-size chunked-prefill batch is
+checked on sampled rows: row i of sequence b is the decode of a context cut at
+its own position.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from paged_kv_cache_size_amd import binding as PB
+from paged_kv_cache_size_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+DEV = "cuda"
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    PB.lib()
+
+
+def bits(t):
+    return t.view(torch.int16)
+
+
+def device_inputs(pb):
+    w = pb.workload
+    return (torch.from_numpy(w.block_tables).to(DEV), torch.from_numpy(w.context_lens).to(DEV))
+
+
+def poison(pb, t):
+    """NaN into unowned blocks and every slot from each sequence's first new
+    position on: the write refills the new positions, the rest of the last
+    block stays NaN."""
+    w = pb.workload
+    ids = torch.from_numpy(w.unowned_blocks).to(DEV)
+    for key in ("k_pool", "v_pool"):
+        t[key][ids] = float("nan")
+    slots = []
+    for b in range(w.num_seqs):
+        L, n = int(w.context_lens[b]), int(pb.query_lens[b])
+        for p in range(L - n, O.num_blocks(L, w.block_size) * w.block_size):
+            slots.append(O.slot_for(w.block_tables[b], p, w.block_size))
+    s = torch.tensor(slots, device=DEV)
+    for key in ("k_pool", "v_pool"):
+        t[key].view(-1, w.num_kv_heads, w.head_dim)[s] = float("nan")
+
+
+def prefill_step(pb, t, partition_size=0):
+    w = pb.workload
+    bt, lens = device_inputs(pb)
+    slots = PB.pa_slot_mapping(bt, lens, w.block_size, query_start_loc=t["query_start_loc"],
+                               num_tokens=pb.num_tokens)
+    PB.pa_reshape_and_cache(t["key"], t["value"], t["k_pool"], t["v_pool"], slots)
+    out = PB.pa_prefill_attention(t["query"], t["k_pool"], t["v_pool"], bt, lens, t["query_start_loc"], w.scale,
+                                  pb.max_query_len, w.max_context_len, partition_size=partition_size)
+    torch.cuda.synchronize()
+    return slots, out
+
+
+def check_prefill(pb, seed=0, partition_size=0, poisoned=False):
+    w = pb.workload
+    say(f"{pb.name} seed={seed} ps={partition_size} poison={poisoned} B={w.num_seqs} T={pb.num_tokens} "
+        f"H={w.num_heads}/{w.num_kv_heads} D={w.head_dim} {w.dtype}")
+    t = W.make_prefill_tensors(pb, seed, DEV)
+    if poisoned:
+        poison(pb, t)
+    kp, vp = W.raw_numpy(t["k_pool"]), W.raw_numpy(t["v_pool"])
+    q, key, val = W.raw_numpy(t["query"]), W.raw_numpy(t["key"]), W.raw_numpy(t["value"])
+    slots, out = prefill_step(pb, t, partition_size)
+
+    ref_slots = O.slot_mapping(w.block_tables, w.context_lens, w.block_size, query_lens=pb.query_lens)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    O.reshape_and_cache(kp, key, ref_slots)
+    O.reshape_and_cache(vp, val, ref_slots)
+    assert np.array_equal(W.raw_numpy(t["k_pool"]).view(np.uint8), kp.view(np.uint8))
+    assert np.array_equal(W.raw_numpy(t["v_pool"]).view(np.uint8), vp.view(np.uint8))
+
+    ref = O.paged_attention(q, kp, vp, w.block_tables, w.context_lens, pb.query_start_loc, w.scale, w.dtype)
+    got = O.widen(W.raw_numpy(out), w.dtype)
+    assert np.isfinite(got).all()
+    err = float(np.max(np.abs(got - ref)))
+    say(f"  max abs err {err:.3e} (tol {TOL})")
+    assert err <= TOL, err
+    return out, t
+
+
+# ------------------------------------------------------------------ mixed batches and splits
+
+@pytest.mark.parametrize("ps", [0, 16, 128, 512, 4096])
+def test_mixed_varlen_batch(ps):
+    check_prefill(W.mixed_varlen_bf16(), partition_size=ps, poisoned=ps in (0, 16))
+
+
+SMALL_LENS = [1, 7, 16, 33, 100, 260]
+SMALL_QLENS = [1, 7, 5, 33, 50, 17]
+
+
+@pytest.mark.parametrize("dtype,d", [("f16", 64), ("f16", 128), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("ps", [0, 32])
+def test_dtypes_and_head_dims(dtype, d, ps):
+    pb = W.prefill_batch(SMALL_LENS, SMALL_QLENS, 8, 2, d, dtype, seed=11, extra_cols=1)
+    check_prefill(pb, seed=1, partition_size=ps, poisoned=True)
+
+
+@pytest.mark.parametrize("h,hkv", [(8, 8), (8, 4), (32, 8), (12, 2), (32, 1), (9, 1), (22, 2), (40, 40)])
+def test_head_groupings(h, hkv):
+    pb = W.prefill_batch(SMALL_LENS, SMALL_QLENS, h, hkv, 128, "bf16", seed=h * 10 + hkv)
+    check_prefill(pb, seed=2, partition_size=0)
+    check_prefill(pb, seed=2, partition_size=48)
+
+
+def test_whole_prompts_only():
+    # every sequence is a fresh prompt: n = L, the full causal triangle
+    lens = [1, 2, 15, 16, 17, 64, 129]
+    check_prefill(W.prefill_batch(lens, lens, 8, 2, 128, "bf16", seed=4), partition_size=0, poisoned=True)
+
+
+# ------------------------------------------------------------------ against the decode kernel
+
+@pytest.mark.parametrize("ps", [64, 256, 1680])
+def test_one_new_token_matches_decode_bitwise(ps):
+    # n_b = 1 everywhere is a decode step; the prefill tile then does the
+    # decode tile's arithmetic in the same order
+    w = W.make_workload("qwen1p5b_bf16")
+    t = W.make_tensors(w, 0, DEV)
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    lens = torch.from_numpy(w.context_lens).to(DEV)
+    qsl = torch.arange(w.num_seqs + 1, dtype=torch.int32, device=DEV)
+    dec = PB.pa_decode_attention(t["query"], t["k_pool"], t["v_pool"], bt, lens, w.scale, w.max_context_len,
+                                 partition_size=ps)
+    pre = PB.pa_prefill_attention(t["query"], t["k_pool"], t["v_pool"], bt, lens, qsl, w.scale, 1,
+                                  w.max_context_len, partition_size=ps)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(dec), bits(pre))
+
+
+# ------------------------------------------------------------------ properties
+
+def test_block_permutation_and_determinism():
+    pb = W.mixed_varlen_bf16(seed=3)
+    w = pb.workload
+    t = W.make_prefill_tensors(pb, 0, DEV)
+    bt, lens = device_inputs(pb)
+    run = lambda kp, vp, tables, ps: PB.pa_prefill_attention(  # noqa: E731
+        t["query"], kp, vp, tables, lens, t["query_start_loc"], w.scale, pb.max_query_len, w.max_context_len,
+        partition_size=ps)
+    base = run(t["k_pool"], t["v_pool"], bt, 256)
+    again = run(t["k_pool"], t["v_pool"], bt, 256)
+    perm = torch.from_numpy(np.random.default_rng(9).permutation(w.num_blocks)).to(DEV)
+    kp2, vp2 = torch.empty_like(t["k_pool"]), torch.empty_like(t["v_pool"])
+    kp2[perm], vp2[perm] = t["k_pool"], t["v_pool"]
+    moved = run(kp2, vp2, perm[bt.long()].to(torch.int32), 256)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(base), bits(again))
+    assert torch.equal(bits(base), bits(moved))
+
+
+# ------------------------------------------------------------------ full size
+
+def bench_partition_size(pb):
+    return 0  # the automatic choice, as the benchmark launches it
+
+
+def test_chunked_prefill_llama_full_size_sampled():
+    pb = W.chunked_prefill_llama_bf16()
+    w = pb.workload
+    say(f"{pb.name} full size, sampled rows")
+    t = W.make_prefill_tensors(pb, 0, DEV)
+    slots, out = prefill_step(pb, t, bench_partition_size(pb))
+    ref_slots = O.slot_mapping(w.block_tables, w.context_lens, w.block_size, query_lens=pb.query_lens)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    assert torch.isfinite(out.float()).all()
+    rng = np.random.default_rng(5)
+    qsl = pb.query_start_loc
+    worst = 0.0
+    for b in sorted(rng.choice(w.num_seqs, 3, replace=False).tolist()):
+        L, n = int(w.context_lens[b]), int(pb.query_lens[b])
+        nb = O.num_blocks(L, w.block_size)
+        ids = torch.tensor(w.block_tables[b, :nb].astype(np.int64), device=DEV)
+        kp, vp = W.raw_numpy(t["k_pool"][ids]), W.raw_numpy(t["v_pool"][ids])
+        table = list(range(nb))
+        for i in (0, 1, n // 2, n - 1):
+            row = int(qsl[b]) + i
+            ref = O.decode_attention(W.raw_numpy(t["query"][row:row + 1]), kp, vp, [table], [L - n + i + 1],
+                                     w.scale, w.dtype)
+            got = O.widen(W.raw_numpy(out[row:row + 1]), w.dtype)
+            worst = max(worst, float(np.max(np.abs(got - ref))))
+    say(f"  sampled rows: max abs err {worst:.3e}")
+    assert worst <= TOL, worst
