@@ -7,6 +7,12 @@ sequence's context (partition kernel + merge kernel).  Default workload: the
 Llama-style GQA layer, 256 sequences x 4096 tokens, 32 query / 8 KV heads,
 head_dim 128, bf16, block 16 (4 GiB of K/V read per step).
 
+``--workload chunked_prefill_llama_bf16`` (or another varlen batch) times the
+prefill form instead: varlen slot mapping, the pool write of every new token
+and causal paged attention of all new tokens, with the roofline taken against
+the dense matrix-core peak (the attention flops per step / the attention
+kernel's time).
+
 Prints ONE JSON line.  ``value`` = decode tokens/s (one new token per
 sequence per step) with every input resident in HBM; ``roofline`` = KV bytes
 the partition kernel must read per launch / its average launch time, timed
@@ -25,9 +31,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}  # MI355X dense matrix-core peaks, published
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_size_amd", "csrc", "pa_kernels.hip")
 METRIC = "paged decode attention tokens/s and KV-read GB/s (% of MI355X HBM peak)"
+PREFILL_METRIC = "chunked-prefill paged attention new tokens/s and TFLOP/s (% of MI355X dense MFMA peak)"
 
 
 def parse():
@@ -46,14 +54,20 @@ def parse():
 
 
 def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel sources (the .hip files and the device header)."""
+    h = hashlib.sha256()
+    csrc = os.path.dirname(KERNEL_SRC)
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith(".hip") or name == "pa_device.h":
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def load_traffic(workload):
-    """HBM bytes per partition-kernel launch from committed counter runs, or
-    None when the kernel source changed since they were taken."""
-    path = os.path.join(PROFILES, f"decode_partition_{workload}_traffic.json")
+def load_traffic(workload, prefix="decode_partition"):
+    """HBM bytes per launch of the dominant kernel from committed counter
+    runs, or None when the kernel source changed since they were taken."""
+    path = os.path.join(PROFILES, f"{prefix}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -116,6 +130,136 @@ def cpu_baseline(w, t, seconds):
                       f"slot mapping + pool write + float64 attention, {dt:.1f} s"}
 
 
+def prefill_cpu_baseline(pb, t, seconds):
+    """The oracle on whole sequences of the batch (every new row of each)."""
+    import time as _t
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from paged_kv_cache_size_amd import workloads as W
+
+    w = pb.workload
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    qsl = pb.query_start_loc
+
+    def run(seqs):
+        dt = 0.0
+        for b in seqs:
+            L = int(w.context_lens[b])
+            nb = O.num_blocks(L, w.block_size)
+            ids = torch.tensor(w.block_tables[b, :nb].astype(np.int64), device="cuda")
+            kp, vp = W.raw_numpy(t["k_pool"][ids]), W.raw_numpy(t["v_pool"][ids])
+            q = W.raw_numpy(t["query"][int(qsl[b]):int(qsl[b + 1])])
+            t0 = _t.perf_counter()
+            O.paged_attention(q, kp, vp, [list(range(nb))], [L], [0, q.shape[0]], w.scale, w.dtype)
+            dt += _t.perf_counter() - t0
+        return dt
+
+    one = run([0])
+    n = int(max(1, min(w.num_seqs, seconds / max(one, 1e-6))))
+    dt = one + (run(list(range(1, n))) if n > 1 else 0.0)
+    rows = int(pb.query_lens[:n].sum())
+    return {"value": rows / dt, "unit": "new tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} of {w.num_seqs} sequences ({rows} new rows, whole contexts) of {pb.name}; "
+                      f"float64 causal attention, {dt:.1f} s"}
+
+
+def main_prefill(args):
+    import torch
+
+    from paged_kv_cache_size_amd import binding as PB
+    from paged_kv_cache_size_amd import workloads as W
+
+    PB.lib()
+    pb = W.PREFILL_BUILDERS[args.workload](seed=args.seed)
+    w = pb.workload
+    t = W.make_prefill_tensors(pb, seed=args.seed, device="cuda")
+    bt = torch.from_numpy(w.block_tables).cuda()
+    lens = torch.from_numpy(w.context_lens).cuda()
+    T, H, D = t["query"].shape
+    ps = args.partition_size
+    ws_bytes = PB.pa_prefill_workspace_bytes(T, H, D, w.max_context_len, w.block_size, ps)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(t["query"])
+    slots = torch.empty(T, dtype=torch.int64, device="cuda")
+    base = None if args.no_cpu_baseline else prefill_cpu_baseline(pb, t, args.cpu_seconds)
+
+    def k_slot():
+        PB.pa_slot_mapping(bt, lens, w.block_size, query_start_loc=t["query_start_loc"], num_tokens=T, out=slots)
+
+    def k_write():
+        PB.pa_reshape_and_cache(t["key"], t["value"], t["k_pool"], t["v_pool"], slots)
+
+    def k_attn():
+        PB.pa_prefill_attention(t["query"], t["k_pool"], t["v_pool"], bt, lens, t["query_start_loc"], w.scale,
+                                pb.max_query_len, w.max_context_len, out=out, workspace=ws, partition_size=ps)
+
+    stages = [k_slot, k_write, k_attn]
+    ms_per_step, per_kernel_ms, wall = time_stages(stages, args.steps, args.warmup)
+    flops = pb.attention_flops()
+    attn_ms = per_kernel_ms[2]
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    rec = {
+        "metric": PREFILL_METRIC, "value": T / (ms_per_step * 1e-3), "unit": "new tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "accumulate": "f32", "data": "synthetic",
+        "config": {"workload": pb.name, "num_seqs": w.num_seqs, "new_tokens": T, "max_query_len": pb.max_query_len,
+                   "context_lens_sum": int(w.context_lens.sum()), "max_context_len": w.max_context_len,
+                   "num_heads": H, "num_kv_heads": w.num_kv_heads, "head_dim": D, "block_size": w.block_size,
+                   "num_blocks": w.num_blocks, "partition_size": ps, "description": pb.description},
+        "attention_flops_per_step": flops,
+        "kernel_us": {"slot_mapping": per_kernel_ms[0] * 1e3, "reshape_and_cache": per_kernel_ms[1] * 1e3,
+                      "prefill_attention": attn_ms * 1e3},
+        "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": load_traffic(pb.name, "prefill_attention")},
+        "kv_read_bytes_per_step": pb.kv_read_bytes(),
+        "cpu_baseline": base,
+        "wall_s_timed": wall,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def time_stages(stages, steps, warmup):
+    """Whole-step time (events around all launches) and per-stage times
+    (events between launches), on torch's current stream where every call
+    is enqueued."""
+    import torch
+
+    def step():
+        for f in stages:
+            f()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = e0.elapsed_time(e1) / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evs[i][0].record()
+        for j, f in enumerate(stages):
+            f()
+            evs[i][j + 1].record()
+    torch.cuda.synchronize()
+    per = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps for j in range(len(stages))]
+    return ms_per_step, per, wall
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -133,6 +277,9 @@ def main():
     from paged_kv_cache_size_amd import binding as PB
     from paged_kv_cache_size_amd import workloads as W
 
+    if args.workload in W.PREFILL_BUILDERS:
+        main_prefill(args)
+        return
     PB.lib()  # fail loudly before any work if the HIP library is missing
     w = W.make_workload(args.workload, seed=args.seed)
     t = W.make_tensors(w, seed=args.seed, device="cuda")
@@ -167,38 +314,7 @@ def main():
         PB.pa_decode_combine(out, lens, w.max_context_len, ps, workspace=ws)
 
     stages = [k_slot, k_write, k_part, k_comb]
-
-    def step():
-        for f in stages:
-            f()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # whole-step throughput
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-
-    # per-kernel launch times, events between the launches
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        evs[i][0].record()
-        for j, f in enumerate(stages):
-            f()
-            evs[i][j + 1].record()
-    torch.cuda.synchronize()
-    per_kernel_ms = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
-                     for j in range(len(stages))]
+    ms_per_step, per_kernel_ms, wall = time_stages(stages, args.steps, args.warmup)
 
     kv_bytes = w.kv_read_bytes()
     part_ms = per_kernel_ms[2]
