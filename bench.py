@@ -11,7 +11,8 @@ head_dim 128, bf16, block 16 (4 GiB of K/V read per step).
 prefill form instead: varlen slot mapping, the pool write of every new token
 and causal paged attention of all new tokens, with the roofline taken against
 the dense matrix-core peak (the attention flops per step / the attention
-kernel's time).
+kernel's time).  ``--workload cow_copy_llama_bf16`` times the copy-on-write
+block copy (8192 whole-block copies in both pools of the Llama-style layer).
 
 Prints ONE JSON line.  ``value`` = decode tokens/s (one new token per
 sequence per step) with every input resident in HBM; ``roofline`` = KV bytes
@@ -36,6 +37,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_size_amd", "csrc", "pa_kernels.hip")
 METRIC = "paged decode attention tokens/s and KV-read GB/s (% of MI355X HBM peak)"
 PREFILL_METRIC = "chunked-prefill paged attention new tokens/s and TFLOP/s (% of MI355X dense MFMA peak)"
+COPY_METRIC = "copy-on-write block copies/s and copy GB/s (% of MI355X HBM peak)"
 
 
 def parse():
@@ -226,6 +228,54 @@ def main_prefill(args):
     print(json.dumps(rec), flush=True)
 
 
+def main_copy(args):
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from paged_kv_cache_size_amd import binding as PB
+    from paged_kv_cache_size_amd import workloads as W
+
+    PB.lib()
+    cb = W.COPY_BUILDERS[args.workload](seed=args.seed)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed)
+    shape = (cb.num_blocks, cb.block_size, cb.num_kv_heads, cb.head_dim)
+    kp = W._randn(shape, cb.dtype, g, "cuda")
+    vp = W._randn(shape, cb.dtype, g, "cuda")
+    src, dst = torch.from_numpy(cb.src).cuda(), torch.from_numpy(cb.dst).cuda()
+    base = None
+    if not args.no_cpu_baseline:
+        n = min(len(cb.src), 2048)
+        pool = W.raw_numpy(kp)
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < args.cpu_seconds / 2:
+            O.copy_blocks(pool, cb.src[:n], cb.dst[:n])
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        base = {"value": 2 * n / dt, "unit": "block copies/s", "cores": 1, "kind": "oracle",
+                "sample": f"{n} of {len(cb.src)} pairs of {cb.name}, K and V pools, {reps} repetitions"}
+        del pool
+    ms, per, wall = time_stages([lambda: PB.pa_copy_blocks(kp, vp, src, dst)], args.steps, args.warmup)
+    nbytes = cb.copy_bytes()
+    achieved = nbytes / (per[0] * 1e-3) / 1e9
+    rec = {
+        "metric": COPY_METRIC, "value": 2 * len(cb.src) / (ms * 1e-3), "unit": "block copies/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cb.dtype, "data": "synthetic",
+        "config": {"workload": cb.name, "num_pairs": int(len(cb.src)), "num_blocks": cb.num_blocks,
+                   "block_size": cb.block_size, "num_kv_heads": cb.num_kv_heads, "head_dim": cb.head_dim,
+                   "block_bytes": cb.block_bytes, "description": cb.description},
+        "copy_bytes_per_step": nbytes,
+        "kernel_us": {"copy_blocks": per[0] * 1e3},
+        "roofline": {"bound": "hbm", "kernel": "copy_blocks_kernel", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(cb.name, "copy_blocks")},
+        "cpu_baseline": base, "wall_s_timed": wall,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def time_stages(stages, steps, warmup):
     """Whole-step time (events around all launches) and per-stage times
     (events between launches), on torch's current stream where every call
@@ -279,6 +329,9 @@ def main():
 
     if args.workload in W.PREFILL_BUILDERS:
         main_prefill(args)
+        return
+    if args.workload in W.COPY_BUILDERS:
+        main_copy(args)
         return
     PB.lib()  # fail loudly before any work if the HIP library is missing
     w = W.make_workload(args.workload, seed=args.seed)

@@ -56,7 +56,8 @@ typedef enum pa_status {
   PA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, inconsistent shape */
   PA_ERR_UNSUPPORTED = 2, /* dtype / head_dim / block_size outside the compiled set */
   PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
-  PA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+  PA_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  PA_ERR_NO_BLOCKS = 5    /* the block pool has too few free blocks; nothing changed */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -281,6 +282,118 @@ int pa_prefill_attention(void* out, const void* query, const void* k_pool, const
  * most the automatic choice can use); 0 for invalid sizes. */
 size_t pa_prefill_workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t block_size, int32_t partition_size);
+
+/*
+ * Whole-block copies inside both pools: for every i < num_pairs, block
+ * dst_blocks[i] of k_pool and of v_pool becomes a copy of block src_blocks[i]
+ * (block_size * num_kv_heads * head_dim elements each), the copy-on-write step
+ * of a forked sequence that writes into a shared, partly filled block
+ * ("KV cache: capacity derivation, paging and reclamation", section on shared
+ * prefixes and reference counts).
+ *   src_blocks, dst_blocks  int64 [num_pairs], device memory.  The dst ids
+ *                           must be distinct and none may be a src id (the
+ *                           copies run concurrently); ids outside
+ *                           [0, num_blocks) skip their pair.
+ * num_pairs = 0 enqueues nothing.  Errors: INVALID_ARG (null pools, null id
+ * arrays with num_pairs > 0, non-positive sizes), UNSUPPORTED (dtype), HIP.
+ */
+int pa_copy_blocks(void* k_pool, void* v_pool, const int64_t* src_blocks, const int64_t* dst_blocks,
+                   int64_t num_pairs, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                   int64_t num_blocks, pa_dtype dtype, void* stream);
+
+/*
+ * Host-side block pool (host memory only; no HIP call, no device memory).
+ * A fixed set of num_blocks physical blocks with a FIFO free queue and a
+ * reference count per block (handbook "分页 KV Cache", section "块表与 slot
+ * mapping": blocks leave from the head of the free queue, an allocation that
+ * cannot be met changes nothing, freed blocks rejoin at the tail), and
+ * sequences built on it: an ordered block list and a token count.  A pool and
+ * its sequences belong to one thread at a time.
+ *
+ * pa_block_pool_create: free_order NULL hands blocks out as 0, 1, ...;
+ *   otherwise a permutation of 0..num_blocks-1 giving the initial queue.
+ *   NULL for invalid arguments or when host memory runs out.
+ * pa_block_pool_allocate: n blocks (reference count 1 each) into blocks[0..n),
+ *   or NO_BLOCKS and nothing changed.
+ * pa_block_pool_free: drops one reference per listed block; a block reaching
+ *   zero rejoins the free queue, in list order.  INVALID_ARG (nothing
+ *   changed) if an id is out of range or listed more often than referenced.
+ * pa_block_pool_num_free / _ref_count: -1 for a NULL pool or an id out of range.
+ *
+ * pa_seq_create: a new, empty sequence handle (handles are reused after release).
+ * pa_seq_fork: a child sharing every block of the parent (one more reference
+ *   each) and its token count (parallel sampling, beam search).
+ * pa_seq_append: num_tokens more tokens: new blocks as the last one fills; if
+ *   the last block is partly filled and shared, it is first replaced by a
+ *   fresh block and (*cow_src, *cow_dst) report the pair to copy on the device
+ *   (pa_copy_blocks) before writing; otherwise both are -1.  NO_BLOCKS if the
+ *   pool cannot supply every block the call needs: nothing changed.
+ * pa_seq_release: drops the sequence's references (in block order); the handle
+ *   becomes invalid.
+ * pa_seq_length: tokens, or -1 for an invalid handle.
+ * pa_seq_block_table: the block ids into table[0..*num_blocks); WORKSPACE if
+ *   *num_blocks > max_blocks (table untouched, *num_blocks still set).
+ */
+typedef struct pa_block_pool pa_block_pool;
+pa_block_pool* pa_block_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order);
+void pa_block_pool_destroy(pa_block_pool* pool);
+int32_t pa_block_pool_num_free(const pa_block_pool* pool);
+int32_t pa_block_pool_ref_count(const pa_block_pool* pool, int32_t block);
+int pa_block_pool_allocate(pa_block_pool* pool, int32_t n, int32_t* blocks);
+int pa_block_pool_free(pa_block_pool* pool, const int32_t* blocks, int32_t n);
+int pa_seq_create(pa_block_pool* pool, int32_t* seq);
+int pa_seq_fork(pa_block_pool* pool, int32_t parent, int32_t* child);
+int pa_seq_append(pa_block_pool* pool, int32_t seq, int64_t num_tokens, int32_t* cow_src, int32_t* cow_dst);
+int pa_seq_release(pa_block_pool* pool, int32_t seq);
+int64_t pa_seq_length(const pa_block_pool* pool, int32_t seq);
+int pa_seq_block_table(const pa_block_pool* pool, int32_t seq, int32_t* table, int32_t max_blocks,
+                       int32_t* num_blocks);
+
+/*
+ * Decode with shared prompt prefixes read once per group (cascade): the
+ * sequences group_start[g] .. group_start[g+1]-1 (consecutive; the groups
+ * cover all num_seqs sequences) share their first prefix_lens[g] tokens -
+ * whole blocks, the same ids in every member's table (forks of one prompt,
+ * parallel sampling: "KV cache: capacity derivation, paging and reclamation",
+ * section on shared prefixes; xxqk.cn PagedAttention article, parallel
+ * sampling).  seq_prefix_lens[b] repeats its group's prefix length.
+ * A prefix pass reads each group's prefix blocks once and scores them against
+ * every member's query; a suffix pass reads each sequence's blocks past the
+ * prefix; a merge combines the two softmax partials per (sequence, head).
+ * The result equals pa_decode_attention's within rounding.
+ *   group_start int32 [num_groups + 1], prefix_lens int32 [num_groups],
+ *   seq_prefix_lens int32 [num_seqs]: device memory (pa_shared_prefix_groups
+ *   computes them on the host from the tables).
+ *   max_group_size, max_prefix_len: host bounds (max_prefix_len a multiple of
+ *   block_size, <= max_context_len).
+ *   workspace: pa_shared_prefix_workspace_bytes(...) bytes, always needed.
+ * fp16 / bf16 only.  Errors as pa_decode_attention.
+ */
+int pa_decode_attention_shared_prefix(void* out, const void* query, const void* k_pool, const void* v_pool,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      const int32_t* group_start, const int32_t* prefix_lens,
+                                      const int32_t* seq_prefix_lens, int32_t num_seqs, int32_t num_groups,
+                                      int32_t max_group_size, int32_t num_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                      int32_t max_context_len, int32_t max_prefix_len, float scale,
+                                      pa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t pa_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                        int32_t max_context_len, int32_t max_prefix_len);
+
+/*
+ * The groups of shared prefixes in a decode batch, from HOST copies of the
+ * block tables and context lengths: maximal runs of consecutive sequences
+ * whose tables share at least min_prefix_blocks leading blocks.  A group's
+ * prefix is the whole blocks all members share before any member's last token;
+ * a run of one sequence is a group with prefix 0.  Outputs (host, caller
+ * allocated): group_start [num_seqs + 1], prefix_lens [num_seqs],
+ * seq_prefix_lens [num_seqs], and the counts and bounds the cascade call takes.
+ */
+int pa_shared_prefix_groups(const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_blocks_per_seq, int32_t block_size, int32_t min_prefix_blocks,
+                            int32_t* group_start, int32_t* prefix_lens, int32_t* seq_prefix_lens,
+                            int32_t* num_groups, int32_t* max_group_size, int32_t* max_prefix_len);
 
 /* Static, human-readable name of a pa_status value. */
 const char* pa_status_string(int status);

@@ -120,6 +120,20 @@ def reshape_and_cache(pool, rows, slots):
     return pool
 
 
+def copy_blocks(pool, src_blocks, dst_blocks):
+    """Copy-on-write at block granularity: block ``dst_blocks[i]`` of the pool
+    becomes a bit copy of block ``src_blocks[i]``, for every i in order
+    ("KV cache: capacity derivation, paging and reclamation", section on
+    shared prefixes and reference counts: the fork that writes into a shared,
+    partly filled block first gets its own copy).  Works in place on ``pool``
+    ``[NB, BS, H_kv, D]`` and returns it.
+    """
+    assert len(src_blocks) == len(dst_blocks)
+    for s, d in zip(src_blocks, dst_blocks):
+        pool[int(d)] = pool[int(s)].copy()
+    return pool
+
+
 def gather(pool, block_table, seq_len):
     """The first ``seq_len`` tokens of one sequence, ``[seq_len, H_kv, D]``.
 

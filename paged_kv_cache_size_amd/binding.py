@@ -17,7 +17,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PA_LIBRARY", os.path.join(HERE, "libpa.so"))
 
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_NO_BLOCKS = range(6)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 
 # Every symbol pa.h declares, with (restype, argtypes).
@@ -40,6 +40,24 @@ SIGNATURES = {
     "pa_prefill_attention": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                             _I32, _I32, _F32, ctypes.c_int, _P, _SZ, _I32, _P]),
     "pa_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I64, ctypes.c_int, _P]),
+    "pa_block_pool_create": (_P, [_I32, _I32, _P]),
+    "pa_block_pool_destroy": (None, [_P]),
+    "pa_block_pool_num_free": (_I32, [_P]),
+    "pa_block_pool_ref_count": (_I32, [_P, _I32]),
+    "pa_block_pool_allocate": (ctypes.c_int, [_P, _I32, _P]),
+    "pa_block_pool_free": (ctypes.c_int, [_P, _P, _I32]),
+    "pa_seq_create": (ctypes.c_int, [_P, _P]),
+    "pa_seq_fork": (ctypes.c_int, [_P, _I32, _P]),
+    "pa_seq_append": (ctypes.c_int, [_P, _I32, _I64, _P, _P]),
+    "pa_seq_release": (ctypes.c_int, [_P, _I32]),
+    "pa_seq_length": (_I64, [_P, _I32]),
+    "pa_seq_block_table": (ctypes.c_int, [_P, _I32, _P, _I32, _P]),
+    "pa_decode_attention_shared_prefix": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                                         _I32, _I32, _I32, _I32, _I32, _I32, _F32, ctypes.c_int,
+                                                         _P, _SZ, _P]),
+    "pa_shared_prefix_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "pa_shared_prefix_groups": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -275,6 +293,161 @@ def pa_prefill_attention(query, k_pool, v_pool, block_tables, context_lens, quer
         int(partition_size), _stream(query))
     _check(rc, "pa_prefill_attention")
     return out
+
+
+def pa_copy_blocks(k_pool, v_pool, src_blocks, dst_blocks):
+    """Copy whole blocks src -> dst in both pools (int64 device id tensors)."""
+    torch = _torch()
+    nb, bs, hkv, d = k_pool.shape
+    if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise ValueError("k_pool and v_pool differ")
+    n = int(src_blocks.numel())
+    if dst_blocks.numel() != n:
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    rc = lib().pa_copy_blocks(_dev(k_pool, "k_pool", ndim=4), _dev(v_pool, "v_pool", ndim=4),
+                              _dev(src_blocks, "src_blocks", torch.int64, 1) if n else None,
+                              _dev(dst_blocks, "dst_blocks", torch.int64, 1) if n else None, n, bs, hkv, d, nb,
+                              pa_dtype(k_pool), _stream(k_pool))
+    _check(rc, "pa_copy_blocks")
+
+
+class SharedPrefixGroups:
+    """Groups of consecutive sequences sharing leading blocks (host arrays)."""
+
+    def __init__(self, group_start, prefix_lens, seq_prefix_lens, max_group_size, max_prefix_len):
+        self.group_start, self.prefix_lens, self.seq_prefix_lens = group_start, prefix_lens, seq_prefix_lens
+        self.max_group_size, self.max_prefix_len = int(max_group_size), int(max_prefix_len)
+
+    @property
+    def num_groups(self) -> int:
+        return int(self.prefix_lens.shape[0])
+
+
+def pa_shared_prefix_groups(block_tables, context_lens, block_size: int, min_prefix_blocks: int = 1):
+    """Find the shared-prefix groups from host (numpy) tables and lengths."""
+    import numpy as np
+    bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    B, mb = bt.shape
+    gs = np.zeros(B + 1, np.int32)
+    pl = np.zeros(B, np.int32)
+    spl = np.zeros(B, np.int32)
+    ng, gmax, pmax = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    p = lambda a: ctypes.c_void_p(a.ctypes.data)  # noqa: E731
+    rc = lib().pa_shared_prefix_groups(p(bt), p(lens), B, mb, int(block_size), int(min_prefix_blocks), p(gs), p(pl),
+                                       p(spl), ctypes.byref(ng), ctypes.byref(gmax), ctypes.byref(pmax))
+    _check(rc, "pa_shared_prefix_groups")
+    n = ng.value
+    return SharedPrefixGroups(gs[:n + 1].copy(), pl[:n].copy(), spl, gmax.value, pmax.value)
+
+
+def pa_decode_attention_shared_prefix(query, k_pool, v_pool, block_tables, context_lens, groups, scale: float,
+                                      max_context_len: int, out=None, workspace=None, device_groups=None):
+    """Cascade decode: shared prefixes read once per group.  ``groups`` is a
+    SharedPrefixGroups; ``device_groups`` optionally its three arrays already
+    on the device (group_start, prefix_lens, seq_prefix_lens)."""
+    torch = _torch()
+    B, H, D = query.shape
+    nb, bs, hkv, d2 = k_pool.shape
+    if d2 != D or k_pool.shape != v_pool.shape or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("shapes do not match")
+    if device_groups is None:
+        device_groups = tuple(torch.from_numpy(x).to(query.device)
+                              for x in (groups.group_start, groups.prefix_lens, groups.seq_prefix_lens))
+    gs, pl, spl = device_groups
+    if out is None:
+        out = torch.empty_like(query)
+    need = int(lib().pa_shared_prefix_workspace_bytes(B, H, D, int(max_context_len), groups.max_prefix_len))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=query.device)
+    rc = lib().pa_decode_attention_shared_prefix(
+        _dev(out, "out", query.dtype, 3), _dev(query, "query", ndim=3), _dev(k_pool, "k_pool", ndim=4),
+        _dev(v_pool, "v_pool", ndim=4), _dev(block_tables, "block_tables", torch.int32, 2),
+        _dev(context_lens, "context_lens", torch.int32, 1), _dev(gs, "group_start", torch.int32, 1),
+        _dev(pl, "prefix_lens", torch.int32, 1), _dev(spl, "seq_prefix_lens", torch.int32, 1), B, groups.num_groups,
+        groups.max_group_size, H, hkv, D, bs, block_tables.shape[1], int(max_context_len), groups.max_prefix_len,
+        float(scale), pa_dtype(query), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(query))
+    _check(rc, "pa_decode_attention_shared_prefix")
+    return out
+
+
+class BlockManager:
+    """The library's host block pool and its sequences (pa_block_pool_*, pa_seq_*)."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        self._order = None
+        ptr = None
+        if free_order is not None:
+            import numpy as np
+            self._order = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+            if self._order.shape != (num_blocks,):
+                raise ValueError("free_order must list every block once")
+            ptr = ctypes.c_void_p(self._order.ctypes.data)
+        self._lib = lib()
+        self._h = self._lib.pa_block_pool_create(int(num_blocks), int(block_size), ptr)
+        if not self._h:
+            raise PAError(PA_ERR_INVALID_ARG, "pa_block_pool_create")
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pa_block_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def num_free(self) -> int:
+        return int(self._lib.pa_block_pool_num_free(self._h))
+
+    def ref_count(self, block: int) -> int:
+        return int(self._lib.pa_block_pool_ref_count(self._h, int(block)))
+
+    def allocate(self, n: int):
+        """n block ids, or None when the pool is short (nothing changes)."""
+        buf = (ctypes.c_int32 * max(int(n), 1))()
+        rc = self._lib.pa_block_pool_allocate(self._h, int(n), buf)
+        if rc == PA_ERR_NO_BLOCKS:
+            return None
+        _check(rc, "pa_block_pool_allocate")
+        return list(buf[:n])
+
+    def free(self, blocks) -> None:
+        arr = (ctypes.c_int32 * max(len(blocks), 1))(*[int(b) for b in blocks])
+        _check(self._lib.pa_block_pool_free(self._h, arr, len(blocks)), "pa_block_pool_free")
+
+    def new_seq(self) -> int:
+        h = ctypes.c_int32()
+        _check(self._lib.pa_seq_create(self._h, ctypes.byref(h)), "pa_seq_create")
+        return h.value
+
+    def fork(self, seq: int) -> int:
+        h = ctypes.c_int32()
+        _check(self._lib.pa_seq_fork(self._h, int(seq), ctypes.byref(h)), "pa_seq_fork")
+        return h.value
+
+    def append(self, seq: int, num_tokens: int):
+        """Grow a sequence; returns the copy-on-write pair (src, dst) or None."""
+        src, dst = ctypes.c_int32(), ctypes.c_int32()
+        _check(self._lib.pa_seq_append(self._h, int(seq), int(num_tokens), ctypes.byref(src), ctypes.byref(dst)),
+               "pa_seq_append")
+        return None if src.value < 0 else (src.value, dst.value)
+
+    def release(self, seq: int) -> None:
+        _check(self._lib.pa_seq_release(self._h, int(seq)), "pa_seq_release")
+
+    def length(self, seq: int) -> int:
+        return int(self._lib.pa_seq_length(self._h, int(seq)))
+
+    def block_table(self, seq: int):
+        n = ctypes.c_int32()
+        rc = self._lib.pa_seq_block_table(self._h, int(seq), None, 0, ctypes.byref(n))
+        if rc not in (PA_OK, PA_ERR_WORKSPACE):
+            _check(rc, "pa_seq_block_table")
+        buf = (ctypes.c_int32 * max(n.value, 1))()
+        _check(self._lib.pa_seq_block_table(self._h, int(seq), buf, n.value, ctypes.byref(n)), "pa_seq_block_table")
+        return list(buf[:n.value])
 
 
 def _decode_common(query, k_pool, v_pool, block_tables, context_lens, out):

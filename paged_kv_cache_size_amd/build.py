@@ -50,9 +50,12 @@ def _run(cmd, verbose):
 def build(verbose: bool = True) -> str:
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="pa_build_") as tmp:
-        host_o = os.path.join(tmp, "pa_host.o")
-        _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
-              os.path.join(CSRC, "pa_host.cpp"), "-o", host_o], verbose)
+        host_objs = []
+        for src in sorted(f for f in os.listdir(CSRC) if f.endswith(".cpp")):
+            obj = os.path.join(tmp, src[:-4] + ".o")
+            _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
+                  os.path.join(CSRC, src), "-o", obj], verbose)
+            host_objs.append(obj)
         dev_objs = []
         for src in sorted(f for f in os.listdir(CSRC) if f.endswith(".hip")):
             obj = os.path.join(tmp, src[:-4] + ".o")
@@ -60,7 +63,7 @@ def build(verbose: bool = True) -> str:
                   "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
             dev_objs.append(obj)
         out_tmp = LIB + ".tmp"
-        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", host_o, *dev_objs, "-o", out_tmp], verbose)
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *host_objs, *dev_objs, "-o", out_tmp], verbose)
         os.replace(out_tmp, LIB)
     return LIB
 

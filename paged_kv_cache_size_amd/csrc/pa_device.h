@@ -268,6 +268,7 @@ __device__ __forceinline__ void merge_partials(uint8_t* out_row, const float* __
   for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[p].x);
 #pragma unroll
   for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
+  if (M == -INFINITY) M = 0.f;  // every partial empty: weights 2^-inf = 0, output 0
   float den = 0.f;
   for (int p = lane; p < np; p += 64) den += ml[p].y * fast_exp2(ml[p].x - M);
 #pragma unroll

@@ -273,6 +273,27 @@ int check_prefill(const void* out, const void* query, const void* k_pool, const 
   return PA_OK;
 }
 
+int shared_prefix_slots(int max_context_len, int max_prefix_len) {
+  const int p1 = num_partitions(max_prefix_len > 0 ? max_prefix_len : 1, kSharedPrefixPartition);
+  const int p2 = num_partitions(max_context_len, kSharedPrefixPartition);
+  return p1 + p2;
+}
+
+int check_shared_prefix(const void* out, const void* query, const void* k_pool, const void* v_pool,
+                        const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_start,
+                        const int32_t* prefix_lens, const int32_t* seq_prefix_lens, const PrefillShape& s,
+                        int num_groups, int max_group_size, int max_prefix_len, float scale) {
+  if (!group_start || !prefix_lens || !seq_prefix_lens) return PA_ERR_INVALID_ARG;
+  const int rc = check_decode(out, query, k_pool, v_pool, block_tables, context_lens, s.d, scale);
+  if (rc != PA_OK) return rc;
+  if (num_groups <= 0 || num_groups > s.d.num_seqs || max_group_size <= 0 || max_group_size > s.d.num_seqs)
+    return PA_ERR_INVALID_ARG;
+  if (max_prefix_len < 0 || max_prefix_len > s.d.max_context_len || max_prefix_len % s.d.block_size != 0)
+    return PA_ERR_INVALID_ARG;
+  if (s.d.dtype == PA_F32) return PA_ERR_UNSUPPORTED;  // both passes run the MFMA prefill tile
+  return PA_OK;
+}
+
 int prefill_tiles(const PrefillShape& s, const DecodeGrid& g) {
   return (int)(((int64_t)s.max_query_len * g.repc + 15) / 16);
 }
@@ -359,6 +380,19 @@ int check_reshape(const void* key, const void* value, const void* k_pool, const 
   return PA_OK;
 }
 
+int check_copy_blocks(const void* k_pool, const void* v_pool, const int64_t* src, const int64_t* dst,
+                      int64_t num_pairs, int block_size, int num_kv_heads, int head_dim, int64_t num_blocks,
+                      int dtype) {
+  if (!k_pool || !v_pool || num_pairs < 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_blocks <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_pairs > 0 && (!src || !dst)) return PA_ERR_INVALID_ARG;
+  if (num_pairs > 0x7fffffffLL) return PA_ERR_INVALID_ARG;  // one grid row per pair
+  if (elem_bytes(dtype) == 0) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)block_size * num_kv_heads * head_dim > (int64_t)1 << 30) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
 int check_slot_mapping(const int64_t* slot_mapping, const int32_t* block_tables,
                        const int32_t* context_lens, const int32_t* query_start_loc, int num_seqs,
                        int max_blocks_per_seq, int block_size, int64_t num_tokens) {
@@ -379,6 +413,7 @@ extern "C" const char* pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: dtype, head_dim or block_size not compiled in";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime or launch error";
+    case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: not enough free blocks in the pool";
     default: return "unknown pa_status";
   }
 }

@@ -96,12 +96,25 @@ int prefill_partition_bounds(const PrefillShape& s, int* min_parts, int* max_par
 // whole waves of `slots` workgroups, plus the merge).  Negated pa_status on error.
 int prefill_partition_size(const PrefillShape& s, int requested, int num_cus, int wg_per_cu);
 
+// Shared-prefix (cascade) decode: partitions of both passes, and the partial
+// slots per (row, head): the prefix's partitions, then the suffix's.
+constexpr int kSharedPrefixPartition = 1024;
+int shared_prefix_slots(int max_context_len, int max_prefix_len);
+int check_shared_prefix(const void* out, const void* query, const void* k_pool, const void* v_pool,
+                        const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_start,
+                        const int32_t* prefix_lens, const int32_t* seq_prefix_lens, const PrefillShape& s,
+                        int num_groups, int max_group_size, int max_prefix_len, float scale);
+
 int check_combine(const void* out, const int32_t* context_lens, int num_seqs, int num_heads, int head_dim,
                   int max_context_len, int partition_size, int dtype);
 
 int check_reshape(const void* key, const void* value, const void* k_pool, const void* v_pool,
                   const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads, int head_dim,
                   int block_size, int64_t num_blocks, int dtype);
+
+int check_copy_blocks(const void* k_pool, const void* v_pool, const int64_t* src, const int64_t* dst,
+                      int64_t num_pairs, int block_size, int num_kv_heads, int head_dim, int64_t num_blocks,
+                      int dtype);
 
 int check_slot_mapping(const int64_t* slot_mapping, const int32_t* block_tables,
                        const int32_t* context_lens, const int32_t* query_start_loc, int num_seqs,

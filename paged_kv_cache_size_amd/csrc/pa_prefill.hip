@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "pa.h"
 #include "pa_device.h"
 #include "pa_host.h"
@@ -35,12 +37,17 @@ struct PrefillArgs {
   const uint8_t* v_pool;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  const int32_t* query_start_loc;  // [B + 1]
-  float* ws_acc;                   // [T, H, P, D]
-  float2* ws_ml;                   // [T, H, P] (running max in log2 units, denominator)
+  const int32_t* query_start_loc;  // [B + 1]; null: sequence b owns row b alone
+  const int32_t* table_rows;       // [B] block-table row of sequence b; null: row b
+  const int32_t* key_begin;        // [B] first key of sequence b's range; null: 0
+  float* ws_acc;                   // [T, H, slots, D]
+  float2* ws_ml;                   // [T, H, slots] (running max in log2 units, denominator)
   int num_heads, num_kv_heads, rep, repc, chunks, max_blocks_per_seq;
   int part_tokens, num_parts, groups, tiles;  // tiles: 16-column tiles per (sequence, wave unit)
-  float qscale;                               // scale * log2(e)
+  int causal;          // 1: row i sits at position L - n + i; 0: every row sees the whole key range
+  int partial_base;    // < 0: final rows, partials only for split rows; >= 0: every partition's
+  int partial_stride;  //   partials go to slot partial_base + s of partial_stride slots per row
+  float qscale;        // scale * log2(e)
 };
 
 // A finite floor for the running max: a column whose keys all lie beyond this
@@ -75,9 +82,11 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
   const int g = unit / a.chunks;
   const int gq = lane >> 4, col = lane & 15;
 
-  const int q0 = a.query_start_loc[b];
-  const int n = a.query_start_loc[b + 1] - q0;  // new tokens of this sequence
+  const int q0 = a.query_start_loc ? a.query_start_loc[b] : b;
+  const int n = a.query_start_loc ? a.query_start_loc[b + 1] - q0 : 1;  // query rows of this sequence
   const int L = a.context_lens[b];
+  const int kb = a.key_begin ? a.key_begin[b] : 0;  // keys [kb, L)
+  const int trow = a.table_rows ? a.table_rows[b] : b;
   const int first_tok = (16 * tile) / a.repc;
   if (first_tok >= n) return;  // the whole wave lies past this sequence's new tokens
   const int last_tok = min(n - 1, (16 * tile + 15) / a.repc);
@@ -87,23 +96,32 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
   const int ti = cc / a.repc;
   const bool live = ti < n;
   const int h = g * a.rep + (unit % a.chunks) * a.repc + cc % a.repc;
-  const int pos = L - n + ti;
+  const int pos = a.causal ? L - n + ti : L - 1;  // last key this column sees
+  const size_t qrow = ((size_t)(q0 + (live ? ti : 0)) * a.num_heads + h);
 
-  const int start = s * a.part_tokens;
+  const int start = kb + s * a.part_tokens;
   const int pend = min(L, start + a.part_tokens);
-  const int end = min(pend, L - n + last_tok + 1);  // keys any column of the wave sees here
-  if (start >= end) return;  // no column's keys in this partition: the merge does not read it
+  const int end = min(pend, a.causal ? L - n + last_tok + 1 : L);  // keys any column of the wave sees here
+  if (start >= end) {  // no column's keys in this partition
+    if (a.partial_base >= 0 && live) {  // slot mode: the merge reads every slot, so mark it empty
+      const size_t idx = qrow * a.partial_stride + a.partial_base + s;
+      float* dst = a.ws_acc + idx * D + gq * DPL;
+#pragma unroll
+      for (int i = 0; i < DPL; i += 4) *reinterpret_cast<float4*>(dst + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (gq == 0) a.ws_ml[idx] = make_float2(-INFINITY, 0.f);
+    }
+    return;
+  }
   const int lim = live ? min(pend, pos + 1) : 0;  // this column's keys are [start, lim)
-  const int col_parts = (pos + a.part_tokens) / a.part_tokens;  // partitions holding its keys
+  const int col_parts = (pos - kb + a.part_tokens) / a.part_tokens;  // partitions holding its keys
   const int blk0 = start / BS;
   const int nblk = (end - start + BS - 1) / BS;  // 1..kMaxPartitionBlocks
   const int last = nblk - 1;
 
-  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk0;
+  const int32_t* bt = a.block_tables + (size_t)trow * a.max_blocks_per_seq + blk0;
   TableSlice tab;
   tab.load(bt, nblk, lane);
 
-  const size_t qrow = ((size_t)(q0 + (live ? ti : 0)) * a.num_heads + h);
   uint4 qop[NKC];
   {
     const uint8_t* qp = (const uint8_t*)a.query + qrow * ROWB + gq * 16;
@@ -212,7 +230,20 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
   }
 
   const float lt = rows_sum(l);
-  if (!live || s >= col_parts) return;  // no keys of this column here
+  if (!live) return;
+  if (a.partial_base >= 0) {  // slot mode: always partials (an empty column: m = -inf, l = 0)
+    const size_t idx = qrow * a.partial_stride + a.partial_base + s;
+    float* dst = a.ws_acc + idx * D + gq * DPL;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int t = 0; t < VPL; t += 4)
+        *reinterpret_cast<float4*>(dst + VPL * r + t) =
+            make_float4(acc[t][r], acc[t + 1][r], acc[t + 2][r], acc[t + 3][r]);
+    if (gq == 0) a.ws_ml[idx] = make_float2(lt > 0.f ? m : -INFINITY, lt);
+    return;
+  }
+  if (s >= col_parts) return;  // no keys of this column here
   if (col_parts == 1) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     float o[DPL];
@@ -263,7 +294,28 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(void* __restrict__
                         ws_ml + (size_t)idx * num_parts, np, lane);
 }
 
+// One wave per (row, head): merges `slots` partials (empty ones hold m = -inf).
+template <int DT, int D>
+__global__ __launch_bounds__(256) void merge_slots_kernel(void* __restrict__ out, const float* __restrict__ ws_acc,
+                                                          const float2* __restrict__ ws_ml, int rows_heads,
+                                                          int slots) {
+  const int lane = threadIdx.x & 63;
+  const int idx = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (idx >= rows_heads) return;
+  merge_partials<DT, D>((uint8_t*)out + (size_t)idx * D * ElemBytes<DT>::value, ws_acc + (size_t)idx * slots * D,
+                        ws_ml + (size_t)idx * slots, slots, lane);
+}
+
 using PrefillFn = void (*)(const PrefillArgs);
+using MergeSlotsFn = void (*)(void*, const float*, const float2*, int, int);
+
+MergeSlotsFn pick_merge_slots(int dtype, int d) {
+  switch (dtype) {
+    case PA_F16: return d == 64 ? merge_slots_kernel<DT_F16, 64> : merge_slots_kernel<DT_F16, 128>;
+    case PA_BF16: return d == 64 ? merge_slots_kernel<DT_BF16, 64> : merge_slots_kernel<DT_BF16, 128>;
+    default: return nullptr;
+  }
+}
 using PrefillCombineFn = void (*)(void*, const float*, const float2*, const int32_t*, const int32_t*, int, int, int,
                                   int, int);
 constexpr int kPrefillRing = 4;
@@ -356,6 +408,11 @@ extern "C" int pa_prefill_attention(void* out, const void* query, const void* k_
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.query_start_loc = query_start_loc;
+  a.table_rows = nullptr;
+  a.key_begin = nullptr;
+  a.causal = 1;
+  a.partial_base = -1;
+  a.partial_stride = parts;
   a.ws_acc = parts > 1 ? static_cast<float*>(workspace) : nullptr;
   a.ws_ml = parts > 1 ? reinterpret_cast<float2*>(static_cast<float*>(workspace) +
                                                   (size_t)num_tokens * num_heads * parts * head_dim)
@@ -380,5 +437,99 @@ extern "C" int pa_prefill_attention(void* out, const void* query, const void* k_
   const int64_t waves = (int64_t)num_tokens * num_heads;
   hipLaunchKernelGGL(cf, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, out, a.ws_acc, a.ws_ml, context_lens,
                      query_start_loc, num_seqs, num_tokens, num_heads, ps, parts);
+  return pa::launch_status();
+}
+
+// ------------------------------------------------------------------ shared-prefix decode
+
+extern "C" size_t pa_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                                   int32_t max_context_len, int32_t max_prefix_len) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0 || max_prefix_len < 0 ||
+      max_prefix_len > max_context_len)
+    return 0;
+  const int slots = pa::shared_prefix_slots(max_context_len, max_prefix_len);
+  return (size_t)num_seqs * num_heads * slots * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+extern "C" int pa_decode_attention_shared_prefix(
+    void* out, const void* query, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+    const int32_t* context_lens, const int32_t* group_start, const int32_t* prefix_lens,
+    const int32_t* seq_prefix_lens, int32_t num_seqs, int32_t num_groups, int32_t max_group_size,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t max_context_len, int32_t max_prefix_len, float scale, pa_dtype dtype, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  const pa::PrefillShape shp{{num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                              max_context_len, (int)dtype},
+                             num_seqs,
+                             1};
+  int rc = pa::check_shared_prefix(out, query, k_pool, v_pool, block_tables, context_lens, group_start, prefix_lens,
+                                   seq_prefix_lens, shp, num_groups, max_group_size, max_prefix_len, scale);
+  if (rc != PA_OK) return rc;
+  const int p1 = pa::num_partitions(std::max(max_prefix_len, 1), pa::kSharedPrefixPartition);
+  const int slots = pa::shared_prefix_slots(max_context_len, max_prefix_len);
+  const int p2 = slots - p1;
+  const size_t need = pa_shared_prefix_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, max_prefix_len);
+  if (workspace == nullptr || workspace_bytes < need) return PA_ERR_WORKSPACE;
+  const pa::DecodeGrid gd = pa::decode_grid(shp.d);
+  PrefillFn fn = pick_prefill(shp.d.dtype, shp.d.head_dim, gd.wpw);
+  MergeSlotsFn mf = pick_merge_slots(shp.d.dtype, shp.d.head_dim);
+  if (!fn || !mf) return PA_ERR_UNSUPPORTED;
+
+  PrefillArgs a;
+  a.out = out;
+  a.query = query;
+  a.k_pool = static_cast<const uint8_t*>(k_pool);
+  a.v_pool = static_cast<const uint8_t*>(v_pool);
+  a.block_tables = block_tables;
+  a.ws_acc = static_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float2*>(static_cast<float*>(workspace) + (size_t)num_seqs * num_heads * slots * head_dim);
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.rep = gd.rep;
+  a.repc = gd.repc;
+  a.chunks = gd.chunks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.part_tokens = pa::kSharedPrefixPartition;
+  a.groups = gd.groups;
+  a.partial_stride = slots;
+  a.qscale = scale * 1.44269504088896340736f;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  // Prefix pass: one "sequence" per group whose rows are the members' queries
+  // and whose keys are the shared prefix, read through the first member's
+  // table; no causal limit inside the prefix (every member's position lies
+  // past it).
+  a.context_lens = prefix_lens;
+  a.query_start_loc = group_start;
+  a.table_rows = group_start;
+  a.key_begin = nullptr;
+  a.causal = 0;
+  a.num_parts = p1;
+  a.partial_base = 0;
+  a.tiles = (int)(((int64_t)max_group_size * gd.repc + 15) / 16);
+  int64_t grid = (int64_t)num_groups * a.tiles * p1 * gd.groups;
+  if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * gd.wpw), 0, st, a);
+  rc = pa::launch_status();
+  if (rc != PA_OK) return rc;
+
+  // Suffix pass: every sequence's own keys past its group's prefix.
+  a.context_lens = context_lens;
+  a.query_start_loc = nullptr;
+  a.table_rows = nullptr;
+  a.key_begin = seq_prefix_lens;
+  a.causal = 1;
+  a.num_parts = p2;
+  a.partial_base = p1;
+  a.tiles = 1;
+  grid = (int64_t)num_seqs * p2 * gd.groups;
+  if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * gd.wpw), 0, st, a);
+  rc = pa::launch_status();
+  if (rc != PA_OK) return rc;
+
+  const int64_t waves = (int64_t)num_seqs * num_heads;
+  hipLaunchKernelGGL(mf, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, out, a.ws_acc, a.ws_ml, (int)waves,
+                     slots);
   return pa::launch_status();
 }

@@ -407,6 +407,53 @@ PREFILL_BUILDERS = {
 
 
 # --------------------------------------------------------------------------
+# Copy-on-write block copies
+# --------------------------------------------------------------------------
+
+@dataclass
+class CopyBatch:
+    """Whole-block copies inside a pool: dst[i] <- src[i] (distinct dst ids,
+    none of them a src id)."""
+    name: str
+    dtype: str
+    num_blocks: int
+    block_size: int
+    num_kv_heads: int
+    head_dim: int
+    src: np.ndarray  # int64 [P]
+    dst: np.ndarray  # int64 [P]
+    description: str = ""
+
+    @property
+    def block_bytes(self) -> int:
+        return self.block_size * self.num_kv_heads * self.head_dim * ELEM_BYTES[self.dtype]
+
+    def copy_bytes(self) -> int:
+        """Bytes read plus bytes written, K and V pools."""
+        return int(self.src.shape[0]) * self.block_bytes * 2 * 2
+
+
+def copy_batch(num_blocks, block_size, num_kv_heads, head_dim, dtype, num_pairs, seed=0, name="copy"):
+    ids = np.random.default_rng(seed).permutation(num_blocks)
+    assert 2 * num_pairs <= num_blocks
+    return CopyBatch(name, dtype, num_blocks, block_size, num_kv_heads, head_dim,
+                     ids[:num_pairs].astype(np.int64), ids[num_pairs:2 * num_pairs].astype(np.int64),
+                     f"{num_pairs} block copies in a {num_blocks}-block pool, H_kv {num_kv_heads}, D {head_dim}, "
+                     f"{dtype}")
+
+
+def cow_copy_llama_bf16(seed: int = 0, num_pairs: int = 8192) -> CopyBatch:
+    """8192 copy-on-write block copies in the Llama-style layer's pool
+    (72090 blocks of 16 tokens x 8 KV heads x 128 dims, bf16: 32 KiB per
+    block and pool), sources and destinations random and disjoint."""
+    cb = copy_batch(72090, 16, 8, 128, "bf16", num_pairs, seed=seed, name="cow_copy_llama_bf16")
+    return cb
+
+
+COPY_BUILDERS = {"cow_copy_llama_bf16": cow_copy_llama_bf16}
+
+
+# --------------------------------------------------------------------------
 # Tensors (torch, on any device)
 # --------------------------------------------------------------------------
 

@@ -1,0 +1,124 @@
+"""GPU parity of the copy-on-write block copy and of a fork-and-decode step
+driven by the library's host block pool.
+
+The block copy is compared bit for bit with the oracle's definition over the
+whole pool; the fork scenario runs copy, slot mapping, pool write and decode
+attention on the device and compares with the oracle doing the same steps.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from paged_kv_cache_size_amd import binding as PB
+from paged_kv_cache_size_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    PB.lib()
+
+
+def pools(nb, bs, hkv, d, dtype, seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    td = W.torch_dtype(dtype)
+    mk = lambda: torch.randn((nb, bs, hkv, d), generator=g, device=DEV, dtype=torch.float32).to(td)  # noqa: E731
+    return mk(), mk()
+
+
+@pytest.mark.parametrize("dtype,bs,hkv,d,pairs", [("bf16", 16, 8, 128, 300), ("f16", 16, 2, 64, 50),
+                                                  ("f32", 16, 3, 64, 7), ("bf16", 3, 1, 5, 20),
+                                                  ("f16", 16, 40, 128, 1)])
+def test_copy_blocks_bit_exact(dtype, bs, hkv, d, pairs):
+    say(f"copy {dtype} bs={bs} hkv={hkv} d={d} pairs={pairs}")
+    cb = W.copy_batch(4 * pairs + 8, bs, hkv, d, dtype, pairs, seed=pairs)
+    kp, vp = pools(cb.num_blocks, bs, hkv, d, dtype, seed=1)
+    ref_k, ref_v = W.raw_numpy(kp), W.raw_numpy(vp)
+    PB.pa_copy_blocks(kp, vp, torch.from_numpy(cb.src).to(DEV), torch.from_numpy(cb.dst).to(DEV))
+    torch.cuda.synchronize()
+    O.copy_blocks(ref_k, cb.src, cb.dst)
+    O.copy_blocks(ref_v, cb.src, cb.dst)
+    assert np.array_equal(W.raw_numpy(kp).view(np.uint8), ref_k.view(np.uint8))
+    assert np.array_equal(W.raw_numpy(vp).view(np.uint8), ref_v.view(np.uint8))
+
+
+def test_copy_blocks_skips_ids_outside_the_pool_and_empty_lists():
+    kp, vp = pools(10, 16, 2, 64, "bf16", seed=2)
+    before_k, before_v = kp.clone(), vp.clone()
+    src = torch.tensor([-1, 3, 10], dtype=torch.int64, device=DEV)
+    dst = torch.tensor([4, 12, 5], dtype=torch.int64, device=DEV)
+    PB.pa_copy_blocks(kp, vp, src, dst)
+    PB.pa_copy_blocks(kp, vp, src[:0], dst[:0])
+    torch.cuda.synchronize()
+    assert torch.equal(kp.view(torch.int16), before_k.view(torch.int16))
+    assert torch.equal(vp.view(torch.int16), before_v.view(torch.int16))
+
+
+def test_fork_copy_on_write_then_decode():
+    # 6 prompts of 37 tokens (2 full blocks + a 5-token tail), each forked into
+    # 3 samples; every sample decodes one token.  Each sample but the last
+    # holder of a tail copies it first; the copies, the slots, the pool write
+    # and the attention run on the device.
+    bs, H, hkv, d, dtype = 16, 8, 2, 128, "bf16"
+    m = PB.BlockManager(64, bs, free_order=np.random.default_rng(3).permutation(64))
+    roots = []
+    for _ in range(6):
+        r = m.new_seq()
+        assert m.append(r, 37) is None
+        roots.append(r)
+    kp, vp = pools(64, bs, hkv, d, dtype, seed=4)
+    seqs = [s for r in roots for s in (m.fork(r), m.fork(r), r)]
+    cows = [m.append(s, 1) for s in seqs]
+    pairs = [c for c in cows if c is not None]
+    assert len(pairs) == 12  # two of every three samples copy the shared tail
+    tables = [m.block_table(s) for s in seqs]
+    width = max(len(t) for t in tables)
+    bt = np.array([t + [t[-1]] * (width - len(t)) for t in tables], dtype=np.int32)
+    lens = np.array([m.length(s) for s in seqs], dtype=np.int32)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    q = torch.randn((len(seqs), H, d), generator=g, device=DEV).to(torch.bfloat16)
+    key = torch.randn((len(seqs), hkv, d), generator=g, device=DEV).to(torch.bfloat16)
+    val = torch.randn((len(seqs), hkv, d), generator=g, device=DEV).to(torch.bfloat16)
+    ref_k, ref_v = W.raw_numpy(kp), W.raw_numpy(vp)
+
+    src = torch.tensor([p[0] for p in pairs], dtype=torch.int64, device=DEV)
+    dst = torch.tensor([p[1] for p in pairs], dtype=torch.int64, device=DEV)
+    PB.pa_copy_blocks(kp, vp, src, dst)
+    bt_d, lens_d = torch.from_numpy(bt).to(DEV), torch.from_numpy(lens).to(DEV)
+    slots = PB.pa_slot_mapping(bt_d, lens_d, bs)
+    PB.pa_reshape_and_cache(key, val, kp, vp, slots)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    out = PB.pa_decode_attention(q, kp, vp, bt_d, lens_d, scale, int(lens.max()))
+    torch.cuda.synchronize()
+
+    for pool in (ref_k, ref_v):
+        O.copy_blocks(pool, [p[0] for p in pairs], [p[1] for p in pairs])
+    ref_slots = O.slot_mapping(tables, lens, bs)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    O.reshape_and_cache(ref_k, W.raw_numpy(key), ref_slots)
+    O.reshape_and_cache(ref_v, W.raw_numpy(val), ref_slots)
+    assert np.array_equal(W.raw_numpy(kp).view(np.uint8), ref_k.view(np.uint8))
+    assert np.array_equal(W.raw_numpy(vp).view(np.uint8), ref_v.view(np.uint8))
+    ref = O.decode_attention(W.raw_numpy(q), ref_k, ref_v, tables, lens, scale, dtype)
+    err = float(np.max(np.abs(O.widen(W.raw_numpy(out), dtype) - ref)))
+    say(f"  fork/copy/decode max abs err {err:.3e}")
+    assert err <= 2e-2
+    # the samples of one prompt share its first 36 tokens: the copied tails
+    # hold the prompt's rows
+    for r in range(6):
+        a, b, c = tables[3 * r:3 * r + 3]
+        assert a[:2] == b[:2] == c[:2] and len({a[2], b[2], c[2]}) == 3

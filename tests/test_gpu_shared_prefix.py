@@ -1,0 +1,118 @@
+"""GPU parity of the shared-prefix (cascade) decode against the float64 oracle.
+
+The cascade reads each group's shared prompt blocks once for all members,
+each sequence's own blocks after the prefix, and merges the two softmax
+partials; the oracle is the plain decode definition over each sequence's
+whole context.  Tolerance 2e-2 (bf16, fp16); also compared with the library's
+plain decode of the same batch.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from paged_kv_cache_size_amd import binding as PB
+from paged_kv_cache_size_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 2e-2
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    PB.lib()
+
+
+def run_cascade(w, t, groups):
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    lens = torch.from_numpy(w.context_lens).to(DEV)
+    casc = PB.pa_decode_attention_shared_prefix(t["query"], t["k_pool"], t["v_pool"], bt, lens, groups, w.scale,
+                                                w.max_context_len)
+    plain = PB.pa_decode_attention(t["query"], t["k_pool"], t["v_pool"], bt, lens, w.scale, w.max_context_len)
+    torch.cuda.synchronize()
+    return casc, plain
+
+
+def check(w, groups, seed=0, rows=None):
+    say(f"{w.name} groups={groups.num_groups} max_group={groups.max_group_size} prefix<= {groups.max_prefix_len} "
+        f"B={w.num_seqs} H={w.num_heads}/{w.num_kv_heads} D={w.head_dim} {w.dtype}")
+    t = W.make_tensors(w, seed, DEV)
+    casc, plain = run_cascade(w, t, groups)
+    sel = list(range(w.num_seqs)) if rows is None else rows
+    ref = O.decode_attention(W.raw_numpy(t["query"])[sel], W.raw_numpy(t["k_pool"]), W.raw_numpy(t["v_pool"]),
+                             w.block_tables[sel], w.context_lens[sel], w.scale, w.dtype)
+    got = O.widen(W.raw_numpy(casc), w.dtype)
+    assert np.isfinite(got).all()
+    err = float(np.max(np.abs(got[sel] - ref)))
+    diff = float((casc.float() - plain.float()).abs().max())
+    say(f"  max abs err {err:.3e}, vs plain decode {diff:.3e}")
+    assert err <= TOL and diff <= TOL
+    return casc
+
+
+def test_parallel_sampling_workload():
+    w = W.make_workload("shared_prefix_bf16")
+    g = PB.pa_shared_prefix_groups(w.block_tables, w.context_lens, w.block_size)
+    assert g.num_groups == 64
+    check(w, g, rows=list(range(0, 384, 7)))
+
+
+def forked_batch(prompts, forks, gens, h, hkv, d, dtype, seed):
+    """Prompts forked into samples that each generate some tokens, built with
+    the library's block pool (copy-on-write pairs replayed by the tensor
+    builder, which copies the prompt rows)."""
+    rng = np.random.default_rng(seed)
+    m = PB.BlockManager(4096, 16, free_order=rng.permutation(4096))
+    seqs, copies = [], []
+    for p, f, gl in zip(prompts, forks, gens):
+        root = m.new_seq()
+        m.append(root, p)
+        members = [m.fork(root) for _ in range(f - 1)] + [root]
+        for s, extra in zip(members, gl):
+            c = m.append(s, extra)
+            if c is not None:
+                copies.append((c[0], c[1], p % 16))
+        seqs += members
+    tables = [m.block_table(s) for s in seqs]
+    lens = np.array([m.length(s) for s in seqs], np.int32)
+    width = max(len(x) for x in tables) + 1
+    used = {b for x in tables for b in x}
+    pad = min(set(range(4096)) - used)
+    bt = np.full((len(seqs), width), pad, np.int32)
+    for i, x in enumerate(tables):
+        bt[i, :len(x)] = x
+    unowned = np.array(sorted(set(range(4096)) - used), np.int64)
+    return W.Workload("forked", dtype, h, hkv, d, 16, 4096, lens, bt, float(np.float32(1 / np.sqrt(d))), pad,
+                      unowned, copies, "forked prompts")
+
+
+@pytest.mark.parametrize("dtype,d,h,hkv", [("bf16", 128, 32, 8), ("f16", 64, 8, 2), ("bf16", 128, 12, 2),
+                                           ("f16", 128, 40, 40)])
+def test_mixed_groups(dtype, d, h, hkv):
+    # groups of 1..7 members; prefixes from none to over 2 partitions of 1024
+    # tokens; suffixes of 1 to 1300 tokens
+    prompts = [37, 2100, 16, 600, 1, 333]
+    forks = [3, 2, 4, 7, 1, 5]
+    rng = np.random.default_rng(7)
+    gens = [[int(x) for x in rng.integers(1, 1300 if i == 1 else 60, f)] for i, f in enumerate(forks)]
+    w = forked_batch(prompts, forks, gens, h, hkv, d, dtype, seed=3)
+    g = PB.pa_shared_prefix_groups(w.block_tables, w.context_lens, 16)
+    assert g.max_prefix_len == 2096 and g.max_group_size == 7
+    check(w, g, seed=1)
+
+
+def test_no_shared_prefix_degenerates_to_plain_decode():
+    w = W.make_workload("qwen1p5b_bf16")
+    g = PB.pa_shared_prefix_groups(w.block_tables, w.context_lens, w.block_size)
+    assert g.max_prefix_len == 0
+    check(w, g)
