@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--workload", default="llama_gqa4k_bf16")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--partition-size", type=int, default=0)
+    p.add_argument("--shared-prefix", action="store_true",
+                   help="decode with shared prompt prefixes read once per group (cascade)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle CPU time")
     p.add_argument("--copy-calibration", action="store_true",
@@ -367,11 +369,31 @@ def main():
         PB.pa_decode_combine(out, lens, w.max_context_len, ps, workspace=ws)
 
     stages = [k_slot, k_write, k_part, k_comb]
+    kernel = "decode_partition_kernel" if w.dtype == "f32" else "decode_mfma_kernel"
+    if args.shared_prefix:
+        # groups found on the host from the tables (scheduler work, untimed)
+        groups = PB.pa_shared_prefix_groups(w.block_tables, w.context_lens, w.block_size)
+        dgroups = tuple(torch.from_numpy(x).to(dev)
+                        for x in (groups.group_start, groups.prefix_lens, groups.seq_prefix_lens))
+        cws = torch.empty(max(1, PB.lib().pa_shared_prefix_workspace_bytes(B, H, D, w.max_context_len,
+                                                                            groups.max_prefix_len)),
+                          dtype=torch.uint8, device=dev)
+
+        def k_cascade():
+            PB.pa_decode_attention_shared_prefix(t["query"], t["k_pool"], t["v_pool"], bt, lens, groups, w.scale,
+                                                 w.max_context_len, out=out, workspace=cws, device_groups=dgroups)
+
+        stages = [k_slot, k_write, k_cascade, lambda: None]
+        kernel = "prefill_mfma_kernel prefix + suffix passes and merge_slots_kernel (one stage)"
+        ps = 0
     ms_per_step, per_kernel_ms, wall = time_stages(stages, args.steps, args.warmup)
 
     kv_bytes = w.kv_read_bytes()
+    # a block several sequences share need be read only once: the roofline
+    # counts the distinct rows (equal to kv_bytes when nothing is shared)
+    kv_unique = w.kv_unique_read_bytes()
     part_ms = per_kernel_ms[2]
-    achieved = kv_bytes / (part_ms * 1e-3) / 1e9
+    achieved = kv_unique / (part_ms * 1e-3) / 1e9
     tokens_per_s = B / (ms_per_step * 1e-3)
     rec = {
         "metric": METRIC,
@@ -390,17 +412,17 @@ def main():
         "config": {"workload": w.name, "num_seqs": B, "context_lens_sum": int(w.context_lens.sum()),
                    "max_context_len": w.max_context_len, "num_heads": H, "num_kv_heads": w.num_kv_heads,
                    "head_dim": D, "block_size": w.block_size, "num_blocks": w.num_blocks,
-                   "partition_size": ps, "description": w.description},
+                   "partition_size": ps, "shared_prefix_cascade": bool(args.shared_prefix),
+                   "description": w.description},
         "kv_read_bytes_per_step": kv_bytes,
+        "kv_unique_read_bytes_per_step": kv_unique,
         "kv_GBps_step": kv_bytes / (ms_per_step * 1e-3) / 1e9,
         "context_tokens_per_s": float(w.context_lens.sum()) / (ms_per_step * 1e-3),
         "kernel_us": {"slot_mapping": per_kernel_ms[0] * 1e3, "reshape_and_cache": per_kernel_ms[1] * 1e3,
                       "decode_partition": per_kernel_ms[2] * 1e3, "combine": per_kernel_ms[3] * 1e3},
-        "roofline": {"bound": "hbm",
-                     "kernel": "decode_partition_kernel" if w.dtype == "f32" else "decode_mfma_kernel",
-                     "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": load_traffic(w.name)},
+                     "traffic": None if args.shared_prefix else load_traffic(w.name)},
         "cpu_baseline": base,
         "wall_s_timed": wall,
     }

@@ -151,6 +151,18 @@ class Workload:
         """K and V bytes of every valid context token (each read once)."""
         return int(self.context_lens.astype(np.int64).sum()) * self.num_kv_heads * self.head_dim * self.elem_bytes * 2
 
+    def kv_unique_read_bytes(self) -> int:
+        """K and V bytes of the distinct pool rows the batch reads: a block
+        shared by several sequences counts once, with the rows its longest
+        user reads."""
+        rows = {}
+        for b in range(self.num_seqs):
+            L = int(self.context_lens[b])
+            for j in range((L + self.block_size - 1) // self.block_size):
+                blk = int(self.block_tables[b, j])
+                rows[blk] = max(rows.get(blk, 0), min(self.block_size, L - j * self.block_size))
+        return sum(rows.values()) * self.num_kv_heads * self.head_dim * self.elem_bytes * 2
+
 
 def _scale(head_dim: int) -> float:
     return float(np.float32(1.0 / math.sqrt(head_dim)))
@@ -256,7 +268,7 @@ def opt13b_mha_f16(seed: int = 0, extra_cols: int = 0) -> Workload:
 
 
 def shared_prefix_bf16(seed: int = 0, extra_cols: int = 0, prompts: int = 64, samples: int = 6,
-                       prompt_len: int = 300, gen_len: int = 150) -> Workload:
+                       prompt_len: int = 300, gen_len: int = 150, name: str = "shared_prefix_bf16") -> Workload:
     """Parallel sampling: 64 prompts of 300 tokens, each forked into 6
     samples that generate 150 tokens; the prompt's blocks are shared by
     reference count and a sample copies the shared, partly filled last prompt
@@ -293,7 +305,7 @@ def shared_prefix_bf16(seed: int = 0, extra_cols: int = 0, prompts: int = 64, sa
         s.blocks = [relabel[b] for b in s.blocks]
     copies = [(relabel[a], relabel[b], r) for a, b, r in copies if a in relabel and b in relabel]
     lens = [total] * len(seqs)
-    return _finish("shared_prefix_bf16", "bf16", 32, 8, 128, bs, seqs, len(live), nb, perm, lens,
+    return _finish(name, "bf16", 32, 8, 128, bs, seqs, len(live), nb, perm, lens,
                    copies, extra_cols,
                    f"{prompts} prompts x {samples} samples, {prompt_len}+{gen_len} tokens, H 32 / Hkv 8, D 128, bf16")
 
@@ -309,12 +321,22 @@ def custom(lens, num_heads: int, num_kv_heads: int, head_dim: int, dtype: str, s
                    extra_cols, f"custom {len(lens)} seqs, H {num_heads} / Hkv {num_kv_heads}, D {head_dim}, {dtype}")
 
 
+def shared_prefix_long_bf16(seed: int = 0, extra_cols: int = 0) -> Workload:
+    """Parallel sampling with long prompts: 32 prompts of 3600 tokens, 8
+    samples each, one decode step after 48 generated tokens (256 sequences at
+    length 3648; 225 shared prompt blocks per group); otherwise as
+    shared_prefix_bf16."""
+    return shared_prefix_bf16(seed, extra_cols, prompts=32, samples=8, prompt_len=3600, gen_len=48,
+                              name="shared_prefix_long_bf16")
+
+
 BUILDERS = {
     "tiny_f32": tiny_f32,
     "qwen1p5b_bf16": qwen1p5b_bf16,
     "llama_gqa4k_bf16": llama_gqa4k_bf16,
     "opt13b_mha_f16": opt13b_mha_f16,
     "shared_prefix_bf16": shared_prefix_bf16,
+    "shared_prefix_long_bf16": shared_prefix_long_bf16,
 }
 
 
