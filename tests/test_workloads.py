@@ -26,7 +26,7 @@ def test_tables_valid_and_deterministic(name):
         assert all(x == w.pad_block for x in w.block_tables[b, nb:])
         for x in used:
             owned_by.setdefault(x, []).append(b)
-    if name != "shared_prefix_bf16":
+    if not name.startswith("shared_prefix"):
         assert all(len(v) == 1 for v in owned_by.values())
     assert len(owned_by) + len(unowned) == w.num_blocks
     assert np.float32(w.scale) == np.float32(1 / np.sqrt(w.head_dim))
