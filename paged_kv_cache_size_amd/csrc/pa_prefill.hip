@@ -22,6 +22,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "pa.h"
 #include "pa_device.h"
@@ -54,6 +55,7 @@ struct PrefillArgs {
 // block (or partition) keeps m at the floor, so alpha = 2^0 and p = 2^-inf = 0
 // instead of the NaN that -inf - -inf would give.
 constexpr float kMaxFloor = -3.0e38f;
+constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold, log2 units
 
 template <int DT, int D, int NBUF, int WPW>
 __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArgs a) {
@@ -181,52 +183,93 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
 #pragma unroll
     for (int c = 0; c < NKC; ++c) kr[c] = *reinterpret_cast<const uint4*>(kb + kread[c]);
   };
-  // One block whose first key is `key0`.  Lane (gq, col) register i holds key
-  // key0 + 4i + gq of column col.  Branch free.
-  auto process = [&](const uint4* kr, const VT* vr, int key0) {
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+  // Keys [start, safe) are visible to every live column of the wave: steps
+  // wholly below `safe` need no masks.
+  const int safe = min(pend, a.causal ? L - n + first_tok + 1 : L);
+
+  // Two blocks (32 keys) whose first key is `key0`.  Lane (gq, col) register i
+  // of the block-A (block-B) score tile holds key key0 + 4i + gq (+ 16) of
+  // column col.  P.V runs on mfma_f32_16x16x32 with the contraction index
+  // k = 8gq + j <-> key 4(j % 4) + gq of block A (j < 4) or B (j >= 4): the
+  // lane's own score registers are its B operand, its own V rows its A operand.
+  // The running max moves only when a score exceeds it by more than 2^8
+  // (probabilities stay <= 256, exact in fp32 sums), so the rescale of the
+  // accumulators is a rare, wave-uniform branch.
+  auto step = [&](const uint4* kra, const uint4* krb, const VT* va_rows, const VT* vb_rows, int key0,
+                  auto interior) {
+    constexpr bool kInterior = decltype(interior)::value;
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NKC; ++c) sacc = Ops::qk(kr[c], qop[c], sacc);
-    float sc[4];
-    VT vm[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = key0 + 4 * i + gq;
-      sc[i] = key < lim ? sacc[i] * a.qscale : -INFINITY;
-      vm[i] = key < end ? vr[i] : VT{};  // rows past the last key (stale, even NaN) must not reach the MFMA
+    for (int c = 0; c < NKC; ++c) {
+      sa = Ops::qk(kra[c], qop[c], sa);
+      sb = Ops::qk(krb[c], qop[c], sb);
     }
-    const float mn = fmaxf(m, rows_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]))));
-    const float alpha = fast_exp2(m - mn);
-    m = mn;
-    float p[4];
+    float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+    VT v[8] = {va_rows[0], va_rows[1], va_rows[2], va_rows[3], vb_rows[0], vb_rows[1], vb_rows[2], vb_rows[3]};
+    if constexpr (!kInterior) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - mn);
-    l = fmaf(l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
-    const uint2 pb = make_uint2(Ops::pack(p[0], p[1]), Ops::pack(p[2], p[3]));
+      for (int i = 0; i < 8; ++i) {
+        const int key = key0 + (i >> 2) * 16 + 4 * (i & 3) + gq;
+        x[i] = key < lim ? x[i] : -INFINITY;
+        v[i] = key < end ? v[i] : VT{};  // rows past the last key (stale, even NaN) must not reach the MFMA
+      }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    const float smax = rows_max(mx) * a.qscale;
+    if (__ballot(smax > m + kRescaleLog2)) {
+      const float mn = fmaxf(m, smax);
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      l *= alpha;
+#pragma unroll
+      for (int t = 0; t < VPL; ++t) acc[t] *= alpha;
+    }
+    const float nm = -m;
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], a.qscale, nm));
+    l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    const uint4 pb = make_uint4(Ops::pack(p[0], p[1]), Ops::pack(p[2], p[3]), Ops::pack(p[4], p[5]),
+                                Ops::pack(p[6], p[7]));
 #pragma unroll
     for (int t = 0; t < VPL; ++t) {
       const int w = t >> 1;
-      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-      const uint2 va = make_uint2(__builtin_amdgcn_perm(vword<VPL>(vm[1], w), vword<VPL>(vm[0], w), sel),
-                                  __builtin_amdgcn_perm(vword<VPL>(vm[3], w), vword<VPL>(vm[2], w), sel));
-      acc[t] *= alpha;
-      acc[t] = Ops::pv(va, pb, acc[t]);
+      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;  // high or low 16-bit halves
+      const uint4 vt = make_uint4(__builtin_amdgcn_perm(vword<VPL>(v[1], w), vword<VPL>(v[0], w), sel),
+                                  __builtin_amdgcn_perm(vword<VPL>(v[3], w), vword<VPL>(v[2], w), sel),
+                                  __builtin_amdgcn_perm(vword<VPL>(v[5], w), vword<VPL>(v[4], w), sel),
+                                  __builtin_amdgcn_perm(vword<VPL>(v[7], w), vword<VPL>(v[6], w), sel));
+      acc[t] = Ops::qk(vt, pb, acc[t]);
     }
   };
+  auto run_step = [&](const uint4* kra, const uint4* krb, const VT* va_rows, const VT* vb_rows, int key0) {
+    if (key0 + 2 * BS <= safe) step(kra, krb, va_rows, vb_rows, key0, std::true_type{});
+    else step(kra, krb, va_rows, vb_rows, key0, std::false_type{});
+  };
 
-  VT vr[NBUF][4];
-#pragma unroll
-  for (int u = 0; u < NBUF - 1; ++u) load_block(u, u, vr[u]);
-  for (int j = 0; j < nblk; j += NBUF) {
-#pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      const int jj = j + u;
-      uint4 kr[NKC];
-      read_k(u, kr);
-      load_block(jj + NBUF - 1, (u + NBUF - 1) % NBUF, vr[(u + NBUF - 1) % NBUF]);
-      __builtin_amdgcn_sched_barrier(0);
-      process(kr, vr[u], start + jj * BS);
-    }
+  // Ring of 4 blocks (K in LDS slots, V in register sets), consumed two at a
+  // time: while a pair is computed the next pair's loads are in flight.  Loads
+  // past the partition go through an empty descriptor, so every wait is an
+  // exact count; steps past the end run fully masked.
+  static_assert(NBUF == 4, "the pair ring has four slots");
+  VT vr[4][4];
+  load_block(0, 0, vr[0]);
+  load_block(1, 1, vr[1]);
+  load_block(2, 2, vr[2]);
+  for (int j = 0; j < nblk; j += 4) {
+    uint4 ka[NKC], kb2[NKC];
+    read_k(0, ka);
+    read_k(1, kb2);
+    load_block(j + 3, 3, vr[3]);
+    __builtin_amdgcn_sched_barrier(0);
+    run_step(ka, kb2, vr[0], vr[1], start + j * BS);
+    load_block(j + 4, 0, vr[0]);
+    read_k(2, ka);
+    read_k(3, kb2);
+    load_block(j + 5, 1, vr[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    run_step(ka, kb2, vr[2], vr[3], start + (j + 2) * BS);
+    load_block(j + 6, 2, vr[2]);
   }
 
   const float lt = rows_sum(l);

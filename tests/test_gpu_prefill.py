@@ -137,9 +137,10 @@ def test_whole_prompts_only():
 # ------------------------------------------------------------------ against the decode kernel
 
 @pytest.mark.parametrize("ps", [64, 256, 1680])
-def test_one_new_token_matches_decode_bitwise(ps):
-    # n_b = 1 everywhere is a decode step; the prefill tile then does the
-    # decode tile's arithmetic in the same order
+def test_one_new_token_matches_decode(ps):
+    # n_b = 1 everywhere is a decode step: the prefill tile (32-key steps,
+    # lazily moved running max) and the decode tile agree to rounding, and
+    # both meet the oracle
     w = W.make_workload("qwen1p5b_bf16")
     t = W.make_tensors(w, 0, DEV)
     bt = torch.from_numpy(w.block_tables).to(DEV)
@@ -150,7 +151,10 @@ def test_one_new_token_matches_decode_bitwise(ps):
     pre = PB.pa_prefill_attention(t["query"], t["k_pool"], t["v_pool"], bt, lens, qsl, w.scale, 1,
                                   w.max_context_len, partition_size=ps)
     torch.cuda.synchronize()
-    assert torch.equal(bits(dec), bits(pre))
+    assert float((dec.float() - pre.float()).abs().max()) <= TOL
+    ref = O.decode_attention(W.raw_numpy(t["query"]), W.raw_numpy(t["k_pool"]), W.raw_numpy(t["v_pool"]),
+                             w.block_tables, w.context_lens, w.scale, w.dtype)
+    assert float(np.max(np.abs(O.widen(W.raw_numpy(pre), w.dtype) - ref))) <= TOL
 
 
 # ------------------------------------------------------------------ properties
