@@ -298,6 +298,24 @@ int prefill_tiles(const PrefillShape& s, const DecodeGrid& g) {
   return (int)(((int64_t)s.max_query_len * g.repc + 15) / 16);
 }
 
+PrefillGrid prefill_grid(const PrefillShape& s) {
+  const DecodeGrid g = decode_grid(s.d);
+  PrefillGrid p;
+  const int64_t cols = (int64_t)s.max_query_len * g.repc;
+  p.wide = cols >= kPrefillWideCols;
+  if (p.wide) {
+    p.tiles = (int)((cols + 127) / 128);
+    p.groups = g.units;
+    p.waves = 4;
+  } else {
+    p.tiles = prefill_tiles(s, g);
+    p.groups = g.groups;
+    p.waves = g.wpw;
+  }
+  p.items = (int64_t)s.d.num_seqs * p.tiles * p.groups;
+  return p;
+}
+
 int prefill_partition_bounds(const PrefillShape& s, int* min_parts, int* max_parts) {
   const int bs = s.d.block_size;
   const int64_t nb = (s.d.max_context_len + bs - 1) / bs;
@@ -317,10 +335,9 @@ int prefill_partition_size(const PrefillShape& s, int requested, int num_cus, in
     if (requested < bs || requested > kMaxPartitionBlocks * bs || requested % bs != 0) return -PA_ERR_INVALID_ARG;
     return requested;
   }
-  const DecodeGrid g = decode_grid(s.d);
+  const PrefillGrid pg = prefill_grid(s);
   const int64_t slots = total_slots(num_cus, wg_per_cu);
   const int64_t nb = (s.d.max_context_len + bs - 1) / bs;
-  const int64_t tiles = prefill_tiles(s, g);
   int lo = 1, hi = 1;
   prefill_partition_bounds(s, &lo, &hi);
   int64_t best_pb = 0, prev_pb = 0;
@@ -331,13 +348,13 @@ int prefill_partition_size(const PrefillShape& s, int requested, int num_cus, in
     prev_pb = pb;
     const int64_t p = (nb + pb - 1) / pb;
     if (p > hi) continue;
-    const int64_t items = (int64_t)s.d.num_seqs * tiles * p * g.groups;
+    const int64_t items = pg.items * p;
     const double item = (double)pb + kItemSetup;
     const int64_t tail = items % slots;
     double cost = (double)(items / slots) * item;
     if (tail > 0) cost += item / std::min(kMaxSpeedup, (double)slots / (double)tail);
     if (p > 1) {  // merge: every partial read once
-      const double wg_block_bytes = (double)g.wpw * 2.0 * bs * s.d.head_dim * elem_bytes(s.d.dtype);
+      const double wg_block_bytes = (double)pg.waves * 2.0 * bs * s.d.head_dim * elem_bytes(s.d.dtype);
       cost += kMergeLaunch + 2.0 * (double)s.num_tokens * s.d.num_heads * p * (s.d.head_dim + 2) * 4.0 /
                                  ((double)slots * wg_block_bytes);
     }

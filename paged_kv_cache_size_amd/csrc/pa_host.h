@@ -86,13 +86,28 @@ int check_prefill(const void* out, const void* query, const void* k_pool, const 
 // Column tiles (16 MFMA columns of (token, query head) pairs) per (sequence, wave unit).
 int prefill_tiles(const PrefillShape& s, const DecodeGrid& g);
 
+// Launch geometry of the prefill kernels.  Narrow column ranges (fewer than
+// kPrefillWideCols columns per (sequence, KV head unit)) run the per-wave
+// tile: `items` workgroups of `waves` waves per partition, one unit per wave.
+// Wide ones run the cooperative tile: 4 waves share one unit's K/V blocks and
+// take 128 columns.
+constexpr int kPrefillWideCols = 64;
+struct PrefillGrid {
+  bool wide;
+  int tiles;       // column tiles (16 columns) or column groups (128 columns) per sequence
+  int groups;      // workgroups per (sequence, tile, partition): unit groups or units
+  int waves;       // waves per workgroup
+  int64_t items;   // workgroups per partition
+};
+PrefillGrid prefill_grid(const PrefillShape& s);
+
 // Partitions the automatic prefill split may use: at least enough for the
 // 256-block table slice, at most one per 128 tokens, and partials within
 // kPrefillWorkspaceCap.
 int prefill_partition_bounds(const PrefillShape& s, int* min_parts, int* max_parts);
 
-// Partition size (tokens) for the prefill kernel: `requested` validated, or 0
-// to pick the candidate of least cost (every tile taken at max_context_len,
+// Partition size (tokens) for the prefill kernels: `requested` validated, or 0
+// to pick the candidate of least cost (every item taken at max_context_len,
 // whole waves of `slots` workgroups, plus the merge).  Negated pa_status on error.
 int prefill_partition_size(const PrefillShape& s, int requested, int num_cus, int wg_per_cu);
 

@@ -57,6 +57,56 @@ struct PrefillArgs {
 constexpr float kMaxFloor = -3.0e38f;
 constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold, log2 units
 
+// The end of one column's work in one partition: lane (gq, col) holds
+// accumulator tile t register r = O[col][dim (D/16)(4gq + r) + t], the
+// column's running max m (log2 units) and denominator lt.
+//  * slot mode (partial_base >= 0): partials into slot partial_base + s,
+//    m = -inf when the column saw no key;
+//  * a column whose keys fit one partition: its output row;
+//  * otherwise: partials for the combine kernel.
+template <int DT, int D>
+__device__ __forceinline__ void store_column(const PrefillArgs& a, const f32x4* acc, float m, float lt, size_t qrow,
+                                             int s, int col_parts, int gq) {
+  constexpr int VPL = D / 16, DPL = 4 * VPL, ROWB = D * 2;
+  auto store_partial = [&](size_t idx, float mm) {
+    float* dst = a.ws_acc + idx * D + gq * DPL;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int t = 0; t < VPL; t += 4)
+        *reinterpret_cast<float4*>(dst + VPL * r + t) =
+            make_float4(acc[t][r], acc[t + 1][r], acc[t + 2][r], acc[t + 3][r]);
+    if (gq == 0) a.ws_ml[idx] = make_float2(mm, lt);
+  };
+  if (a.partial_base >= 0) {
+    store_partial(qrow * a.partial_stride + a.partial_base + s, lt > 0.f ? m : -INFINITY);
+    return;
+  }
+  if (s >= col_parts) return;  // no keys of this column here
+  if (col_parts == 1) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float o[DPL];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int t = 0; t < VPL; ++t) o[VPL * r + t] = acc[t][r] * inv;
+    store_row<DT, DPL>((uint8_t*)a.out + qrow * ROWB + gq * DPL * 2, o);
+  } else {
+    store_partial(qrow * a.num_parts + s, m);
+  }
+}
+
+// Marks one column's slot empty (m = -inf, l = 0, acc = 0) in slot mode.
+template <int D>
+__device__ __forceinline__ void store_empty_slot(const PrefillArgs& a, size_t qrow, int s, int gq) {
+  constexpr int DPL = D / 4;
+  const size_t idx = qrow * a.partial_stride + a.partial_base + s;
+  float* dst = a.ws_acc + idx * D + gq * DPL;
+#pragma unroll
+  for (int i = 0; i < DPL; i += 4) *reinterpret_cast<float4*>(dst + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (gq == 0) a.ws_ml[idx] = make_float2(-INFINITY, 0.f);
+}
+
 template <int DT, int D, int NBUF, int WPW>
 __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArgs a) {
   using Ops = MfmaOps<DT>;
@@ -64,7 +114,6 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
   constexpr int ROWB = D * 2;
   constexpr int NKC = D / 32;      // QK k-chunks
   constexpr int VPL = D / 16;      // V elements per lane and row = PV output tiles
-  constexpr int DPL = 4 * VPL;     // output dims owned by a lane
   constexpr int CPR = ROWB / 16;   // 16-byte chunks per K row
   constexpr int NLI = BS * CPR / 64;  // K load instructions per block
   constexpr int KBYTES = BS * ROWB;
@@ -105,13 +154,7 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
   const int pend = min(L, start + a.part_tokens);
   const int end = min(pend, a.causal ? L - n + last_tok + 1 : L);  // keys any column of the wave sees here
   if (start >= end) {  // no column's keys in this partition
-    if (a.partial_base >= 0 && live) {  // slot mode: the merge reads every slot, so mark it empty
-      const size_t idx = qrow * a.partial_stride + a.partial_base + s;
-      float* dst = a.ws_acc + idx * D + gq * DPL;
-#pragma unroll
-      for (int i = 0; i < DPL; i += 4) *reinterpret_cast<float4*>(dst + i) = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (gq == 0) a.ws_ml[idx] = make_float2(-INFINITY, 0.f);
-    }
+    if (a.partial_base >= 0 && live) store_empty_slot<D>(a, qrow, s, gq);  // the merge reads every slot
     return;
   }
   const int lim = live ? min(pend, pos + 1) : 0;  // this column's keys are [start, lim)
@@ -273,38 +316,279 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
   }
 
   const float lt = rows_sum(l);
-  if (!live) return;
-  if (a.partial_base >= 0) {  // slot mode: always partials (an empty column: m = -inf, l = 0)
-    const size_t idx = qrow * a.partial_stride + a.partial_base + s;
-    float* dst = a.ws_acc + idx * D + gq * DPL;
+  if (live) store_column<DT, D>(a, acc, m, lt, qrow, s, col_parts, gq);
+}
+
+// s_waitcnt vmcnt(N), the other counters left free (gfx9 field layout:
+// vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Cooperative form for wide column ranges (long varlen rows, chunked
+// prefill): the 4 waves of a workgroup take 128 consecutive columns of one
+// (sequence, KV head unit) - 32 per wave, as two 16-column tiles - and share
+// one copy of each K/V block.  The blocks stream through an LDS ring of
+// 2 * NP blocks, K swizzled as in the per-wave tile and V row-major, filled by
+// direct-to-LDS loads that the four waves split between them; one barrier
+// per two-block step publishes a pair and frees the pair read in the step
+// before.  Each wave reads K (the QK A operand) and its V rows (the P.V A
+// operand) from LDS once per step and applies them to both of its tiles.
+// Arithmetic per tile is that of prefill_mfma_kernel: 32-key steps, P.V on
+// 16x16x32, lazily moved running max, mask-free interior steps.
+constexpr int kWgCols = 128;   // columns per workgroup
+constexpr int kWaveCols = 32;  // columns per wave (two MFMA tiles)
+
+template <int DT, int D, int NP>
+__global__ __launch_bounds__(256) void prefill_wg_kernel(const PrefillArgs a) {
+  using Ops = MfmaOps<DT>;
+  constexpr int BS = pa::kBlockSize;
+  constexpr int ROWB = D * 2;
+  constexpr int NKC = D / 32;
+  constexpr int VPL = D / 16;
+  constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
+  constexpr int KI = BS * CPR / 64;         // load instructions per block for K (and for V)
+  constexpr int DPW = 2 * KI / 4;           // load instructions per block and wave (K and V split over 4 waves)
+  constexpr int KBYTES = BS * ROWB;
+  constexpr int RB = 2 * NP;                // ring blocks
+  using VT = typename VRow<VPL>::T;
+  static_assert(BS == 16 && DPW >= 1 && (2 * KI) % 4 == 0, "tile shape");
+  static_assert(NP == 3, "the ring is unrolled for three pairs");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar load shares, no waterfall
+  const int gq = lane >> 4, col = lane & 15;
+  int rest = xcd_remap(blockIdx.x, gridDim.x);
+  const int s = rest % a.num_parts;
+  rest /= a.num_parts;
+  const int k = rest % a.tiles;  // column group
+  rest /= a.tiles;
+  const int unit = rest % a.groups;  // (KV head, chunk of query heads)
+  const int b = rest / a.groups;
+  const int g = unit / a.chunks;
+
+  const int q0 = a.query_start_loc ? a.query_start_loc[b] : b;
+  const int n = a.query_start_loc ? a.query_start_loc[b + 1] - q0 : 1;
+  const int L = a.context_lens[b];
+  const int kb = a.key_begin ? a.key_begin[b] : 0;
+  const int trow = a.table_rows ? a.table_rows[b] : b;
+  if ((kWgCols * k) / a.repc >= n) return;  // the whole workgroup lies past this sequence's rows
+  const int last_tok = min(n - 1, (kWgCols * k + kWgCols - 1) / a.repc);
+  const int start = kb + s * a.part_tokens;
+  const int pend = min(L, start + a.part_tokens);
+  const int end = min(pend, a.causal ? L - n + last_tok + 1 : L);  // keys any column here sees
+
+  // This lane's two columns.
+  int pos[2], lim[2], col_parts[2];
+  bool live[2];
+  size_t qrow[2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+  for (int tt = 0; tt < 2; ++tt) {
+    const int cc = kWgCols * k + kWaveCols * wave + 16 * tt + col;
+    const int ti = cc / a.repc;
+    live[tt] = ti < n;
+    const int h = g * a.rep + (unit % a.chunks) * a.repc + cc % a.repc;
+    pos[tt] = a.causal ? L - n + ti : L - 1;
+    qrow[tt] = (size_t)(q0 + (live[tt] ? ti : 0)) * a.num_heads + h;
+    lim[tt] = live[tt] ? min(pend, pos[tt] + 1) : 0;
+    col_parts[tt] = (pos[tt] - kb + a.part_tokens) / a.part_tokens;
+  }
+  if (start >= end) {  // uniform over the workgroup
+    if (a.partial_base >= 0)
 #pragma unroll
-      for (int t = 0; t < VPL; t += 4)
-        *reinterpret_cast<float4*>(dst + VPL * r + t) =
-            make_float4(acc[t][r], acc[t + 1][r], acc[t + 2][r], acc[t + 3][r]);
-    if (gq == 0) a.ws_ml[idx] = make_float2(lt > 0.f ? m : -INFINITY, lt);
+      for (int tt = 0; tt < 2; ++tt)
+        if (live[tt]) store_empty_slot<D>(a, qrow[tt], s, gq);
     return;
   }
-  if (s >= col_parts) return;  // no keys of this column here
-  if (col_parts == 1) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    float o[DPL];
+  // Steps wholly below `safe` need no masks for this wave's columns.
+  const int wave_tok = (kWgCols * k + kWaveCols * wave) / a.repc;
+  const int safe = wave_tok < n ? min(pend, a.causal ? L - n + wave_tok + 1 : L) : end;
+  const int blk0 = start / BS;
+  const int nblk = (end - start + BS - 1) / BS;
+  const int last = nblk - 1;
+
+  const int32_t* bt = a.block_tables + (size_t)trow * a.max_blocks_per_seq + blk0;
+  TableSlice tab;
+  tab.load(bt, nblk, lane);
+
+  uint4 qop[2][NKC];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+  for (int tt = 0; tt < 2; ++tt) {
+    const uint8_t* qp = (const uint8_t*)a.query + qrow[tt] * ROWB + gq * 16;
 #pragma unroll
-      for (int t = 0; t < VPL; ++t) o[VPL * r + t] = acc[t][r] * inv;
-    store_row<DT, DPL>((uint8_t*)a.out + qrow * ROWB + gq * DPL * 2, o);
-  } else {
-    const size_t idx = qrow * a.num_parts + s;
-    float* dst = a.ws_acc + idx * D + gq * DPL;
+    for (int c = 0; c < NKC; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qp + c * 64);
+      qop[tt][c] = live[tt] ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // This wave's share of every block's loads: instructions wave*DPW ..
+  // +DPW of the 2*KI (the first KI fill K, the rest V); lane l of
+  // instruction i fills LDS chunk 64*(i mod KI) + l = (row t, position q):
+  // K with the row's chunk q ^ swizzle(t), V with chunk q.
+  const uint32_t row_stride = (uint32_t)a.num_kv_heads * ROWB;
+  const size_t block_stride = (size_t)BS * row_stride;
+  uint32_t goff[DPW];
+  bool is_k[DPW];
+  int lds_off[DPW];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+  for (int i = 0; i < DPW; ++i) {
+    const int ins = wave * DPW + i;
+    is_k[i] = ins < KI;
+    const int idx = is_k[i] ? ins : ins - KI;
+    const int sl = 64 * idx + lane, t = sl / CPR, q = sl % CPR;
+    goff[i] = (uint32_t)t * row_stride + (uint32_t)g * ROWB + (uint32_t)((is_k[i] ? (q ^ kswz_t<CPR>(t)) : q) * 16);
+    lds_off[i] = idx * 1024;
+  }
+  uint32_t kread[NKC];  // QK A operand: token 4*(col%4) + col/4, chunk 4c + gq
+  {
+    const int t = 4 * (col & 3) + (col >> 2);
 #pragma unroll
-      for (int t = 0; t < VPL; t += 4)
-        *reinterpret_cast<float4*>(dst + VPL * r + t) =
-            make_float4(acc[t][r], acc[t + 1][r], acc[t + 2][r], acc[t + 3][r]);
-    if (gq == 0) a.ws_ml[idx] = make_float2(m, lt);
+    for (int c = 0; c < NKC; ++c) kread[c] = (uint32_t)(t * CPR + ((4 * c + gq) ^ kswz_t<CPR>(t))) * 16;
+  }
+  const uint32_t vread = (uint32_t)gq * ROWB + col * VPL * 2;  // row gq (+4i), this lane's dims
+
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[KBYTES], ks1[KBYTES], ks2[KBYTES], ks3[KBYTES],
+      ks4[KBYTES], ks5[KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[KBYTES], vs1[KBYTES], vs2[KBYTES], vs3[KBYTES],
+      vs4[KBYTES], vs5[KBYTES];
+  auto kslot = [&](int x) -> uint8_t* {
+    return x == 0 ? ks0 : x == 1 ? ks1 : x == 2 ? ks2 : x == 3 ? ks3 : x == 4 ? ks4 : ks5;
+  };
+  auto vslot = [&](int x) -> uint8_t* {
+    return x == 0 ? vs0 : x == 1 ? vs1 : x == 2 ? vs2 : x == 3 ? vs3 : x == 4 ? vs4 : vs5;
+  };
+
+  f32x4 acc[2][VPL];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int t = 0; t < VPL; ++t) acc[tt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {kMaxFloor, kMaxFloor}, l[2] = {0.f, 0.f};
+
+  // Loads past the partition go through an empty descriptor (zeros, no
+  // memory access), so every wait count is exact.
+  auto load_block = [&](int j, int x) {
+    const bool real = j <= last;
+    const size_t off = (size_t)(uint32_t)tab.get(real ? j : last) * block_stride;
+    const uint32_t span = real ? (uint32_t)block_stride : 0u;
+    const __amdgpu_buffer_rsrc_t rk = make_block_rsrc(a.k_pool + off, span);
+    const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, span);
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+      if (is_k[i])
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kslot(x) + lds_off[i]),
+                                                 16, (int)goff[i], 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vslot(x) + lds_off[i]),
+                                                 16, (int)goff[i], 0, 0, 0);
+    }
+  };
+
+  // One pair of blocks from ring slots xa, xb whose first key is key0.
+  auto step = [&](int xa, int xb, int key0, auto interior) {
+    constexpr bool kInterior = decltype(interior)::value;
+    uint4 kra[NKC], krb[NKC];
+    VT v[8];
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      kra[c] = *reinterpret_cast<const uint4*>(kslot(xa) + kread[c]);
+      krb[c] = *reinterpret_cast<const uint4*>(kslot(xb) + kread[c]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = *reinterpret_cast<const VT*>(vslot(xa) + vread + 4 * i * ROWB);
+      v[4 + i] = *reinterpret_cast<const VT*>(vslot(xb) + vread + 4 * i * ROWB);
+    }
+    if constexpr (!kInterior) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int key = key0 + (i >> 2) * 16 + 4 * (i & 3) + gq;
+        v[i] = key < end ? v[i] : VT{};  // rows past the last key (stale, even NaN) must not reach the MFMA
+      }
+    }
+    uint4 pb[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) {
+        sa = Ops::qk(kra[c], qop[tt][c], sa);
+        sb = Ops::qk(krb[c], qop[tt][c], sb);
+      }
+      float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+      if constexpr (!kInterior) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int key = key0 + (i >> 2) * 16 + 4 * (i & 3) + gq;
+          x[i] = key < lim[tt] ? x[i] : -INFINITY;
+        }
+      }
+      const float mx =
+          fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      const float smax = rows_max(mx) * a.qscale;
+      if (__ballot(smax > m[tt] + kRescaleLog2)) {
+        const float mn = fmaxf(m[tt], smax);
+        const float alpha = fast_exp2(m[tt] - mn);
+        m[tt] = mn;
+        l[tt] *= alpha;
+#pragma unroll
+        for (int t = 0; t < VPL; ++t) acc[tt][t] *= alpha;
+      }
+      const float nm = -m[tt];
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], a.qscale, nm));
+      l[tt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      pb[tt] = make_uint4(Ops::pack(p[0], p[1]), Ops::pack(p[2], p[3]), Ops::pack(p[4], p[5]),
+                          Ops::pack(p[6], p[7]));
+    }
+#pragma unroll
+    for (int t = 0; t < VPL; ++t) {
+      const int w = t >> 1;
+      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+      const uint4 vt = make_uint4(__builtin_amdgcn_perm(vword<VPL>(v[1], w), vword<VPL>(v[0], w), sel),
+                                  __builtin_amdgcn_perm(vword<VPL>(v[3], w), vword<VPL>(v[2], w), sel),
+                                  __builtin_amdgcn_perm(vword<VPL>(v[5], w), vword<VPL>(v[4], w), sel),
+                                  __builtin_amdgcn_perm(vword<VPL>(v[7], w), vword<VPL>(v[6], w), sel));
+      acc[0][t] = Ops::qk(vt, pb[0], acc[0][t]);
+      acc[1][t] = Ops::qk(vt, pb[1], acc[1][t]);
+    }
+  };
+  // One ring step: wait for this wave's loads of the pair in slots (xa, xb),
+  // barrier (every wave's loads of it have landed and every wave has finished
+  // the previous step), refill the previous step's slots (xp, xq) with the
+  // blocks 2*(NP-1) ahead, then compute.
+  auto ring_step = [&](int jp, int xa, int xb, int xp, int xq) {
+    wait_vmcnt<(NP - 2) * 2 * DPW>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    load_block(jp + 2 * (NP - 1), xp);
+    load_block(jp + 2 * (NP - 1) + 1, xq);
+    __builtin_amdgcn_sched_barrier(0);
+    const int key0 = start + jp * BS;
+    if (key0 < end) {
+      if (key0 + 2 * BS <= safe) step(xa, xb, key0, std::true_type{});
+      else step(xa, xb, key0, std::false_type{});
+    }
+  };
+
+  load_block(0, 0);
+  load_block(1, 1);
+  load_block(2, 2);
+  load_block(3, 3);
+  for (int j = 0; j < nblk; j += RB) {
+    ring_step(j, 0, 1, 4, 5);
+    ring_step(j + 2, 2, 3, 0, 1);
+    ring_step(j + 4, 4, 5, 2, 3);
+  }
+
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const float lt = rows_sum(l[tt]);
+    if (live[tt]) store_column<DT, D>(a, acc[tt], m[tt], lt, qrow[tt], s, col_parts[tt], gq);
   }
 }
 
@@ -373,6 +657,17 @@ PrefillFn pick_prefill_wpw(int wpw) {
   }
 }
 
+constexpr int kPrefillPairs = 3;  // ring pairs of the cooperative tile
+
+PrefillFn pick_prefill_wide(int dtype, int d) {
+  switch (dtype) {
+    case PA_F16: return d == 64 ? prefill_wg_kernel<DT_F16, 64, kPrefillPairs> : prefill_wg_kernel<DT_F16, 128, kPrefillPairs>;
+    case PA_BF16:
+      return d == 64 ? prefill_wg_kernel<DT_BF16, 64, kPrefillPairs> : prefill_wg_kernel<DT_BF16, 128, kPrefillPairs>;
+    default: return nullptr;
+  }
+}
+
 PrefillFn pick_prefill(int dtype, int d, int wpw) {
   switch (dtype) {
     case PA_F16: return d == 64 ? pick_prefill_wpw<DT_F16, 64>(wpw) : pick_prefill_wpw<DT_F16, 128>(wpw);
@@ -426,12 +721,14 @@ extern "C" int pa_prefill_attention(void* out, const void* query, const void* k_
   int rc = pa::check_prefill(out, query, k_pool, v_pool, block_tables, context_lens, query_start_loc, shp, scale);
   if (rc != PA_OK) return rc;
   const pa::DecodeGrid gd = pa::decode_grid(shp.d);
-  PrefillFn fn = pick_prefill(shp.d.dtype, shp.d.head_dim, gd.wpw);
+  const pa::PrefillGrid pg = pa::prefill_grid(shp);
+  PrefillFn fn = pg.wide ? pick_prefill_wide(shp.d.dtype, shp.d.head_dim)
+                         : pick_prefill(shp.d.dtype, shp.d.head_dim, gd.wpw);
   if (!fn) return PA_ERR_UNSUPPORTED;
   int cus = 256, per_cu = 1;
   if (partition_size == 0) {
     cus = pa::device_cu_count();
-    per_cu = pa::resident_per_cu(reinterpret_cast<const void*>(fn), 64 * gd.wpw);
+    per_cu = pa::resident_per_cu(reinterpret_cast<const void*>(fn), 64 * pg.waves);
     if (cus <= 0 || per_cu <= 0) return PA_ERR_HIP;
   }
   const int ps = pa::prefill_partition_size(shp, partition_size, cus, per_cu);
@@ -439,8 +736,7 @@ extern "C" int pa_prefill_attention(void* out, const void* query, const void* k_
   const int parts = pa::num_partitions(max_context_len, ps);
   const size_t need = prefill_workspace(shp, parts);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
-  const int tiles = pa::prefill_tiles(shp, gd);
-  const int64_t grid = (int64_t)num_seqs * tiles * parts * gd.groups;
+  const int64_t grid = pg.items * parts;
   if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
 
   PrefillArgs a;
@@ -468,11 +764,11 @@ extern "C" int pa_prefill_attention(void* out, const void* query, const void* k_
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.part_tokens = ps;
   a.num_parts = parts;
-  a.groups = gd.groups;
-  a.tiles = tiles;
+  a.groups = pg.groups;
+  a.tiles = pg.tiles;
   a.qscale = scale * 1.44269504088896340736f;  // log2(e)
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * gd.wpw), 0, st, a);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * pg.waves), 0, st, a);
   rc = pa::launch_status();
   if (rc != PA_OK || parts <= 1) return rc;
   PrefillCombineFn cf = pick_prefill_combine(shp.d.dtype, shp.d.head_dim);
