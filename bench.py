@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--workload", default="llama_gqa4k_bf16")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--partition-size", type=int, default=0)
+    p.add_argument("--block-size", type=int, default=0,
+                   help="pool block size for the Llama-layer workload (default 16)")
     p.add_argument("--shared-prefix", action="store_true",
                    help="decode with shared prompt prefixes read once per group (cascade)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -336,7 +338,8 @@ def main():
         main_copy(args)
         return
     PB.lib()  # fail loudly before any work if the HIP library is missing
-    w = W.make_workload(args.workload, seed=args.seed)
+    extra = {"block_size": args.block_size} if args.block_size else {}
+    w = W.make_workload(args.workload, seed=args.seed, **extra)
     t = W.make_tensors(w, seed=args.seed, device="cuda")
     dev = "cuda"
     bt = torch.from_numpy(w.block_tables).to(dev)

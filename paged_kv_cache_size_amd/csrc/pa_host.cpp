@@ -37,10 +37,16 @@ int check_decode(const void* out, const void* query, const void* k_pool, const v
   if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
   if (elem_bytes(s.dtype) == 0) return PA_ERR_UNSUPPORTED;
   if (s.head_dim != 64 && s.head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (s.block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (!decode_block_size_ok(s.block_size, s.dtype)) return PA_ERR_UNSUPPORTED;
   // grid: num_seqs * partitions * head groups workgroups must fit a 32-bit grid
   if ((int64_t)s.num_seqs * s.num_heads > (int64_t)1 << 30) return PA_ERR_INVALID_ARG;
   return PA_OK;
+}
+
+bool decode_block_size_ok(int block_size, int dtype) {
+  if (block_size <= 0 || (block_size & (block_size - 1)) != 0) return false;  // powers of two
+  if (dtype == PA_F32) return block_size == kBlockSize;  // the VALU tile reads whole 16-row blocks
+  return block_size >= kMinDecodeBlock && block_size <= kMaxDecodeBlock;
 }
 
 int num_partitions(int max_context_len, int partition) {
@@ -87,7 +93,7 @@ constexpr double kMaxSpeedup = 2.0;
 // O(items + makespan).
 double simulate_partitions(const DecodeShape& s, const DecodeGrid& g, const int32_t* lens, int64_t pb,
                            int64_t parts, int64_t slots) {
-  const int bs = s.block_size;
+  const int bs = kBlockSize;  // the kernels' step: 16 tokens, whatever the pool's block size
   const int64_t items = (int64_t)s.num_seqs * parts * g.groups;
   const int64_t xcd_slots = std::max<int64_t>(1, slots / 8);
   const int64_t per = items / 8, rem = items % 8;
@@ -160,7 +166,7 @@ namespace {
 
 double merge_cost(const DecodeShape& s, const DecodeGrid& g, int64_t parts, int64_t slots) {
   if (parts <= 1) return 0.0;  // merge: read every partial once, write the output
-  const double wg_block_bytes = (double)g.wpw * 2.0 * s.block_size * s.head_dim * elem_bytes(s.dtype);
+  const double wg_block_bytes = (double)g.wpw * 2.0 * kBlockSize * s.head_dim * elem_bytes(s.dtype);
   return kMergeLaunch + 2.0 * (double)s.num_seqs * s.num_heads * parts * (s.head_dim + 2) * 4.0 /
                             ((double)slots * wg_block_bytes);
 }
@@ -176,7 +182,7 @@ double cost_lower_bound(const DecodeShape& s, const DecodeGrid& g, const int32_t
   double work = 0.0;
   int64_t longest = 0;
   for (int b = 0; b < s.num_seqs; ++b) {
-    const int64_t nblk = (std::max<int64_t>(0, lens[b]) + s.block_size - 1) / s.block_size;
+    const int64_t nblk = (std::max<int64_t>(0, lens[b]) + kBlockSize - 1) / kBlockSize;
     const int64_t used = std::min<int64_t>(parts, (nblk + pb - 1) / pb);
     work += (double)nblk + kItemSetup * used + kEmptyItem * (parts - used);
     longest = std::max(longest, std::min(nblk, pb));
@@ -191,7 +197,7 @@ double cost_lower_bound(const DecodeShape& s, const DecodeGrid& g, const int32_t
 double decode_cost(const DecodeShape& s, int64_t pb, const int32_t* lens, int num_cus, int wg_per_cu) {
   const DecodeGrid g = decode_grid(s);
   const int64_t slots = total_slots(num_cus, wg_per_cu);
-  const int64_t nb = (s.max_context_len + s.block_size - 1) / s.block_size;
+  const int64_t nb = (s.max_context_len + kBlockSize - 1) / kBlockSize;
   const int64_t parts = (nb + pb - 1) / pb;
   double cost;
   if (lens) {
@@ -206,19 +212,30 @@ double decode_cost(const DecodeShape& s, int64_t pb, const int32_t* lens, int nu
   return cost + merge_cost(s, g, parts, slots);
 }
 
+int partition_granule(int block_size) { return block_size > kBlockSize ? block_size : kBlockSize; }
+
+int max_partition_tokens(int block_size) { return kMaxPartitionBlocks * block_size; }
+
+int validate_partition(int requested, int block_size) {
+  const int gran = partition_granule(block_size);
+  if (requested < gran || requested > max_partition_tokens(block_size) || requested % gran != 0)
+    return -PA_ERR_INVALID_ARG;
+  return requested;
+}
+
 int partition_size(const DecodeShape& s, int requested, int num_cus, int wg_per_cu, const int32_t* lens) {
-  const int bs = s.block_size;
-  const int max_ps = kMaxPartitionBlocks * bs;
-  if (requested != 0) {
-    if (requested < bs || requested > max_ps || requested % bs != 0) return -PA_ERR_INVALID_ARG;
-    return requested;
-  }
+  if (requested != 0) return validate_partition(requested, s.block_size);
+  // The model counts 16-token steps; a partition is a whole number of pool
+  // blocks (spb steps each) and holds at most kMaxPartitionBlocks of them.
   // Without the lengths the batch is taken to be at max_context_len and the
   // partitions are kept short enough to balance a ragged one; with them the
   // launch is simulated and any size up to the table-slice limit may win.
-  const int64_t cap = lens ? kMaxPartitionBlocks : kMaxAutoPartitionBlocks;
-  const int64_t nb = (s.max_context_len + bs - 1) / bs;
-  const int64_t bound = auto_partition_bound(s.max_context_len, bs);
+  const int64_t spb = partition_granule(s.block_size) / kBlockSize;
+  const int64_t max_steps = max_partition_tokens(s.block_size) / kBlockSize;
+  int64_t cap = lens ? max_steps : std::min<int64_t>(kMaxAutoPartitionBlocks, max_steps);
+  cap = std::max<int64_t>(spb, cap / spb * spb);
+  const int64_t nb = (s.max_context_len + kBlockSize - 1) / kBlockSize;
+  const int64_t bound = auto_partition_bound(s.max_context_len, s.block_size);
   struct Cand {
     int64_t pb;
     double lb;
@@ -227,12 +244,12 @@ int partition_size(const DecodeShape& s, int requested, int num_cus, int wg_per_
   const DecodeGrid g = decode_grid(s);
   const int64_t slots = total_slots(num_cus, wg_per_cu);
   for (int64_t parts = 1; parts <= bound; ++parts) {
-    const int64_t pb = (nb + parts - 1) / parts;  // blocks per partition
+    const int64_t pb = ((nb + parts - 1) / parts + spb - 1) / spb * spb;  // steps per partition
     if (pb > cap || (!cands.empty() && cands.back().pb == pb)) continue;
     const int64_t p = (nb + pb - 1) / pb;
     cands.push_back({pb, lens ? cost_lower_bound(s, g, lens, pb, p, slots) : 0.0});
   }
-  if (cands.empty()) return (int)(std::min<int64_t>(cap, nb > 0 ? nb : 1) * bs);
+  if (cands.empty()) return (int)(std::min<int64_t>(cap, std::max<int64_t>(spb, nb)) * kBlockSize);
   // Simulate in order of the lower bound; stop once no bound can win.  Near
   // ties go to the longer partition (fewer partials to write and merge).
   std::stable_sort(cands.begin(), cands.end(), [](const Cand& x, const Cand& y) { return x.lb < y.lb; });
@@ -246,7 +263,7 @@ int partition_size(const DecodeShape& s, int requested, int num_cus, int wg_per_
       best_pb = c.pb;
     }
   }
-  return (int)(best_pb * bs);
+  return (int)(best_pb * kBlockSize);
 }
 
 int check_partition_query(const DecodeShape& s) {
@@ -255,8 +272,8 @@ int check_partition_query(const DecodeShape& s) {
 }
 
 int auto_partition_bound(int max_context_len, int block_size) {
-  (void)block_size;
-  int b = (max_context_len + kMinPartition - 1) / kMinPartition;
+  const int least = block_size > kMinPartition ? block_size : kMinPartition;  // smallest automatic partition
+  int b = (max_context_len + least - 1) / least;
   return b < 1 ? 1 : b;
 }
 
@@ -269,6 +286,7 @@ int check_prefill(const void* out, const void* query, const void* k_pool, const 
   if (s.num_tokens <= 0 || s.max_query_len <= 0 || s.max_query_len > s.num_tokens) return PA_ERR_INVALID_ARG;
   if (s.max_query_len > s.d.max_context_len) return PA_ERR_INVALID_ARG;
   if (s.d.dtype == PA_F32) return PA_ERR_UNSUPPORTED;  // the prefill tile is an MFMA tile (16-bit inputs)
+  if (s.d.block_size != kBlockSize) return PA_ERR_UNSUPPORTED;  // and reads whole 16-row blocks
   if ((int64_t)s.num_tokens * s.d.num_heads > (int64_t)1 << 30) return PA_ERR_INVALID_ARG;
   return PA_OK;
 }
@@ -291,6 +309,7 @@ int check_shared_prefix(const void* out, const void* query, const void* k_pool, 
   if (max_prefix_len < 0 || max_prefix_len > s.d.max_context_len || max_prefix_len % s.d.block_size != 0)
     return PA_ERR_INVALID_ARG;
   if (s.d.dtype == PA_F32) return PA_ERR_UNSUPPORTED;  // both passes run the MFMA prefill tile
+  if (s.d.block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
@@ -377,7 +396,7 @@ int check_combine(const void* out, const int32_t* context_lens, int num_seqs, in
   if (!out || !context_lens) return PA_ERR_INVALID_ARG;
   if (num_seqs <= 0 || num_heads <= 0 || max_context_len <= 0) return PA_ERR_INVALID_ARG;
   if (partition_size < kBlockSize || partition_size % kBlockSize != 0 ||
-      partition_size > kMaxPartitionBlocks * kBlockSize)
+      partition_size > max_partition_tokens(kMaxDecodeBlock))
     return PA_ERR_INVALID_ARG;
   if (elem_bytes(dtype) == 0) return PA_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
@@ -449,7 +468,7 @@ extern "C" size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_hea
   if (partition_size == 0)
     return pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, block_size);
   if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0 || block_size <= 0 ||
-      partition_size < block_size || partition_size % block_size != 0)
+      pa::validate_partition(partition_size, block_size) <= 0)
     return 0;
   return pa::workspace_bytes(num_seqs, num_heads, head_dim,
                              pa::num_partitions(max_context_len, partition_size));

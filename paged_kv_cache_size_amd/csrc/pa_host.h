@@ -19,6 +19,17 @@ constexpr int kMaxAutoPartitionBlocks = 64;  // automatic choice without the con
 
 int elem_bytes(int dtype);  // 0 for an unknown dtype
 
+// Pool block sizes the decode path runs (powers of two, 1..256): the 16-bit
+// MFMA tile takes 16-token steps, so a larger block holds several steps and a
+// smaller one contributes a few rows to a step; fp32 (VALU tile), prefill and
+// the cascade read whole 16-row blocks only.
+constexpr int kMinDecodeBlock = 1;
+constexpr int kMaxDecodeBlock = 256;
+bool decode_block_size_ok(int block_size, int dtype);
+int partition_granule(int block_size);     // partitions are multiples of max(16, block_size) tokens
+int max_partition_tokens(int block_size);  // kMaxPartitionBlocks pool blocks
+int validate_partition(int requested, int block_size);  // requested, or a negated pa_status
+
 // Query heads served per wave: the largest divisor of rep that is <= cap.
 int rep_per_wave(int rep, int cap);
 // The cap for a dtype's decode kernel (fp32: VALU kernel; fp16/bf16: MFMA kernel).

@@ -89,6 +89,7 @@ struct DecodeArgs {
   float* ws_acc;   // [B, H, P, D]
   float2* ws_ml;   // [B, H, P] (running max in log2 units, softmax denominator)
   int num_heads, num_kv_heads, rep, chunks, max_blocks_per_seq;
+  int block_shift;  // pool blocks of 16 << block_shift tokens (the MFMA tile's steps are 16 tokens)
   int part_tokens, num_parts, groups;  // groups = head-group workgroups per (sequence, partition)
   float qscale;    // scale * log2(e): scores come out in log2 units for exp2
 };
@@ -309,8 +310,20 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
 // The running max of a head is kept uniform over the four row groups (a
 // permlane max per block); denominators are per-lane partial sums.
 
-template <int DT, int D, int NBUF, int WPW>
+// Pool block sizes (the MFMA tile always takes 16-token steps):
+//  * kBlocks16: blocks and steps coincide;
+//  * kBlocksLarge: blocks of 16 << a.block_shift tokens; a step is a window of
+//    16 rows inside one block (table entry step >> shift, row offset
+//    16 * (step & mask));
+//  * kBlocksSmall: blocks of 16 >> a.block_shift tokens; a step's 16 rows
+//    come from 1 << shift blocks, so every lane addresses its own row's block
+//    (direct-to-LDS and V loads from per-lane global addresses).
+constexpr int kBlocks16 = 0, kBlocksLarge = 1, kBlocksSmall = 2;
+
+template <int DT, int D, int NBUF, int WPW, int MODE>
 __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs a) {
+  constexpr bool SUB = MODE == kBlocksLarge;
+  constexpr bool GATHER = MODE == kBlocksSmall;
   using Ops = MfmaOps<DT>;
   constexpr int BS = pa::kBlockSize;
   constexpr int ROWB = D * 2;
@@ -350,13 +363,16 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
   }
   const int end = min(L, start + a.part_tokens);
   const int seq_parts = (L + a.part_tokens - 1) / a.part_tokens;
-  const int blk0 = start / BS;
-  const int nblk = (end - start + BS - 1) / BS;  // 1..kMaxPartitionBlocks
+  const int pshift = MODE != kBlocks16 ? a.block_shift : 0;
+  const int pool_bs = SUB ? BS << pshift : GATHER ? BS >> pshift : BS;  // tokens per pool block
+  const int blk0 = start / pool_bs;  // partitions start on a pool block
+  const int nblk = (end - start + BS - 1) / BS;  // 16-token steps
+  const int nent = MODE == kBlocks16 ? nblk : (end - start + pool_bs - 1) / pool_bs;  // 1..kMaxPartitionBlocks
   const int last = nblk - 1;
 
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk0;
   TableSlice tab;
-  tab.load(bt, nblk, lane);
+  tab.load(bt, nent, lane);
 
   // Q^T as the QK B operand: column col = head h0 + col, k-chunk c = dims 32c + 8gq .. +8.
   uint4 qop[NKC];
@@ -389,6 +405,24 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
     for (int c = 0; c < NKC; ++c) kread[c] = (uint32_t)(t * CPR + ((4 * c + gq) ^ kswz(t))) * 16;
   }
   const uint32_t voff = (uint32_t)gq * row_stride + (uint32_t)g * ROWB + col * VPL * 2;
+  // Small blocks: for each row a lane loads, which block of the step holds it
+  // and the byte offset inside that block.
+  int kblk[GATHER ? NLI : 1], vblk[GATHER ? 4 : 1];
+  uint32_t kin[GATHER ? NLI : 1], vin[GATHER ? 4 : 1];
+  if constexpr (GATHER) {
+#pragma unroll
+    for (int n = 0; n < NLI; ++n) {
+      const int slot = 64 * n + lane, t = slot / CPR, q = slot % CPR;
+      kblk[n] = t / pool_bs;
+      kin[n] = (uint32_t)(t % pool_bs) * row_stride + (uint32_t)g * ROWB + (uint32_t)((q ^ kswz(t)) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * i + gq;
+      vblk[i] = t / pool_bs;
+      vin[i] = (uint32_t)(t % pool_bs) * row_stride + (uint32_t)g * ROWB + col * VPL * 2;
+    }
+  }
   // One LDS object per ring slot, so that the compiler's wait counting can
   // tell a slot being read from the slots whose loads are still in flight.
   __shared__ __attribute__((aligned(1024))) uint8_t kslot0[NBUF > 0 ? WPW : 1][KBYTES];
@@ -418,7 +452,33 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
   // zeros without touching memory.
   auto load_block = [&](int j, int slot, VT* vr) {
     const bool real = j <= last;
-    const size_t off = (size_t)(uint32_t)tab.get(real ? j : last) * block_stride;
+    const int jj = real ? j : last;
+    if constexpr (GATHER) {  // per-lane rows; past the end the last step is re-read (cached, masked)
+      const size_t pool_block = (size_t)pool_bs * row_stride;
+      size_t kb[NLI], vb[4];
+#pragma unroll
+      for (int n = 0; n < NLI; ++n) kb[n] = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vb[i] = 0;
+      for (int k = 0; k < (1 << pshift); ++k) {
+        const size_t base = (size_t)(uint32_t)tab.get(min((jj << pshift) + k, nent - 1)) * pool_block;
+#pragma unroll
+        for (int n = 0; n < NLI; ++n) kb[n] = kblk[n] == k ? base : kb[n];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vb[i] = vblk[i] == k ? base : vb[i];
+      }
+#pragma unroll
+      for (int n = 0; n < NLI; ++n)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(a.k_pool + kb[n] + kin[n]),
+            (__attribute__((address_space(3))) void*)(slot_base(slot) + n * 1024), 16, 0, kKCpol);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vr[i] = *reinterpret_cast<const VT*>(a.v_pool + vb[i] + vin[i]);
+      return;
+    }
+    const size_t off = SUB ? (size_t)(uint32_t)tab.get(jj >> pshift) * (block_stride << pshift) +
+                                 (size_t)(jj & ((1 << pshift) - 1)) * block_stride
+                           : (size_t)(uint32_t)tab.get(jj) * block_stride;
     const uint32_t span = real ? (uint32_t)block_stride : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_block_rsrc(a.k_pool + off, span);
     const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, span);
@@ -557,23 +617,38 @@ DecodeFn pick_rep(int repc) {
   }
 }
 
-template <int DT, int D>
+template <int DT, int D, int MODE>
 DecodeFn pick_mfma(int wpw) {
   switch (wpw) {
-    case 1: return decode_mfma_kernel<DT, D, kRing, 1>;
-    case 2: return decode_mfma_kernel<DT, D, kRing, 2>;
-    case 4: return decode_mfma_kernel<DT, D, kRing, 4>;
+    case 1: return decode_mfma_kernel<DT, D, kRing, 1, MODE>;
+    case 2: return decode_mfma_kernel<DT, D, kRing, 2, MODE>;
+    case 4: return decode_mfma_kernel<DT, D, kRing, 4, MODE>;
     default: return nullptr;
   }
 }
 
+template <int DT, int D>
+DecodeFn pick_mfma_bs(int wpw, int block_size) {
+  if (block_size == pa::kBlockSize) return pick_mfma<DT, D, kBlocks16>(wpw);
+  if (block_size > pa::kBlockSize) return pick_mfma<DT, D, kBlocksLarge>(wpw);
+  return pick_mfma<DT, D, kBlocksSmall>(wpw);
+}
+
+int log2_int(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
 // fp32: VALU kernel (one instantiation per heads-per-wave); fp16/bf16: MFMA
 // kernel (one per waves-per-workgroup).
-DecodeFn pick_decode(int dtype, int d, const pa::DecodeGrid& g) {
+DecodeFn pick_decode(int dtype, int d, const pa::DecodeGrid& g, int block_size) {
   switch (dtype) {
     case PA_F32: return d == 64 ? pick_rep<DT_F32, 64>(g.repc) : pick_rep<DT_F32, 128>(g.repc);
-    case PA_F16: return d == 64 ? pick_mfma<DT_F16, 64>(g.wpw) : pick_mfma<DT_F16, 128>(g.wpw);
-    case PA_BF16: return d == 64 ? pick_mfma<DT_BF16, 64>(g.wpw) : pick_mfma<DT_BF16, 128>(g.wpw);
+    case PA_F16:
+      return d == 64 ? pick_mfma_bs<DT_F16, 64>(g.wpw, block_size) : pick_mfma_bs<DT_F16, 128>(g.wpw, block_size);
+    case PA_BF16:
+      return d == 64 ? pick_mfma_bs<DT_BF16, 64>(g.wpw, block_size) : pick_mfma_bs<DT_BF16, 128>(g.wpw, block_size);
     default: return nullptr;
   }
 }
@@ -606,7 +681,7 @@ int plan_decode(const void* out, const void* query, const void* k_pool, const vo
   if (partition_req == 0) {
     cus = pa::device_cu_count();
     const pa::DecodeGrid g = pa::decode_grid(shp);
-    DecodeFn fn = pick_decode(shp.dtype, shp.head_dim, g);
+    DecodeFn fn = pick_decode(shp.dtype, shp.head_dim, g, shp.block_size);
     if (!fn) return PA_ERR_UNSUPPORTED;
     per_cu = pa::resident_per_cu(reinterpret_cast<const void*>(fn), 64 * g.wpw);
     if (cus <= 0 || per_cu <= 0) return PA_ERR_HIP;
@@ -632,7 +707,7 @@ int launch_partitions(void* out, const void* query, const void* k_pool, const vo
   const pa::DecodeGrid gd = pa::decode_grid(shp);
   const int64_t grid = (int64_t)shp.num_seqs * plan.parts * gd.groups;
   if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-  DecodeFn fn = pick_decode(shp.dtype, shp.head_dim, gd);
+  DecodeFn fn = pick_decode(shp.dtype, shp.head_dim, gd, shp.block_size);
   if (!fn) return PA_ERR_UNSUPPORTED;
 
   DecodeArgs a;
@@ -649,6 +724,8 @@ int launch_partitions(void* out, const void* query, const void* k_pool, const vo
   a.rep = gd.rep;
   a.chunks = gd.chunks;
   a.max_blocks_per_seq = shp.max_blocks_per_seq;
+  a.block_shift = shp.block_size >= pa::kBlockSize ? log2_int(shp.block_size / pa::kBlockSize)
+                                                  : log2_int(pa::kBlockSize / shp.block_size);
   a.part_tokens = plan.ps;
   a.num_parts = plan.parts;
   a.groups = gd.groups;
@@ -846,7 +923,7 @@ extern "C" int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads,
   const int rc = pa::check_partition_query(shp);
   if (rc != PA_OK) return -rc;
   const pa::DecodeGrid g = pa::decode_grid(shp);
-  DecodeFn fn = pick_decode(shp.dtype, shp.head_dim, g);
+  DecodeFn fn = pick_decode(shp.dtype, shp.head_dim, g, shp.block_size);
   if (!fn) return -PA_ERR_UNSUPPORTED;
   const int cus = pa::device_cu_count();
   const int per_cu = pa::resident_per_cu(reinterpret_cast<const void*>(fn), 64 * g.wpw);

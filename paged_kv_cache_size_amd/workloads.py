@@ -233,16 +233,18 @@ def qwen1p5b_bf16(seed: int = 0, extra_cols: int = 0) -> Workload:
 
 
 def llama_gqa4k_bf16(seed: int = 0, extra_cols: int = 0, num_seqs: int = 256,
-                     context: int = 4096) -> Workload:
+                     context: int = 4096, block_size: int = 16) -> Workload:
     """Llama-style GQA layer: 256 sequences of exactly 4096 tokens (256
     blocks each); 32 query / 8 KV heads; D 128; bf16; the 65536 used blocks
-    are a random sample of a 72090-block pool, in random order."""
+    are a random sample of a 72090-block pool, in random order.  Another
+    block_size keeps the bytes and scales the block counts."""
     lens = [context] * num_seqs
-    bs = 16
+    bs = int(block_size)
     seqs, used, copies = _alloc_plain(lens, bs)
     nb = max(math.ceil(1.1 * used), used + 1)
     perm = np.random.default_rng(seed).permutation(nb)
-    return _finish("llama_gqa4k_bf16", "bf16", 32, 8, 128, bs, seqs, used, nb, perm, lens, copies,
+    name = "llama_gqa4k_bf16" if bs == 16 else f"llama_gqa4k_bf16_bs{bs}"
+    return _finish(name, "bf16", 32, 8, 128, bs, seqs, used, nb, perm, lens, copies,
                    extra_cols, f"{num_seqs} seqs x {context} tokens, H 32 / Hkv 8, D 128, bf16, NB {nb}")
 
 
@@ -311,9 +313,9 @@ def shared_prefix_bf16(seed: int = 0, extra_cols: int = 0, prompts: int = 64, sa
 
 
 def custom(lens, num_heads: int, num_kv_heads: int, head_dim: int, dtype: str, seed: int = 0,
-           extra_cols: int = 0, slack: float = 0.1, name: str = "custom") -> Workload:
+           extra_cols: int = 0, slack: float = 0.1, name: str = "custom", block_size: int = 16) -> Workload:
     """Any batch of context lengths with shuffled physical ids (edge cases)."""
-    bs = 16
+    bs = int(block_size)
     seqs, used, copies = _alloc_plain(lens, bs)
     nb = max(math.ceil((1.0 + slack) * used), used + 1)
     perm = np.random.default_rng(seed).permutation(nb)

@@ -64,7 +64,12 @@ def decode(**kw):
     (dict(scale=float("inf")), B.PA_ERR_INVALID_ARG),
     (dict(dtype=7), B.PA_ERR_UNSUPPORTED),
     (dict(D=96), B.PA_ERR_UNSUPPORTED),
-    (dict(bs=32, mb=4), B.PA_ERR_UNSUPPORTED),
+    (dict(bs=24, mb=6), B.PA_ERR_UNSUPPORTED),    # not a power of two
+    (dict(bs=512, mb=1), B.PA_ERR_UNSUPPORTED),
+    (dict(dtype=B.PA_F32, bs=32, mb=4), B.PA_ERR_UNSUPPORTED),
+    (dict(bs=32, mb=4, ps=16), B.PA_ERR_INVALID_ARG),  # partitions hold whole blocks
+    (dict(bs=4, mb=32, ps=8), B.PA_ERR_INVALID_ARG),   # and whole 16-token steps
+    (dict(bs=1, mb=128, ps=272), B.PA_ERR_INVALID_ARG),  # above 256 blocks
     (dict(ps=24), B.PA_ERR_INVALID_ARG),          # not a multiple of the block size
     (dict(ps=4112, maxlen=128), B.PA_ERR_INVALID_ARG),  # above 256 blocks
     (dict(ps=-16), B.PA_ERR_INVALID_ARG),
@@ -111,7 +116,7 @@ def prefill(**kw):
     (dict(scale=float("nan")), B.PA_ERR_INVALID_ARG),
     (dict(dtype=B.PA_F32), B.PA_ERR_UNSUPPORTED),  # the prefill tile runs on the matrix cores
     (dict(D=96), B.PA_ERR_UNSUPPORTED),
-    (dict(bs=32, mb=4), B.PA_ERR_UNSUPPORTED),
+    (dict(bs=32, mb=4), B.PA_ERR_UNSUPPORTED),    # the prefill tile reads whole 16-row blocks
     (dict(ps=24), B.PA_ERR_INVALID_ARG),
     (dict(ps=4112), B.PA_ERR_INVALID_ARG),
     (dict(ps=16), B.PA_ERR_WORKSPACE),            # 8 partitions need a workspace

@@ -293,3 +293,28 @@ def test_reshape_skips_out_of_range_slots():
     PB.pa_reshape_and_cache(t["key"], t["value"], t["k_pool"], t["v_pool"], slots)
     torch.cuda.synchronize()
     assert torch.equal(bits(before), bits(t["k_pool"]))
+
+
+# ------------------------------------------------------------------ pool block sizes
+
+BS_LENS = [1, 5, 16, 17, 100, 700, 1300, 33]
+
+
+@pytest.mark.parametrize("bs", [1, 2, 4, 8, 32, 64, 128, 256])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
+def test_block_sizes(bs, dtype, d):
+    # blocks smaller than the 16-token MFMA step are gathered row by row,
+    # larger ones are walked in 16-row windows; NaN in every unowned slot
+    w = W.custom(BS_LENS, 8, 2, d, dtype, seed=bs, extra_cols=1, block_size=bs)
+    check_whole(w, seed=bs, partition_size=0, poisoned=True)
+    check_whole(w, seed=bs, partition_size=max(16, bs), poisoned=True)
+
+
+@pytest.mark.parametrize("bs", [4, 64])
+def test_block_sizes_full_partition_policy(bs):
+    # the policy's choice given the lengths, as a scheduler would launch it
+    w = W.custom([4096] * 8 + [37, 900], 32, 8, 128, "bf16", seed=3, block_size=bs)
+    ps = PB.pa_decode_partition_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.max_context_len,
+                                     w.block_size, torch.bfloat16, context_lens=w.context_lens)
+    assert ps % max(16, bs) == 0 and ps <= 256 * bs
+    check_whole(w, seed=1, partition_size=ps)

@@ -97,3 +97,24 @@ def test_plan_argument_checks():
     assert e.value.status == B.PA_ERR_UNSUPPORTED
     with pytest.raises(ValueError):
         plan(a, np.zeros(3, np.int32))  # one length per sequence
+
+
+@pytest.mark.parametrize("bs", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+def test_block_sizes_give_whole_blocks_within_the_slice(bs):
+    lens = np.array([4096] * 64 + [100, 3000], np.int32)
+    a = (66, 32, 8, 128, 4096, bs, B.PA_BF16)
+    for l in (None, lens):
+        ps = plan(a, l)
+        assert ps % max(16, bs) == 0 and max(16, bs) <= ps <= 256 * bs
+
+
+def test_block_size_support():
+    lib = B.lib()
+    f = lambda bs, dt: lib.pa_decode_plan_partition_size(4, 8, 2, 128, 256, bs, dt, None, 256, 2)  # noqa: E731
+    for bs in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+        assert f(bs, B.PA_BF16) > 0 and f(bs, B.PA_F16) > 0
+    for bs in (3, 12, 24, 512):
+        assert f(bs, B.PA_BF16) == -B.PA_ERR_UNSUPPORTED
+    assert f(16, B.PA_F32) > 0
+    for bs in (8, 32):
+        assert f(bs, B.PA_F32) == -B.PA_ERR_UNSUPPORTED  # the fp32 tile reads whole 16-row blocks
