@@ -12,7 +12,9 @@ prefill form instead: varlen slot mapping, the pool write of every new token
 and causal paged attention of all new tokens, with the roofline taken against
 the dense matrix-core peak (the attention flops per step / the attention
 kernel's time).  ``--workload cow_copy_llama_bf16`` times the copy-on-write
-block copy (8192 whole-block copies in both pools of the Llama-style layer).
+block copy (8192 whole-block copies in both pools of the Llama-style layer),
+``--workload swap_llama_bf16`` the swap of 2048 blocks to pinned host memory
+and back.
 
 Prints ONE JSON line.  ``value`` = decode tokens/s (one new token per
 sequence per step) with every input resident in HBM; ``roofline`` = KV bytes
@@ -38,6 +40,8 @@ KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_size_amd", "csrc", "pa_kernels.h
 METRIC = "paged decode attention tokens/s and KV-read GB/s (% of MI355X HBM peak)"
 PREFILL_METRIC = "chunked-prefill paged attention new tokens/s and TFLOP/s (% of MI355X dense MFMA peak)"
 COPY_METRIC = "copy-on-write block copies/s and copy GB/s (% of MI355X HBM peak)"
+SWAP_METRIC = "block swap-out + swap-in GB/s between HBM and pinned host memory (% of a PCIe Gen5 x16 link)"
+HOST_LINK_GBPS = 64.0  # PCIe Gen5 x16, one direction, published
 
 
 def parse():
@@ -280,6 +284,62 @@ def main_copy(args):
     print(json.dumps(rec), flush=True)
 
 
+def main_swap(args):
+    import torch
+
+    import oracle as O
+    from paged_kv_cache_size_amd import binding as PB
+    from paged_kv_cache_size_amd import workloads as W
+
+    PB.lib()
+    cb = W.SWAP_BUILDERS[args.workload](seed=args.seed)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed)
+    shape = (cb.num_blocks, cb.block_size, cb.num_kv_heads, cb.head_dim)
+    kp = W._randn(shape, cb.dtype, g, "cuda")
+    vp = W._randn(shape, cb.dtype, g, "cuda")
+    n = len(cb.src)
+    hshape = (n,) + shape[1:]
+    hk = torch.empty(hshape, dtype=kp.dtype, pin_memory=True)
+    hv = torch.empty(hshape, dtype=kp.dtype, pin_memory=True)
+    dev_ids, host_ids = torch.from_numpy(cb.src).cuda(), torch.from_numpy(cb.dst).cuda()
+    base = None
+    if not args.no_cpu_baseline:
+        pool, host = W.raw_numpy(kp[:1]), None
+        sub = min(n, 1024)
+        src_np = W.raw_numpy(kp[dev_ids[:sub]])  # the blocks themselves, host side
+        host = W.raw_numpy(hk[:sub])
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < args.cpu_seconds / 2:
+            O.swap_blocks(host, src_np, list(range(sub)), list(range(sub)))
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        base = {"value": 2 * sub * cb.block_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"{sub} of {n} K blocks, host array to host array, {reps} repetitions"}
+        del pool
+    out = lambda: PB.pa_swap_blocks(hk, hv, kp, vp, dev_ids, host_ids)  # noqa: E731
+    back = lambda: PB.pa_swap_blocks(kp, vp, hk, hv, host_ids, dev_ids)  # noqa: E731
+    ms, per, wall = time_stages([out, back], args.steps, args.warmup)
+    moved = n * cb.block_bytes * 2  # K and V, one direction
+    gbps = [moved / (x * 1e-3) / 1e9 for x in per]
+    rec = {
+        "metric": SWAP_METRIC, "value": 2 * moved / (ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cb.dtype, "data": "synthetic",
+        "config": {"workload": cb.name, "num_blocks_moved": n, "block_bytes": cb.block_bytes,
+                   "description": cb.description},
+        "bytes_per_direction": moved,
+        "kernel_us": {"swap_out": per[0] * 1e3, "swap_in": per[1] * 1e3},
+        "GBps": {"swap_out": gbps[0], "swap_in": gbps[1]},
+        "roofline": {"bound": "host-link", "kernel": "copy_blocks_kernel (device <-> pinned host)",
+                     "achieved": min(gbps), "peak": HOST_LINK_GBPS, "unit": "GB/s",
+                     "frac": min(gbps) / HOST_LINK_GBPS, "traffic": None},
+        "cpu_baseline": base, "wall_s_timed": wall,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def time_stages(stages, steps, warmup):
     """Whole-step time (events around all launches) and per-stage times
     (events between launches), on torch's current stream where every call
@@ -336,6 +396,9 @@ def main():
         return
     if args.workload in W.COPY_BUILDERS:
         main_copy(args)
+        return
+    if args.workload in W.SWAP_BUILDERS:
+        main_swap(args)
         return
     PB.lib()  # fail loudly before any work if the HIP library is missing
     extra = {"block_size": args.block_size} if args.block_size else {}

@@ -302,6 +302,22 @@ int pa_copy_blocks(void* k_pool, void* v_pool, const int64_t* src_blocks, const 
                    int64_t num_blocks, pa_dtype dtype, void* stream);
 
 /*
+ * Whole-block copies between two pairs of pools of the same block shape:
+ * block dst_blocks[i] of (dst_k_pool, dst_v_pool) becomes a copy of block
+ * src_blocks[i] of (src_k_pool, src_v_pool).  One pair may live in pinned
+ * host memory (hipHostMalloc / a pinned torch tensor, which the device
+ * addresses directly): swapping a preempted sequence's blocks out of HBM and
+ * back in (handbook "分页 KV Cache", section on scheduling when memory runs
+ * short).  Id arrays in device memory; ids outside either pool skip their
+ * pair; dst ids distinct.  Errors as pa_copy_blocks (INVALID_ARG also for
+ * null source pools or src_num_blocks <= 0).
+ */
+int pa_swap_blocks(void* dst_k_pool, void* dst_v_pool, int64_t dst_num_blocks, const void* src_k_pool,
+                   const void* src_v_pool, int64_t src_num_blocks, const int64_t* src_blocks,
+                   const int64_t* dst_blocks, int64_t num_pairs, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, pa_dtype dtype, void* stream);
+
+/*
  * Host-side block pool (host memory only; no HIP call, no device memory).
  * A fixed set of num_blocks physical blocks with a FIFO free queue and a
  * reference count per block (handbook "分页 KV Cache", section "块表与 slot

@@ -21,6 +21,7 @@ title and section:
 
 from .paged_attention import (  # noqa: F401
     copy_blocks,
+    swap_blocks,
     widen,
     slot_for,
     slot_mapping,

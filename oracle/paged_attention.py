@@ -134,6 +134,19 @@ def copy_blocks(pool, src_blocks, dst_blocks):
     return pool
 
 
+def swap_blocks(dst_pool, src_pool, src_blocks, dst_blocks):
+    """Swap-out / swap-in of whole blocks between two pools of one block
+    shape (handbook "分页 KV Cache", section on scheduling when memory runs
+    short: a preempted sequence's blocks move to host memory and back):
+    ``dst_pool[dst_blocks[i]] = src_pool[src_blocks[i]]`` bit for bit, in
+    order.  Works in place on ``dst_pool`` and returns it."""
+    assert dst_pool.shape[1:] == src_pool.shape[1:] and dst_pool.dtype == src_pool.dtype
+    assert len(src_blocks) == len(dst_blocks)
+    for s, d in zip(src_blocks, dst_blocks):
+        dst_pool[int(d)] = src_pool[int(s)]
+    return dst_pool
+
+
 def gather(pool, block_table, seq_len):
     """The first ``seq_len`` tokens of one sequence, ``[seq_len, H_kv, D]``.
 

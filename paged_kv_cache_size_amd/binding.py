@@ -41,6 +41,7 @@ SIGNATURES = {
                                             _I32, _I32, _F32, ctypes.c_int, _P, _SZ, _I32, _P]),
     "pa_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I64, ctypes.c_int, _P]),
+    "pa_swap_blocks": (ctypes.c_int, [_P, _P, _I64, _P, _P, _I64, _P, _P, _I64, _I32, _I32, _I32, ctypes.c_int, _P]),
     "pa_block_pool_create": (_P, [_I32, _I32, _P]),
     "pa_block_pool_destroy": (None, [_P]),
     "pa_block_pool_num_free": (_I32, [_P]),
@@ -309,6 +310,29 @@ def pa_copy_blocks(k_pool, v_pool, src_blocks, dst_blocks):
                               _dev(dst_blocks, "dst_blocks", torch.int64, 1) if n else None, n, bs, hkv, d, nb,
                               pa_dtype(k_pool), _stream(k_pool))
     _check(rc, "pa_copy_blocks")
+
+
+def pa_swap_blocks(dst_k_pool, dst_v_pool, src_k_pool, src_v_pool, src_blocks, dst_blocks, stream_of=None):
+    """Copy whole blocks src pools -> dst pools (either pair may be pinned
+    host tensors); id tensors (int64) on the device."""
+    torch = _torch()
+    if dst_k_pool.shape[1:] != src_k_pool.shape[1:] or dst_k_pool.dtype != src_k_pool.dtype:
+        raise ValueError("pools differ in block shape or dtype")
+    for t in (dst_k_pool, dst_v_pool, src_k_pool, src_v_pool):
+        if not t.is_contiguous() or not (t.is_cuda or t.is_pinned()):
+            raise ValueError("pools must be contiguous device tensors or pinned host tensors")
+    n = int(src_blocks.numel())
+    if dst_blocks.numel() != n:
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    _, bs, hkv, d = dst_k_pool.shape
+    dev = stream_of if stream_of is not None else (src_blocks if n else dst_k_pool)
+    rc = lib().pa_swap_blocks(
+        ctypes.c_void_p(dst_k_pool.data_ptr()), ctypes.c_void_p(dst_v_pool.data_ptr()), dst_k_pool.shape[0],
+        ctypes.c_void_p(src_k_pool.data_ptr()), ctypes.c_void_p(src_v_pool.data_ptr()), src_k_pool.shape[0],
+        _dev(src_blocks, "src_blocks", torch.int64, 1) if n else None,
+        _dev(dst_blocks, "dst_blocks", torch.int64, 1) if n else None, n, bs, hkv, d, pa_dtype(dst_k_pool),
+        _stream(dev) if dev.is_cuda else None)
+    _check(rc, "pa_swap_blocks")
 
 
 class SharedPrefixGroups:

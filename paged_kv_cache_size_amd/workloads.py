@@ -474,7 +474,18 @@ def cow_copy_llama_bf16(seed: int = 0, num_pairs: int = 8192) -> CopyBatch:
     return cb
 
 
+def swap_llama_bf16(seed: int = 0, num_pairs: int = 2048) -> CopyBatch:
+    """Swap-out of 2048 random blocks of the Llama-style layer's pool (a
+    preempted batch's 2048 x 16 tokens, 128 MiB of K and V) into a host pool
+    of 2048 blocks, in order; the swap-in reverses the pairs."""
+    ids = np.random.default_rng(seed).permutation(72090)[:num_pairs].astype(np.int64)
+    return CopyBatch("swap_llama_bf16", "bf16", 72090, 16, 8, 128, ids, np.arange(num_pairs, dtype=np.int64),
+                     f"{num_pairs} blocks of a 72090-block pool to a {num_pairs}-block pinned host pool and back, "
+                     "H_kv 8, D 128, bf16")
+
+
 COPY_BUILDERS = {"cow_copy_llama_bf16": cow_copy_llama_bf16}
+SWAP_BUILDERS = {"swap_llama_bf16": swap_llama_bf16}
 
 
 # --------------------------------------------------------------------------

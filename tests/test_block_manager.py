@@ -198,3 +198,29 @@ def test_copy_on_write_keeps_both_views():
     np.testing.assert_array_equal(kp[2], snapshot[1])  # the whole block, tail rows included
     others = [b for b in range(16) if b != 2]
     np.testing.assert_array_equal(kp[others], snapshot[others])
+
+
+def test_swap_out_and_in_keeps_attention():
+    # a preempted sequence's blocks go to a host pool and come back to other
+    # device blocks: with the table renumbered, attention is unchanged, and
+    # no other block of either pool moves
+    rng = np.random.default_rng(2)
+    dev_k = rng.standard_normal((12, 4, 2, 8)).astype(np.float32)
+    dev_v = rng.standard_normal((12, 4, 2, 8)).astype(np.float32)
+    host_k = np.zeros((5, 4, 2, 8), np.float32)
+    host_v = np.zeros_like(host_k)
+    table, L = [7, 2, 9], 11
+    q = rng.standard_normal((1, 4, 8)).astype(np.float32)
+    before = O.decode_attention(q, dev_k, dev_v, [table], [L], 0.35, "f32")
+    snap_k, snap_v = dev_k.copy(), dev_v.copy()
+    O.swap_blocks(host_k, dev_k, table, [4, 0, 3])
+    O.swap_blocks(host_v, dev_v, table, [4, 0, 3])
+    assert not host_k[[1, 2]].any()
+    new_table = [5, 11, 0]
+    O.swap_blocks(dev_k, host_k, [4, 0, 3], new_table)
+    O.swap_blocks(dev_v, host_v, [4, 0, 3], new_table)
+    after = O.decode_attention(q, dev_k, dev_v, [new_table], [L], 0.35, "f32")
+    np.testing.assert_array_equal(before, after)
+    others = [b for b in range(12) if b not in new_table]
+    np.testing.assert_array_equal(dev_k[others], snap_k[others])
+    np.testing.assert_array_equal(dev_v[others], snap_v[others])

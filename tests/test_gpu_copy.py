@@ -122,3 +122,45 @@ def test_fork_copy_on_write_then_decode():
     for r in range(6):
         a, b, c = tables[3 * r:3 * r + 3]
         assert a[:2] == b[:2] == c[:2] and len({a[2], b[2], c[2]}) == 3
+
+
+@pytest.mark.parametrize("dtype,bs,hkv,d", [("bf16", 16, 8, 128), ("f32", 16, 2, 64), ("f16", 4, 2, 128)])
+def test_swap_out_to_host_and_back(dtype, bs, hkv, d):
+    # swap-out of a batch's blocks into a pinned host pool, swap-in to other
+    # device blocks; both moves bit-exact, and decode over the renumbered
+    # tables gives the same output, bit for bit
+    h = 8 if hkv == 2 else 32  # a pool twice the used blocks, so they can come back elsewhere
+    w = W.custom([40, 300, 17, 999], h, hkv, d, dtype, seed=8, block_size=bs, slack=1.2)
+    t = W.make_tensors(w, 0, DEV)
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    lens = torch.from_numpy(w.context_lens).to(DEV)
+    out0 = PB.pa_decode_attention(t["query"], t["k_pool"], t["v_pool"], bt, lens, w.scale, w.max_context_len)
+    used = sorted({int(x) for b in range(w.num_seqs)
+                   for x in w.block_tables[b, :O.num_blocks(int(w.context_lens[b]), bs)]})
+    nh = len(used) + 3
+    host_k = torch.empty((nh,) + tuple(t["k_pool"].shape[1:]), dtype=t["k_pool"].dtype, pin_memory=True)
+    host_v = torch.empty_like(host_k, pin_memory=True)
+    host_k.zero_()
+    host_v.zero_()
+    host_ids = np.random.default_rng(1).permutation(nh)[:len(used)]
+    src = torch.tensor(used, dtype=torch.int64, device=DEV)
+    hid = torch.tensor(host_ids, dtype=torch.int64, device=DEV)
+    ref_k, ref_v = W.raw_numpy(t["k_pool"]), W.raw_numpy(t["v_pool"])
+    PB.pa_swap_blocks(host_k, host_v, t["k_pool"], t["v_pool"], src, hid)
+    torch.cuda.synchronize()
+    hk_ref = O.swap_blocks(W.raw_numpy(torch.zeros_like(host_k)), ref_k, used, host_ids)
+    assert np.array_equal(W.raw_numpy(host_k).view(np.uint8), hk_ref.view(np.uint8))
+    # back in, onto free device blocks
+    free = [b for b in range(w.num_blocks) if b not in set(used)]
+    new_ids = np.random.default_rng(2).permutation(free)[:len(used)]
+    PB.pa_swap_blocks(t["k_pool"], t["v_pool"], host_k, host_v, hid,
+                      torch.tensor(new_ids, dtype=torch.int64, device=DEV))
+    remap = dict(zip(used, new_ids.tolist()))
+    bt2 = np.array([[remap.get(int(x), int(x)) for x in row] for row in w.block_tables], np.int32)
+    out1 = PB.pa_decode_attention(t["query"], t["k_pool"], t["v_pool"], torch.from_numpy(bt2).to(DEV), lens,
+                                  w.scale, w.max_context_len)
+    torch.cuda.synchronize()
+    ref_v2 = O.swap_blocks(ref_v.copy(), ref_v, used, new_ids)
+    assert np.array_equal(W.raw_numpy(t["v_pool"]).view(np.uint8), ref_v2.view(np.uint8))
+    bits = (lambda x: x.view(torch.int32)) if dtype == "f32" else (lambda x: x.view(torch.int16))
+    assert torch.equal(bits(out0), bits(out1))
