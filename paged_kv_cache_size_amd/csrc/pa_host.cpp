@@ -323,9 +323,9 @@ PrefillGrid prefill_grid(const PrefillShape& s) {
   const int64_t cols = (int64_t)s.max_query_len * g.repc;
   p.wide = cols >= kPrefillWideCols;
   if (p.wide) {
-    p.tiles = (int)((cols + 127) / 128);
+    p.tiles = (int)((cols + 32 * kPrefillWgWaves - 1) / (32 * kPrefillWgWaves));
     p.groups = g.units;
-    p.waves = 4;
+    p.waves = kPrefillWgWaves;
   } else {
     p.tiles = prefill_tiles(s, g);
     p.groups = g.groups;

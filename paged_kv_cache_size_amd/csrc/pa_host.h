@@ -103,6 +103,10 @@ int prefill_tiles(const PrefillShape& s, const DecodeGrid& g);
 // Wide ones run the cooperative tile: 4 waves share one unit's K/V blocks and
 // take 128 columns.
 constexpr int kPrefillWideCols = 64;
+#ifndef PA_PREFILL_WG_WAVES
+#define PA_PREFILL_WG_WAVES 4
+#endif
+constexpr int kPrefillWgWaves = PA_PREFILL_WG_WAVES;  // waves of the cooperative tile, 32 columns each
 struct PrefillGrid {
   bool wide;
   int tiles;       // column tiles (16 columns) or column groups (128 columns) per sequence

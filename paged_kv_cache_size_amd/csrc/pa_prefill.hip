@@ -328,21 +328,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Cooperative form for wide column ranges (long varlen rows, chunked
-// prefill): the 4 waves of a workgroup take 128 consecutive columns of one
-// (sequence, KV head unit) - 32 per wave, as two 16-column tiles - and share
+// prefill): the waves of a workgroup take 32 consecutive columns each of one
+// (sequence, KV head unit), as two 16-column tiles, and share
 // one copy of each K/V block.  The blocks stream through an LDS ring of
 // 2 * NP blocks, K swizzled as in the per-wave tile and V row-major, filled by
-// direct-to-LDS loads that the four waves split between them; one barrier
+// direct-to-LDS loads that the waves split between them; one barrier
 // per two-block step publishes a pair and frees the pair read in the step
 // before.  Each wave reads K (the QK A operand) and its V rows (the P.V A
 // operand) from LDS once per step and applies them to both of its tiles.
 // Arithmetic per tile is that of prefill_mfma_kernel: 32-key steps, P.V on
 // 16x16x32, lazily moved running max, mask-free interior steps.
-constexpr int kWgCols = 128;   // columns per workgroup
-constexpr int kWaveCols = 32;  // columns per wave (two MFMA tiles)
+constexpr int kWaveCols = 32;                           // columns per wave (two MFMA tiles)
+constexpr int kWgWaves = pa::kPrefillWgWaves;           // waves per workgroup (8 measured 6% slower)
+constexpr int kWgCols = kWaveCols * kWgWaves;           // columns per workgroup
 
 template <int DT, int D, int NP>
-__global__ __launch_bounds__(256) void prefill_wg_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const PrefillArgs a) {
   using Ops = MfmaOps<DT>;
   constexpr int BS = pa::kBlockSize;
   constexpr int ROWB = D * 2;
@@ -350,11 +351,13 @@ __global__ __launch_bounds__(256) void prefill_wg_kernel(const PrefillArgs a) {
   constexpr int VPL = D / 16;
   constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
   constexpr int KI = BS * CPR / 64;         // load instructions per block for K (and for V)
-  constexpr int DPW = 2 * KI / 4;           // load instructions per block and wave (K and V split over 4 waves)
+  // load instructions per block and wave: K and V split over the waves (with
+  // more waves than instructions the last waves issue none)
+  constexpr int DPW = (2 * KI + kWgWaves - 1) / kWgWaves;
   constexpr int KBYTES = BS * ROWB;
   constexpr int RB = 2 * NP;                // ring blocks
   using VT = typename VRow<VPL>::T;
-  static_assert(BS == 16 && DPW >= 1 && (2 * KI) % 4 == 0, "tile shape");
+  static_assert(BS == 16 && (2 * KI) % DPW == 0, "tile shape");
   static_assert(NP == 3, "the ring is unrolled for three pairs");
 
   const int lane = threadIdx.x & 63;
@@ -431,11 +434,12 @@ __global__ __launch_bounds__(256) void prefill_wg_kernel(const PrefillArgs a) {
   const uint32_t row_stride = (uint32_t)a.num_kv_heads * ROWB;
   const size_t block_stride = (size_t)BS * row_stride;
   uint32_t goff[DPW];
-  bool is_k[DPW];
+  bool is_k[DPW], has[DPW];
   int lds_off[DPW];
 #pragma unroll
   for (int i = 0; i < DPW; ++i) {
     const int ins = wave * DPW + i;
+    has[i] = (2 * KI) % kWgWaves == 0 || ins < 2 * KI;  // every wave loads when the split is even
     is_k[i] = ins < KI;
     const int idx = is_k[i] ? ins : ins - KI;
     const int sl = 64 * idx + lane, t = sl / CPR, q = sl % CPR;
@@ -478,6 +482,7 @@ __global__ __launch_bounds__(256) void prefill_wg_kernel(const PrefillArgs a) {
     const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, span);
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
+      if (!has[i]) continue;
       if (is_k[i])
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kslot(x) + lds_off[i]),
                                                  16, (int)goff[i], 0, 0, 0);
