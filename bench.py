@@ -213,6 +213,11 @@ def main_prefill(args):
     ms_per_step, per_kernel_ms, wall = time_stages(stages, args.steps, args.warmup)
     flops = pb.attention_flops()
     attn_ms = per_kernel_ms[2]
+    # the library runs the cooperative tile once a sequence brings 64 or more
+    # (token, query head) columns per KV head
+    rep = H // w.num_kv_heads
+    repc = max(c for c in range(1, 17) if rep % c == 0)
+    kernel = "prefill_wg_kernel" if pb.max_query_len * repc >= 64 else "prefill_mfma_kernel"
     achieved = flops / (attn_ms * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[w.dtype]
     rec = {
@@ -226,7 +231,7 @@ def main_prefill(args):
         "attention_flops_per_step": flops,
         "kernel_us": {"slot_mapping": per_kernel_ms[0] * 1e3, "reshape_and_cache": per_kernel_ms[1] * 1e3,
                       "prefill_attention": attn_ms * 1e3},
-        "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel", "achieved": achieved, "peak": peak,
+        "roofline": {"bound": "mfma", "kernel": kernel, "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": load_traffic(pb.name, "prefill_attention")},
         "kv_read_bytes_per_step": pb.kv_read_bytes(),
