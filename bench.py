@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--workload", default="llama_gqa4k_bf16")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--partition-size", type=int, default=0)
+    p.add_argument("--replicas", type=int, default=1,
+                   help="rotate over this many copies of the pools (cold caches for small batches)")
     p.add_argument("--block-size", type=int, default=0,
                    help="pool block size for the Llama-layer workload (default 16)")
     p.add_argument("--shared-prefix", action="store_true",
@@ -410,6 +412,14 @@ def main():
     w = W.make_workload(args.workload, seed=args.seed, **extra)
     t = W.make_tensors(w, seed=args.seed, device="cuda")
     dev = "cuda"
+    # Batches smaller than the 256 MiB MALL stay cache-resident when one pool
+    # is re-read every step; --replicas R rotates the steps over R copies.
+    pools = [(t["k_pool"], t["v_pool"])] + [(t["k_pool"].clone(), t["v_pool"].clone())
+                                            for _ in range(max(1, args.replicas) - 1)]
+    turn = [0]
+
+    def pool():
+        return pools[turn[0] % len(pools)]
     bt = torch.from_numpy(w.block_tables).to(dev)
     lens = torch.from_numpy(w.context_lens).to(dev)
     B, H, D = t["query"].shape
@@ -430,10 +440,11 @@ def main():
         PB.pa_slot_mapping(bt, lens, w.block_size, out=slots)
 
     def k_write():
-        PB.pa_reshape_and_cache(t["key"], t["value"], t["k_pool"], t["v_pool"], slots)
+        turn[0] += 1
+        PB.pa_reshape_and_cache(t["key"], t["value"], *pool(), slots)
 
     def k_part():
-        PB.pa_decode_partitions(t["query"], t["k_pool"], t["v_pool"], bt, lens, w.scale, w.max_context_len, ps,
+        PB.pa_decode_partitions(t["query"], *pool(), bt, lens, w.scale, w.max_context_len, ps,
                                 workspace=ws, out=out)
 
     def k_comb():
@@ -451,7 +462,7 @@ def main():
                           dtype=torch.uint8, device=dev)
 
         def k_cascade():
-            PB.pa_decode_attention_shared_prefix(t["query"], t["k_pool"], t["v_pool"], bt, lens, groups, w.scale,
+            PB.pa_decode_attention_shared_prefix(t["query"], *pool(), bt, lens, groups, w.scale,
                                                  w.max_context_len, out=out, workspace=cws, device_groups=dgroups)
 
         stages = [k_slot, k_write, k_cascade, lambda: None]
@@ -484,6 +495,7 @@ def main():
                    "max_context_len": w.max_context_len, "num_heads": H, "num_kv_heads": w.num_kv_heads,
                    "head_dim": D, "block_size": w.block_size, "num_blocks": w.num_blocks,
                    "partition_size": ps, "shared_prefix_cascade": bool(args.shared_prefix),
+                   "pool_replicas": len(pools),
                    "description": w.description},
         "kv_read_bytes_per_step": kv_bytes,
         "kv_unique_read_bytes_per_step": kv_unique,

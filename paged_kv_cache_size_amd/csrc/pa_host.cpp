@@ -323,7 +323,7 @@ PrefillGrid prefill_grid(const PrefillShape& s) {
   const int64_t cols = (int64_t)s.max_query_len * g.repc;
   p.wide = cols >= kPrefillWideCols;
   if (p.wide) {
-    p.tiles = (int)((cols + 32 * kPrefillWgWaves - 1) / (32 * kPrefillWgWaves));
+    p.tiles = (int)((cols + kPrefillWgCols - 1) / kPrefillWgCols);
     p.groups = g.units;
     p.waves = kPrefillWgWaves;
   } else {

@@ -106,7 +106,12 @@ constexpr int kPrefillWideCols = 64;
 #ifndef PA_PREFILL_WG_WAVES
 #define PA_PREFILL_WG_WAVES 4
 #endif
-constexpr int kPrefillWgWaves = PA_PREFILL_WG_WAVES;  // waves of the cooperative tile, 32 columns each
+constexpr int kPrefillWgWaves = PA_PREFILL_WG_WAVES;  // waves of the cooperative tile
+#ifndef PA_PREFILL_WAVE_TILES
+#define PA_PREFILL_WAVE_TILES 2
+#endif
+constexpr int kPrefillWaveTiles = PA_PREFILL_WAVE_TILES;  // 16-column MFMA tiles per wave of the cooperative tile
+constexpr int kPrefillWgCols = 16 * kPrefillWaveTiles * kPrefillWgWaves;  // columns per cooperative workgroup
 struct PrefillGrid {
   bool wide;
   int tiles;       // column tiles (16 columns) or column groups (128 columns) per sequence

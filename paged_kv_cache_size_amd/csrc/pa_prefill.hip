@@ -338,7 +338,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // operand) from LDS once per step and applies them to both of its tiles.
 // Arithmetic per tile is that of prefill_mfma_kernel: 32-key steps, P.V on
 // 16x16x32, lazily moved running max, mask-free interior steps.
-constexpr int kWaveCols = 32;                           // columns per wave (two MFMA tiles)
+constexpr int kWaveTiles = pa::kPrefillWaveTiles;      // 16-column MFMA tiles per wave
+constexpr int kWaveCols = 16 * kWaveTiles;             // columns per wave
 constexpr int kWgWaves = pa::kPrefillWgWaves;           // waves per workgroup (8 measured 6% slower)
 constexpr int kWgCols = kWaveCols * kWgWaves;           // columns per workgroup
 
@@ -384,11 +385,11 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
   const int end = min(pend, a.causal ? L - n + last_tok + 1 : L);  // keys any column here sees
 
   // This lane's two columns.
-  int pos[2], lim[2], col_parts[2];
-  bool live[2];
-  size_t qrow[2];
+  int pos[kWaveTiles], lim[kWaveTiles], col_parts[kWaveTiles];
+  bool live[kWaveTiles];
+  size_t qrow[kWaveTiles];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < kWaveTiles; ++tt) {
     const int cc = kWgCols * k + kWaveCols * wave + 16 * tt + col;
     const int ti = cc / a.repc;
     live[tt] = ti < n;
@@ -401,7 +402,7 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
   if (start >= end) {  // uniform over the workgroup
     if (a.partial_base >= 0)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < kWaveTiles; ++tt)
         if (live[tt]) store_empty_slot<D>(a, qrow[tt], s, gq);
     return;
   }
@@ -416,9 +417,9 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
   TableSlice tab;
   tab.load(bt, nblk, lane);
 
-  uint4 qop[2][NKC];
+  uint4 qop[kWaveTiles][NKC];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < kWaveTiles; ++tt) {
     const uint8_t* qp = (const uint8_t*)a.query + qrow[tt] * ROWB + gq * 16;
 #pragma unroll
     for (int c = 0; c < NKC; ++c) {
@@ -465,12 +466,17 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
     return x == 0 ? vs0 : x == 1 ? vs1 : x == 2 ? vs2 : x == 3 ? vs3 : x == 4 ? vs4 : vs5;
   };
 
-  f32x4 acc[2][VPL];
+  f32x4 acc[kWaveTiles][VPL];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+  for (int tt = 0; tt < kWaveTiles; ++tt)
 #pragma unroll
     for (int t = 0; t < VPL; ++t) acc[tt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {kMaxFloor, kMaxFloor}, l[2] = {0.f, 0.f};
+  float m[kWaveTiles], l[kWaveTiles];
+#pragma unroll
+  for (int tt = 0; tt < kWaveTiles; ++tt) {
+    m[tt] = kMaxFloor;
+    l[tt] = 0.f;
+  }
 
   // Loads past the partition go through an empty descriptor (zeros, no
   // memory access), so every wait count is exact.
@@ -514,9 +520,9 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
         v[i] = key < end ? v[i] : VT{};  // rows past the last key (stale, even NaN) must not reach the MFMA
       }
     }
-    uint4 pb[2];
+    uint4 pb[kWaveTiles];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < kWaveTiles; ++tt) {
       f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NKC; ++c) {
@@ -558,8 +564,8 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
                                   __builtin_amdgcn_perm(vword<VPL>(v[3], w), vword<VPL>(v[2], w), sel),
                                   __builtin_amdgcn_perm(vword<VPL>(v[5], w), vword<VPL>(v[4], w), sel),
                                   __builtin_amdgcn_perm(vword<VPL>(v[7], w), vword<VPL>(v[6], w), sel));
-      acc[0][t] = Ops::qk(vt, pb[0], acc[0][t]);
-      acc[1][t] = Ops::qk(vt, pb[1], acc[1][t]);
+#pragma unroll
+      for (int tt = 0; tt < kWaveTiles; ++tt) acc[tt][t] = Ops::qk(vt, pb[tt], acc[tt][t]);
     }
   };
   // One ring step: wait for this wave's loads of the pair in slots (xa, xb),
@@ -591,7 +597,7 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
   }
 
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < kWaveTiles; ++tt) {
     const float lt = rows_sum(l[tt]);
     if (live[tt]) store_column<DT, D>(a, acc[tt], m[tt], lt, qrow[tt], s, col_parts[tt], gq);
   }
