@@ -47,7 +47,7 @@ HOST_LINK_GBPS = 64.0  # PCIe Gen5 x16, one direction, published
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llama_gqa4k_bf16")
     p.add_argument("--seed", type=int, default=0)
@@ -59,20 +59,28 @@ def parse():
     p.add_argument("--shared-prefix", action="store_true",
                    help="decode with shared prompt prefixes read once per group (cascade)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle CPU time")
+    p.add_argument("--cpu-seconds", type=float, default=16.0,
+                   help="target oracle time (split between the one-thread and all-cores runs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device copy (counter calibration) and exit")
     return p.parse_args()
 
 
-def kernel_source_hash():
-    """Hash of the kernel sources (the .hip files and the device header)."""
+# the device sources each counted kernel is built from
+KERNEL_SOURCES = {
+    "decode_partition": ("pa_kernels.hip", "pa_device.h"),
+    "prefill_attention": ("pa_prefill.hip", "pa_device.h"),
+    "copy_blocks": ("pa_copy.hip",),
+}
+
+
+def kernel_source_hash(prefix="decode_partition"):
+    """Hash of the device sources of one kernel family."""
     h = hashlib.sha256()
     csrc = os.path.dirname(KERNEL_SRC)
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith(".hip") or name == "pa_device.h":
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(f.read())
+    for name in KERNEL_SOURCES[prefix]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -84,7 +92,7 @@ def load_traffic(workload, prefix="decode_partition"):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(prefix):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -100,46 +108,117 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
 
 
-def cpu_baseline(w, t, seconds):
+def cpu_pool_size():
+    """Worker processes for the all-cores oracle run: the cores this process
+    may use, at most 16 (one GPU's share of a host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def start_oracle_pool():
+    """Workers for the all-cores oracle run, forked before this process first
+    touches the GPU (they never do), each limited to one BLAS thread."""
+    import multiprocessing as mp
+    return mp.get_context("fork").Pool(cpu_pool_size(), initializer=_oracle_worker_init)
+
+
+def _oracle_worker_init():
+    from threadpoolctl import threadpool_limits
+    global _WORKER_LIMITS
+    _WORKER_LIMITS = threadpool_limits(1)
+
+
+def _oracle_seq(task):
+    """Slot mapping, pool write and float64 decode attention (the oracle) of
+    one sequence whose compacted inputs sit in a host file mapping; returns
+    the seconds spent."""
+    import numpy as np
+
+    import oracle as O
+    path, fields, table, L, block_size, scale, dtype = task
+    mm = np.memmap(path, dtype=np.uint8, mode="r+")
+    a = {k: np.ndarray(shape, np.dtype(dt), buffer=mm, offset=off) for k, (off, shape, dt) in fields.items()}
+    t0 = time.perf_counter()
+    slots = O.slot_mapping([table], [L], block_size)
+    O.reshape_and_cache(a["kp"], a["key"], slots)
+    O.reshape_and_cache(a["vp"], a["val"], slots)
+    O.decode_attention(a["q"], a["kp"], a["vp"], [table], [L], scale, dtype)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(w, t, seconds, pool):
     """The oracle as it stands, timed on the host on whole sequences of the
-    same batch: slot mapping, pool write and decode attention."""
+    same batch (slot mapping, pool write, float64 decode attention): on one
+    thread, and on all cores with one sequence per worker process.  Each
+    sequence's blocks are compacted into a host file mapping that the workers
+    share; copying them there is not timed."""
+    import tempfile
+
     import numpy as np
     import torch
+    from threadpoolctl import threadpool_limits
 
     import oracle as O
     from paged_kv_cache_size_amd import workloads as W
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    nproc = pool._processes
+    bs = w.block_size
 
-    def run(seqs):
-        blocks = sorted({int(x) for b in seqs
-                         for x in w.block_tables[b, :O.num_blocks(int(w.context_lens[b]), w.block_size)]})
-        remap = {x: i for i, x in enumerate(blocks)}
-        idx = torch.tensor(blocks, device="cuda")
-        kp, vp = W.raw_numpy(t["k_pool"][idx]), W.raw_numpy(t["v_pool"][idx])
-        tables = [[remap[int(x)] for x in w.block_tables[b, :O.num_blocks(int(w.context_lens[b]), w.block_size)]]
-                  for b in seqs]
-        lens = [int(w.context_lens[b]) for b in seqs]
-        sel = torch.tensor(seqs, device="cuda")
-        q, key, val = (W.raw_numpy(t[k][sel]) for k in ("query", "key", "value"))
+    def seq_arrays(b):
+        nb = O.num_blocks(int(w.context_lens[b]), bs)
+        idx = torch.from_numpy(w.block_tables[b, :nb].astype(np.int64)).to(t["k_pool"].device)
+        return {"kp": W.raw_numpy(t["k_pool"][idx]), "vp": W.raw_numpy(t["v_pool"][idx]),
+                "q": W.raw_numpy(t["query"][b:b + 1]), "key": W.raw_numpy(t["key"][b:b + 1]),
+                "val": W.raw_numpy(t["value"][b:b + 1])}, list(range(nb))
+
+    def run_one(b, arrays, table):
         t0 = time.perf_counter()
-        slots = O.slot_mapping(tables, lens, w.block_size)
-        O.reshape_and_cache(kp, key, slots)
-        O.reshape_and_cache(vp, val, slots)
-        O.decode_attention(q, kp, vp, tables, lens, w.scale, w.dtype)
+        slots = O.slot_mapping([table], [int(w.context_lens[b])], bs)
+        O.reshape_and_cache(arrays["kp"], arrays["key"], slots)
+        O.reshape_and_cache(arrays["vp"], arrays["val"], slots)
+        O.decode_attention(arrays["q"], arrays["kp"], arrays["vp"], [table], [int(w.context_lens[b])], w.scale,
+                           w.dtype)
         return time.perf_counter() - t0
 
-    one = run([0])
-    n = int(max(1, min(w.num_seqs, seconds / max(one, 1e-6))))
-    seqs = list(range(n))
-    dt = run(seqs)
-    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} of {w.num_seqs} sequences (whole contexts) of {w.name}; "
-                      f"slot mapping + pool write + float64 attention, {dt:.1f} s"}
+    half = seconds / 2
+    with threadpool_limits(1):
+        a0, tab0 = seq_arrays(0)
+        one = run_one(0, a0, tab0)
+        n1 = int(max(1, min(w.num_seqs, half / max(one, 1e-6))))
+        single = 0.0
+        for b in range(n1):
+            arrays, table = seq_arrays(b)
+            single += run_one(b, arrays, table)
+    n2 = int(max(1, min(w.num_seqs, half * nproc / max(one, 1e-6))))
+
+    fd, path = tempfile.mkstemp(prefix="pa_oracle_", dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+    os.close(fd)
+    try:
+        tasks, off, chunks = [], 0, []
+        for b in range(n2):
+            arrays, table = seq_arrays(b)
+            fields = {}
+            for k, x in arrays.items():
+                fields[k] = (off, x.shape, x.dtype.str)
+                chunks.append((off, x))
+                off += (x.nbytes + 63) // 64 * 64
+            tasks.append((path, fields, table, int(w.context_lens[b]), bs, w.scale, w.dtype))
+        mm = np.memmap(path, dtype=np.uint8, mode="w+", shape=(max(off, 1),))
+        for o, x in chunks:
+            mm[o:o + x.nbytes] = np.ascontiguousarray(x).view(np.uint8).reshape(-1)
+        mm.flush()
+        del mm, chunks
+        t0 = time.perf_counter()
+        busy = sum(pool.map(_oracle_seq, tasks, chunksize=1))
+        wall = time.perf_counter() - t0
+    finally:
+        os.unlink(path)
+    return {"value": n2 / wall, "unit": "tokens/s", "cores": nproc, "kind": "oracle",
+            "sample": f"{n2} of {w.num_seqs} sequences (whole contexts) of {w.name}, one per worker process, "
+                      f"{nproc} processes of one thread: slot mapping + pool write + float64 attention, "
+                      f"{wall:.1f} s wall ({busy:.1f} s busy)",
+            "single_thread": {"value": n1 / single, "unit": "tokens/s", "cores": 1,
+                              "sample": f"{n1} sequences, {single:.1f} s"},
+            "os_cpu_count": os.cpu_count(), "sched_affinity": len(os.sched_getaffinity(0))}
 
 
 def prefill_cpu_baseline(pb, t, seconds):
@@ -377,8 +456,44 @@ def time_stages(stages, steps, warmup):
             f()
             evs[i][j + 1].record()
     torch.cuda.synchronize()
-    per = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps for j in range(len(stages))]
+    samples = [[evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)] for j in range(len(stages))]
+    per = [sum(x) / steps for x in samples]
+    time_stages.samples = samples  # per stage, per step (ms)
     return ms_per_step, per, wall
+
+
+def percentiles_us(ms):
+    """p10 / p50 / p90 of a list of times in ms, in us."""
+    import numpy as np
+    p10, p50, p90 = np.percentile(np.asarray(ms, dtype=np.float64) * 1e3, [10, 50, 90])
+    return {"p10": float(p10), "p50": float(p50), "p90": float(p90)}
+
+
+def stream_ceiling(buffers, reps=20):
+    """The device's streaming read rate over the given device tensors (each
+    read once per rep with pa_stream_read), default and non-temporal loads."""
+    import torch
+
+    from paged_kv_cache_size_amd import binding as PB
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nbytes = sum(b.numel() * b.element_size() for b in buffers)
+    res = {"bytes": nbytes}
+    for name, nt in (("default_GBps", False), ("nontemporal_GBps", True)):
+        def rep():
+            for b in buffers:
+                PB.pa_stream_read(b, sink, nontemporal=nt)
+        for _ in range(3):
+            rep()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            rep()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    res["GBps"] = max(res["default_GBps"], res["nontemporal_GBps"])
+    return res
 
 
 def main():
@@ -395,7 +510,6 @@ def main():
         copy_calibration()
         return
 
-    from paged_kv_cache_size_amd import binding as PB
     from paged_kv_cache_size_amd import workloads as W
 
     if args.workload in W.PREFILL_BUILDERS:
@@ -407,6 +521,22 @@ def main():
     if args.workload in W.SWAP_BUILDERS:
         main_swap(args)
         return
+    # the oracle's worker processes are forked before anything touches the GPU
+    oracle_pool = None if args.no_cpu_baseline else start_oracle_pool()
+    try:
+        main_decode(args, oracle_pool)
+    finally:
+        if oracle_pool is not None:
+            oracle_pool.terminate()
+            oracle_pool.join()
+
+
+def main_decode(args, oracle_pool):
+    import torch
+
+    from paged_kv_cache_size_amd import binding as PB
+    from paged_kv_cache_size_amd import workloads as W
+
     PB.lib()  # fail loudly before any work if the HIP library is missing
     extra = {"block_size": args.block_size} if args.block_size else {}
     w = W.make_workload(args.workload, seed=args.seed, **extra)
@@ -433,8 +563,8 @@ def main():
     slots = torch.empty(B, dtype=torch.int64, device=dev)
 
     base = None
-    if not args.no_cpu_baseline:
-        base = cpu_baseline(w, t, args.cpu_seconds)
+    if oracle_pool is not None:
+        base = cpu_baseline(w, t, args.cpu_seconds, oracle_pool)
 
     def k_slot():
         PB.pa_slot_mapping(bt, lens, w.block_size, out=slots)
@@ -469,6 +599,9 @@ def main():
         kernel = "prefill_mfma_kernel prefix + suffix passes and merge_slots_kernel (one stage)"
         ps = 0
     ms_per_step, per_kernel_ms, wall = time_stages(stages, args.steps, args.warmup)
+    part_pct = percentiles_us(time_stages.samples[2])
+    step_pct = percentiles_us([sum(x) for x in zip(*time_stages.samples)])
+    ceiling = stream_ceiling([t["k_pool"], t["v_pool"]])
 
     kv_bytes = w.kv_read_bytes()
     # a block several sequences share need be read only once: the roofline
@@ -503,9 +636,13 @@ def main():
         "context_tokens_per_s": float(w.context_lens.sum()) / (ms_per_step * 1e-3),
         "kernel_us": {"slot_mapping": per_kernel_ms[0] * 1e3, "reshape_and_cache": per_kernel_ms[1] * 1e3,
                       "decode_partition": per_kernel_ms[2] * 1e3, "combine": per_kernel_ms[3] * 1e3},
+        "decode_partition_us_percentiles": part_pct,
+        "step_us_percentiles": step_pct,
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None if args.shared_prefix else load_traffic(w.name)},
+                     "traffic": None if args.shared_prefix else load_traffic(w.name),
+                     "stream_read_GBps": ceiling["GBps"], "frac_of_stream_read": achieved / ceiling["GBps"]},
+        "stream_read_ceiling": ceiling,
         "cpu_baseline": base,
         "wall_s_timed": wall,
     }

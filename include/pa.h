@@ -411,6 +411,20 @@ int pa_shared_prefix_groups(const int32_t* block_tables, const int32_t* context_
                             int32_t* group_start, int32_t* prefix_lens, int32_t* seq_prefix_lens,
                             int32_t* num_groups, int32_t* max_group_size, int32_t* max_prefix_len);
 
+/*
+ * Measurement: a streaming read of `bytes` bytes of device memory at `src`
+ * (16-byte aligned, bytes a multiple of 16), each byte loaded once in 16-byte
+ * vector loads spread over the whole device, non-temporal if `nontemporal` is
+ * non-zero.  The rate a plain linear read reaches on this device: the ceiling
+ * the decode kernel's KV-read bandwidth (each context token's K and V rows
+ * read once, handbook "分页 KV Cache", section on paged attention) is
+ * compared against besides the published HBM peak.  Nothing is written
+ * unless the XOR of the words one thread reads equals 0x5a17c0de; then that
+ * value goes to `sink` (4 bytes, device, caller owned).  Errors: INVALID_ARG
+ * (null pointers, misaligned or zero size), HIP (launch failure).
+ */
+int pa_stream_read(const void* src, size_t bytes, void* sink, int nontemporal, void* stream);
+
 /* Static, human-readable name of a pa_status value. */
 const char* pa_status_string(int status);
 

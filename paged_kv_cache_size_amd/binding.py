@@ -59,6 +59,7 @@ SIGNATURES = {
                                                          _P, _SZ, _P]),
     "pa_shared_prefix_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "pa_shared_prefix_groups": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
+    "pa_stream_read": (ctypes.c_int, [_P, _SZ, _P, ctypes.c_int, _P]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -333,6 +334,17 @@ def pa_swap_blocks(dst_k_pool, dst_v_pool, src_k_pool, src_v_pool, src_blocks, d
         _dev(dst_blocks, "dst_blocks", torch.int64, 1) if n else None, n, bs, hkv, d, pa_dtype(dst_k_pool),
         _stream(dev) if dev.is_cuda else None)
     _check(rc, "pa_swap_blocks")
+
+
+def pa_stream_read(buf, sink, nontemporal: bool = False):
+    """Read every byte of the device tensor ``buf`` once (a measurement of
+    the device's streaming read rate); ``sink`` is a device int32 tensor."""
+    _dev(buf, "buf")
+    _dev(sink, "sink", _torch().int32)
+    nbytes = buf.numel() * buf.element_size()
+    rc = lib().pa_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                              int(bool(nontemporal)), _stream(buf))
+    _check(rc, "pa_stream_read")
 
 
 class SharedPrefixGroups:

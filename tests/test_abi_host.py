@@ -168,6 +168,15 @@ def test_slot_mapping_argument_checks():
     assert f(FAKE, FAKE, FAKE, FAKE, 4, 8, 0, 9, None) == B.PA_ERR_INVALID_ARG
 
 
+def test_stream_read_argument_checks():
+    f = B.lib().pa_stream_read
+    assert f(None, 1024, FAKE, 0, None) == B.PA_ERR_INVALID_ARG
+    assert f(FAKE, 1024, None, 0, None) == B.PA_ERR_INVALID_ARG
+    assert f(FAKE, 0, FAKE, 0, None) == B.PA_ERR_INVALID_ARG
+    assert f(FAKE, 1000, FAKE, 1, None) == B.PA_ERR_INVALID_ARG  # not a whole number of 16-byte vectors
+    assert f(ctypes.c_void_p(0x1008), 1024, FAKE, 0, None) == B.PA_ERR_INVALID_ARG  # misaligned
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_LIB", None)
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
