@@ -35,3 +35,4 @@ from .paged_attention import (  # noqa: F401
     brute_force_decode,
 )
 from .capacity import kv_bytes, kv_bytes_per_token, paged_utilisation  # noqa: F401
+from .layout import convert_blocks, fuse_kv, reshape_and_cache_fused, split_kv  # noqa: F401
