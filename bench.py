@@ -56,6 +56,8 @@ def parse():
                    help="rotate over this many copies of the pools (cold caches for small batches)")
     p.add_argument("--block-size", type=int, default=0,
                    help="pool block size for the Llama-layer workload (default 16)")
+    p.add_argument("--layout", choices=("split", "fused"), default="split",
+                   help="pool layout: split K and V pools, or one fused [NB, H_kv, BS, 2D] pool")
     p.add_argument("--shared-prefix", action="store_true",
                    help="decode with shared prompt prefixes read once per group (cascade)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -582,6 +584,25 @@ def main_decode(args, oracle_pool):
 
     stages = [k_slot, k_write, k_part, k_comb]
     kernel = "decode_partition_kernel" if w.dtype == "f32" else "decode_mfma_kernel"
+    stream_buffers = [t["k_pool"], t["v_pool"]]
+    if args.layout == "fused":
+        if args.shared_prefix or len(pools) > 1:
+            raise SystemExit("--layout fused runs without --shared-prefix and --replicas")
+        # the same rows rearranged on the device into one fused pool
+        fused = torch.empty((w.num_blocks, w.num_kv_heads, w.block_size, 2 * w.head_dim), dtype=t["k_pool"].dtype,
+                            device=dev)
+        every = torch.arange(w.num_blocks, dtype=torch.int64, device=dev)
+        PB.pa_convert_blocks(fused, None, PB.PA_KV_FUSED, t["k_pool"], t["v_pool"], PB.PA_KV_SPLIT, every, every)
+
+        def k_write():
+            PB.pa_reshape_and_cache(t["key"], t["value"], fused, None, slots, layout=PB.PA_KV_FUSED)
+
+        def k_part():  # the merge kernel runs inside when a sequence spans several partitions
+            PB.pa_decode_attention(t["query"], fused, None, bt, lens, w.scale, w.max_context_len, out=out,
+                                   workspace=ws, partition_size=ps, layout=PB.PA_KV_FUSED)
+
+        stages = [k_slot, k_write, k_part, lambda: None]
+        stream_buffers = [fused]
     if args.shared_prefix:
         # groups found on the host from the tables (scheduler work, untimed)
         groups = PB.pa_shared_prefix_groups(w.block_tables, w.context_lens, w.block_size)
@@ -601,7 +622,7 @@ def main_decode(args, oracle_pool):
     ms_per_step, per_kernel_ms, wall = time_stages(stages, args.steps, args.warmup)
     part_pct = percentiles_us(time_stages.samples[2])
     step_pct = percentiles_us([sum(x) for x in zip(*time_stages.samples)])
-    ceiling = stream_ceiling([t["k_pool"], t["v_pool"]])
+    ceiling = stream_ceiling(stream_buffers)
 
     kv_bytes = w.kv_read_bytes()
     # a block several sequences share need be read only once: the roofline
@@ -628,6 +649,7 @@ def main_decode(args, oracle_pool):
                    "max_context_len": w.max_context_len, "num_heads": H, "num_kv_heads": w.num_kv_heads,
                    "head_dim": D, "block_size": w.block_size, "num_blocks": w.num_blocks,
                    "partition_size": ps, "shared_prefix_cascade": bool(args.shared_prefix),
+                   "pool_layout": args.layout,
                    "pool_replicas": len(pools),
                    "description": w.description},
         "kv_read_bytes_per_step": kv_bytes,

@@ -67,6 +67,24 @@ typedef enum pa_dtype {
 } pa_dtype;
 
 /*
+ * Physical arrangement of a layer's K/V pool (the _layout entry points).
+ *   PA_KV_SPLIT  one K pool and one V pool, each [num_blocks, block_size,
+ *                num_kv_heads, head_dim] (HB, "实现") - what every entry point
+ *                without a layout argument takes;
+ *   PA_KV_FUSED  one pool [num_blocks, num_kv_heads, block_size, 2*head_dim]
+ *                with a token's K row in the first head_dim elements of its
+ *                row and the V row in the second (HB, "源码对照": the tensor
+ *                shape of vLLM's FlashAttention backend, K and V joined on the
+ *                last axis).  A head's rows of one block are contiguous.
+ * Both hold the same logical K[slot][h][:], V[slot][h][:]; only addresses
+ * differ, so every result is the same in both layouts.
+ */
+typedef enum pa_kv_layout {
+  PA_KV_SPLIT = 0,
+  PA_KV_FUSED = 1
+} pa_kv_layout;
+
+/*
  * pa_slot_mapping - physical slot of every new token of one step.
  *
  * Position p of a sequence lives in logical block p / block_size at offset
@@ -410,6 +428,56 @@ int pa_shared_prefix_groups(const int32_t* block_tables, const int32_t* context_
                             int32_t max_blocks_per_seq, int32_t block_size, int32_t min_prefix_blocks,
                             int32_t* group_start, int32_t* prefix_lens, int32_t* seq_prefix_lens,
                             int32_t* num_groups, int32_t* max_group_size, int32_t* max_prefix_len);
+
+/*
+ * Entry points over either pool layout (pa_kv_layout).  Each behaves exactly
+ * as the entry point of the same name without "_layout" - same arguments,
+ * device-content rules and errors - with the pool given by `layout`:
+ *   PA_KV_SPLIT  k_pool and v_pool as everywhere else;
+ *   PA_KV_FUSED  k_pool = the one pool [num_blocks, num_kv_heads, block_size,
+ *                2*head_dim] and v_pool = NULL.
+ * INVALID_ARG also for an unknown layout, a NULL v_pool with PA_KV_SPLIT or
+ * a non-NULL one with PA_KV_FUSED, or a block over 2 GiB.  A result does not
+ * depend on the layout: the kernels read the same rows in the same order.
+ */
+int pa_reshape_and_cache_layout(const void* key, const void* value, void* k_pool, void* v_pool,
+                                const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                                pa_kv_layout layout, void* stream);
+int pa_decode_attention_layout(void* out, const void* query, const void* k_pool, const void* v_pool,
+                               const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype,
+                               void* workspace, size_t workspace_bytes, int32_t partition_size,
+                               pa_kv_layout layout, void* stream);
+int pa_prefill_attention_layout(void* out, const void* query, const void* k_pool, const void* v_pool,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                                int32_t max_query_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                                int32_t partition_size, pa_kv_layout layout, void* stream);
+
+/*
+ * Whole-block copies between two pools of any layouts: block dst_blocks[i] of
+ * the destination gets the K and V rows of block src_blocks[i] of the source,
+ * rearranged when the layouts differ (HB, "源码对照": attention backends
+ * differ in KV layout, so moving KV between them converts it).  Pools as in
+ * the _layout entry points; either may be pinned host memory (as for
+ * pa_swap_blocks); the block shape (block_size, num_kv_heads, head_dim, dtype)
+ * is shared.  Same layouts: a plain whole-block copy (copy-on-write or swap of
+ * a fused pool).  Id arrays int64 in device memory; a pair with an id outside
+ * its pool is skipped; destination ids distinct; source and destination
+ * blocks must not overlap.  num_pairs = 0 enqueues nothing.
+ * Errors: INVALID_ARG (pool pointers not matching their layouts, unknown
+ * layouts, null id arrays with num_pairs > 0, non-positive sizes),
+ * UNSUPPORTED (dtype), HIP.
+ */
+int pa_convert_blocks(void* dst_k_pool, void* dst_v_pool, pa_kv_layout dst_layout, int64_t dst_num_blocks,
+                      const void* src_k_pool, const void* src_v_pool, pa_kv_layout src_layout,
+                      int64_t src_num_blocks, const int64_t* src_blocks, const int64_t* dst_blocks,
+                      int64_t num_pairs, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                      pa_dtype dtype, void* stream);
 
 /*
  * Measurement: a streaming read of `bytes` bytes of device memory at `src`

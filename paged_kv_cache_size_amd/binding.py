@@ -59,6 +59,15 @@ SIGNATURES = {
                                                          _P, _SZ, _P]),
     "pa_shared_prefix_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "pa_shared_prefix_groups": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
+    "pa_reshape_and_cache_layout": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I64, ctypes.c_int,
+                                                   ctypes.c_int, _P]),
+    "pa_decode_attention_layout": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                  _F32, ctypes.c_int, _P, _SZ, _I32, ctypes.c_int, _P]),
+    "pa_prefill_attention_layout": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                   _I32, _I32, _I32, _F32, ctypes.c_int, _P, _SZ, _I32,
+                                                   ctypes.c_int, _P]),
+    "pa_convert_blocks": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _P, _P, ctypes.c_int, _I64, _P, _P, _I64, _I32,
+                                         _I32, _I32, ctypes.c_int, _P]),
     "pa_stream_read": (ctypes.c_int, [_P, _SZ, _P, ctypes.c_int, _P]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
@@ -129,6 +138,38 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+PA_KV_SPLIT, PA_KV_FUSED = 0, 1  # pa_kv_layout
+
+
+def _pool(k_pool, v_pool, layout, host_ok=False):
+    """(num_blocks, block_size, num_kv_heads, head_dim) of a pool in
+    ``layout`` and its two C pointers (the second None for the fused pool
+    [NB, H_kv, BS, 2D], passed as ``k_pool`` with ``v_pool=None``)."""
+    check = _host_or_dev if host_ok else _dev
+    if layout == PA_KV_SPLIT:
+        if v_pool is None or v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+            raise ValueError("the split layout takes a K and a V pool of one shape and dtype")
+        nb, bs, hkv, d = k_pool.shape
+        return (nb, bs, hkv, d), check(k_pool, "k_pool", ndim=4), check(v_pool, "v_pool", ndim=4)
+    if layout == PA_KV_FUSED:
+        if v_pool is not None:
+            raise ValueError("the fused layout takes one pool [NB, H_kv, BS, 2D] (v_pool=None)")
+        nb, hkv, bs, d2 = k_pool.shape
+        if d2 % 2:
+            raise ValueError("a fused pool's last axis holds K and V: 2 * head_dim")
+        return (nb, bs, hkv, d2 // 2), check(k_pool, "kv_pool", ndim=4), None
+    raise ValueError(f"unknown layout {layout}")
+
+
+def _host_or_dev(t, name, ndim=None):
+    """Pointer of a contiguous device tensor or pinned host tensor."""
+    if not t.is_contiguous() or not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be a contiguous device tensor or pinned host tensor")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
 def pa_slot_mapping(block_tables, context_lens, block_size: int, query_start_loc=None,
                     num_tokens: int | None = None, out=None):
     """int64 slot of every new token (see pa.h).  Decode when
@@ -151,23 +192,26 @@ def pa_slot_mapping(block_tables, context_lens, block_size: int, query_start_loc
     return out
 
 
-def pa_reshape_and_cache(key, value, k_pool, v_pool, slot_mapping):
-    """Write key/value rows [N, H_kv, D] into the pools at slot_mapping."""
+def pa_reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, layout: int = PA_KV_SPLIT):
+    """Write key/value rows [N, H_kv, D] into the pools at slot_mapping
+    (``layout`` PA_KV_FUSED: ``k_pool`` is the fused pool, ``v_pool`` None)."""
     torch = _torch()
-    if key.shape != value.shape or k_pool.shape != v_pool.shape:
-        raise ValueError("key/value and k_pool/v_pool shapes must match")
-    if not (key.dtype == value.dtype == k_pool.dtype == v_pool.dtype):
+    (nb, bs, hkv, d), kp, vp = _pool(k_pool, v_pool, layout)
+    if key.shape != value.shape:
+        raise ValueError("key/value shapes must match")
+    if not (key.dtype == value.dtype == k_pool.dtype):
         raise TypeError("key, value and pools must share a dtype")
-    nb, bs, hkv, d = k_pool.shape
     if tuple(key.shape[1:]) != (hkv, d):
         raise ValueError(f"key rows {tuple(key.shape[1:])} do not match pool rows {(hkv, d)}")
     n = key.shape[0]
     if slot_mapping.shape != (n,):
         raise ValueError("slot_mapping must be [num_tokens]")
-    rc = lib().pa_reshape_and_cache(
-        _dev(key, "key", ndim=3), _dev(value, "value", ndim=3), _dev(k_pool, "k_pool", ndim=4),
-        _dev(v_pool, "v_pool", ndim=4), _dev(slot_mapping, "slot_mapping", torch.int64, 1),
-        n, hkv, d, bs, nb, pa_dtype(key), _stream(key))
+    args = (_dev(key, "key", ndim=3), _dev(value, "value", ndim=3), kp, vp,
+            _dev(slot_mapping, "slot_mapping", torch.int64, 1), n, hkv, d, bs, nb, pa_dtype(key))
+    if layout == PA_KV_SPLIT:
+        rc = lib().pa_reshape_and_cache(*args, _stream(key))
+    else:
+        rc = lib().pa_reshape_and_cache_layout(*args, int(layout), _stream(key))
     _check(rc, "pa_reshape_and_cache")
 
 
@@ -221,18 +265,19 @@ def pa_decode_plan_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, m
 
 def pa_decode_attention(query, k_pool, v_pool, block_tables, context_lens, scale: float,
                         max_context_len: int | None = None, out=None, workspace=None,
-                        partition_size: int = 0):
+                        partition_size: int = 0, layout: int = PA_KV_SPLIT):
     """One decode step of paged attention; returns ``out`` [B, H, D].
 
     ``max_context_len`` is a host int bounding context_lens (reading it from
     the device would synchronise; pass it when known).  The workspace is
-    allocated with PyTorch when not given."""
+    allocated with PyTorch when not given.  ``layout`` PA_KV_FUSED: ``k_pool``
+    is the fused pool and ``v_pool`` None."""
     torch = _torch()
     B, H, D = query.shape
-    nb, bs, hkv, d2 = k_pool.shape
-    if d2 != D or k_pool.shape != v_pool.shape:
+    (nb, bs, hkv, d2), kp, vp = _pool(k_pool, v_pool, layout)
+    if d2 != D:
         raise ValueError("pool shape does not match query")
-    if not (query.dtype == k_pool.dtype == v_pool.dtype):
+    if query.dtype != k_pool.dtype:
         raise TypeError("query and pools must share a dtype")
     if block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_tables / context_lens batch mismatch")
@@ -246,11 +291,14 @@ def pa_decode_attention(query, k_pool, v_pool, block_tables, context_lens, scale
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
     ws_ptr = None if workspace is None else _dev(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib().pa_decode_attention_ex(
-        _dev(out, "out", query.dtype, 3), _dev(query, "query", ndim=3), _dev(k_pool, "k_pool", ndim=4),
-        _dev(v_pool, "v_pool", ndim=4), _dev(block_tables, "block_tables", torch.int32, 2),
-        _dev(context_lens, "context_lens", torch.int32, 1), B, H, hkv, D, bs, mb, int(max_context_len),
-        float(scale), pa_dtype(query), ws_ptr, ws_bytes, int(partition_size), _stream(query))
+    args = (_dev(out, "out", query.dtype, 3), _dev(query, "query", ndim=3), kp, vp,
+            _dev(block_tables, "block_tables", torch.int32, 2), _dev(context_lens, "context_lens", torch.int32, 1),
+            B, H, hkv, D, bs, mb, int(max_context_len), float(scale), pa_dtype(query), ws_ptr, ws_bytes,
+            int(partition_size))
+    if layout == PA_KV_SPLIT:
+        rc = lib().pa_decode_attention_ex(*args, _stream(query))
+    else:
+        rc = lib().pa_decode_attention_layout(*args, int(layout), _stream(query))
     _check(rc, "pa_decode_attention")
     return out
 
@@ -263,19 +311,20 @@ def pa_prefill_workspace_bytes(num_tokens, num_heads, head_dim, max_context_len,
 
 def pa_prefill_attention(query, k_pool, v_pool, block_tables, context_lens, query_start_loc, scale: float,
                          max_query_len: int, max_context_len: int, out=None, workspace=None,
-                         partition_size: int = 0):
+                         partition_size: int = 0, layout: int = PA_KV_SPLIT):
     """Paged attention of several new tokens per sequence; returns ``out`` [T, H, D].
 
     ``query_start_loc`` (int32 [B+1], device) delimits each sequence's rows of
     ``query``; ``context_lens`` include the new tokens, whose K/V must already
-    be in the pools.  ``max_query_len`` / ``max_context_len`` are host bounds."""
+    be in the pools.  ``max_query_len`` / ``max_context_len`` are host bounds.
+    ``layout`` PA_KV_FUSED: ``k_pool`` is the fused pool and ``v_pool`` None."""
     torch = _torch()
     T, H, D = query.shape
-    nb, bs, hkv, d2 = k_pool.shape
+    (nb, bs, hkv, d2), kp, vp = _pool(k_pool, v_pool, layout)
     B = block_tables.shape[0]
-    if d2 != D or k_pool.shape != v_pool.shape:
+    if d2 != D:
         raise ValueError("pool shape does not match query")
-    if not (query.dtype == k_pool.dtype == v_pool.dtype):
+    if query.dtype != k_pool.dtype:
         raise TypeError("query and pools must share a dtype")
     if context_lens.shape != (B,) or query_start_loc.shape != (B + 1,):
         raise ValueError("context_lens / query_start_loc do not match the block tables' batch")
@@ -286,13 +335,15 @@ def pa_prefill_attention(query, k_pool, v_pool, block_tables, context_lens, quer
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
     ws_ptr = None if workspace is None else _dev(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib().pa_prefill_attention(
-        _dev(out, "out", query.dtype, 3), _dev(query, "query", ndim=3), _dev(k_pool, "k_pool", ndim=4),
-        _dev(v_pool, "v_pool", ndim=4), _dev(block_tables, "block_tables", torch.int32, 2),
-        _dev(context_lens, "context_lens", torch.int32, 1),
-        _dev(query_start_loc, "query_start_loc", torch.int32, 1), B, T, int(max_query_len), H, hkv, D, bs,
-        block_tables.shape[1], int(max_context_len), float(scale), pa_dtype(query), ws_ptr, ws_bytes,
-        int(partition_size), _stream(query))
+    args = (_dev(out, "out", query.dtype, 3), _dev(query, "query", ndim=3), kp, vp,
+            _dev(block_tables, "block_tables", torch.int32, 2), _dev(context_lens, "context_lens", torch.int32, 1),
+            _dev(query_start_loc, "query_start_loc", torch.int32, 1), B, T, int(max_query_len), H, hkv, D, bs,
+            block_tables.shape[1], int(max_context_len), float(scale), pa_dtype(query), ws_ptr, ws_bytes,
+            int(partition_size))
+    if layout == PA_KV_SPLIT:
+        rc = lib().pa_prefill_attention(*args, _stream(query))
+    else:
+        rc = lib().pa_prefill_attention_layout(*args, int(layout), _stream(query))
     _check(rc, "pa_prefill_attention")
     return out
 
@@ -334,6 +385,27 @@ def pa_swap_blocks(dst_k_pool, dst_v_pool, src_k_pool, src_v_pool, src_blocks, d
         _dev(dst_blocks, "dst_blocks", torch.int64, 1) if n else None, n, bs, hkv, d, pa_dtype(dst_k_pool),
         _stream(dev) if dev.is_cuda else None)
     _check(rc, "pa_swap_blocks")
+
+
+def pa_convert_blocks(dst_k, dst_v, dst_layout: int, src_k, src_v, src_layout: int, src_blocks, dst_blocks):
+    """Copy whole blocks between pools of any layouts (either may be pinned
+    host tensors); id tensors int64 on the device."""
+    torch = _torch()
+    dshape, dk, dv = _pool(dst_k, dst_v, dst_layout, host_ok=True)
+    sshape, sk, sv = _pool(src_k, src_v, src_layout, host_ok=True)
+    if dshape[1:] != sshape[1:] or dst_k.dtype != src_k.dtype:
+        raise ValueError("pools differ in block shape or dtype")
+    n = int(src_blocks.numel())
+    if dst_blocks.numel() != n:
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    _, bs, hkv, d = dshape
+    dev = src_blocks if n else (dst_k if dst_k.is_cuda else src_k)
+    rc = lib().pa_convert_blocks(
+        dk, dv, int(dst_layout), dshape[0], sk, sv, int(src_layout), sshape[0],
+        _dev(src_blocks, "src_blocks", torch.int64, 1) if n else None,
+        _dev(dst_blocks, "dst_blocks", torch.int64, 1) if n else None, n, bs, hkv, d, pa_dtype(dst_k),
+        _stream(dev) if dev.is_cuda else None)
+    _check(rc, "pa_convert_blocks")
 
 
 def pa_stream_read(buf, sink, nontemporal: bool = False):

@@ -416,6 +416,50 @@ int check_reshape(const void* key, const void* value, const void* k_pool, const 
   return PA_OK;
 }
 
+int pool_view(const void* k_pool, const void* v_pool, int layout, int block_size, int num_kv_heads, int head_dim,
+              int dtype, PoolView* pv) {
+  const int64_t e = elem_bytes(dtype);
+  if (e == 0) return PA_ERR_UNSUPPORTED;
+  if (!k_pool || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0) return PA_ERR_INVALID_ARG;
+  const int64_t rowb = (int64_t)head_dim * e;
+  const uint8_t* k = static_cast<const uint8_t*>(k_pool);
+  if (layout == PA_KV_SPLIT) {
+    if (!v_pool) return PA_ERR_INVALID_ARG;
+    pv->k = k;
+    pv->v = static_cast<const uint8_t*>(v_pool);
+    pv->head_stride = rowb;
+    pv->row_stride = (int64_t)num_kv_heads * rowb;
+    pv->block_stride = (int64_t)block_size * pv->row_stride;
+    return pv->block_stride <= kMaxBlockBytes ? PA_OK : PA_ERR_INVALID_ARG;
+  }
+  if (layout == PA_KV_FUSED) {
+    if (v_pool) return PA_ERR_INVALID_ARG;  // the fused pool holds V itself
+    pv->k = k;
+    pv->v = k + rowb;
+    pv->row_stride = 2 * rowb;
+    pv->head_stride = (int64_t)block_size * pv->row_stride;
+    pv->block_stride = (int64_t)num_kv_heads * pv->head_stride;
+    return pv->block_stride <= kMaxBlockBytes ? PA_OK : PA_ERR_INVALID_ARG;
+  }
+  return PA_ERR_INVALID_ARG;
+}
+
+int check_convert_blocks(const void* dst_k, const void* dst_v, int dst_layout, int64_t dst_num_blocks,
+                         const void* src_k, const void* src_v, int src_layout, int64_t src_num_blocks,
+                         const int64_t* src, const int64_t* dst, int64_t num_pairs, int block_size,
+                         int num_kv_heads, int head_dim, int dtype) {
+  if (num_pairs < 0 || dst_num_blocks <= 0 || src_num_blocks <= 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs > 0 && (!src || !dst)) return PA_ERR_INVALID_ARG;
+  if (num_pairs > 0x7fffffffLL) return PA_ERR_INVALID_ARG;  // one grid row per pair
+  PoolView a, b;
+  int rc = pool_view(dst_k, dst_v, dst_layout, block_size, num_kv_heads, head_dim, dtype, &a);
+  if (rc != PA_OK) return rc;
+  rc = pool_view(src_k, src_v, src_layout, block_size, num_kv_heads, head_dim, dtype, &b);
+  if (rc != PA_OK) return rc;
+  if ((int64_t)block_size * num_kv_heads * head_dim > (int64_t)1 << 30) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
 int check_copy_blocks(const void* k_pool, const void* v_pool, const int64_t* src, const int64_t* dst,
                       int64_t num_pairs, int block_size, int num_kv_heads, int head_dim, int64_t num_blocks,
                       int dtype) {

@@ -40,6 +40,34 @@ struct DecodeShape {
   int dtype;
 };
 
+// Byte geometry of a K/V pool pair in one of the pa_kv_layout layouts: the K
+// row of (block p, token t, KV head h) starts at k + p*block_stride +
+// t*row_stride + h*head_stride, its V row at the same offset from v.
+//  * PA_KV_SPLIT: two pools [NB, BS, H_kv, D];
+//  * PA_KV_FUSED: one pool [NB, H_kv, BS, 2D], K in the first D elements of
+//    each row and V in the second (v = k + D elements).
+struct PoolView {
+  const uint8_t* k = nullptr;
+  const uint8_t* v = nullptr;
+  int64_t block_stride = 0;
+  int64_t row_stride = 0;
+  int64_t head_stride = 0;
+  // bytes from a block's first byte (at head 0) to the end of the last row of
+  // the last head of its first 16 tokens: what one 16-token step may touch
+  int64_t step_span(int head_dim_bytes, int num_kv_heads) const {
+    return (int64_t)(num_kv_heads - 1) * head_stride + 15 * row_stride + head_dim_bytes;
+  }
+};
+
+// Kernels address inside one block with 32-bit offsets.
+constexpr int64_t kMaxBlockBytes = (int64_t)1 << 31;
+
+// INVALID_ARG for a block larger than kMaxBlockBytes, a null k_pool, an unknown layout, a null v_pool with the
+// split layout or a non-null one with the fused layout; UNSUPPORTED for an
+// unknown dtype.  Sizes must already be positive.
+int pool_view(const void* k_pool, const void* v_pool, int layout, int block_size, int num_kv_heads, int head_dim,
+              int dtype, PoolView* pv);
+
 // Argument checks of pa_decode_attention that do not depend on the device.
 int check_decode(const void* out, const void* query, const void* k_pool, const void* v_pool,
                  const int32_t* block_tables, const int32_t* context_lens, const DecodeShape& s,
@@ -146,6 +174,12 @@ int check_combine(const void* out, const int32_t* context_lens, int num_seqs, in
 int check_reshape(const void* key, const void* value, const void* k_pool, const void* v_pool,
                   const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads, int head_dim,
                   int block_size, int64_t num_blocks, int dtype);
+
+// pa_convert_blocks: both views built, ids present when pairs > 0.
+int check_convert_blocks(const void* dst_k, const void* dst_v, int dst_layout, int64_t dst_num_blocks,
+                         const void* src_k, const void* src_v, int src_layout, int64_t src_num_blocks,
+                         const int64_t* src, const int64_t* dst, int64_t num_pairs, int block_size,
+                         int num_kv_heads, int head_dim, int dtype);
 
 int check_copy_blocks(const void* k_pool, const void* v_pool, const int64_t* src, const int64_t* dst,
                       int64_t num_pairs, int block_size, int num_kv_heads, int head_dim, int64_t num_blocks,

@@ -65,16 +65,26 @@ __global__ void slot_mapping_varlen_kernel(int64_t* __restrict__ slots, const in
 
 // ------------------------------------------------------------------ pool write
 
+// One workgroup per (token, K or V).  Strides in units of V: the head rows
+// of a token are head_vecs apart in key/value and head_stride apart in the
+// pool (contiguous in the split layout, a block's head planes apart in the
+// fused one).
 template <typename V>
 __global__ void reshape_and_cache_kernel(const V* __restrict__ key, const V* __restrict__ value,
                                          V* __restrict__ k_pool, V* __restrict__ v_pool,
-                                         const int64_t* __restrict__ slots, int row_vecs, int64_t num_slots) {
+                                         const int64_t* __restrict__ slots, int head_vecs, int num_kv_heads,
+                                         int block_size, int64_t block_stride, int64_t row_stride,
+                                         int64_t head_stride, int64_t num_slots) {
   const int64_t i = blockIdx.x;
   const int64_t slot = slots[i];
   if (slot < 0 || slot >= num_slots) return;
+  const int row_vecs = head_vecs * num_kv_heads;
   const V* src = (blockIdx.y == 0 ? key : value) + i * row_vecs;
-  V* dst = (blockIdx.y == 0 ? k_pool : v_pool) + slot * row_vecs;
-  for (int t = threadIdx.x; t < row_vecs; t += blockDim.x) dst[t] = src[t];
+  V* dst = (blockIdx.y == 0 ? k_pool : v_pool) + (slot / block_size) * block_stride + (slot % block_size) * row_stride;
+  for (int t = threadIdx.x; t < row_vecs; t += blockDim.x) {
+    const int h = t / head_vecs;
+    dst[h * head_stride + (t - h * head_vecs)] = src[t];
+  }
 }
 
 // ------------------------------------------------------------------ decode attention
@@ -92,6 +102,11 @@ struct DecodeArgs {
   int block_shift;  // pool blocks of 16 << block_shift tokens (the MFMA tile's steps are 16 tokens)
   int part_tokens, num_parts, groups;  // groups = head-group workgroups per (sequence, partition)
   float qscale;    // scale * log2(e): scores come out in log2 units for exp2
+  // pool geometry in bytes (layout): K row (block p, token t, head h) at
+  // k_pool + p*block_stride + t*row_stride + h*head_stride, V likewise;
+  // span = what one 16-token step of a block may touch from its first byte
+  int64_t block_stride;
+  uint32_t row_stride, head_stride, span;
 };
 
 template <int DT, int D, int REPC>
@@ -161,9 +176,9 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
     }
   }
 
-  const size_t row_stride = (size_t)a.num_kv_heads * ROWB;
-  const size_t block_stride = (size_t)BS * row_stride;
-  const size_t lane_off = (size_t)r * row_stride + (size_t)g * ROWB + (size_t)c * 16;
+  const size_t row_stride = a.row_stride;
+  const size_t block_stride = (size_t)a.block_stride;
+  const size_t lane_off = (size_t)r * row_stride + (size_t)g * a.head_stride + (size_t)c * 16;
   const uint8_t* kbase = a.k_pool + lane_off;
   const uint8_t* vbase = a.v_pool + lane_off;
 
@@ -390,13 +405,14 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
   //     LDS slot 64n + l = (token t, position q) with the row's 16-byte chunk
   //     q ^ f(t), so the row-order MFMA reads below hit 16 distinct bank groups.
   //  V: row-coalesced into registers, row gq (+4i).
-  const uint32_t row_stride = (uint32_t)a.num_kv_heads * ROWB;
-  const size_t block_stride = (size_t)BS * row_stride;
+  const uint32_t row_stride = a.row_stride;
+  const uint32_t hoff = (uint32_t)g * a.head_stride;
+  const size_t step_stride = (size_t)BS * row_stride;  // 16-token steps inside a larger block
   uint32_t kdma[NLI];
 #pragma unroll
   for (int n = 0; n < NLI; ++n) {
     const int slot = 64 * n + lane, t = slot / CPR, q = slot % CPR;
-    kdma[n] = (uint32_t)t * row_stride + (uint32_t)g * ROWB + (uint32_t)((q ^ kswz(t)) * 16);
+    kdma[n] = (uint32_t)t * row_stride + hoff + (uint32_t)((q ^ kswz(t)) * 16);
   }
   uint32_t kread[NKC];  // QK A operand: token 4*(col%4) + col/4, chunk 4c + gq
   {
@@ -404,7 +420,7 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
 #pragma unroll
     for (int c = 0; c < NKC; ++c) kread[c] = (uint32_t)(t * CPR + ((4 * c + gq) ^ kswz(t))) * 16;
   }
-  const uint32_t voff = (uint32_t)gq * row_stride + (uint32_t)g * ROWB + col * VPL * 2;
+  const uint32_t voff = (uint32_t)gq * row_stride + hoff + col * VPL * 2;
   // Small blocks: for each row a lane loads, which block of the step holds it
   // and the byte offset inside that block.
   int kblk[GATHER ? NLI : 1], vblk[GATHER ? 4 : 1];
@@ -414,13 +430,13 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
     for (int n = 0; n < NLI; ++n) {
       const int slot = 64 * n + lane, t = slot / CPR, q = slot % CPR;
       kblk[n] = t / pool_bs;
-      kin[n] = (uint32_t)(t % pool_bs) * row_stride + (uint32_t)g * ROWB + (uint32_t)((q ^ kswz(t)) * 16);
+      kin[n] = (uint32_t)(t % pool_bs) * row_stride + hoff + (uint32_t)((q ^ kswz(t)) * 16);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 4 * i + gq;
       vblk[i] = t / pool_bs;
-      vin[i] = (uint32_t)(t % pool_bs) * row_stride + (uint32_t)g * ROWB + col * VPL * 2;
+      vin[i] = (uint32_t)(t % pool_bs) * row_stride + hoff + col * VPL * 2;
     }
   }
   // One LDS object per ring slot, so that the compiler's wait counting can
@@ -454,7 +470,7 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
     const bool real = j <= last;
     const int jj = real ? j : last;
     if constexpr (GATHER) {  // per-lane rows; past the end the last step is re-read (cached, masked)
-      const size_t pool_block = (size_t)pool_bs * row_stride;
+      const size_t pool_block = (size_t)a.block_stride;
       size_t kb[NLI], vb[4];
 #pragma unroll
       for (int n = 0; n < NLI; ++n) kb[n] = 0;
@@ -476,10 +492,10 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
       for (int i = 0; i < 4; ++i) vr[i] = *reinterpret_cast<const VT*>(a.v_pool + vb[i] + vin[i]);
       return;
     }
-    const size_t off = SUB ? (size_t)(uint32_t)tab.get(jj >> pshift) * (block_stride << pshift) +
-                                 (size_t)(jj & ((1 << pshift) - 1)) * block_stride
-                           : (size_t)(uint32_t)tab.get(jj) * block_stride;
-    const uint32_t span = real ? (uint32_t)block_stride : 0u;
+    const size_t off = SUB ? (size_t)(uint32_t)tab.get(jj >> pshift) * (size_t)a.block_stride +
+                                 (size_t)(jj & ((1 << pshift) - 1)) * step_stride
+                           : (size_t)(uint32_t)tab.get(jj) * (size_t)a.block_stride;
+    const uint32_t span = real ? a.span : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_block_rsrc(a.k_pool + off, span);
     const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, span);
 #pragma unroll
@@ -701,9 +717,9 @@ float2* ml_region(void* workspace, const pa::DecodeShape& shp, int parts) {
                                    (size_t)shp.num_seqs * shp.num_heads * parts * shp.head_dim);
 }
 
-int launch_partitions(void* out, const void* query, const void* k_pool, const void* v_pool,
-                      const int32_t* block_tables, const int32_t* context_lens, const pa::DecodeShape& shp,
-                      float scale, void* workspace, const DecodePlan& plan, void* stream) {
+int launch_partitions(void* out, const void* query, const pa::PoolView& pv, const int32_t* block_tables,
+                      const int32_t* context_lens, const pa::DecodeShape& shp, float scale, void* workspace,
+                      const DecodePlan& plan, void* stream) {
   const pa::DecodeGrid gd = pa::decode_grid(shp);
   const int64_t grid = (int64_t)shp.num_seqs * plan.parts * gd.groups;
   if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
@@ -713,8 +729,12 @@ int launch_partitions(void* out, const void* query, const void* k_pool, const vo
   DecodeArgs a;
   a.out = out;
   a.query = query;
-  a.k_pool = static_cast<const uint8_t*>(k_pool);
-  a.v_pool = static_cast<const uint8_t*>(v_pool);
+  a.k_pool = pv.k;
+  a.v_pool = pv.v;
+  a.block_stride = pv.block_stride;
+  a.row_stride = (uint32_t)pv.row_stride;
+  a.head_stride = (uint32_t)pv.head_stride;
+  a.span = (uint32_t)pv.step_span(shp.head_dim * pa::elem_bytes(shp.dtype), shp.num_kv_heads);
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.ws_acc = static_cast<float*>(workspace);
@@ -810,49 +830,97 @@ extern "C" int pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_table
   return pa::launch_status();
 }
 
+namespace {
+
+template <typename V>
+void launch_reshape(const void* key, const void* value, const pa::PoolView& pv, const int64_t* slots,
+                    int64_t num_tokens, int num_kv_heads, int head_bytes, int block_size, int64_t num_slots,
+                    int threads, hipStream_t st) {
+  constexpr int64_t W = sizeof(V);
+  hipLaunchKernelGGL(reshape_and_cache_kernel<V>, dim3((unsigned)num_tokens, 2), dim3(threads), 0, st,
+                     (const V*)key, (const V*)value, (V*)const_cast<uint8_t*>(pv.k), (V*)const_cast<uint8_t*>(pv.v),
+                     slots, (int)(head_bytes / W), num_kv_heads, block_size, pv.block_stride / W, pv.row_stride / W,
+                     pv.head_stride / W, num_slots);
+}
+
+}  // namespace
+
+extern "C" int pa_reshape_and_cache_layout(const void* key, const void* value, void* k_pool, void* v_pool,
+                                           const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                           pa_dtype dtype, pa_kv_layout layout, void* stream) {
+  pa::PoolView pv;
+  int rc = pa::check_reshape(key, value, k_pool, layout == PA_KV_FUSED ? k_pool : v_pool, slot_mapping, num_tokens,
+                             num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (rc != PA_OK) return rc;
+  rc = pa::pool_view(k_pool, v_pool, (int)layout, block_size, num_kv_heads, head_dim, (int)dtype, &pv);
+  if (rc != PA_OK) return rc;
+  if (num_tokens == 0) return PA_OK;
+  const int head_bytes = head_dim * pa::elem_bytes(dtype);
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_bytes;
+  const int64_t num_slots = num_blocks * block_size;
+  const uintptr_t align = (uintptr_t)key | (uintptr_t)value | (uintptr_t)pv.k | (uintptr_t)pv.v;
+  int vec = 16;
+  while (vec > 1 && ((head_bytes % vec) != 0 || (align % vec) != 0)) vec >>= 1;
+  const int64_t row_vecs = row_bytes / vec;
+  const int threads = row_vecs >= 256 ? 256 : (row_vecs > 64 ? 128 : 64);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (vec) {
+    case 16:
+      launch_reshape<uint4>(key, value, pv, slot_mapping, num_tokens, num_kv_heads, head_bytes, block_size,
+                            num_slots, threads, st);
+      break;
+    case 8:
+      launch_reshape<uint2>(key, value, pv, slot_mapping, num_tokens, num_kv_heads, head_bytes, block_size,
+                            num_slots, threads, st);
+      break;
+    case 4:
+      launch_reshape<uint32_t>(key, value, pv, slot_mapping, num_tokens, num_kv_heads, head_bytes, block_size,
+                               num_slots, threads, st);
+      break;
+    case 2:
+      launch_reshape<uint16_t>(key, value, pv, slot_mapping, num_tokens, num_kv_heads, head_bytes, block_size,
+                               num_slots, threads, st);
+      break;
+    default:
+      launch_reshape<uint8_t>(key, value, pv, slot_mapping, num_tokens, num_kv_heads, head_bytes, block_size,
+                              num_slots, threads, st);
+      break;
+  }
+  return pa::launch_status();
+}
+
 extern "C" int pa_reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
                                     const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
                                     int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype dtype,
                                     void* stream) {
-  int rc = pa::check_reshape(key, value, k_pool, v_pool, slot_mapping, num_tokens, num_kv_heads, head_dim,
-                             block_size, num_blocks, dtype);
+  if (!v_pool) return PA_ERR_INVALID_ARG;
+  return pa_reshape_and_cache_layout(key, value, k_pool, v_pool, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                                     block_size, num_blocks, dtype, PA_KV_SPLIT, stream);
+}
+
+extern "C" int pa_decode_attention_layout(void* out, const void* query, const void* k_pool, const void* v_pool,
+                                          const int32_t* block_tables, const int32_t* context_lens,
+                                          int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                          int32_t max_context_len, float scale, pa_dtype dtype, void* workspace,
+                                          size_t workspace_bytes, int32_t partition_size, pa_kv_layout layout,
+                                          void* stream) {
+  const pa::DecodeShape shp{num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                            max_context_len, (int)dtype};
+  pa::PoolView pv;
+  int rc = pa::check_decode(out, query, k_pool, layout == PA_KV_FUSED ? k_pool : v_pool, block_tables,
+                            context_lens, shp, scale);
   if (rc != PA_OK) return rc;
-  if (num_tokens == 0) return PA_OK;
-  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * pa::elem_bytes(dtype);
-  const int64_t num_slots = num_blocks * block_size;
-  const uintptr_t align = (uintptr_t)key | (uintptr_t)value | (uintptr_t)k_pool | (uintptr_t)v_pool;
-  int vec = 16;
-  while (vec > 1 && ((row_bytes % vec) != 0 || (align % vec) != 0)) vec >>= 1;
-  const int row_vecs = (int)(row_bytes / vec);
-  const int threads = row_vecs >= 256 ? 256 : (row_vecs > 64 ? 128 : 64);
-  const dim3 grid((unsigned)num_tokens, 2);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  switch (vec) {
-    case 16:
-      hipLaunchKernelGGL(reshape_and_cache_kernel<uint4>, grid, dim3(threads), 0, st, (const uint4*)key,
-                         (const uint4*)value, (uint4*)k_pool, (uint4*)v_pool, slot_mapping, row_vecs, num_slots);
-      break;
-    case 8:
-      hipLaunchKernelGGL(reshape_and_cache_kernel<uint2>, grid, dim3(threads), 0, st, (const uint2*)key,
-                         (const uint2*)value, (uint2*)k_pool, (uint2*)v_pool, slot_mapping, row_vecs, num_slots);
-      break;
-    case 4:
-      hipLaunchKernelGGL(reshape_and_cache_kernel<uint32_t>, grid, dim3(threads), 0, st, (const uint32_t*)key,
-                         (const uint32_t*)value, (uint32_t*)k_pool, (uint32_t*)v_pool, slot_mapping, row_vecs,
-                         num_slots);
-      break;
-    case 2:
-      hipLaunchKernelGGL(reshape_and_cache_kernel<uint16_t>, grid, dim3(threads), 0, st, (const uint16_t*)key,
-                         (const uint16_t*)value, (uint16_t*)k_pool, (uint16_t*)v_pool, slot_mapping, row_vecs,
-                         num_slots);
-      break;
-    default:
-      hipLaunchKernelGGL(reshape_and_cache_kernel<uint8_t>, grid, dim3(threads), 0, st, (const uint8_t*)key,
-                         (const uint8_t*)value, (uint8_t*)k_pool, (uint8_t*)v_pool, slot_mapping, row_vecs,
-                         num_slots);
-      break;
-  }
-  return pa::launch_status();
+  rc = pa::pool_view(k_pool, v_pool, (int)layout, block_size, num_kv_heads, head_dim, (int)dtype, &pv);
+  if (rc != PA_OK) return rc;
+  DecodePlan plan;
+  rc = plan_decode(out, query, pv.k, pv.v, block_tables, context_lens, shp, scale, workspace, workspace_bytes,
+                   partition_size, &plan);
+  if (rc != PA_OK) return rc;
+  rc = launch_partitions(out, query, pv, block_tables, context_lens, shp, scale, workspace, plan, stream);
+  if (rc != PA_OK) return rc;
+  return launch_combine(out, context_lens, shp, workspace, plan, stream);
 }
 
 extern "C" int pa_decode_attention_ex(void* out, const void* query, const void* k_pool, const void* v_pool,
@@ -861,16 +929,10 @@ extern "C" int pa_decode_attention_ex(void* out, const void* query, const void* 
                                       int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len,
                                       float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
                                       int32_t partition_size, void* stream) {
-  const pa::DecodeShape shp{num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                            max_context_len, (int)dtype};
-  DecodePlan plan;
-  int rc = plan_decode(out, query, k_pool, v_pool, block_tables, context_lens, shp, scale, workspace,
-                       workspace_bytes, partition_size, &plan);
-  if (rc != PA_OK) return rc;
-  rc = launch_partitions(out, query, k_pool, v_pool, block_tables, context_lens, shp, scale, workspace, plan,
-                         stream);
-  if (rc != PA_OK) return rc;
-  return launch_combine(out, context_lens, shp, workspace, plan, stream);
+  if (!v_pool) return PA_ERR_INVALID_ARG;
+  return pa_decode_attention_layout(out, query, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
+                                    num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_context_len, scale,
+                                    dtype, workspace, workspace_bytes, partition_size, PA_KV_SPLIT, stream);
 }
 
 extern "C" int pa_decode_attention(void* out, const void* query, const void* k_pool, const void* v_pool,
@@ -896,8 +958,10 @@ extern "C" int pa_decode_partitions(void* out, const void* query, const void* k_
   int rc = plan_decode(out, query, k_pool, v_pool, block_tables, context_lens, shp, scale, workspace,
                        workspace_bytes, partition_size, &plan);
   if (rc != PA_OK) return rc;
-  return launch_partitions(out, query, k_pool, v_pool, block_tables, context_lens, shp, scale, workspace, plan,
-                           stream);
+  pa::PoolView pv;
+  rc = pa::pool_view(k_pool, v_pool, PA_KV_SPLIT, block_size, num_kv_heads, head_dim, (int)dtype, &pv);
+  if (rc != PA_OK) return rc;
+  return launch_partitions(out, query, pv, block_tables, context_lens, shp, scale, workspace, plan, stream);
 }
 
 extern "C" int pa_decode_combine(void* out, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,

@@ -49,6 +49,11 @@ struct PrefillArgs {
   int partial_base;    // < 0: final rows, partials only for split rows; >= 0: every partition's
   int partial_stride;  //   partials go to slot partial_base + s of partial_stride slots per row
   float qscale;        // scale * log2(e)
+  // pool geometry in bytes (layout): K row (block p, token t, head h) at
+  // k_pool + p*block_stride + t*row_stride + h*head_stride, V likewise;
+  // span = what one block may touch from its first byte
+  int64_t block_stride;
+  uint32_t row_stride, head_stride, span;
 };
 
 // A finite floor for the running max: a column whose keys all lie beyond this
@@ -177,13 +182,14 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
     }
   }
 
-  const uint32_t row_stride = (uint32_t)a.num_kv_heads * ROWB;
-  const size_t block_stride = (size_t)BS * row_stride;
+  const uint32_t row_stride = a.row_stride;
+  const uint32_t hoff = (uint32_t)g * a.head_stride;
+  const size_t block_stride = (size_t)a.block_stride;
   uint32_t kdma[NLI];
 #pragma unroll
   for (int i = 0; i < NLI; ++i) {
     const int slot = 64 * i + lane, t = slot / CPR, q = slot % CPR;
-    kdma[i] = (uint32_t)t * row_stride + (uint32_t)g * ROWB + (uint32_t)((q ^ kswz_t<CPR>(t)) * 16);
+    kdma[i] = (uint32_t)t * row_stride + hoff + (uint32_t)((q ^ kswz_t<CPR>(t)) * 16);
   }
   uint32_t kread[NKC];  // QK A operand: token 4*(col%4) + col/4, chunk 4c + gq
   {
@@ -191,7 +197,7 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
 #pragma unroll
     for (int c = 0; c < NKC; ++c) kread[c] = (uint32_t)(t * CPR + ((4 * c + gq) ^ kswz_t<CPR>(t))) * 16;
   }
-  const uint32_t voff = (uint32_t)gq * row_stride + (uint32_t)g * ROWB + col * VPL * 2;
+  const uint32_t voff = (uint32_t)gq * row_stride + hoff + col * VPL * 2;
   __shared__ __attribute__((aligned(1024))) uint8_t kslot0[WPW][KBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t kslot1[WPW][KBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t kslot2[NBUF > 2 ? WPW : 1][KBYTES];
@@ -211,7 +217,7 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
   auto load_block = [&](int j, int slot, VT* vr) {
     const bool real = j <= last;
     const size_t off = (size_t)(uint32_t)tab.get(real ? j : last) * block_stride;
-    const uint32_t span = real ? (uint32_t)block_stride : 0u;
+    const uint32_t span = real ? a.span : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_block_rsrc(a.k_pool + off, span);
     const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, span);
 #pragma unroll
@@ -432,8 +438,9 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
   // +DPW of the 2*KI (the first KI fill K, the rest V); lane l of
   // instruction i fills LDS chunk 64*(i mod KI) + l = (row t, position q):
   // K with the row's chunk q ^ swizzle(t), V with chunk q.
-  const uint32_t row_stride = (uint32_t)a.num_kv_heads * ROWB;
-  const size_t block_stride = (size_t)BS * row_stride;
+  const uint32_t row_stride = a.row_stride;
+  const uint32_t hoff = (uint32_t)g * a.head_stride;
+  const size_t block_stride = (size_t)a.block_stride;
   uint32_t goff[DPW];
   bool is_k[DPW], has[DPW];
   int lds_off[DPW];
@@ -444,7 +451,7 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
     is_k[i] = ins < KI;
     const int idx = is_k[i] ? ins : ins - KI;
     const int sl = 64 * idx + lane, t = sl / CPR, q = sl % CPR;
-    goff[i] = (uint32_t)t * row_stride + (uint32_t)g * ROWB + (uint32_t)((is_k[i] ? (q ^ kswz_t<CPR>(t)) : q) * 16);
+    goff[i] = (uint32_t)t * row_stride + hoff + (uint32_t)((is_k[i] ? (q ^ kswz_t<CPR>(t)) : q) * 16);
     lds_off[i] = idx * 1024;
   }
   uint32_t kread[NKC];  // QK A operand: token 4*(col%4) + col/4, chunk 4c + gq
@@ -483,7 +490,7 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
   auto load_block = [&](int j, int x) {
     const bool real = j <= last;
     const size_t off = (size_t)(uint32_t)tab.get(real ? j : last) * block_stride;
-    const uint32_t span = real ? (uint32_t)block_stride : 0u;
+    const uint32_t span = real ? a.span : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_block_rsrc(a.k_pool + off, span);
     const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, span);
 #pragma unroll
@@ -699,6 +706,15 @@ size_t prefill_workspace(const pa::PrefillShape& s, int parts) {
   return pa::workspace_bytes(s.num_tokens, s.d.num_heads, s.d.head_dim, parts);
 }
 
+void set_pool(PrefillArgs* a, const pa::PoolView& pv, const pa::DecodeShape& s) {
+  a->k_pool = pv.k;
+  a->v_pool = pv.v;
+  a->block_stride = pv.block_stride;
+  a->row_stride = (uint32_t)pv.row_stride;
+  a->head_stride = (uint32_t)pv.head_stride;
+  a->span = (uint32_t)pv.step_span(s.head_dim * pa::elem_bytes(s.dtype), s.num_kv_heads);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ C ABI
@@ -718,18 +734,23 @@ extern "C" size_t pa_prefill_workspace_bytes(int32_t num_tokens, int32_t num_hea
   return prefill_workspace(s, parts);
 }
 
-extern "C" int pa_prefill_attention(void* out, const void* query, const void* k_pool, const void* v_pool,
-                                    const int32_t* block_tables, const int32_t* context_lens,
-                                    const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
-                                    int32_t max_query_len, int32_t num_heads, int32_t num_kv_heads,
-                                    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                                    int32_t max_context_len, float scale, pa_dtype dtype, void* workspace,
-                                    size_t workspace_bytes, int32_t partition_size, void* stream) {
+extern "C" int pa_prefill_attention_layout(void* out, const void* query, const void* k_pool, const void* v_pool,
+                                           const int32_t* block_tables, const int32_t* context_lens,
+                                           const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                                           int32_t max_query_len, int32_t num_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                           int32_t max_context_len, float scale, pa_dtype dtype, void* workspace,
+                                           size_t workspace_bytes, int32_t partition_size, pa_kv_layout layout,
+                                           void* stream) {
   const pa::PrefillShape shp{{num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                               max_context_len, (int)dtype},
                              num_tokens,
                              max_query_len};
-  int rc = pa::check_prefill(out, query, k_pool, v_pool, block_tables, context_lens, query_start_loc, shp, scale);
+  int rc = pa::check_prefill(out, query, k_pool, layout == PA_KV_FUSED ? k_pool : v_pool, block_tables,
+                             context_lens, query_start_loc, shp, scale);
+  if (rc != PA_OK) return rc;
+  pa::PoolView pv;
+  rc = pa::pool_view(k_pool, v_pool, (int)layout, block_size, num_kv_heads, head_dim, (int)dtype, &pv);
   if (rc != PA_OK) return rc;
   const pa::DecodeGrid gd = pa::decode_grid(shp.d);
   const pa::PrefillGrid pg = pa::prefill_grid(shp);
@@ -751,10 +772,9 @@ extern "C" int pa_prefill_attention(void* out, const void* query, const void* k_
   if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
 
   PrefillArgs a;
+  set_pool(&a, pv, shp.d);
   a.out = out;
   a.query = query;
-  a.k_pool = static_cast<const uint8_t*>(k_pool);
-  a.v_pool = static_cast<const uint8_t*>(v_pool);
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.query_start_loc = query_start_loc;
@@ -788,6 +808,20 @@ extern "C" int pa_prefill_attention(void* out, const void* query, const void* k_
   hipLaunchKernelGGL(cf, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, out, a.ws_acc, a.ws_ml, context_lens,
                      query_start_loc, num_seqs, num_tokens, num_heads, ps, parts);
   return pa::launch_status();
+}
+
+extern "C" int pa_prefill_attention(void* out, const void* query, const void* k_pool, const void* v_pool,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                                    int32_t max_query_len, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                    int32_t max_context_len, float scale, pa_dtype dtype, void* workspace,
+                                    size_t workspace_bytes, int32_t partition_size, void* stream) {
+  if (!v_pool) return PA_ERR_INVALID_ARG;
+  return pa_prefill_attention_layout(out, query, k_pool, v_pool, block_tables, context_lens, query_start_loc,
+                                     num_seqs, num_tokens, max_query_len, num_heads, num_kv_heads, head_dim,
+                                     block_size, max_blocks_per_seq, max_context_len, scale, dtype, workspace,
+                                     workspace_bytes, partition_size, PA_KV_SPLIT, stream);
 }
 
 // ------------------------------------------------------------------ shared-prefix decode
@@ -825,11 +859,13 @@ extern "C" int pa_decode_attention_shared_prefix(
   MergeSlotsFn mf = pick_merge_slots(shp.d.dtype, shp.d.head_dim);
   if (!fn || !mf) return PA_ERR_UNSUPPORTED;
 
+  pa::PoolView pv;
+  rc = pa::pool_view(k_pool, v_pool, PA_KV_SPLIT, block_size, num_kv_heads, head_dim, (int)dtype, &pv);
+  if (rc != PA_OK) return rc;
   PrefillArgs a;
+  set_pool(&a, pv, shp.d);
   a.out = out;
   a.query = query;
-  a.k_pool = static_cast<const uint8_t*>(k_pool);
-  a.v_pool = static_cast<const uint8_t*>(v_pool);
   a.block_tables = block_tables;
   a.ws_acc = static_cast<float*>(workspace);
   a.ws_ml = reinterpret_cast<float2*>(static_cast<float*>(workspace) + (size_t)num_seqs * num_heads * slots * head_dim);

@@ -177,6 +177,56 @@ def test_stream_read_argument_checks():
     assert f(ctypes.c_void_p(0x1008), 1024, FAKE, 0, None) == B.PA_ERR_INVALID_ARG  # misaligned
 
 
+def decode_layout(layout, **kw):
+    a = dict(out=FAKE, query=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, B=4, H=8, Hkv=2, D=128, bs=16,
+             mb=8, maxlen=128, scale=0.088, dtype=B.PA_BF16, ws=None, wsb=0, ps=128)
+    a.update(kw)
+    return B.lib().pa_decode_attention_layout(a["out"], a["query"], a["k"], a["v"], a["bt"], a["lens"], a["B"],
+                                              a["H"], a["Hkv"], a["D"], a["bs"], a["mb"], a["maxlen"], a["scale"],
+                                              a["dtype"], a["ws"], a["wsb"], a["ps"], layout, None)
+
+
+def test_layout_argument_checks():
+    # the fused pool is one pointer: a V pool alongside it is an error, and
+    # the split layout still needs both
+    assert decode_layout(B.PA_KV_FUSED) == B.PA_ERR_INVALID_ARG
+    assert decode_layout(B.PA_KV_SPLIT, v=None) == B.PA_ERR_INVALID_ARG
+    assert decode_layout(2, v=None) == B.PA_ERR_INVALID_ARG
+    assert decode_layout(B.PA_KV_FUSED, v=None, dtype=7) == B.PA_ERR_UNSUPPORTED
+    assert decode_layout(B.PA_KV_FUSED, v=None, k=None) == B.PA_ERR_INVALID_ARG
+    assert decode_layout(B.PA_KV_FUSED, v=None, ps=16) == B.PA_ERR_WORKSPACE  # checks reached the plan
+    # a block over 2 GiB cannot be addressed with 32-bit offsets
+    assert decode_layout(B.PA_KV_FUSED, v=None, Hkv=1 << 20, H=1 << 20, bs=256, mb=1, maxlen=256,
+                         ps=256) == B.PA_ERR_INVALID_ARG
+    lib = B.lib()
+    rs = lib.pa_reshape_and_cache_layout
+    assert rs(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 64, 16, 10, B.PA_BF16, B.PA_KV_FUSED, None) == B.PA_ERR_INVALID_ARG
+    assert rs(FAKE, FAKE, FAKE, None, FAKE, 4, 2, 64, 16, 10, B.PA_BF16, B.PA_KV_SPLIT, None) == B.PA_ERR_INVALID_ARG
+    assert rs(FAKE, FAKE, FAKE, None, FAKE, 0, 2, 64, 16, 10, B.PA_BF16, B.PA_KV_FUSED, None) == B.PA_OK
+    assert lib.pa_reshape_and_cache(FAKE, FAKE, FAKE, None, FAKE, 0, 2, 64, 16, 10, B.PA_BF16,
+                                    None) == B.PA_ERR_INVALID_ARG
+    cv = lib.pa_convert_blocks
+    ok = [FAKE, None, B.PA_KV_FUSED, 10, FAKE, FAKE, B.PA_KV_SPLIT, 10, FAKE, FAKE, 3, 16, 2, 64, B.PA_BF16, None]
+
+    def conv(**kw):
+        a = list(ok)
+        names = ["dk", "dv", "dl", "dn", "sk", "sv", "sl", "sn", "src", "dst", "n", "bs", "hkv", "d", "dt", "st"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return cv(*a)
+    assert conv(n=0) == B.PA_OK
+    assert conv(dv=FAKE) == B.PA_ERR_INVALID_ARG        # fused destination with a V pool
+    assert conv(sv=None) == B.PA_ERR_INVALID_ARG        # split source without one
+    assert conv(dl=5) == B.PA_ERR_INVALID_ARG
+    assert conv(src=None) == B.PA_ERR_INVALID_ARG
+    assert conv(n=-1) == B.PA_ERR_INVALID_ARG
+    assert conv(dn=0) == B.PA_ERR_INVALID_ARG
+    assert conv(dt=9) == B.PA_ERR_UNSUPPORTED
+    pf = lib.pa_prefill_attention_layout
+    assert pf(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 4, 8, 2, 128, 16, 8, 128, 0.088, B.PA_BF16, None, 0, 0,
+              B.PA_KV_FUSED, None) == B.PA_ERR_INVALID_ARG
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_LIB", None)
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
