@@ -353,7 +353,14 @@ def main_copy(args):
         base = {"value": 2 * n / dt, "unit": "block copies/s", "cores": 1, "kind": "oracle",
                 "sample": f"{n} of {len(cb.src)} pairs of {cb.name}, K and V pools, {reps} repetitions"}
         del pool
-    ms, per, wall = time_stages([lambda: PB.pa_copy_blocks(kp, vp, src, dst)], args.steps, args.warmup)
+    stage, kernel = (lambda: PB.pa_copy_blocks(kp, vp, src, dst)), "copy_blocks_kernel"
+    if args.layout == "fused":
+        # the same pairs copied out of the split pools into a fused pool: the layout conversion
+        fused = torch.empty((cb.num_blocks, cb.num_kv_heads, cb.block_size, 2 * cb.head_dim), dtype=kp.dtype,
+                            device="cuda")
+        stage = lambda: PB.pa_convert_blocks(fused, None, PB.PA_KV_FUSED, kp, vp, PB.PA_KV_SPLIT, src, dst)  # noqa: E731
+        kernel = "convert_blocks_kernel"
+    ms, per, wall = time_stages([stage], args.steps, args.warmup)
     nbytes = cb.copy_bytes()
     achieved = nbytes / (per[0] * 1e-3) / 1e9
     rec = {
@@ -362,11 +369,13 @@ def main_copy(args):
         "scaling": "weak", "vs_baseline": None, "dtype": cb.dtype, "data": "synthetic",
         "config": {"workload": cb.name, "num_pairs": int(len(cb.src)), "num_blocks": cb.num_blocks,
                    "block_size": cb.block_size, "num_kv_heads": cb.num_kv_heads, "head_dim": cb.head_dim,
-                   "block_bytes": cb.block_bytes, "description": cb.description},
+                   "block_bytes": cb.block_bytes, "description": cb.description,
+                   "destination_layout": args.layout},
         "copy_bytes_per_step": nbytes,
-        "kernel_us": {"copy_blocks": per[0] * 1e3},
-        "roofline": {"bound": "hbm", "kernel": "copy_blocks_kernel", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(cb.name, "copy_blocks")},
+        "kernel_us": {kernel.replace("_kernel", ""): per[0] * 1e3},
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": load_traffic(cb.name, "copy_blocks") if args.layout == "split" else None},
         "cpu_baseline": base, "wall_s_timed": wall,
     }
     print(json.dumps(rec), flush=True)
