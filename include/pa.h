@@ -171,8 +171,9 @@ size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_heads, int32_t
  *                  pa_decode_workspace_bytes(...), or NULL/0 when
  *                  max_context_len needs a single partition
  *
- * Supported: dtype F32/F16/BF16, head_dim 64 or 128, block_size 16,
- * num_heads a multiple of num_kv_heads.
+ * Supported: dtype F32/F16/BF16, head_dim 64 or 128, num_heads a multiple
+ * of num_kv_heads; block_size a power of two from 1 to 256 for F16/BF16 (the
+ * handbook's block-size trade-off, section "块大小怎么选"), 16 for F32.
  * Device contents: block ids must address blocks of the pools and
  * context_lens must lie in [0, max_context_len]; anything else is undefined
  * (reads outside the pools).  A context length of 0 yields zeros.
@@ -190,7 +191,8 @@ int pa_decode_attention(void* out, const void* query, const void* k_pool, const 
 
 /*
  * As pa_decode_attention with an explicit partition size in tokens: a
- * multiple of block_size in [block_size, 256*block_size], or 0 to let the
+ * multiple of max(16, block_size) of at most 256*block_size (whole pool
+ * blocks and whole 16-token steps of the matrix-core tile), or 0 to let the
  * library choose.  INVALID_ARG for other values.
  */
 int pa_decode_attention_ex(void* out, const void* query, const void* k_pool, const void* v_pool,
@@ -279,10 +281,11 @@ int32_t pa_decode_plan_partition_size(int32_t num_seqs, int32_t num_heads, int32
  *                    L_b - n_b + i and attends to positions 0 .. L_b - n_b + i.
  *   max_query_len    host bound of n_b; 1 <= max_query_len <= num_tokens.
  *   other arguments  as pa_decode_attention (pools, tables, scale, dtype, stream).
- * fp16 and bf16 only (the tile runs on the matrix cores): UNSUPPORTED for fp32.
+ * fp16 and bf16 only (the tile runs on the matrix cores): UNSUPPORTED for fp32;
+ * block sizes as pa_decode_attention.
  * partition_size: 0 lets the library choose (it may split long contexts into
  * partitions merged by a second kernel, keeping the partials within 256 MiB),
- * or a multiple of block_size in [block_size, 256*block_size].  The workspace
+ * or a size pa_decode_attention_ex accepts.  The workspace
  * must hold pa_prefill_workspace_bytes(...) for the same partition_size (0 when
  * the context fits one partition).  Rows past query_start_loc[num_seqs] are
  * not written.  Device contents are the caller's contract (n_b <= L_b <=
@@ -401,7 +404,9 @@ int pa_seq_block_table(const pa_block_pool* pool, int32_t seq, int32_t* table, i
  *   max_group_size, max_prefix_len: host bounds (max_prefix_len a multiple of
  *   block_size, <= max_context_len).
  *   workspace: pa_shared_prefix_workspace_bytes(...) bytes, always needed.
- * fp16 / bf16 only.  Errors as pa_decode_attention.
+ * fp16 / bf16 only; block_size a power of two from 4 to 256 (both passes split
+ * keys at 1024 tokens, which must fit 256 blocks): UNSUPPORTED otherwise.
+ * Errors as pa_decode_attention.
  */
 int pa_decode_attention_shared_prefix(void* out, const void* query, const void* k_pool, const void* v_pool,
                                       const int32_t* block_tables, const int32_t* context_lens,

@@ -139,6 +139,31 @@ struct TableSlice {
   }
 };
 
+// Pool block sizes against the 16-token steps of the MFMA tiles:
+//  * kBlocks16: blocks and steps coincide;
+//  * kBlocksLarge: blocks of 16 << shift tokens; a step is a window of 16
+//    rows inside one block (table entry step >> shift, rows 16 * (step & mask));
+//  * kBlocksSmall: blocks of 16 >> shift tokens; a step's 16 rows come from
+//    1 << shift blocks, so every lane addresses its own row's block.
+constexpr int kBlocks16 = 0, kBlocksLarge = 1, kBlocksSmall = 2;
+
+// kBlocksSmall: byte offset of the pool block holding each of N rows a lane
+// touches in step jj; blk[i] = index of row i's block within the step (row /
+// block size).  The step's blocks are table entries (jj << shift) + k, clamped
+// to the partition's last entry (nent - 1) past its end, so every address
+// stays inside a block the caller owns.
+template <int N>
+__device__ __forceinline__ void step_block_bases(const TableSlice& tab, int jj, int shift, int nent,
+                                                 size_t block_stride, const int* blk, size_t* base) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) base[i] = 0;
+  for (int k = 0; k < (1 << shift); ++k) {
+    const size_t b = (size_t)(uint32_t)tab.get(min((jj << shift) + k, nent - 1)) * block_stride;
+#pragma unroll
+    for (int i = 0; i < N; ++i) base[i] = blk[i] == k ? b : base[i];
+  }
+}
+
 // Workgroup id -> logical id such that each XCD (workgroups are dealt to the
 // 8 XCDs round-robin) receives one contiguous range of logical ids; a bijection
 // whatever the hardware order.

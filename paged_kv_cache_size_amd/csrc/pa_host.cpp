@@ -216,6 +216,13 @@ int partition_granule(int block_size) { return block_size > kBlockSize ? block_s
 
 int max_partition_tokens(int block_size) { return kMaxPartitionBlocks * block_size; }
 
+int block_shift(int block_size) {
+  const int ratio = block_size >= kBlockSize ? block_size / kBlockSize : kBlockSize / block_size;
+  int r = 0;
+  while ((1 << r) < ratio) ++r;
+  return r;
+}
+
 int validate_partition(int requested, int block_size) {
   const int gran = partition_granule(block_size);
   if (requested < gran || requested > max_partition_tokens(block_size) || requested % gran != 0)
@@ -286,7 +293,6 @@ int check_prefill(const void* out, const void* query, const void* k_pool, const 
   if (s.num_tokens <= 0 || s.max_query_len <= 0 || s.max_query_len > s.num_tokens) return PA_ERR_INVALID_ARG;
   if (s.max_query_len > s.d.max_context_len) return PA_ERR_INVALID_ARG;
   if (s.d.dtype == PA_F32) return PA_ERR_UNSUPPORTED;  // the prefill tile is an MFMA tile (16-bit inputs)
-  if (s.d.block_size != kBlockSize) return PA_ERR_UNSUPPORTED;  // and reads whole 16-row blocks
   if ((int64_t)s.num_tokens * s.d.num_heads > (int64_t)1 << 30) return PA_ERR_INVALID_ARG;
   return PA_OK;
 }
@@ -309,7 +315,8 @@ int check_shared_prefix(const void* out, const void* query, const void* k_pool, 
   if (max_prefix_len < 0 || max_prefix_len > s.d.max_context_len || max_prefix_len % s.d.block_size != 0)
     return PA_ERR_INVALID_ARG;
   if (s.d.dtype == PA_F32) return PA_ERR_UNSUPPORTED;  // both passes run the MFMA prefill tile
-  if (s.d.block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
+  // the passes split keys at kSharedPrefixPartition tokens, which must fit one table slice
+  if (max_partition_tokens(s.d.block_size) < kSharedPrefixPartition) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
@@ -337,8 +344,8 @@ PrefillGrid prefill_grid(const PrefillShape& s) {
 
 int prefill_partition_bounds(const PrefillShape& s, int* min_parts, int* max_parts) {
   const int bs = s.d.block_size;
-  const int64_t nb = (s.d.max_context_len + bs - 1) / bs;
-  const int64_t lo = (nb + kMaxPartitionBlocks - 1) / kMaxPartitionBlocks;
+  const int64_t most = max_partition_tokens(bs);  // a multiple of the granule
+  const int64_t lo = (s.d.max_context_len + most - 1) / most;
   int64_t hi = auto_partition_bound(s.d.max_context_len, bs);
   const size_t per_part = (size_t)s.num_tokens * s.d.num_heads * ((size_t)s.d.head_dim + 2) * sizeof(float);
   const int64_t cap = per_part > 0 ? (int64_t)(kPrefillWorkspaceCap / per_part) : hi;
@@ -350,40 +357,41 @@ int prefill_partition_bounds(const PrefillShape& s, int* min_parts, int* max_par
 
 int prefill_partition_size(const PrefillShape& s, int requested, int num_cus, int wg_per_cu) {
   const int bs = s.d.block_size;
-  if (requested != 0) {
-    if (requested < bs || requested > kMaxPartitionBlocks * bs || requested % bs != 0) return -PA_ERR_INVALID_ARG;
-    return requested;
-  }
+  if (requested != 0) return validate_partition(requested, bs);
+  // Partitions are whole granules (max(16, block size) tokens); costs count
+  // 16-token steps.
+  const int64_t gran = partition_granule(bs);
+  const int64_t steps_per_gran = gran / kBlockSize;
   const PrefillGrid pg = prefill_grid(s);
   const int64_t slots = total_slots(num_cus, wg_per_cu);
-  const int64_t nb = (s.d.max_context_len + bs - 1) / bs;
+  const int64_t ng = (s.d.max_context_len + gran - 1) / gran;
   int lo = 1, hi = 1;
   prefill_partition_bounds(s, &lo, &hi);
-  int64_t best_pb = 0, prev_pb = 0;
+  int64_t best_pg = 0, prev_pg = 0;
   double best = 0.0;
   for (int64_t parts = lo; parts <= hi; ++parts) {
-    const int64_t pb = (nb + parts - 1) / parts;
-    if (pb == prev_pb) continue;
-    prev_pb = pb;
-    const int64_t p = (nb + pb - 1) / pb;
-    if (p > hi) continue;
+    const int64_t pgr = (ng + parts - 1) / parts;  // granules per partition
+    if (pgr == prev_pg) continue;
+    prev_pg = pgr;
+    const int64_t p = (ng + pgr - 1) / pgr;
+    if (p > hi || pgr * gran > max_partition_tokens(bs)) continue;
     const int64_t items = pg.items * p;
-    const double item = (double)pb + kItemSetup;
+    const double item = (double)(pgr * steps_per_gran) + kItemSetup;
     const int64_t tail = items % slots;
     double cost = (double)(items / slots) * item;
     if (tail > 0) cost += item / std::min(kMaxSpeedup, (double)slots / (double)tail);
     if (p > 1) {  // merge: every partial read once
-      const double wg_block_bytes = (double)pg.waves * 2.0 * bs * s.d.head_dim * elem_bytes(s.d.dtype);
+      const double wg_step_bytes = (double)pg.waves * 2.0 * kBlockSize * s.d.head_dim * elem_bytes(s.d.dtype);
       cost += kMergeLaunch + 2.0 * (double)s.num_tokens * s.d.num_heads * p * (s.d.head_dim + 2) * 4.0 /
-                                 ((double)slots * wg_block_bytes);
+                                 ((double)slots * wg_step_bytes);
     }
-    if (best_pb == 0 || cost < best - 1e-9) {
+    if (best_pg == 0 || cost < best - 1e-9) {
       best = cost;
-      best_pb = pb;
+      best_pg = pgr;
     }
   }
-  if (best_pb == 0) best_pb = std::min<int64_t>(kMaxPartitionBlocks, nb);
-  return (int)(best_pb * bs);
+  if (best_pg == 0) best_pg = std::min<int64_t>(max_partition_tokens(bs) / gran, ng);
+  return (int)(best_pg * gran);
 }
 
 size_t workspace_bytes(int num_seqs, int num_heads, int head_dim, int parts) {

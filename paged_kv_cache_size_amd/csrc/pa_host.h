@@ -19,14 +19,16 @@ constexpr int kMaxAutoPartitionBlocks = 64;  // automatic choice without the con
 
 int elem_bytes(int dtype);  // 0 for an unknown dtype
 
-// Pool block sizes the decode path runs (powers of two, 1..256): the 16-bit
-// MFMA tile takes 16-token steps, so a larger block holds several steps and a
-// smaller one contributes a few rows to a step; fp32 (VALU tile), prefill and
-// the cascade read whole 16-row blocks only.
+// Pool block sizes the 16-bit paths run (powers of two, 1..256): the MFMA
+// tiles take 16-token steps, so a larger block holds several steps and a
+// smaller one contributes a few rows to a step; fp32 (VALU tile) reads whole
+// 16-row blocks only.
 constexpr int kMinDecodeBlock = 1;
 constexpr int kMaxDecodeBlock = 256;
 bool decode_block_size_ok(int block_size, int dtype);
-int partition_granule(int block_size);     // partitions are multiples of max(16, block_size) tokens
+int partition_granule(int block_size);  // partitions are multiples of max(16, block_size) tokens
+// log2 of block_size / 16 (blocks of 16 or more tokens) or 16 / block_size.
+int block_shift(int block_size);
 int max_partition_tokens(int block_size);  // kMaxPartitionBlocks pool blocks
 int validate_partition(int requested, int block_size);  // requested, or a negated pa_status
 

@@ -333,7 +333,6 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
 //  * kBlocksSmall: blocks of 16 >> a.block_shift tokens; a step's 16 rows
 //    come from 1 << shift blocks, so every lane addresses its own row's block
 //    (direct-to-LDS and V loads from per-lane global addresses).
-constexpr int kBlocks16 = 0, kBlocksLarge = 1, kBlocksSmall = 2;
 
 template <int DT, int D, int NBUF, int WPW, int MODE>
 __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs a) {
@@ -650,12 +649,6 @@ DecodeFn pick_mfma_bs(int wpw, int block_size) {
   return pick_mfma<DT, D, kBlocksSmall>(wpw);
 }
 
-int log2_int(int x) {
-  int r = 0;
-  while ((1 << r) < x) ++r;
-  return r;
-}
-
 // fp32: VALU kernel (one instantiation per heads-per-wave); fp16/bf16: MFMA
 // kernel (one per waves-per-workgroup).
 DecodeFn pick_decode(int dtype, int d, const pa::DecodeGrid& g, int block_size) {
@@ -744,8 +737,7 @@ int launch_partitions(void* out, const void* query, const pa::PoolView& pv, cons
   a.rep = gd.rep;
   a.chunks = gd.chunks;
   a.max_blocks_per_seq = shp.max_blocks_per_seq;
-  a.block_shift = shp.block_size >= pa::kBlockSize ? log2_int(shp.block_size / pa::kBlockSize)
-                                                  : log2_int(pa::kBlockSize / shp.block_size);
+  a.block_shift = pa::block_shift(shp.block_size);
   a.part_tokens = plan.ps;
   a.num_parts = plan.parts;
   a.groups = gd.groups;

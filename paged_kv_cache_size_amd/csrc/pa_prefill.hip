@@ -44,6 +44,7 @@ struct PrefillArgs {
   float* ws_acc;                   // [T, H, slots, D]
   float2* ws_ml;                   // [T, H, slots] (running max in log2 units, denominator)
   int num_heads, num_kv_heads, rep, repc, chunks, max_blocks_per_seq;
+  int block_shift;  // pool blocks of 16 << shift (kBlocksLarge) or 16 >> shift (kBlocksSmall) tokens
   int part_tokens, num_parts, groups, tiles;  // tiles: 16-column tiles per (sequence, wave unit)
   int causal;          // 1: row i sits at position L - n + i; 0: every row sees the whole key range
   int partial_base;    // < 0: final rows, partials only for split rows; >= 0: every partition's
@@ -112,8 +113,10 @@ __device__ __forceinline__ void store_empty_slot(const PrefillArgs& a, size_t qr
   if (gq == 0) a.ws_ml[idx] = make_float2(-INFINITY, 0.f);
 }
 
-template <int DT, int D, int NBUF, int WPW>
+template <int DT, int D, int NBUF, int WPW, int MODE>
 __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArgs a) {
+  constexpr bool SUB = MODE == kBlocksLarge;
+  constexpr bool GATHER = MODE == kBlocksSmall;
   using Ops = MfmaOps<DT>;
   constexpr int BS = pa::kBlockSize;
   constexpr int ROWB = D * 2;
@@ -164,13 +167,16 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
   }
   const int lim = live ? min(pend, pos + 1) : 0;  // this column's keys are [start, lim)
   const int col_parts = (pos - kb + a.part_tokens) / a.part_tokens;  // partitions holding its keys
-  const int blk0 = start / BS;
-  const int nblk = (end - start + BS - 1) / BS;  // 1..kMaxPartitionBlocks
+  const int pshift = MODE != kBlocks16 ? a.block_shift : 0;
+  const int pool_bs = SUB ? BS << pshift : GATHER ? BS >> pshift : BS;  // tokens per pool block
+  const int blk0 = start / pool_bs;  // partitions start on a pool block
+  const int nblk = (end - start + BS - 1) / BS;  // 16-token steps
+  const int nent = MODE == kBlocks16 ? nblk : (end - start + pool_bs - 1) / pool_bs;  // 1..kMaxPartitionBlocks
   const int last = nblk - 1;
 
   const int32_t* bt = a.block_tables + (size_t)trow * a.max_blocks_per_seq + blk0;
   TableSlice tab;
-  tab.load(bt, nblk, lane);
+  tab.load(bt, nent, lane);
 
   uint4 qop[NKC];
   {
@@ -198,6 +204,25 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
     for (int c = 0; c < NKC; ++c) kread[c] = (uint32_t)(t * CPR + ((4 * c + gq) ^ kswz_t<CPR>(t))) * 16;
   }
   const uint32_t voff = (uint32_t)gq * row_stride + hoff + col * VPL * 2;
+  const size_t step_stride = (size_t)BS * row_stride;  // 16-token windows inside a larger block
+  // Small blocks: for each row a lane loads, its block within the step and
+  // its byte offset inside that block.
+  int kblk[GATHER ? NLI : 1], vblk[GATHER ? 4 : 1];
+  uint32_t kin[GATHER ? NLI : 1], vin[GATHER ? 4 : 1];
+  if constexpr (GATHER) {
+#pragma unroll
+    for (int i = 0; i < NLI; ++i) {
+      const int slot = 64 * i + lane, t = slot / CPR, q = slot % CPR;
+      kblk[i] = t / pool_bs;
+      kin[i] = (uint32_t)(t % pool_bs) * row_stride + hoff + (uint32_t)((q ^ kswz_t<CPR>(t)) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * i + gq;
+      vblk[i] = t / pool_bs;
+      vin[i] = (uint32_t)(t % pool_bs) * row_stride + hoff + col * VPL * 2;
+    }
+  }
   __shared__ __attribute__((aligned(1024))) uint8_t kslot0[WPW][KBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t kslot1[WPW][KBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t kslot2[NBUF > 2 ? WPW : 1][KBYTES];
@@ -212,11 +237,29 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
   for (int t = 0; t < VPL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = kMaxFloor, l = 0.f;
 
-  // Loads past the partition's last block go through an empty descriptor
-  // (zeros, no memory access), so every wait stays an exact count.
+  // Loads past the partition's last step go through an empty descriptor
+  // (zeros, no memory access), so every wait stays an exact count; with small
+  // blocks (per-lane addresses) they re-read the last step's rows instead
+  // (masked).
   auto load_block = [&](int j, int slot, VT* vr) {
     const bool real = j <= last;
-    const size_t off = (size_t)(uint32_t)tab.get(real ? j : last) * block_stride;
+    const int jj = real ? j : last;
+    if constexpr (GATHER) {
+      size_t kbase[NLI], vbase[4];
+      step_block_bases<NLI>(tab, jj, pshift, nent, block_stride, kblk, kbase);
+      step_block_bases<4>(tab, jj, pshift, nent, block_stride, vblk, vbase);
+#pragma unroll
+      for (int i = 0; i < NLI; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(a.k_pool + kbase[i] + kin[i]),
+            (__attribute__((address_space(3))) void*)(slot_base(slot) + i * 1024), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vr[i] = *reinterpret_cast<const VT*>(a.v_pool + vbase[i] + vin[i]);
+      return;
+    }
+    const size_t off = SUB ? (size_t)(uint32_t)tab.get(jj >> pshift) * block_stride +
+                                 (size_t)(jj & ((1 << pshift) - 1)) * step_stride
+                           : (size_t)(uint32_t)tab.get(jj) * block_stride;
     const uint32_t span = real ? a.span : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_block_rsrc(a.k_pool + off, span);
     const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, span);
@@ -349,8 +392,10 @@ constexpr int kWaveCols = 16 * kWaveTiles;             // columns per wave
 constexpr int kWgWaves = pa::kPrefillWgWaves;           // waves per workgroup (8 measured 6% slower)
 constexpr int kWgCols = kWaveCols * kWgWaves;           // columns per workgroup
 
-template <int DT, int D, int NP>
+template <int DT, int D, int NP, int MODE>
 __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const PrefillArgs a) {
+  constexpr bool SUB = MODE == kBlocksLarge;
+  constexpr bool GATHER = MODE == kBlocksSmall;
   using Ops = MfmaOps<DT>;
   constexpr int BS = pa::kBlockSize;
   constexpr int ROWB = D * 2;
@@ -415,13 +460,16 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
   // Steps wholly below `safe` need no masks for this wave's columns.
   const int wave_tok = (kWgCols * k + kWaveCols * wave) / a.repc;
   const int safe = wave_tok < n ? min(pend, a.causal ? L - n + wave_tok + 1 : L) : end;
-  const int blk0 = start / BS;
-  const int nblk = (end - start + BS - 1) / BS;
+  const int pshift = MODE != kBlocks16 ? a.block_shift : 0;
+  const int pool_bs = SUB ? BS << pshift : GATHER ? BS >> pshift : BS;  // tokens per pool block
+  const int blk0 = start / pool_bs;  // partitions start on a pool block
+  const int nblk = (end - start + BS - 1) / BS;  // 16-token steps
+  const int nent = MODE == kBlocks16 ? nblk : (end - start + pool_bs - 1) / pool_bs;
   const int last = nblk - 1;
 
   const int32_t* bt = a.block_tables + (size_t)trow * a.max_blocks_per_seq + blk0;
   TableSlice tab;
-  tab.load(bt, nblk, lane);
+  tab.load(bt, nent, lane);
 
   uint4 qop[kWaveTiles][NKC];
 #pragma unroll
@@ -441,9 +489,10 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
   const uint32_t row_stride = a.row_stride;
   const uint32_t hoff = (uint32_t)g * a.head_stride;
   const size_t block_stride = (size_t)a.block_stride;
+  const size_t step_stride = (size_t)BS * row_stride;  // 16-token windows inside a larger block
   uint32_t goff[DPW];
   bool is_k[DPW], has[DPW];
-  int lds_off[DPW];
+  int lds_off[DPW], rblk[DPW];  // rblk: with small blocks, the row's block within the step
 #pragma unroll
   for (int i = 0; i < DPW; ++i) {
     const int ins = wave * DPW + i;
@@ -451,7 +500,9 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
     is_k[i] = ins < KI;
     const int idx = is_k[i] ? ins : ins - KI;
     const int sl = 64 * idx + lane, t = sl / CPR, q = sl % CPR;
-    goff[i] = (uint32_t)t * row_stride + hoff + (uint32_t)((is_k[i] ? (q ^ kswz_t<CPR>(t)) : q) * 16);
+    const int tr = GATHER ? t % pool_bs : t;  // the row inside its pool block
+    rblk[i] = GATHER ? t / pool_bs : 0;
+    goff[i] = (uint32_t)tr * row_stride + hoff + (uint32_t)((is_k[i] ? (q ^ kswz_t<CPR>(t)) : q) * 16);
     lds_off[i] = idx * 1024;
   }
   uint32_t kread[NKC];  // QK A operand: token 4*(col%4) + col/4, chunk 4c + gq
@@ -486,10 +537,29 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
   }
 
   // Loads past the partition go through an empty descriptor (zeros, no
-  // memory access), so every wait count is exact.
+  // memory access), so every wait count is exact; with small blocks
+  // (per-lane addresses) they re-read the last step's rows instead, which
+  // the step past `end` never uses.
   auto load_block = [&](int j, int x) {
     const bool real = j <= last;
-    const size_t off = (size_t)(uint32_t)tab.get(real ? j : last) * block_stride;
+    const int jj = real ? j : last;
+    if constexpr (GATHER) {
+      size_t base[DPW];
+      step_block_bases<DPW>(tab, jj, pshift, nent, block_stride, rblk, base);
+#pragma unroll
+      for (int i = 0; i < DPW; ++i) {
+        if (!has[i]) continue;
+        const uint8_t* src = (is_k[i] ? a.k_pool : a.v_pool) + base[i] + goff[i];
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)((is_k[i] ? kslot(x) : vslot(x)) +
+                                                                                   lds_off[i]),
+                                         16, 0, 0);
+      }
+      return;
+    }
+    const size_t off = SUB ? (size_t)(uint32_t)tab.get(jj >> pshift) * block_stride +
+                                 (size_t)(jj & ((1 << pshift) - 1)) * step_stride
+                           : (size_t)(uint32_t)tab.get(jj) * block_stride;
     const uint32_t span = real ? a.span : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_block_rsrc(a.k_pool + off, span);
     const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, span);
@@ -665,31 +735,48 @@ using PrefillCombineFn = void (*)(void*, const float*, const float2*, const int3
                                   int, int);
 constexpr int kPrefillRing = 4;
 
-template <int DT, int D>
+template <int DT, int D, int MODE>
 PrefillFn pick_prefill_wpw(int wpw) {
   switch (wpw) {
-    case 1: return prefill_mfma_kernel<DT, D, kPrefillRing, 1>;
-    case 2: return prefill_mfma_kernel<DT, D, kPrefillRing, 2>;
-    case 4: return prefill_mfma_kernel<DT, D, kPrefillRing, 4>;
+    case 1: return prefill_mfma_kernel<DT, D, kPrefillRing, 1, MODE>;
+    case 2: return prefill_mfma_kernel<DT, D, kPrefillRing, 2, MODE>;
+    case 4: return prefill_mfma_kernel<DT, D, kPrefillRing, 4, MODE>;
     default: return nullptr;
   }
+}
+
+template <int DT, int D>
+PrefillFn pick_prefill_bs(int wpw, int block_size) {
+  if (block_size == pa::kBlockSize) return pick_prefill_wpw<DT, D, kBlocks16>(wpw);
+  if (block_size > pa::kBlockSize) return pick_prefill_wpw<DT, D, kBlocksLarge>(wpw);
+  return pick_prefill_wpw<DT, D, kBlocksSmall>(wpw);
 }
 
 constexpr int kPrefillPairs = 3;  // ring pairs of the cooperative tile
 
-PrefillFn pick_prefill_wide(int dtype, int d) {
+template <int DT, int D>
+PrefillFn pick_prefill_wide_bs(int block_size) {
+  if (block_size == pa::kBlockSize) return prefill_wg_kernel<DT, D, kPrefillPairs, kBlocks16>;
+  if (block_size > pa::kBlockSize) return prefill_wg_kernel<DT, D, kPrefillPairs, kBlocksLarge>;
+  return prefill_wg_kernel<DT, D, kPrefillPairs, kBlocksSmall>;
+}
+
+PrefillFn pick_prefill_wide(int dtype, int d, int block_size) {
   switch (dtype) {
-    case PA_F16: return d == 64 ? prefill_wg_kernel<DT_F16, 64, kPrefillPairs> : prefill_wg_kernel<DT_F16, 128, kPrefillPairs>;
+    case PA_F16:
+      return d == 64 ? pick_prefill_wide_bs<DT_F16, 64>(block_size) : pick_prefill_wide_bs<DT_F16, 128>(block_size);
     case PA_BF16:
-      return d == 64 ? prefill_wg_kernel<DT_BF16, 64, kPrefillPairs> : prefill_wg_kernel<DT_BF16, 128, kPrefillPairs>;
+      return d == 64 ? pick_prefill_wide_bs<DT_BF16, 64>(block_size) : pick_prefill_wide_bs<DT_BF16, 128>(block_size);
     default: return nullptr;
   }
 }
 
-PrefillFn pick_prefill(int dtype, int d, int wpw) {
+PrefillFn pick_prefill(int dtype, int d, int wpw, int block_size) {
   switch (dtype) {
-    case PA_F16: return d == 64 ? pick_prefill_wpw<DT_F16, 64>(wpw) : pick_prefill_wpw<DT_F16, 128>(wpw);
-    case PA_BF16: return d == 64 ? pick_prefill_wpw<DT_BF16, 64>(wpw) : pick_prefill_wpw<DT_BF16, 128>(wpw);
+    case PA_F16:
+      return d == 64 ? pick_prefill_bs<DT_F16, 64>(wpw, block_size) : pick_prefill_bs<DT_F16, 128>(wpw, block_size);
+    case PA_BF16:
+      return d == 64 ? pick_prefill_bs<DT_BF16, 64>(wpw, block_size) : pick_prefill_bs<DT_BF16, 128>(wpw, block_size);
     default: return nullptr;
   }
 }
@@ -709,6 +796,7 @@ size_t prefill_workspace(const pa::PrefillShape& s, int parts) {
 void set_pool(PrefillArgs* a, const pa::PoolView& pv, const pa::DecodeShape& s) {
   a->k_pool = pv.k;
   a->v_pool = pv.v;
+  a->block_shift = pa::block_shift(s.block_size);
   a->block_stride = pv.block_stride;
   a->row_stride = (uint32_t)pv.row_stride;
   a->head_stride = (uint32_t)pv.head_stride;
@@ -728,7 +816,7 @@ extern "C" size_t pa_prefill_workspace_bytes(int32_t num_tokens, int32_t num_hea
     int lo = 1;
     pa::prefill_partition_bounds(s, &lo, &parts);
   } else {
-    if (partition_size < block_size || partition_size % block_size != 0) return 0;
+    if (pa::validate_partition(partition_size, block_size) < 0) return 0;
     parts = pa::num_partitions(max_context_len, partition_size);
   }
   return prefill_workspace(s, parts);
@@ -754,8 +842,8 @@ extern "C" int pa_prefill_attention_layout(void* out, const void* query, const v
   if (rc != PA_OK) return rc;
   const pa::DecodeGrid gd = pa::decode_grid(shp.d);
   const pa::PrefillGrid pg = pa::prefill_grid(shp);
-  PrefillFn fn = pg.wide ? pick_prefill_wide(shp.d.dtype, shp.d.head_dim)
-                         : pick_prefill(shp.d.dtype, shp.d.head_dim, gd.wpw);
+  PrefillFn fn = pg.wide ? pick_prefill_wide(shp.d.dtype, shp.d.head_dim, block_size)
+                         : pick_prefill(shp.d.dtype, shp.d.head_dim, gd.wpw, block_size);
   if (!fn) return PA_ERR_UNSUPPORTED;
   int cus = 256, per_cu = 1;
   if (partition_size == 0) {
@@ -855,7 +943,7 @@ extern "C" int pa_decode_attention_shared_prefix(
   const size_t need = pa_shared_prefix_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, max_prefix_len);
   if (workspace == nullptr || workspace_bytes < need) return PA_ERR_WORKSPACE;
   const pa::DecodeGrid gd = pa::decode_grid(shp.d);
-  PrefillFn fn = pick_prefill(shp.d.dtype, shp.d.head_dim, gd.wpw);
+  PrefillFn fn = pick_prefill(shp.d.dtype, shp.d.head_dim, gd.wpw, block_size);
   MergeSlotsFn mf = pick_merge_slots(shp.d.dtype, shp.d.head_dim);
   if (!fn || !mf) return PA_ERR_UNSUPPORTED;
 

@@ -389,12 +389,12 @@ class PrefillBatch:
 
 
 def prefill_batch(lens, query_lens, num_heads: int, num_kv_heads: int, head_dim: int, dtype: str,
-                  seed: int = 0, name: str = "prefill", extra_cols: int = 0) -> PrefillBatch:
+                  seed: int = 0, name: str = "prefill", extra_cols: int = 0, block_size: int = 16) -> PrefillBatch:
     q = np.asarray(query_lens, dtype=np.int32)
     lens = np.asarray(lens, dtype=np.int32)
     assert q.shape == lens.shape and (q >= 1).all() and (q <= lens).all()
     w = custom(lens.tolist(), num_heads, num_kv_heads, head_dim, dtype, seed=seed, extra_cols=extra_cols,
-               name=name)
+               name=name, block_size=block_size)
     return PrefillBatch(w, q, f"{len(lens)} seqs, {int(q.sum())} new tokens, contexts {lens.min()}..{lens.max()}")
 
 

@@ -116,7 +116,11 @@ def prefill(**kw):
     (dict(scale=float("nan")), B.PA_ERR_INVALID_ARG),
     (dict(dtype=B.PA_F32), B.PA_ERR_UNSUPPORTED),  # the prefill tile runs on the matrix cores
     (dict(D=96), B.PA_ERR_UNSUPPORTED),
-    (dict(bs=32, mb=4), B.PA_ERR_UNSUPPORTED),    # the prefill tile reads whole 16-row blocks
+    (dict(bs=24, mb=6), B.PA_ERR_UNSUPPORTED),    # block sizes are powers of two
+    (dict(bs=512, mb=1), B.PA_ERR_UNSUPPORTED),
+    (dict(bs=32, mb=4, ps=16), B.PA_ERR_INVALID_ARG),  # partitions hold whole blocks
+    (dict(bs=4, mb=32, ps=8), B.PA_ERR_INVALID_ARG),   # and whole 16-token steps
+    (dict(bs=1, mb=128, ps=272), B.PA_ERR_INVALID_ARG),  # at most 256 blocks
     (dict(ps=24), B.PA_ERR_INVALID_ARG),
     (dict(ps=4112), B.PA_ERR_INVALID_ARG),
     (dict(ps=16), B.PA_ERR_WORKSPACE),            # 8 partitions need a workspace
@@ -126,12 +130,25 @@ def test_prefill_argument_checks(kw, status):
     assert prefill(**kw) == status
 
 
+def test_shared_prefix_block_sizes():
+    # the cascade splits keys at 1024 tokens: blocks of 1 and 2 tokens cannot
+    # hold that in one 256-entry table slice
+    lib = B.lib()
+    f = lib.pa_decode_attention_shared_prefix
+    for bs in (1, 2, 24):
+        mb = -(-4096 // bs)
+        assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 2, 8, 2, 128, bs, mb, 4096, 0,
+                 0.088, B.PA_BF16, FAKE, 1 << 30, None) == B.PA_ERR_UNSUPPORTED
+
+
 def test_prefill_workspace_sizes():
     lib = B.lib()
     # explicit partition: T*H*P*(D+2)*4 bytes, none for a single partition
     assert lib.pa_prefill_workspace_bytes(40, 8, 128, 128, 16, 16) == 40 * 8 * 8 * 130 * 4
     assert lib.pa_prefill_workspace_bytes(40, 8, 128, 128, 16, 128) == 0
     assert lib.pa_prefill_workspace_bytes(40, 8, 128, 128, 16, 24) == 0
+    assert lib.pa_prefill_workspace_bytes(40, 8, 128, 128, 4, 8) == 0  # not whole 16-token steps
+    assert lib.pa_prefill_workspace_bytes(40, 8, 128, 128, 4, 16) == 40 * 8 * 8 * 130 * 4
     # automatic: at most one partition per 128 tokens, partials within 256 MiB
     assert lib.pa_prefill_workspace_bytes(40, 8, 128, 4096, 16, 0) == 40 * 8 * 32 * 130 * 4
     assert lib.pa_prefill_workspace_bytes(8192, 32, 128, 4096, 16, 0) == 0  # one split alone exceeds the cap

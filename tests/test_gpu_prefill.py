@@ -128,6 +128,19 @@ def test_head_groupings(h, hkv):
     check_prefill(pb, seed=2, partition_size=48)
 
 
+@pytest.mark.parametrize("bs", [1, 2, 4, 8, 32, 64, 256])
+@pytest.mark.parametrize("wide", [False, True])
+def test_block_sizes(bs, wide):
+    # pool blocks smaller than the 16-token step are gathered row by row,
+    # larger ones walked in 16-row windows; narrow rows run the per-wave tile,
+    # long new-token runs the cooperative one; NaN in every unowned slot
+    lens = [1, 7, 16, 33, 100, 260, 1100]
+    qlens = [1, 7, 5, 12, 9, 3, 11] if not wide else [1, 7, 16, 33, 50, 17, 400]
+    pb = W.prefill_batch(lens, qlens, 8, 2, 128, "bf16", seed=bs, extra_cols=1, block_size=bs)
+    check_prefill(pb, seed=bs, partition_size=0, poisoned=True)
+    check_prefill(pb, seed=bs, partition_size=max(16, bs), poisoned=True)
+
+
 def test_whole_prompts_only():
     # every sequence is a fresh prompt: n = L, the full causal triangle
     lens = [1, 2, 15, 16, 17, 64, 129]

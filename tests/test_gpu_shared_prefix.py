@@ -67,12 +67,12 @@ def test_parallel_sampling_workload():
     check(w, g, rows=list(range(0, 384, 7)))
 
 
-def forked_batch(prompts, forks, gens, h, hkv, d, dtype, seed):
+def forked_batch(prompts, forks, gens, h, hkv, d, dtype, seed, bs=16):
     """Prompts forked into samples that each generate some tokens, built with
     the library's block pool (copy-on-write pairs replayed by the tensor
     builder, which copies the prompt rows)."""
     rng = np.random.default_rng(seed)
-    m = PB.BlockManager(4096, 16, free_order=rng.permutation(4096))
+    m = PB.BlockManager(4096, bs, free_order=rng.permutation(4096))
     seqs, copies = [], []
     for p, f, gl in zip(prompts, forks, gens):
         root = m.new_seq()
@@ -81,7 +81,7 @@ def forked_batch(prompts, forks, gens, h, hkv, d, dtype, seed):
         for s, extra in zip(members, gl):
             c = m.append(s, extra)
             if c is not None:
-                copies.append((c[0], c[1], p % 16))
+                copies.append((c[0], c[1], p % bs))
         seqs += members
     tables = [m.block_table(s) for s in seqs]
     lens = np.array([m.length(s) for s in seqs], np.int32)
@@ -92,7 +92,7 @@ def forked_batch(prompts, forks, gens, h, hkv, d, dtype, seed):
     for i, x in enumerate(tables):
         bt[i, :len(x)] = x
     unowned = np.array(sorted(set(range(4096)) - used), np.int64)
-    return W.Workload("forked", dtype, h, hkv, d, 16, 4096, lens, bt, float(np.float32(1 / np.sqrt(d))), pad,
+    return W.Workload("forked", dtype, h, hkv, d, bs, 4096, lens, bt, float(np.float32(1 / np.sqrt(d))), pad,
                       unowned, copies, "forked prompts")
 
 
@@ -109,6 +109,20 @@ def test_mixed_groups(dtype, d, h, hkv):
     g = PB.pa_shared_prefix_groups(w.block_tables, w.context_lens, 16)
     assert g.max_prefix_len == 2096 and g.max_group_size == 7
     check(w, g, seed=1)
+
+
+@pytest.mark.parametrize("bs", [4, 8, 32, 64, 256])
+def test_mixed_groups_block_sizes(bs):
+    # prefixes are whole pool blocks; the passes gather small blocks row by
+    # row and walk large ones in 16-row windows
+    prompts = [37, 2100, 16, 600, 1, 333]
+    forks = [3, 2, 4, 7, 1, 5]
+    rng = np.random.default_rng(bs)
+    gens = [[int(x) for x in rng.integers(1, 1300 if i == 1 else 60, f)] for i, f in enumerate(forks)]
+    w = forked_batch(prompts, forks, gens, 32, 8, 128, "bf16", seed=bs, bs=bs)
+    g = PB.pa_shared_prefix_groups(w.block_tables, w.context_lens, bs)
+    assert g.max_group_size == 7 and g.max_prefix_len % bs == 0 and g.max_prefix_len >= 2100 // bs * bs - bs
+    check(w, g, seed=2)
 
 
 def test_no_shared_prefix_degenerates_to_plain_decode():
