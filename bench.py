@@ -663,6 +663,7 @@ def main_decode(args, oracle_pool):
                    "description": w.description},
         "kv_read_bytes_per_step": kv_bytes,
         "kv_unique_read_bytes_per_step": kv_unique,
+        "aux_bytes_per_step": w.aux_bytes(),
         "kv_GBps_step": kv_bytes / (ms_per_step * 1e-3) / 1e9,
         "context_tokens_per_s": float(w.context_lens.sum()) / (ms_per_step * 1e-3),
         "kernel_us": {"slot_mapping": per_kernel_ms[0] * 1e3, "reshape_and_cache": per_kernel_ms[1] * 1e3,

@@ -151,6 +151,18 @@ class Workload:
         """K and V bytes of every valid context token (each read once)."""
         return int(self.context_lens.astype(np.int64).sum()) * self.num_kv_heads * self.head_dim * self.elem_bytes * 2
 
+    def aux_bytes(self) -> dict:
+        """Bytes a decode step moves besides the valid K/V rows: the query
+        and output rows, the block-table entries in use, and the unused rows
+        of each sequence's last block (a kernel that reads whole blocks
+        fetches them)."""
+        lens = self.context_lens.astype(np.int64)
+        row = self.num_kv_heads * self.head_dim * self.elem_bytes * 2  # K + V row of one token
+        used_blocks = (lens + self.block_size - 1) // self.block_size
+        qo = self.num_seqs * self.num_heads * self.head_dim * self.elem_bytes
+        return {"query": int(qo), "out": int(qo), "block_table_entries": int(used_blocks.sum()) * 4,
+                "tail_slots": int((used_blocks * self.block_size - lens).sum()) * row}
+
     def kv_unique_read_bytes(self) -> int:
         """K and V bytes of the distinct pool rows the batch reads: a block
         shared by several sequences counts once, with the rows its longest

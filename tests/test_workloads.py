@@ -90,3 +90,14 @@ def test_tensors_replay_copy_on_write():
         assert torch.equal(t["k_pool"][dst, :rows], t["k_pool"][src, :rows])
         assert not torch.equal(t["k_pool"][dst, rows:], t["k_pool"][src, rows:])
     assert t["query"].dtype == torch.bfloat16 and t["query"].shape == (6, 32, 128)
+
+
+def test_aux_bytes_tiny_and_llama():
+    # tiny: lengths 1, 7, 16, 33 leave 15 + 9 + 0 + 15 unused rows in the last
+    # blocks, each a K and a V row of 2 heads x 64 fp32 values
+    a = W.make_workload("tiny_f32").aux_bytes()
+    assert a == {"query": 4 * 4 * 64 * 4, "out": 4 * 4 * 64 * 4, "block_table_entries": 6 * 4,
+                 "tail_slots": 39 * 2 * 64 * 4 * 2}
+    # the Llama layer: 2 MiB of queries, 2 MiB of outputs, 256 KiB of table entries, full blocks
+    a = W.make_workload("llama_gqa4k_bf16").aux_bytes()
+    assert a == {"query": 2 << 20, "out": 2 << 20, "block_table_entries": 256 << 10, "tail_slots": 0}
