@@ -281,8 +281,9 @@ int32_t pa_decode_plan_partition_size(int32_t num_seqs, int32_t num_heads, int32
  *                    L_b - n_b + i and attends to positions 0 .. L_b - n_b + i.
  *   max_query_len    host bound of n_b; 1 <= max_query_len <= num_tokens.
  *   other arguments  as pa_decode_attention (pools, tables, scale, dtype, stream).
- * fp16 and bf16 only (the tile runs on the matrix cores): UNSUPPORTED for fp32;
- * block sizes as pa_decode_attention.
+ * fp16 and bf16 run matrix-core tiles shared by the rows of a sequence; fp32
+ * runs every row as a decode query with its own causal context (the VALU
+ * tile; block_size 16).  Block sizes as pa_decode_attention.
  * partition_size: 0 lets the library choose (it may split long contexts into
  * partitions merged by a second kernel, keeping the partials within 256 MiB),
  * or a size pa_decode_attention_ex accepts.  The workspace

@@ -292,7 +292,6 @@ int check_prefill(const void* out, const void* query, const void* k_pool, const 
   if (rc != PA_OK) return rc;
   if (s.num_tokens <= 0 || s.max_query_len <= 0 || s.max_query_len > s.num_tokens) return PA_ERR_INVALID_ARG;
   if (s.max_query_len > s.d.max_context_len) return PA_ERR_INVALID_ARG;
-  if (s.d.dtype == PA_F32) return PA_ERR_UNSUPPORTED;  // the prefill tile is an MFMA tile (16-bit inputs)
   if ((int64_t)s.num_tokens * s.d.num_heads > (int64_t)1 << 30) return PA_ERR_INVALID_ARG;
   return PA_OK;
 }

@@ -107,6 +107,12 @@ struct DecodeArgs {
   // span = what one 16-token step of a block may touch from its first byte
   int64_t block_stride;
   uint32_t row_stride, head_stride, span;
+  // Row mode (VALU kernel only): non-null query_start_loc [num_seqs + 1]
+  // makes each work row one query row of a varlen batch - row r of sequence b
+  // at position L_b - n_b + i sees keys [0, L_b - n_b + i] - instead of one
+  // decode query per sequence.
+  const int32_t* query_start_loc;
+  int num_seqs;
 };
 
 template <int DT, int D, int REPC>
@@ -138,19 +144,33 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
   const int grp = logical % a.groups;
   const int seq_part = logical / a.groups;
   const int s = seq_part % a.num_parts;
-  const int b = seq_part / a.num_parts;
+  const int row = seq_part / a.num_parts;  // sequence (decode) or query row (row mode)
   const int unit = grp * wpw + wave;
   const int g = unit / a.chunks;
   const int h0 = g * a.rep + (unit % a.chunks) * REPC;
   const int r = lane / LPR, c = lane % LPR;
 
-  const int L = a.context_lens[b];
+  int b = row, L;
+  if (a.query_start_loc) {  // the sequence owning this row: largest b with qsl[b] <= row
+    int lo = 0, hi = a.num_seqs;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.query_start_loc[mid] <= row) lo = mid;
+      else hi = mid;
+    }
+    b = lo;
+    const int q0 = a.query_start_loc[b], n = a.query_start_loc[b + 1] - q0;
+    if (row >= q0 + n) return;  // a row no sequence owns
+    L = a.context_lens[b] - n + (row - q0) + 1;
+  } else {
+    L = a.context_lens[b];
+  }
   const int start = s * a.part_tokens;
   if (start >= L) {
     if (s == 0 && r == 0) {  // empty context: zeros
       float z[EPL] = {};
       for (int h = 0; h < REPC; ++h)
-        store_row<DT, EPL>((uint8_t*)a.out + ((size_t)b * a.num_heads + h0 + h) * ROWB + c * 16, z);
+        store_row<DT, EPL>((uint8_t*)a.out + ((size_t)row * a.num_heads + h0 + h) * ROWB + c * 16, z);
     }
     return;
   }
@@ -167,7 +187,7 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
   // Query rows of the REPC heads, scaled into log2 units.
   float q[REPC][EPL];
   {
-    const uint8_t* qp = (const uint8_t*)a.query + ((size_t)b * a.num_heads + h0) * ROWB + c * 16;
+    const uint8_t* qp = (const uint8_t*)a.query + ((size_t)row * a.num_heads + h0) * ROWB + c * 16;
 #pragma unroll
     for (int h = 0; h < REPC; ++h) {
       unpack16<DT>(*reinterpret_cast<const uint4*>(qp + h * ROWB), q[h]);
@@ -288,12 +308,12 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
       float o[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[e] = acc[h][e] * inv;
-      store_row<DT, EPL>((uint8_t*)a.out + ((size_t)b * a.num_heads + h0 + h) * ROWB + c * 16, o);
+      store_row<DT, EPL>((uint8_t*)a.out + ((size_t)row * a.num_heads + h0 + h) * ROWB + c * 16, o);
     }
   } else {
 #pragma unroll
     for (int h = 0; h < REPC; ++h) {
-      const size_t idx = ((size_t)b * a.num_heads + h0 + h) * a.num_parts + s;
+      const size_t idx = ((size_t)row * a.num_heads + h0 + h) * a.num_parts + s;
       float* dst = a.ws_acc + idx * D + c * EPL;
 #pragma unroll
       for (int e = 0; e < EPL; e += 4)
@@ -730,6 +750,8 @@ int launch_partitions(void* out, const void* query, const pa::PoolView& pv, cons
   a.span = (uint32_t)pv.step_span(shp.head_dim * pa::elem_bytes(shp.dtype), shp.num_kv_heads);
   a.block_tables = block_tables;
   a.context_lens = context_lens;
+  a.query_start_loc = nullptr;
+  a.num_seqs = shp.num_seqs;
   a.ws_acc = static_cast<float*>(workspace);
   a.ws_ml = ml_region(workspace, shp, plan.parts);
   a.num_heads = shp.num_heads;
@@ -778,6 +800,50 @@ int device_cu_count() {
 }
 
 int launch_status() { return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+const void* decode_rows_kernel(const DecodeShape& s, int* threads) {
+  const DecodeGrid g = decode_grid(s);
+  *threads = 64 * g.wpw;
+  return reinterpret_cast<const void*>(pick_decode(s.dtype, s.head_dim, g, s.block_size));
+}
+
+int launch_decode_rows(void* out, const void* query, const PoolView& pv, const int32_t* block_tables,
+                       const int32_t* context_lens, const int32_t* query_start_loc, const DecodeShape& s,
+                       int num_rows, float scale, void* ws_acc, void* ws_ml, int part_tokens, int num_parts,
+                       void* stream) {
+  const DecodeGrid gd = decode_grid(s);
+  const int64_t grid = (int64_t)num_rows * num_parts * gd.groups;
+  if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
+  DecodeFn fn = pick_decode(s.dtype, s.head_dim, gd, s.block_size);
+  if (!fn) return PA_ERR_UNSUPPORTED;
+  DecodeArgs a;
+  a.out = out;
+  a.query = query;
+  a.k_pool = pv.k;
+  a.v_pool = pv.v;
+  a.block_stride = pv.block_stride;
+  a.row_stride = (uint32_t)pv.row_stride;
+  a.head_stride = (uint32_t)pv.head_stride;
+  a.span = (uint32_t)pv.step_span(s.head_dim * elem_bytes(s.dtype), s.num_kv_heads);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.num_seqs = s.num_seqs;
+  a.ws_acc = static_cast<float*>(ws_acc);
+  a.ws_ml = static_cast<float2*>(ws_ml);
+  a.num_heads = s.num_heads;
+  a.num_kv_heads = s.num_kv_heads;
+  a.rep = gd.rep;
+  a.chunks = gd.chunks;
+  a.max_blocks_per_seq = s.max_blocks_per_seq;
+  a.block_shift = block_shift(s.block_size);
+  a.part_tokens = part_tokens;
+  a.num_parts = num_parts;
+  a.groups = gd.groups;
+  a.qscale = scale * 1.44269504088896340736f;  // log2(e)
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * gd.wpw), 0, static_cast<hipStream_t>(stream), a);
+  return launch_status();
+}
 
 // Workgroups of `fn` (with `threads` threads) resident per compute unit, cached
 // per (device, kernel).  0 on failure.

@@ -783,6 +783,7 @@ PrefillFn pick_prefill(int dtype, int d, int wpw, int block_size) {
 
 PrefillCombineFn pick_prefill_combine(int dtype, int d) {
   switch (dtype) {
+    case PA_F32: return d == 64 ? prefill_combine_kernel<DT_F32, 64> : prefill_combine_kernel<DT_F32, 128>;
     case PA_F16: return d == 64 ? prefill_combine_kernel<DT_F16, 64> : prefill_combine_kernel<DT_F16, 128>;
     case PA_BF16: return d == 64 ? prefill_combine_kernel<DT_BF16, 64> : prefill_combine_kernel<DT_BF16, 128>;
     default: return nullptr;
@@ -791,6 +792,56 @@ PrefillCombineFn pick_prefill_combine(int dtype, int d) {
 
 size_t prefill_workspace(const pa::PrefillShape& s, int parts) {
   return pa::workspace_bytes(s.num_tokens, s.d.num_heads, s.d.head_dim, parts);
+}
+
+// fp32: every query row runs the VALU decode tile with its own causal
+// context (row i of sequence b sees keys 0 .. L_b - n_b + i), partials merged
+// as for the 16-bit tiles.  Rows share no K/V reads inside a workgroup: a
+// correctness path for fp32 pools, not a matrix-core one.
+int prefill_rows(void* out, const void* query, const pa::PoolView& pv, const int32_t* block_tables,
+                 const int32_t* context_lens, const int32_t* query_start_loc, const pa::PrefillShape& shp,
+                 float scale, void* workspace, size_t workspace_bytes, int32_t partition_size, void* stream) {
+  const pa::DecodeShape& d = shp.d;
+  int ps;
+  if (partition_size != 0) {
+    ps = pa::validate_partition(partition_size, d.block_size);
+    if (ps < 0) return -ps;
+  } else {
+    int threads = 0;
+    const void* fn = pa::decode_rows_kernel(d, &threads);
+    if (!fn) return PA_ERR_UNSUPPORTED;
+    const int cus = pa::device_cu_count();
+    const int per_cu = pa::resident_per_cu(fn, threads);
+    if (cus <= 0 || per_cu <= 0) return PA_ERR_HIP;
+    pa::DecodeShape rows = d;
+    rows.num_seqs = shp.num_tokens;  // every row taken at max_context_len
+    ps = pa::partition_size(rows, 0, cus, per_cu);
+    if (ps <= 0) return -ps;
+    int lo = 1, hi = 1;  // stay within the workspace pa_prefill_workspace_bytes sizes
+    pa::prefill_partition_bounds(shp, &lo, &hi);
+    if (pa::num_partitions(d.max_context_len, ps) > hi) {
+      const int gran = pa::partition_granule(d.block_size);
+      ps = (d.max_context_len + hi - 1) / hi;
+      ps = (ps + gran - 1) / gran * gran;
+    }
+  }
+  const int parts = pa::num_partitions(d.max_context_len, ps);
+  const size_t need = prefill_workspace(shp, parts);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  float* ws_acc = parts > 1 ? static_cast<float*>(workspace) : nullptr;
+  float2* ws_ml = parts > 1 ? reinterpret_cast<float2*>(static_cast<float*>(workspace) +
+                                                        (size_t)shp.num_tokens * d.num_heads * parts * d.head_dim)
+                            : nullptr;
+  int rc = pa::launch_decode_rows(out, query, pv, block_tables, context_lens, query_start_loc, d, shp.num_tokens,
+                                  scale, ws_acc, ws_ml, ps, parts, stream);
+  if (rc != PA_OK || parts <= 1) return rc;
+  PrefillCombineFn cf = pick_prefill_combine(d.dtype, d.head_dim);
+  if (!cf) return PA_ERR_UNSUPPORTED;
+  const int64_t waves = (int64_t)shp.num_tokens * d.num_heads;
+  hipLaunchKernelGGL(cf, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, static_cast<hipStream_t>(stream), out,
+                     ws_acc, ws_ml, context_lens, query_start_loc, d.num_seqs, shp.num_tokens, d.num_heads, ps,
+                     parts);
+  return pa::launch_status();
 }
 
 void set_pool(PrefillArgs* a, const pa::PoolView& pv, const pa::DecodeShape& s) {
@@ -840,6 +891,9 @@ extern "C" int pa_prefill_attention_layout(void* out, const void* query, const v
   pa::PoolView pv;
   rc = pa::pool_view(k_pool, v_pool, (int)layout, block_size, num_kv_heads, head_dim, (int)dtype, &pv);
   if (rc != PA_OK) return rc;
+  if (dtype == PA_F32)
+    return prefill_rows(out, query, pv, block_tables, context_lens, query_start_loc, shp, scale, workspace,
+                        workspace_bytes, partition_size, stream);
   const pa::DecodeGrid gd = pa::decode_grid(shp.d);
   const pa::PrefillGrid pg = pa::prefill_grid(shp);
   PrefillFn fn = pg.wide ? pick_prefill_wide(shp.d.dtype, shp.d.head_dim, block_size)

@@ -114,7 +114,9 @@ def prefill(**kw):
     (dict(H=6, Hkv=4), B.PA_ERR_INVALID_ARG),
     (dict(maxlen=129), B.PA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), B.PA_ERR_INVALID_ARG),
-    (dict(dtype=B.PA_F32), B.PA_ERR_UNSUPPORTED),  # the prefill tile runs on the matrix cores
+    (dict(dtype=B.PA_F32, bs=32, mb=4), B.PA_ERR_UNSUPPORTED),  # fp32 rows run the 16-row VALU tile
+    (dict(dtype=B.PA_F32, ps=16), B.PA_ERR_WORKSPACE),  # fp32 is accepted: 8 partitions need a workspace
+    (dict(dtype=B.PA_F32, ps=24), B.PA_ERR_INVALID_ARG),
     (dict(D=96), B.PA_ERR_UNSUPPORTED),
     (dict(bs=24, mb=6), B.PA_ERR_UNSUPPORTED),    # block sizes are powers of two
     (dict(bs=512, mb=1), B.PA_ERR_UNSUPPORTED),
