@@ -220,11 +220,22 @@ def test_edge_lengths_all_dtypes(dtype, d, ps):
 
 
 @pytest.mark.parametrize("h,hkv", [(4, 4), (8, 4), (12, 4), (16, 4), (10, 2), (12, 2), (14, 2), (16, 2),
-                                   (32, 2), (32, 1), (9, 1), (22, 2)])
+                                   (32, 2), (32, 1), (9, 1), (22, 2), (64, 1), (128, 8), (64, 64)])
 def test_head_groupings(h, hkv):
     w = W.custom([1, 40, 300, 777], h, hkv, 128, "bf16", seed=h * 100 + hkv)
     check_whole(w, seed=3, partition_size=128)
     check_whole(w, seed=3, partition_size=0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_very_long_contexts(dtype):
+    # contexts far beyond one partition's 256 blocks: up to 128K tokens, an odd
+    # length one past a power of two, a single token; the policy's partition
+    # given the lengths, the blind one, and a fixed 4096
+    lens = [131072, 65537, 1, 4097] if dtype == "bf16" else [70001, 16385, 1]
+    w = W.custom(lens, 32, 8, 128, dtype, seed=11, extra_cols=1)
+    for ps in (bench_partition_size(w), 0, 4096):
+        check_whole(w, seed=3, partition_size=ps)
 
 
 def test_zero_length_context_gives_zeros():
