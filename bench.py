@@ -60,6 +60,8 @@ def parse():
                    help="pool layout: split K and V pools, or one fused [NB, H_kv, BS, 2D] pool")
     p.add_argument("--shared-prefix", action="store_true",
                    help="decode with shared prompt prefixes read once per group (cascade)")
+    p.add_argument("--graph", action="store_true",
+                   help="time the step as one captured HIP graph (launch costs gone; per-kernel times stay eager)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=16.0,
                    help="target oracle time (split between the one-thread and all-cores runs)")
@@ -473,6 +475,36 @@ def time_stages(stages, steps, warmup):
     return ms_per_step, per, wall
 
 
+def time_graph(stages, steps, warmup):
+    """The step captured once as a HIP graph and replayed: time per replay
+    (events around all replays on the current stream)."""
+    import torch
+
+    def step():
+        for f in stages:
+            f()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside capture, as torch requires
+        for _ in range(3):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def percentiles_us(ms):
     """p10 / p50 / p90 of a list of times in ms, in us."""
     import numpy as np
@@ -629,6 +661,11 @@ def main_decode(args, oracle_pool):
         kernel = "prefill_mfma_kernel prefix + suffix passes and merge_slots_kernel (one stage)"
         ps = 0
     ms_per_step, per_kernel_ms, wall = time_stages(stages, args.steps, args.warmup)
+    eager_ms = ms_per_step
+    if args.graph:
+        if len(pools) > 1:
+            raise SystemExit("--graph captures one pool; it runs without --replicas")
+        ms_per_step = time_graph(stages, args.steps, args.warmup)
     part_pct = percentiles_us(time_stages.samples[2])
     step_pct = percentiles_us([sum(x) for x in zip(*time_stages.samples)])
     ceiling = stream_ceiling(stream_buffers)
@@ -658,12 +695,13 @@ def main_decode(args, oracle_pool):
                    "max_context_len": w.max_context_len, "num_heads": H, "num_kv_heads": w.num_kv_heads,
                    "head_dim": D, "block_size": w.block_size, "num_blocks": w.num_blocks,
                    "partition_size": ps, "shared_prefix_cascade": bool(args.shared_prefix),
-                   "pool_layout": args.layout,
+                   "pool_layout": args.layout, "hip_graph": bool(args.graph),
                    "pool_replicas": len(pools),
                    "description": w.description},
         "kv_read_bytes_per_step": kv_bytes,
         "kv_unique_read_bytes_per_step": kv_unique,
         "aux_bytes_per_step": w.aux_bytes(),
+        "ms_per_step_eager": eager_ms,
         "kv_GBps_step": kv_bytes / (ms_per_step * 1e-3) / 1e9,
         "context_tokens_per_s": float(w.context_lens.sum()) / (ms_per_step * 1e-3),
         "kernel_us": {"slot_mapping": per_kernel_ms[0] * 1e3, "reshape_and_cache": per_kernel_ms[1] * 1e3,
