@@ -410,7 +410,7 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
   constexpr int RB = 2 * NP;                // ring blocks
   using VT = typename VRow<VPL>::T;
   static_assert(BS == 16 && (2 * KI) % DPW == 0, "tile shape");
-  static_assert(NP == 3, "the ring is unrolled for three pairs");
+  static_assert(NP == 3 || NP == 4, "the ring is unrolled for three or four pairs");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar load shares, no waterfall
@@ -513,15 +513,16 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
   }
   const uint32_t vread = (uint32_t)gq * ROWB + col * VPL * 2;  // row gq (+4i), this lane's dims
 
+  constexpr int XB = NP > 3 ? KBYTES : 16;  // slots 6 and 7 exist with four pairs
   __shared__ __attribute__((aligned(1024))) uint8_t ks0[KBYTES], ks1[KBYTES], ks2[KBYTES], ks3[KBYTES],
-      ks4[KBYTES], ks5[KBYTES];
+      ks4[KBYTES], ks5[KBYTES], ks6[XB], ks7[XB];
   __shared__ __attribute__((aligned(1024))) uint8_t vs0[KBYTES], vs1[KBYTES], vs2[KBYTES], vs3[KBYTES],
-      vs4[KBYTES], vs5[KBYTES];
+      vs4[KBYTES], vs5[KBYTES], vs6[XB], vs7[XB];
   auto kslot = [&](int x) -> uint8_t* {
-    return x == 0 ? ks0 : x == 1 ? ks1 : x == 2 ? ks2 : x == 3 ? ks3 : x == 4 ? ks4 : ks5;
+    return x == 0 ? ks0 : x == 1 ? ks1 : x == 2 ? ks2 : x == 3 ? ks3 : x == 4 ? ks4 : x == 5 ? ks5 : x == 6 ? ks6 : ks7;
   };
   auto vslot = [&](int x) -> uint8_t* {
-    return x == 0 ? vs0 : x == 1 ? vs1 : x == 2 ? vs2 : x == 3 ? vs3 : x == 4 ? vs4 : vs5;
+    return x == 0 ? vs0 : x == 1 ? vs1 : x == 2 ? vs2 : x == 3 ? vs3 : x == 4 ? vs4 : x == 5 ? vs5 : x == 6 ? vs6 : vs7;
   };
 
   f32x4 acc[kWaveTiles][VPL];
@@ -663,14 +664,19 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
     }
   };
 
-  load_block(0, 0);
-  load_block(1, 1);
-  load_block(2, 2);
-  load_block(3, 3);
+#pragma unroll
+  for (int x = 0; x < 2 * (NP - 1); ++x) load_block(x, x);
   for (int j = 0; j < nblk; j += RB) {
-    ring_step(j, 0, 1, 4, 5);
-    ring_step(j + 2, 2, 3, 0, 1);
-    ring_step(j + 4, 4, 5, 2, 3);
+    if constexpr (NP == 3) {
+      ring_step(j, 0, 1, 4, 5);
+      ring_step(j + 2, 2, 3, 0, 1);
+      ring_step(j + 4, 4, 5, 2, 3);
+    } else {
+      ring_step(j, 0, 1, 6, 7);
+      ring_step(j + 2, 2, 3, 0, 1);
+      ring_step(j + 4, 4, 5, 2, 3);
+      ring_step(j + 6, 6, 7, 4, 5);
+    }
   }
 
 #pragma unroll
@@ -752,7 +758,10 @@ PrefillFn pick_prefill_bs(int wpw, int block_size) {
   return pick_prefill_wpw<DT, D, kBlocksSmall>(wpw);
 }
 
-constexpr int kPrefillPairs = 3;  // ring pairs of the cooperative tile
+#ifndef PA_PREFILL_PAIRS
+#define PA_PREFILL_PAIRS 3
+#endif
+constexpr int kPrefillPairs = PA_PREFILL_PAIRS;  // ring pairs of the cooperative tile
 
 template <int DT, int D>
 PrefillFn pick_prefill_wide_bs(int block_size) {

@@ -238,6 +238,25 @@ def test_very_long_contexts(dtype):
         check_whole(w, seed=3, partition_size=ps)
 
 
+def test_split_kv_agrees_with_one_partition():
+    # fp32 (the tile computes scores, probabilities and P.V in float32): the
+    # split-context merge changes only the summation order, so every
+    # partition size agrees with the single-partition result to a few float32
+    # ulps of the sums.  (The 16-bit tiles round probabilities to the input
+    # dtype relative to each partition's own running max, so there the
+    # partitions differ by that rounding and the oracle tolerance applies.)
+    w = W.custom([1, 16, 17, 300, 1000, 2047], 8, 2, 128, "f32", seed=4)
+    t = W.make_tensors(w, 2, DEV)
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    lens = torch.from_numpy(w.context_lens).to(DEV)
+    run = lambda ps: PB.pa_decode_attention(t["query"], t["k_pool"], t["v_pool"], bt, lens, w.scale,  # noqa: E731
+                                            w.max_context_len, partition_size=ps)
+    one = run(2048)
+    for ps in (16, 128, 512, 1024):
+        diff = (run(ps) - one).abs()
+        assert float(diff.max()) <= 4e-6 * max(1.0, float(one.abs().max())), ps
+
+
 def test_zero_length_context_gives_zeros():
     w = W.custom([0, 5, 0, 20], 4, 2, 64, "f32", seed=2)
     t = W.make_tensors(w, 0, DEV)
