@@ -164,7 +164,7 @@ def cpu_baseline(w, t, seconds, pool):
     import oracle as O
     from paged_kv_cache_size_amd import workloads as W
 
-    nproc = pool._processes
+    nproc = cpu_pool_size()  # the pool's size (start_oracle_pool)
     bs = w.block_size
 
     def seq_arrays(b):
