@@ -137,6 +137,15 @@ struct TableSlice {
     }
     return v;
   }
+  // Per-lane entries that all lie in one register of the slice: lane l gets
+  // entry 64 * reg + lo_l (reg wave-uniform, lo_l in 0..63), by a cross-lane
+  // permute.
+  __device__ __forceinline__ int lanes_get(int reg, int lo) const {
+    int src = r[0];
+#pragma unroll
+    for (int i = 1; i < kTabRegs; ++i) src = (reg == i) ? r[i] : src;
+    return __builtin_amdgcn_ds_bpermute(lo << 2, src);
+  }
 };
 
 // Pool block sizes against the 16-token steps of the MFMA tiles:
@@ -151,16 +160,17 @@ constexpr int kBlocks16 = 0, kBlocksLarge = 1, kBlocksSmall = 2;
 // touches in step jj; blk[i] = index of row i's block within the step (row /
 // block size).  The step's blocks are table entries (jj << shift) + k, clamped
 // to the partition's last entry (nent - 1) past its end, so every address
-// stays inside a block the caller owns.
+// stays inside a block the caller owns.  A step's 1 << shift entries start at
+// a multiple of 1 << shift (which divides 64), so they share one register of
+// the slice and each lane fetches its own with one permute per row.
 template <int N>
 __device__ __forceinline__ void step_block_bases(const TableSlice& tab, int jj, int shift, int nent,
                                                  size_t block_stride, const int* blk, size_t* base) {
+  const int e0 = jj << shift;
 #pragma unroll
-  for (int i = 0; i < N; ++i) base[i] = 0;
-  for (int k = 0; k < (1 << shift); ++k) {
-    const size_t b = (size_t)(uint32_t)tab.get(min((jj << shift) + k, nent - 1)) * block_stride;
-#pragma unroll
-    for (int i = 0; i < N; ++i) base[i] = blk[i] == k ? b : base[i];
+  for (int i = 0; i < N; ++i) {
+    const int e = min(e0 + blk[i], nent - 1);
+    base[i] = (size_t)(uint32_t)tab.lanes_get(e0 >> 6, e & 63) * block_stride;
   }
 }
 

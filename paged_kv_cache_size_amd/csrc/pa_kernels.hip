@@ -489,19 +489,9 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
     const bool real = j <= last;
     const int jj = real ? j : last;
     if constexpr (GATHER) {  // per-lane rows; past the end the last step is re-read (cached, masked)
-      const size_t pool_block = (size_t)a.block_stride;
       size_t kb[NLI], vb[4];
-#pragma unroll
-      for (int n = 0; n < NLI; ++n) kb[n] = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vb[i] = 0;
-      for (int k = 0; k < (1 << pshift); ++k) {
-        const size_t base = (size_t)(uint32_t)tab.get(min((jj << pshift) + k, nent - 1)) * pool_block;
-#pragma unroll
-        for (int n = 0; n < NLI; ++n) kb[n] = kblk[n] == k ? base : kb[n];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vb[i] = vblk[i] == k ? base : vb[i];
-      }
+      step_block_bases<NLI>(tab, jj, pshift, nent, (size_t)a.block_stride, kblk, kb);
+      step_block_bases<4>(tab, jj, pshift, nent, (size_t)a.block_stride, vblk, vb);
 #pragma unroll
       for (int n = 0; n < NLI; ++n)
         __builtin_amdgcn_global_load_lds(
