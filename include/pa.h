@@ -191,9 +191,10 @@ int pa_decode_attention(void* out, const void* query, const void* k_pool, const 
 
 /*
  * As pa_decode_attention with an explicit partition size in tokens: a
- * multiple of max(16, block_size) of at most 256*block_size (whole pool
- * blocks and whole 16-token steps of the matrix-core tile), or 0 to let the
- * library choose.  INVALID_ARG for other values.
+ * multiple of max(16, block_size) (whole pool blocks and whole 16-token steps
+ * of the matrix-core tile) of at most 256 blocks - 1024 blocks for blocks
+ * under 16 tokens - or 0 to let the library choose.  INVALID_ARG for other
+ * values.
  */
 int pa_decode_attention_ex(void* out, const void* query, const void* k_pool, const void* v_pool,
                            const int32_t* block_tables, const int32_t* context_lens,
@@ -244,7 +245,8 @@ int pa_decode_combine(void* out, const int32_t* context_lens, int32_t num_seqs,
  * so that a ragged batch still balances.  With the lengths the library
  * simulates the launch (its workgroups dealt to the XCDs and list-scheduled
  * onto the resident slots, each costing its blocks plus a fixed setup) for
- * every candidate size up to 256 blocks and returns the fastest, merge
+ * every candidate size up to the partition limit (256 blocks, 1024 for
+ * blocks under 16 tokens) and returns the fastest, merge
  * included; the host work is O(num_seqs x partitions) per candidate.
  *
  * The choice depends on the compute-unit count and on how many workgroups of
@@ -286,7 +288,7 @@ int32_t pa_decode_plan_partition_size(int32_t num_seqs, int32_t num_heads, int32
  * tile; block_size 16).  Block sizes as pa_decode_attention.
  * partition_size: 0 lets the library choose (it may split long contexts into
  * partitions merged by a second kernel, keeping the partials within 256 MiB),
- * or a size pa_decode_attention_ex accepts.  The workspace
+ * or a multiple of max(16, block_size) of at most 256 blocks.  The workspace
  * must hold pa_prefill_workspace_bytes(...) for the same partition_size (0 when
  * the context fits one partition).  Rows past query_start_loc[num_seqs] are
  * not written.  Device contents are the caller's contract (n_b <= L_b <=

@@ -214,7 +214,11 @@ double decode_cost(const DecodeShape& s, int64_t pb, const int32_t* lens, int nu
 
 int partition_granule(int block_size) { return block_size > kBlockSize ? block_size : kBlockSize; }
 
-int max_partition_tokens(int block_size) { return kMaxPartitionBlocks * block_size; }
+int max_partition_tokens(int block_size) {
+  return (block_size < kBlockSize ? kMaxSmallBlockPartition : kMaxPartitionBlocks) * block_size;
+}
+
+int max_prefill_partition_tokens(int block_size) { return kMaxPartitionBlocks * block_size; }
 
 int block_shift(int block_size) {
   const int ratio = block_size >= kBlockSize ? block_size / kBlockSize : kBlockSize / block_size;
@@ -226,6 +230,13 @@ int block_shift(int block_size) {
 int validate_partition(int requested, int block_size) {
   const int gran = partition_granule(block_size);
   if (requested < gran || requested > max_partition_tokens(block_size) || requested % gran != 0)
+    return -PA_ERR_INVALID_ARG;
+  return requested;
+}
+
+int validate_prefill_partition(int requested, int block_size) {
+  const int gran = partition_granule(block_size);
+  if (requested < gran || requested > max_prefill_partition_tokens(block_size) || requested % gran != 0)
     return -PA_ERR_INVALID_ARG;
   return requested;
 }
@@ -315,7 +326,7 @@ int check_shared_prefix(const void* out, const void* query, const void* k_pool, 
     return PA_ERR_INVALID_ARG;
   if (s.d.dtype == PA_F32) return PA_ERR_UNSUPPORTED;  // both passes run the MFMA prefill tile
   // the passes split keys at kSharedPrefixPartition tokens, which must fit one table slice
-  if (max_partition_tokens(s.d.block_size) < kSharedPrefixPartition) return PA_ERR_UNSUPPORTED;
+  if (max_prefill_partition_tokens(s.d.block_size) < kSharedPrefixPartition) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
@@ -343,7 +354,7 @@ PrefillGrid prefill_grid(const PrefillShape& s) {
 
 int prefill_partition_bounds(const PrefillShape& s, int* min_parts, int* max_parts) {
   const int bs = s.d.block_size;
-  const int64_t most = max_partition_tokens(bs);  // a multiple of the granule
+  const int64_t most = max_prefill_partition_tokens(bs);  // a multiple of the granule
   const int64_t lo = (s.d.max_context_len + most - 1) / most;
   int64_t hi = auto_partition_bound(s.d.max_context_len, bs);
   const size_t per_part = (size_t)s.num_tokens * s.d.num_heads * ((size_t)s.d.head_dim + 2) * sizeof(float);
@@ -356,7 +367,7 @@ int prefill_partition_bounds(const PrefillShape& s, int* min_parts, int* max_par
 
 int prefill_partition_size(const PrefillShape& s, int requested, int num_cus, int wg_per_cu) {
   const int bs = s.d.block_size;
-  if (requested != 0) return validate_partition(requested, bs);
+  if (requested != 0) return validate_prefill_partition(requested, bs);
   // Partitions are whole granules (max(16, block size) tokens); costs count
   // 16-token steps.
   const int64_t gran = partition_granule(bs);
@@ -373,7 +384,7 @@ int prefill_partition_size(const PrefillShape& s, int requested, int num_cus, in
     if (pgr == prev_pg) continue;
     prev_pg = pgr;
     const int64_t p = (ng + pgr - 1) / pgr;
-    if (p > hi || pgr * gran > max_partition_tokens(bs)) continue;
+    if (p > hi || pgr * gran > max_prefill_partition_tokens(bs)) continue;
     const int64_t items = pg.items * p;
     const double item = (double)(pgr * steps_per_gran) + kItemSetup;
     const int64_t tail = items % slots;
@@ -389,7 +400,7 @@ int prefill_partition_size(const PrefillShape& s, int requested, int num_cus, in
       best_pg = pgr;
     }
   }
-  if (best_pg == 0) best_pg = std::min<int64_t>(max_partition_tokens(bs) / gran, ng);
+  if (best_pg == 0) best_pg = std::min<int64_t>(max_prefill_partition_tokens(bs) / gran, ng);
   return (int)(best_pg * gran);
 }
 

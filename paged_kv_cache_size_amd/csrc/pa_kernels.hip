@@ -401,12 +401,23 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
   const int pool_bs = SUB ? BS << pshift : GATHER ? BS >> pshift : BS;  // tokens per pool block
   const int blk0 = start / pool_bs;  // partitions start on a pool block
   const int nblk = (end - start + BS - 1) / BS;  // 16-token steps
-  const int nent = MODE == kBlocks16 ? nblk : (end - start + pool_bs - 1) / pool_bs;  // 1..kMaxPartitionBlocks
+  // table entries: 1..kMaxPartitionBlocks (kMaxSmallBlockPartition for small blocks)
+  const int nent = MODE == kBlocks16 ? nblk : (end - start + pool_bs - 1) / pool_bs;
   const int last = nblk - 1;
 
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk0;
+  // Blocks of 16 tokens or more: the partition's table slice in VGPR lanes,
+  // read per block with readlane.  Small blocks (up to 1024 entries per
+  // partition): the table in LDS, shared by the workgroup's waves (they all
+  // serve the same sequence and partition), read per row by each lane.
   TableSlice tab;
-  tab.load(bt, nent, lane);
+  __shared__ int32_t stab[GATHER ? pa::kMaxSmallBlockPartition : 1];
+  if constexpr (GATHER) {
+    for (int k = threadIdx.x; k < nent; k += 64 * WPW) stab[k] = bt[k];
+    __syncthreads();
+  } else {
+    tab.load(bt, nent, lane);
+  }
 
   // Q^T as the QK B operand: column col = head h0 + col, k-chunk c = dims 32c + 8gq .. +8.
   uint4 qop[NKC];
@@ -490,8 +501,11 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
     const int jj = real ? j : last;
     if constexpr (GATHER) {  // per-lane rows; past the end the last step is re-read (cached, masked)
       size_t kb[NLI], vb[4];
-      step_block_bases<NLI>(tab, jj, pshift, nent, (size_t)a.block_stride, kblk, kb);
-      step_block_bases<4>(tab, jj, pshift, nent, (size_t)a.block_stride, vblk, vb);
+      const int e0 = jj << pshift;  // the step's first table entry; clamped to the partition's last
+#pragma unroll
+      for (int n = 0; n < NLI; ++n) kb[n] = (size_t)(uint32_t)stab[min(e0 + kblk[n], nent - 1)] * a.block_stride;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vb[i] = (size_t)(uint32_t)stab[min(e0 + vblk[i], nent - 1)] * a.block_stride;
 #pragma unroll
       for (int n = 0; n < NLI; ++n)
         __builtin_amdgcn_global_load_lds(

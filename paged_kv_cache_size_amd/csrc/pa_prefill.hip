@@ -876,7 +876,7 @@ extern "C" size_t pa_prefill_workspace_bytes(int32_t num_tokens, int32_t num_hea
     int lo = 1;
     pa::prefill_partition_bounds(s, &lo, &parts);
   } else {
-    if (pa::validate_partition(partition_size, block_size) < 0) return 0;
+    if (pa::validate_prefill_partition(partition_size, block_size) < 0) return 0;
     parts = pa::num_partitions(max_context_len, partition_size);
   }
   return prefill_workspace(s, parts);

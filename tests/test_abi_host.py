@@ -69,7 +69,8 @@ def decode(**kw):
     (dict(dtype=B.PA_F32, bs=32, mb=4), B.PA_ERR_UNSUPPORTED),
     (dict(bs=32, mb=4, ps=16), B.PA_ERR_INVALID_ARG),  # partitions hold whole blocks
     (dict(bs=4, mb=32, ps=8), B.PA_ERR_INVALID_ARG),   # and whole 16-token steps
-    (dict(bs=1, mb=128, ps=272), B.PA_ERR_INVALID_ARG),  # above 256 blocks
+    (dict(bs=1, mb=2048, maxlen=2048, ps=1040), B.PA_ERR_INVALID_ARG),  # small blocks: above 1024 blocks
+    (dict(bs=32, mb=129, maxlen=4128, ps=8224), B.PA_ERR_INVALID_ARG),  # above 256 blocks
     (dict(ps=24), B.PA_ERR_INVALID_ARG),          # not a multiple of the block size
     (dict(ps=4112, maxlen=128), B.PA_ERR_INVALID_ARG),  # above 256 blocks
     (dict(ps=-16), B.PA_ERR_INVALID_ARG),

@@ -340,6 +340,14 @@ def test_block_sizes(bs, dtype, d):
     check_whole(w, seed=bs, partition_size=max(16, bs), poisoned=True)
 
 
+@pytest.mark.parametrize("bs,ps", [(1, 1024), (2, 2048), (8, 8192), (1, 1008)])
+def test_small_blocks_long_partitions(bs, ps):
+    # blocks under 16 tokens: the partition's table (up to 1024 entries) sits
+    # in LDS, so partitions may hold 1024 blocks
+    w = W.custom(BS_LENS + [3000, 8192], 8, 2, 128, "bf16", seed=bs, extra_cols=1, block_size=bs)
+    check_whole(w, seed=bs, partition_size=ps, poisoned=True)
+
+
 @pytest.mark.parametrize("bs", [4, 64])
 def test_block_sizes_full_partition_policy(bs):
     # the policy's choice given the lengths, as a scheduler would launch it

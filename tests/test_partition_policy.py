@@ -103,9 +103,10 @@ def test_plan_argument_checks():
 def test_block_sizes_give_whole_blocks_within_the_slice(bs):
     lens = np.array([4096] * 64 + [100, 3000], np.int32)
     a = (66, 32, 8, 128, 4096, bs, B.PA_BF16)
+    slice_blocks = 1024 if bs < 16 else 256  # small blocks: the table sits in LDS, up to 1024 entries
     for l in (None, lens):
         ps = plan(a, l)
-        assert ps % max(16, bs) == 0 and max(16, bs) <= ps <= 256 * bs
+        assert ps % max(16, bs) == 0 and max(16, bs) <= ps <= slice_blocks * bs
 
 
 def test_block_size_support():
