@@ -288,7 +288,7 @@ int32_t pa_decode_plan_partition_size(int32_t num_seqs, int32_t num_heads, int32
  * tile; block_size 16).  Block sizes as pa_decode_attention.
  * partition_size: 0 lets the library choose (it may split long contexts into
  * partitions merged by a second kernel, keeping the partials within 256 MiB),
- * or a multiple of max(16, block_size) of at most 256 blocks.  The workspace
+ * or a size pa_decode_attention_ex accepts.  The workspace
  * must hold pa_prefill_workspace_bytes(...) for the same partition_size (0 when
  * the context fits one partition).  Rows past query_start_loc[num_seqs] are
  * not written.  Device contents are the caller's contract (n_b <= L_b <=
@@ -407,9 +407,8 @@ int pa_seq_block_table(const pa_block_pool* pool, int32_t seq, int32_t* table, i
  *   max_group_size, max_prefix_len: host bounds (max_prefix_len a multiple of
  *   block_size, <= max_context_len).
  *   workspace: pa_shared_prefix_workspace_bytes(...) bytes, always needed.
- * fp16 / bf16 only; block_size a power of two from 4 to 256 (both passes split
- * keys at 1024 tokens, which must fit 256 blocks): UNSUPPORTED otherwise.
- * Errors as pa_decode_attention.
+ * fp16 / bf16 only; block sizes as pa_decode_attention.  Errors as
+ * pa_decode_attention.
  */
 int pa_decode_attention_shared_prefix(void* out, const void* query, const void* k_pool, const void* v_pool,
                                       const int32_t* block_tables, const int32_t* context_lens,

@@ -117,42 +117,27 @@ __device__ __forceinline__ float across_groups_sum(float x) {
 }
 
 // A partition's block-table slice, staged on chip: entry j sits in lane j % 64
-// of register j / 64, so one wave holds up to 64 * R entries.
-template <int R>
-struct TableSliceN {
-  static constexpr int kRegs = R;
-  int r[R];
+// of register j / 64, so one wave holds up to 64 * kTabRegs entries.
+constexpr int kTabRegs = pa::kMaxPartitionBlocks / 64;
+struct TableSlice {
+  int r[kTabRegs];
   __device__ __forceinline__ void load(const int32_t* bt, int n, int lane) {
 #pragma unroll
-    for (int k = 0; k < R; ++k) r[k] = (64 * k + lane < n) ? bt[64 * k + lane] : 0;
+    for (int k = 0; k < kTabRegs; ++k) r[k] = (64 * k + lane < n) ? bt[64 * k + lane] : 0;
   }
-  // entry j (wave-uniform j < 64 * R), as a scalar: one readlane per
+  // entry j (wave-uniform j < 64 * kTabRegs), as a scalar: one readlane per
   // register and scalar selects (no dynamic register indexing)
   __device__ __forceinline__ int get(int j) const {
     const int lane = j & 63, k = j >> 6;
     int v = __builtin_amdgcn_readlane(r[0], lane);
 #pragma unroll
-    for (int i = 1; i < R; ++i) {
+    for (int i = 1; i < kTabRegs; ++i) {
       const int e = __builtin_amdgcn_readlane(r[i], lane);
       v = (k == i) ? e : v;
     }
     return v;
   }
-  // register `reg` (wave-uniform) of the slice, for lanes_get
-  __device__ __forceinline__ int reg_of(int reg) const {
-    int src = r[0];
-#pragma unroll
-    for (int i = 1; i < R; ++i) src = (reg == i) ? r[i] : src;
-    return src;
-  }
 };
-constexpr int kTabRegs = pa::kMaxPartitionBlocks / 64;
-constexpr int kTabRegsSmall = pa::kMaxSmallBlockPartition / 64;
-using TableSlice = TableSliceN<kTabRegs>;
-
-// Per-lane entries of one register of a slice (reg_of): lane l gets entry
-// 64 * reg + lo_l, lo_l in 0..63, by a cross-lane permute.
-__device__ __forceinline__ int lanes_get(int src, int lo) { return __builtin_amdgcn_ds_bpermute(lo << 2, src); }
 
 // Pool block sizes against the 16-token steps of the MFMA tiles:
 //  * kBlocks16: blocks and steps coincide;
@@ -162,23 +147,25 @@ __device__ __forceinline__ int lanes_get(int src, int lo) { return __builtin_amd
 //    1 << shift blocks, so every lane addresses its own row's block.
 constexpr int kBlocks16 = 0, kBlocksLarge = 1, kBlocksSmall = 2;
 
-// kBlocksSmall: byte offset of the pool block holding each of N rows a lane
-// touches in step jj; blk[i] = index of row i's block within the step (row /
-// block size).  The step's blocks are table entries (jj << shift) + k, clamped
-// to the partition's last entry (nent - 1) past its end, so every address
-// stays inside a block the caller owns.  A step's 1 << shift entries start at
-// a multiple of 1 << shift (which divides 64), so they share one register of
-// the slice and each lane fetches its own with one permute per row.
-template <int N, class Tab>
-__device__ __forceinline__ void step_block_bases(const Tab& tab, int jj, int shift, int nent, size_t block_stride,
-                                                 const int* blk, size_t* base) {
+// kBlocksSmall: the partition's table (up to kMaxSmallBlockPartition
+// entries) staged in LDS by the whole workgroup - every wave of a workgroup
+// serves the same sequence and partition - then read per row by each lane.
+// Callers reach this from every wave of the workgroup (it ends in a barrier).
+__device__ __forceinline__ void stage_table(int32_t* stab, const int32_t* bt, int nent) {
+  for (int k = threadIdx.x; k < nent; k += blockDim.x) stab[k] = bt[k];
+  __syncthreads();
+}
+// Byte offset of the pool block holding each of N rows a lane touches in
+// step jj; blk[i] = index of row i's block within the step (row / block
+// size).  The step's blocks are table entries (jj << shift) + k, clamped to
+// the partition's last entry (nent - 1) past its end, so every address stays
+// inside a block the caller owns.
+template <int N>
+__device__ __forceinline__ void step_block_bases(const int32_t* stab, int jj, int shift, int nent,
+                                                 size_t block_stride, const int* blk, size_t* base) {
   const int e0 = jj << shift;
-  const int src = tab.reg_of(e0 >> 6);
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int e = min(e0 + blk[i], nent - 1);
-    base[i] = (size_t)(uint32_t)lanes_get(src, e & 63) * block_stride;
-  }
+  for (int i = 0; i < N; ++i) base[i] = (size_t)(uint32_t)stab[min(e0 + blk[i], nent - 1)] * block_stride;
 }
 
 // Workgroup id -> logical id such that each XCD (workgroups are dealt to the

@@ -218,7 +218,7 @@ int max_partition_tokens(int block_size) {
   return (block_size < kBlockSize ? kMaxSmallBlockPartition : kMaxPartitionBlocks) * block_size;
 }
 
-int max_prefill_partition_tokens(int block_size) { return kMaxPartitionBlocks * block_size; }
+int max_prefill_partition_tokens(int block_size) { return max_partition_tokens(block_size); }
 
 int block_shift(int block_size) {
   const int ratio = block_size >= kBlockSize ? block_size / kBlockSize : kBlockSize / block_size;

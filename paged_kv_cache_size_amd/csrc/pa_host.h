@@ -14,7 +14,7 @@ constexpr int kMaxRepPerWaveValu = 8;    // query heads a VALU (fp32) wave serve
 constexpr int kMaxRepPerWaveMfma = 16;   // query heads an MFMA (16-bit) wave serves: the 16 MFMA columns
 constexpr int kMinPartition = 128;       // smallest partition the library picks itself
 constexpr int kMaxPartitionBlocks = 256;  // a partition's table slice: 4 VGPRs of a wave, one entry per lane
-constexpr int kMaxSmallBlockPartition = 1024;  // decode with blocks under 16 tokens: a 16-VGPR slice
+constexpr int kMaxSmallBlockPartition = 1024;  // blocks under 16 tokens: the table in LDS (4 KiB)
 constexpr int kMaxAutoPartitionBlocks = 64;  // automatic choice without the context lengths: short
                                              // enough partitions to balance a ragged batch
 
@@ -30,9 +30,9 @@ bool decode_block_size_ok(int block_size, int dtype);
 int partition_granule(int block_size);  // partitions are multiples of max(16, block_size) tokens
 // log2 of block_size / 16 (blocks of 16 or more tokens) or 16 / block_size.
 int block_shift(int block_size);
-// Largest partition in tokens: the decode tiles take kMaxPartitionBlocks
-// pool blocks (kMaxSmallBlockPartition for blocks under 16 tokens), the
-// prefill tiles and the cascade kMaxPartitionBlocks.
+// Largest partition in tokens: kMaxPartitionBlocks pool blocks, or
+// kMaxSmallBlockPartition for blocks under 16 tokens (their table is staged in
+// LDS instead of VGPR lanes); the same for the decode and prefill tiles.
 int max_partition_tokens(int block_size);
 int max_prefill_partition_tokens(int block_size);
 int validate_partition(int requested, int block_size);  // decode: requested, or a negated pa_status

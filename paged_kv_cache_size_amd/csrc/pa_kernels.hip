@@ -412,12 +412,10 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
   // serve the same sequence and partition), read per row by each lane.
   TableSlice tab;
   __shared__ int32_t stab[GATHER ? pa::kMaxSmallBlockPartition : 1];
-  if constexpr (GATHER) {
-    for (int k = threadIdx.x; k < nent; k += 64 * WPW) stab[k] = bt[k];
-    __syncthreads();
-  } else {
+  if constexpr (GATHER)
+    stage_table(stab, bt, nent);
+  else
     tab.load(bt, nent, lane);
-  }
 
   // Q^T as the QK B operand: column col = head h0 + col, k-chunk c = dims 32c + 8gq .. +8.
   uint4 qop[NKC];
@@ -501,11 +499,8 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
     const int jj = real ? j : last;
     if constexpr (GATHER) {  // per-lane rows; past the end the last step is re-read (cached, masked)
       size_t kb[NLI], vb[4];
-      const int e0 = jj << pshift;  // the step's first table entry; clamped to the partition's last
-#pragma unroll
-      for (int n = 0; n < NLI; ++n) kb[n] = (size_t)(uint32_t)stab[min(e0 + kblk[n], nent - 1)] * a.block_stride;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vb[i] = (size_t)(uint32_t)stab[min(e0 + vblk[i], nent - 1)] * a.block_stride;
+      step_block_bases<NLI>(stab, jj, pshift, nent, (size_t)a.block_stride, kblk, kb);
+      step_block_bases<4>(stab, jj, pshift, nent, (size_t)a.block_stride, vblk, vb);
 #pragma unroll
       for (int n = 0; n < NLI; ++n)
         __builtin_amdgcn_global_load_lds(

@@ -175,8 +175,12 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
   const int last = nblk - 1;
 
   const int32_t* bt = a.block_tables + (size_t)trow * a.max_blocks_per_seq + blk0;
-  TableSlice tab;
-  tab.load(bt, nent, lane);
+  TableSlice tab;  // blocks of 16 tokens or more: the slice in VGPR lanes
+  __shared__ int32_t stab[GATHER ? pa::kMaxSmallBlockPartition : 1];  // small blocks: in LDS
+  if constexpr (GATHER)
+    stage_table(stab, bt, nent);
+  else
+    tab.load(bt, nent, lane);
 
   uint4 qop[NKC];
   {
@@ -246,8 +250,8 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
     const int jj = real ? j : last;
     if constexpr (GATHER) {
       size_t kbase[NLI], vbase[4];
-      step_block_bases<NLI>(tab, jj, pshift, nent, block_stride, kblk, kbase);
-      step_block_bases<4>(tab, jj, pshift, nent, block_stride, vblk, vbase);
+      step_block_bases<NLI>(stab, jj, pshift, nent, block_stride, kblk, kbase);
+      step_block_bases<4>(stab, jj, pshift, nent, block_stride, vblk, vbase);
 #pragma unroll
       for (int i = 0; i < NLI; ++i)
         __builtin_amdgcn_global_load_lds(
@@ -468,8 +472,12 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
   const int last = nblk - 1;
 
   const int32_t* bt = a.block_tables + (size_t)trow * a.max_blocks_per_seq + blk0;
-  TableSlice tab;
-  tab.load(bt, nent, lane);
+  TableSlice tab;  // blocks of 16 tokens or more: the slice in VGPR lanes
+  __shared__ int32_t stab[GATHER ? pa::kMaxSmallBlockPartition : 1];  // small blocks: in LDS
+  if constexpr (GATHER)
+    stage_table(stab, bt, nent);
+  else
+    tab.load(bt, nent, lane);
 
   uint4 qop[kWaveTiles][NKC];
 #pragma unroll
@@ -546,7 +554,7 @@ __global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const Prefill
     const int jj = real ? j : last;
     if constexpr (GATHER) {
       size_t base[DPW];
-      step_block_bases<DPW>(tab, jj, pshift, nent, block_stride, rblk, base);
+      step_block_bases<DPW>(stab, jj, pshift, nent, block_stride, rblk, base);
 #pragma unroll
       for (int i = 0; i < DPW; ++i) {
         if (!has[i]) continue;

@@ -123,7 +123,8 @@ def prefill(**kw):
     (dict(bs=512, mb=1), B.PA_ERR_UNSUPPORTED),
     (dict(bs=32, mb=4, ps=16), B.PA_ERR_INVALID_ARG),  # partitions hold whole blocks
     (dict(bs=4, mb=32, ps=8), B.PA_ERR_INVALID_ARG),   # and whole 16-token steps
-    (dict(bs=1, mb=128, ps=272), B.PA_ERR_INVALID_ARG),  # at most 256 blocks
+    (dict(bs=1, mb=2048, maxlen=2048, ps=1040), B.PA_ERR_INVALID_ARG),  # small blocks: at most 1024
+    (dict(bs=32, mb=129, maxlen=4128, ps=8224), B.PA_ERR_INVALID_ARG),  # at most 256 blocks
     (dict(ps=24), B.PA_ERR_INVALID_ARG),
     (dict(ps=4112), B.PA_ERR_INVALID_ARG),
     (dict(ps=16), B.PA_ERR_WORKSPACE),            # 8 partitions need a workspace
@@ -134,11 +135,11 @@ def test_prefill_argument_checks(kw, status):
 
 
 def test_shared_prefix_block_sizes():
-    # the cascade splits keys at 1024 tokens: blocks of 1 and 2 tokens cannot
-    # hold that in one 256-entry table slice
+    # block sizes are powers of two (the passes split keys at 1024 tokens,
+    # which every supported block size holds in one partition)
     lib = B.lib()
     f = lib.pa_decode_attention_shared_prefix
-    for bs in (1, 2, 24):
+    for bs in (24, 512):
         mb = -(-4096 // bs)
         assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 2, 8, 2, 128, bs, mb, 4096, 0,
                  0.088, B.PA_BF16, FAKE, 1 << 30, None) == B.PA_ERR_UNSUPPORTED

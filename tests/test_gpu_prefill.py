@@ -154,6 +154,15 @@ def test_fp32_rows(h, hkv):
     check_prefill(pb, seed=5, partition_size=64, poisoned=True)
 
 
+@pytest.mark.parametrize("bs,ps", [(1, 1024), (2, 2048), (4, 2048)])
+def test_small_blocks_long_partitions(bs, ps):
+    # blocks under 16 tokens: the partition's table (up to 1024 entries) is
+    # staged in LDS, so partitions may hold 1024 blocks
+    lens, qlens = [1, 7, 33, 1100, 2500], [1, 7, 20, 300, 40]
+    pb = W.prefill_batch(lens, qlens, 8, 2, 128, "bf16", seed=bs + 7, extra_cols=1, block_size=bs)
+    check_prefill(pb, seed=bs, partition_size=ps, poisoned=True)
+
+
 def test_whole_prompts_only():
     # every sequence is a fresh prompt: n = L, the full causal triangle
     lens = [1, 2, 15, 16, 17, 64, 129]

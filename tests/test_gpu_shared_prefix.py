@@ -72,7 +72,8 @@ def forked_batch(prompts, forks, gens, h, hkv, d, dtype, seed, bs=16):
     the library's block pool (copy-on-write pairs replayed by the tensor
     builder, which copies the prompt rows)."""
     rng = np.random.default_rng(seed)
-    m = PB.BlockManager(4096, bs, free_order=rng.permutation(4096))
+    nb = 4096 * max(1, 16 // bs)  # room for every token at any block size
+    m = PB.BlockManager(nb, bs, free_order=rng.permutation(nb))
     seqs, copies = [], []
     for p, f, gl in zip(prompts, forks, gens):
         root = m.new_seq()
@@ -87,12 +88,12 @@ def forked_batch(prompts, forks, gens, h, hkv, d, dtype, seed, bs=16):
     lens = np.array([m.length(s) for s in seqs], np.int32)
     width = max(len(x) for x in tables) + 1
     used = {b for x in tables for b in x}
-    pad = min(set(range(4096)) - used)
+    pad = min(set(range(nb)) - used)
     bt = np.full((len(seqs), width), pad, np.int32)
     for i, x in enumerate(tables):
         bt[i, :len(x)] = x
-    unowned = np.array(sorted(set(range(4096)) - used), np.int64)
-    return W.Workload("forked", dtype, h, hkv, d, bs, 4096, lens, bt, float(np.float32(1 / np.sqrt(d))), pad,
+    unowned = np.array(sorted(set(range(nb)) - used), np.int64)
+    return W.Workload("forked", dtype, h, hkv, d, bs, nb, lens, bt, float(np.float32(1 / np.sqrt(d))), pad,
                       unowned, copies, "forked prompts")
 
 
@@ -111,7 +112,7 @@ def test_mixed_groups(dtype, d, h, hkv):
     check(w, g, seed=1)
 
 
-@pytest.mark.parametrize("bs", [4, 8, 32, 64, 256])
+@pytest.mark.parametrize("bs", [1, 2, 4, 8, 32, 64, 256])
 def test_mixed_groups_block_sizes(bs):
     # prefixes are whole pool blocks; the passes gather small blocks row by
     # row and walk large ones in 16-row windows

@@ -66,7 +66,7 @@ def cascade(**kw):
     (dict(maxpre=144), B.PA_ERR_INVALID_ARG),     # longer than any context
     (dict(dtype=B.PA_F32), B.PA_ERR_UNSUPPORTED),
     (dict(D=96), B.PA_ERR_UNSUPPORTED),
-    (dict(bs=2, mb=64, maxpre=64), B.PA_ERR_UNSUPPORTED),  # 1024-token passes exceed a 256-block slice
+    (dict(bs=24, mb=6, maxpre=48), B.PA_ERR_UNSUPPORTED),  # block sizes are powers of two
     (dict(bs=32, mb=4, maxpre=48), B.PA_ERR_INVALID_ARG),  # the prefix is whole blocks
     (dict(ws=None), B.PA_ERR_WORKSPACE),
     (dict(wsb=100), B.PA_ERR_WORKSPACE),
