@@ -55,7 +55,7 @@ def parse():
     p.add_argument("--replicas", type=int, default=1,
                    help="rotate over this many copies of the pools (cold caches for small batches)")
     p.add_argument("--block-size", type=int, default=0,
-                   help="pool block size for the Llama-layer workload (default 16)")
+                   help="pool block size for the Llama-layer decode and chunked-prefill workloads (default 16)")
     p.add_argument("--layout", choices=("split", "fused"), default="split",
                    help="pool layout: split K and V pools, or one fused [NB, H_kv, BS, 2D] pool")
     p.add_argument("--shared-prefix", action="store_true",
@@ -271,7 +271,8 @@ def main_prefill(args):
     from paged_kv_cache_size_amd import workloads as W
 
     PB.lib()
-    pb = W.PREFILL_BUILDERS[args.workload](seed=args.seed)
+    extra = {"block_size": args.block_size} if args.block_size else {}
+    pb = W.PREFILL_BUILDERS[args.workload](seed=args.seed, **extra)
     w = pb.workload
     t = W.make_prefill_tensors(pb, seed=args.seed, device="cuda")
     bt = torch.from_numpy(w.block_tables).cuda()

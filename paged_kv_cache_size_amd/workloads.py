@@ -411,12 +411,13 @@ def prefill_batch(lens, query_lens, num_heads: int, num_kv_heads: int, head_dim:
 
 
 def chunked_prefill_llama_bf16(seed: int = 0, num_seqs: int = 16, context: int = 4096,
-                               chunk: int = 512) -> PrefillBatch:
+                               chunk: int = 512, block_size: int = 16) -> PrefillBatch:
     """Chunked prefill of the Llama-style GQA layer: 16 sequences each add a
     512-token chunk on top of 3584 cached tokens (context 4096); 32 query /
     8 KV heads; D 128; bf16; physical ids shuffled in a pool with 10% slack."""
     pb = prefill_batch([context] * num_seqs, [chunk] * num_seqs, 32, 8, 128, "bf16", seed=seed,
-                       name="chunked_prefill_llama_bf16")
+                       name="chunked_prefill_llama_bf16" + ("" if block_size == 16 else f"_bs{block_size}"),
+                       block_size=block_size)
     pb.description = (f"{num_seqs} seqs x {chunk}-token chunks on {context - chunk} cached tokens, "
                       f"H 32 / Hkv 8, D 128, bf16")
     return pb
