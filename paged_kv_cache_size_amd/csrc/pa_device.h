@@ -303,11 +303,25 @@ __device__ __forceinline__ void merge_partials(uint8_t* out_row, const float* __
 #pragma unroll
   for (int x = 1; x < 64; x <<= 1) den += __shfl_xor(den, x);
 
+  // partials in chunks of 8 whose loads are all issued before any is used
+  // (the loads, not the arithmetic, bound this loop); summed in partition order
+  constexpr int kChunk = 8;
   float o[DPL] = {};
-  for (int p = 0; p < np; ++p) {
-    const float f = fast_exp2(ml[p].x - M);
+  for (int p0 = 0; p0 < np; p0 += kChunk) {
+    float f[kChunk], v[kChunk][DPL];
 #pragma unroll
-    for (int d = 0; d < DPL; ++d) o[d] = fmaf(f, acc[(size_t)p * D + lane * DPL + d], o[d]);
+    for (int i = 0; i < kChunk; ++i) {
+      const int p = min(p0 + i, np - 1);  // past np: a weight of 0 on a valid address
+      f[i] = p0 + i < np ? ml[p].x : -INFINITY;
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) v[i][d] = acc[(size_t)p * D + lane * DPL + d];
+    }
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const float w = fast_exp2(f[i] - M);
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) o[d] = fmaf(w, v[i][d], o[d]);
+    }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   uint8_t* dst = out_row + lane * DPL * EB;
