@@ -295,6 +295,20 @@ def main_prefill(args):
         PB.pa_prefill_attention(t["query"], t["k_pool"], t["v_pool"], bt, lens, t["query_start_loc"], w.scale,
                                 pb.max_query_len, w.max_context_len, out=out, workspace=ws, partition_size=ps)
 
+    if args.layout == "fused":  # the same rows rearranged on the device into one fused pool
+        fused = torch.empty((w.num_blocks, w.num_kv_heads, w.block_size, 2 * D), dtype=t["k_pool"].dtype,
+                            device="cuda")
+        every = torch.arange(w.num_blocks, dtype=torch.int64, device="cuda")
+        PB.pa_convert_blocks(fused, None, PB.PA_KV_FUSED, t["k_pool"], t["v_pool"], PB.PA_KV_SPLIT, every, every)
+
+        def k_write():
+            PB.pa_reshape_and_cache(t["key"], t["value"], fused, None, slots, layout=PB.PA_KV_FUSED)
+
+        def k_attn():
+            PB.pa_prefill_attention(t["query"], fused, None, bt, lens, t["query_start_loc"], w.scale,
+                                    pb.max_query_len, w.max_context_len, out=out, workspace=ws, partition_size=ps,
+                                    layout=PB.PA_KV_FUSED)
+
     stages = [k_slot, k_write, k_attn]
     ms_per_step, per_kernel_ms, wall = time_stages(stages, args.steps, args.warmup)
     flops = pb.attention_flops()
@@ -313,7 +327,8 @@ def main_prefill(args):
         "config": {"workload": pb.name, "num_seqs": w.num_seqs, "new_tokens": T, "max_query_len": pb.max_query_len,
                    "context_lens_sum": int(w.context_lens.sum()), "max_context_len": w.max_context_len,
                    "num_heads": H, "num_kv_heads": w.num_kv_heads, "head_dim": D, "block_size": w.block_size,
-                   "num_blocks": w.num_blocks, "partition_size": ps, "description": pb.description},
+                   "num_blocks": w.num_blocks, "partition_size": ps, "pool_layout": args.layout,
+                   "description": pb.description},
         "attention_flops_per_step": flops,
         "kernel_us": {"slot_mapping": per_kernel_ms[0] * 1e3, "reshape_and_cache": per_kernel_ms[1] * 1e3,
                       "prefill_attention": attn_ms * 1e3},
