@@ -334,7 +334,7 @@ def main_prefill(args):
                       "prefill_attention": attn_ms * 1e3},
         "roofline": {"bound": "mfma", "kernel": kernel, "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": load_traffic(pb.name, "prefill_attention")},
+                     "traffic": load_traffic(pb.name, "prefill_attention") if args.layout == "split" else None},
         "kv_read_bytes_per_step": pb.kv_read_bytes(),
         "cpu_baseline": base,
         "wall_s_timed": wall,
@@ -726,7 +726,7 @@ def main_decode(args, oracle_pool):
         "step_us_percentiles": step_pct,
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None if args.shared_prefix else load_traffic(w.name),
+                     "traffic": None if args.shared_prefix or args.layout != "split" else load_traffic(w.name),
                      "stream_read_GBps": ceiling["GBps"], "frac_of_stream_read": achieved / ceiling["GBps"]},
         "stream_read_ceiling": ceiling,
         "cpu_baseline": base,
