@@ -313,11 +313,11 @@ def main_prefill(args):
     ms_per_step, per_kernel_ms, wall = time_stages(stages, args.steps, args.warmup)
     flops = pb.attention_flops()
     attn_ms = per_kernel_ms[2]
-    # the library runs the cooperative tile once a sequence brings 64 or more
-    # (token, query head) columns per KV head
+    # the library runs the cooperative tile once a sequence brings more than
+    # 16 (token, query head) columns per KV head
     rep = H // w.num_kv_heads
     repc = max(c for c in range(1, 17) if rep % c == 0)
-    kernel = "prefill_wg_kernel" if pb.max_query_len * repc >= 64 else "prefill_mfma_kernel"
+    kernel = "prefill_wg_kernel" if pb.max_query_len * repc > 16 else "prefill_mfma_kernel"
     achieved = flops / (attn_ms * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[w.dtype]
     rec = {

@@ -339,10 +339,21 @@ PrefillGrid prefill_grid(const PrefillShape& s) {
   PrefillGrid p;
   const int64_t cols = (int64_t)s.max_query_len * g.repc;
   p.wide = cols >= kPrefillWideCols;
+  p.wave_tiles = 1;
   if (p.wide) {
-    p.tiles = (int)((cols + kPrefillWgCols - 1) / kPrefillWgCols);
+    if (cols <= 32) {
+      p.waves = 2;
+      p.wave_tiles = 1;
+    } else if (cols <= 64) {
+      p.waves = 2;
+      p.wave_tiles = 2;
+    } else {
+      p.waves = kPrefillWgWaves;
+      p.wave_tiles = kPrefillWaveTiles;
+    }
+    const int64_t wg_cols = 16 * p.wave_tiles * p.waves;
+    p.tiles = (int)((cols + wg_cols - 1) / wg_cols);
     p.groups = g.units;
-    p.waves = kPrefillWgWaves;
   } else {
     p.tiles = prefill_tiles(s, g);
     p.groups = g.groups;

@@ -133,12 +133,14 @@ int check_prefill(const void* out, const void* query, const void* k_pool, const 
 // Column tiles (16 MFMA columns of (token, query head) pairs) per (sequence, wave unit).
 int prefill_tiles(const PrefillShape& s, const DecodeGrid& g);
 
-// Launch geometry of the prefill kernels.  Narrow column ranges (fewer than
-// kPrefillWideCols columns per (sequence, KV head unit)) run the per-wave
-// tile: `items` workgroups of `waves` waves per partition, one unit per wave.
-// Wide ones run the cooperative tile: 4 waves share one unit's K/V blocks and
-// take 128 columns.
-constexpr int kPrefillWideCols = 64;
+// Launch geometry of the prefill kernels.  Up to 16 columns per (sequence,
+// KV head unit) run the per-wave tile: `items` workgroups of `waves` waves per
+// partition, one unit per wave.  More run the cooperative tile, whose waves
+// share one unit's K/V blocks: 2 waves of one 16-column tile (32 columns),
+// 2 waves of two tiles (64 columns), or kPrefillWgWaves waves of
+// kPrefillWaveTiles tiles (128 columns) - the smallest shape that covers the
+// columns, so no wave streams K/V for columns it does not have.
+constexpr int kPrefillWideCols = 17;
 #ifndef PA_PREFILL_WG_WAVES
 #define PA_PREFILL_WG_WAVES 4
 #endif
@@ -147,12 +149,12 @@ constexpr int kPrefillWgWaves = PA_PREFILL_WG_WAVES;  // waves of the cooperativ
 #define PA_PREFILL_WAVE_TILES 2
 #endif
 constexpr int kPrefillWaveTiles = PA_PREFILL_WAVE_TILES;  // 16-column MFMA tiles per wave of the cooperative tile
-constexpr int kPrefillWgCols = 16 * kPrefillWaveTiles * kPrefillWgWaves;  // columns per cooperative workgroup
 struct PrefillGrid {
   bool wide;
-  int tiles;       // column tiles (16 columns) or column groups (128 columns) per sequence
+  int tiles;       // column tiles (16 columns) or column groups (wg_cols columns) per sequence
   int groups;      // workgroups per (sequence, tile, partition): unit groups or units
   int waves;       // waves per workgroup
+  int wave_tiles;  // cooperative tile: 16-column tiles per wave
   int64_t items;   // workgroups per partition
 };
 PrefillGrid prefill_grid(const PrefillShape& s);

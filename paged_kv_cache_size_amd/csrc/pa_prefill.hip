@@ -391,13 +391,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 // operand) from LDS once per step and applies them to both of its tiles.
 // Arithmetic per tile is that of prefill_mfma_kernel: 32-key steps, P.V on
 // 16x16x32, lazily moved running max, mask-free interior steps.
-constexpr int kWaveTiles = pa::kPrefillWaveTiles;      // 16-column MFMA tiles per wave
-constexpr int kWaveCols = 16 * kWaveTiles;             // columns per wave
-constexpr int kWgWaves = pa::kPrefillWgWaves;           // waves per workgroup (8 measured 6% slower)
-constexpr int kWgCols = kWaveCols * kWgWaves;           // columns per workgroup
-
-template <int DT, int D, int NP, int MODE>
-__global__ __launch_bounds__(64 * kWgWaves) void prefill_wg_kernel(const PrefillArgs a) {
+// WAVES waves of TILES 16-column tiles each: 128 columns for long runs of new
+// tokens (4 x 2; 8 waves measured 6% slower), 64 or 32 for short ones (2 x 2,
+// 2 x 1).
+template <int DT, int D, int NP, int MODE, int WAVES, int TILES>
+__global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArgs a) {
+  constexpr int kWaveTiles = TILES;               // 16-column MFMA tiles per wave
+  constexpr int kWaveCols = 16 * kWaveTiles;      // columns per wave
+  constexpr int kWgWaves = WAVES;                 // waves per workgroup
+  constexpr int kWgCols = kWaveCols * kWgWaves;   // columns per workgroup
   constexpr bool SUB = MODE == kBlocksLarge;
   constexpr bool GATHER = MODE == kBlocksSmall;
   using Ops = MfmaOps<DT>;
@@ -771,19 +773,30 @@ PrefillFn pick_prefill_bs(int wpw, int block_size) {
 #endif
 constexpr int kPrefillPairs = PA_PREFILL_PAIRS;  // ring pairs of the cooperative tile
 
-template <int DT, int D>
+template <int DT, int D, int WAVES, int TILES>
 PrefillFn pick_prefill_wide_bs(int block_size) {
-  if (block_size == pa::kBlockSize) return prefill_wg_kernel<DT, D, kPrefillPairs, kBlocks16>;
-  if (block_size > pa::kBlockSize) return prefill_wg_kernel<DT, D, kPrefillPairs, kBlocksLarge>;
-  return prefill_wg_kernel<DT, D, kPrefillPairs, kBlocksSmall>;
+  if (block_size == pa::kBlockSize) return prefill_wg_kernel<DT, D, kPrefillPairs, kBlocks16, WAVES, TILES>;
+  if (block_size > pa::kBlockSize) return prefill_wg_kernel<DT, D, kPrefillPairs, kBlocksLarge, WAVES, TILES>;
+  return prefill_wg_kernel<DT, D, kPrefillPairs, kBlocksSmall, WAVES, TILES>;
 }
 
-PrefillFn pick_prefill_wide(int dtype, int d, int block_size) {
+template <int DT, int D>
+PrefillFn pick_prefill_wide_shape(const pa::PrefillGrid& g, int block_size) {
+  if (g.waves == 2 && g.wave_tiles == 1) return pick_prefill_wide_bs<DT, D, 2, 1>(block_size);
+  if (g.waves == 2 && g.wave_tiles == 2) return pick_prefill_wide_bs<DT, D, 2, 2>(block_size);
+  if (g.waves == pa::kPrefillWgWaves && g.wave_tiles == pa::kPrefillWaveTiles)
+    return pick_prefill_wide_bs<DT, D, pa::kPrefillWgWaves, pa::kPrefillWaveTiles>(block_size);
+  return nullptr;
+}
+
+PrefillFn pick_prefill_wide(int dtype, int d, const pa::PrefillGrid& g, int block_size) {
   switch (dtype) {
     case PA_F16:
-      return d == 64 ? pick_prefill_wide_bs<DT_F16, 64>(block_size) : pick_prefill_wide_bs<DT_F16, 128>(block_size);
+      return d == 64 ? pick_prefill_wide_shape<DT_F16, 64>(g, block_size)
+                     : pick_prefill_wide_shape<DT_F16, 128>(g, block_size);
     case PA_BF16:
-      return d == 64 ? pick_prefill_wide_bs<DT_BF16, 64>(block_size) : pick_prefill_wide_bs<DT_BF16, 128>(block_size);
+      return d == 64 ? pick_prefill_wide_shape<DT_BF16, 64>(g, block_size)
+                     : pick_prefill_wide_shape<DT_BF16, 128>(g, block_size);
     default: return nullptr;
   }
 }
@@ -913,7 +926,7 @@ extern "C" int pa_prefill_attention_layout(void* out, const void* query, const v
                         workspace_bytes, partition_size, stream);
   const pa::DecodeGrid gd = pa::decode_grid(shp.d);
   const pa::PrefillGrid pg = pa::prefill_grid(shp);
-  PrefillFn fn = pg.wide ? pick_prefill_wide(shp.d.dtype, shp.d.head_dim, block_size)
+  PrefillFn fn = pg.wide ? pick_prefill_wide(shp.d.dtype, shp.d.head_dim, pg, block_size)
                          : pick_prefill(shp.d.dtype, shp.d.head_dim, gd.wpw, block_size);
   if (!fn) return PA_ERR_UNSUPPORTED;
   int cus = 256, per_cu = 1;
