@@ -22,6 +22,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "pa.h"
@@ -49,7 +50,8 @@ struct PrefillArgs {
   int causal;          // 1: row i sits at position L - n + i; 0: every row sees the whole key range
   int partial_base;    // < 0: final rows, partials only for split rows; >= 0: every partition's
   int partial_stride;  //   partials go to slot partial_base + s of partial_stride slots per row
-  float qscale;        // scale * log2(e)
+  float qscale;        // |scale| * log2(e)
+  int qneg;            // scale < 0: the query's signs are flipped as it is loaded, so qscale >= 0
   // pool geometry in bytes (layout): K row (block p, token t, head h) at
   // k_pool + p*block_stride + t*row_stride + h*head_stride, V likewise;
   // span = what one block may touch from its first byte
@@ -62,6 +64,65 @@ struct PrefillArgs {
 // instead of the NaN that -inf - -inf would give.
 constexpr float kMaxFloor = -3.0e38f;
 constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold, log2 units
+
+// NaN-propagating maximum: v_maximum3_f32 on gfx950, which unlike fmaxf needs
+// no quieting of its inputs.  Masked scores enter as -inf, so only a NaN
+// input can make the result NaN.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max8(const float (&x)[8]) {
+  return vmax(vmax(vmax(vmax(x[0], x[1]), x[2]), vmax(vmax(x[3], x[4]), x[5])), vmax(vmax(x[6], x[7]), -INFINITY));
+}
+__device__ __forceinline__ float rows_maximum(float x) {  // over the 4 row groups of a 16x16 tile
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// The online-softmax update of one column tile for a pair of 16-key blocks.
+// x[i]: the lane's raw score (scale not applied) of key 4(i%4) + gq of block
+// i/4; ok[i] (boundary steps only): that key is visible to the lane's column.
+// Moves the running max m (log2 units) when a score exceeds it by more than
+// 2^8 (probabilities stay <= 256, exact in fp32 sums) and then rescales l and
+// the accumulators - a rare, wave-uniform branch; adds the probabilities to l
+// and returns them packed as the P.V B operand.  Absent keys get p = 0 by a
+// select after the exponential (not a -inf score, which times a zero scale
+// would be NaN).  qscale >= 0, so the max of the raw scores scales to the max
+// of the scaled ones.
+template <int DT, int VPL, bool kInterior>
+__device__ __forceinline__ uint4 softmax_pair(const float (&x)[8], const bool (&ok)[8], float qscale, float& m,
+                                              float& l, f32x4* acc) {
+  using Ops = MfmaOps<DT>;
+  float xm[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xm[i] = kInterior || ok[i] ? x[i] : -INFINITY;
+  const float smax = rows_maximum(max8(xm)) * qscale;
+  if (__ballot(smax > m + kRescaleLog2)) {
+    const float mn = fmaxf(m, smax);
+    const float alpha = fast_exp2(m - mn);
+    m = mn;
+    l *= alpha;
+#pragma unroll
+    for (int t = 0; t < VPL; ++t) acc[t] *= alpha;
+  }
+  const float nm = -m;
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float e = fast_exp2(fmaf(x[i], qscale, nm));
+    p[i] = kInterior || ok[i] ? e : 0.f;
+  }
+  l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  return make_uint4(Ops::pack(p[0], p[1]), Ops::pack(p[2], p[3]), Ops::pack(p[4], p[5]), Ops::pack(p[6], p[7]));
+}
+
+// A query operand chunk (8 16-bit values) as loaded, with every sign flipped
+// when the scale is negative.
+__device__ __forceinline__ uint4 query_chunk(const uint8_t* p, bool live, int qneg) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t f = qneg ? 0x80008000u : 0u;
+  return live ? make_uint4(v.x ^ f, v.y ^ f, v.z ^ f, v.w ^ f) : make_uint4(0, 0, 0, 0);
+}
 
 // The end of one column's work in one partition: lane (gq, col) holds
 // accumulator tile t register r = O[col][dim (D/16)(4gq + r) + t], the
@@ -186,10 +247,7 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
   {
     const uint8_t* qp = (const uint8_t*)a.query + qrow * ROWB + gq * 16;
 #pragma unroll
-    for (int c = 0; c < NKC; ++c) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qp + c * 64);
-      qop[c] = live ? v : make_uint4(0, 0, 0, 0);
-    }
+    for (int c = 0; c < NKC; ++c) qop[c] = query_chunk(qp + c * 64, live, a.qneg);
   }
 
   const uint32_t row_stride = a.row_stride;
@@ -300,33 +358,17 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
       sa = Ops::qk(kra[c], qop[c], sa);
       sb = Ops::qk(krb[c], qop[c], sb);
     }
-    float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+    const float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
     VT v[8] = {va_rows[0], va_rows[1], va_rows[2], va_rows[3], vb_rows[0], vb_rows[1], vb_rows[2], vb_rows[3]};
-    if constexpr (!kInterior) {
+    bool ok[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int key = key0 + (i >> 2) * 16 + 4 * (i & 3) + gq;
-        x[i] = key < lim ? x[i] : -INFINITY;
+    for (int i = 0; i < 8; ++i) {
+      const int key = key0 + (i >> 2) * 16 + 4 * (i & 3) + gq;
+      ok[i] = key < lim;
+      if constexpr (!kInterior)
         v[i] = key < end ? v[i] : VT{};  // rows past the last key (stale, even NaN) must not reach the MFMA
-      }
     }
-    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    const float smax = rows_max(mx) * a.qscale;
-    if (__ballot(smax > m + kRescaleLog2)) {
-      const float mn = fmaxf(m, smax);
-      const float alpha = fast_exp2(m - mn);
-      m = mn;
-      l *= alpha;
-#pragma unroll
-      for (int t = 0; t < VPL; ++t) acc[t] *= alpha;
-    }
-    const float nm = -m;
-    float p[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], a.qscale, nm));
-    l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    const uint4 pb = make_uint4(Ops::pack(p[0], p[1]), Ops::pack(p[2], p[3]), Ops::pack(p[4], p[5]),
-                                Ops::pack(p[6], p[7]));
+    const uint4 pb = softmax_pair<DT, VPL, kInterior>(x, ok, a.qscale, m, l, acc);
 #pragma unroll
     for (int t = 0; t < VPL; ++t) {
       const int w = t >> 1;
@@ -413,7 +455,6 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
   // more waves than instructions the last waves issue none)
   constexpr int DPW = (2 * KI + kWgWaves - 1) / kWgWaves;
   constexpr int KBYTES = BS * ROWB;
-  constexpr int RB = 2 * NP;                // ring blocks
   using VT = typename VRow<VPL>::T;
   static_assert(BS == 16 && (2 * KI) % DPW == 0, "tile shape");
   static_assert(NP == 3 || NP == 4, "the ring is unrolled for three or four pairs");
@@ -486,10 +527,7 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
   for (int tt = 0; tt < kWaveTiles; ++tt) {
     const uint8_t* qp = (const uint8_t*)a.query + qrow[tt] * ROWB + gq * 16;
 #pragma unroll
-    for (int c = 0; c < NKC; ++c) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qp + c * 64);
-      qop[tt][c] = live[tt] ? v : make_uint4(0, 0, 0, 0);
-    }
+    for (int c = 0; c < NKC; ++c) qop[tt][c] = query_chunk(qp + c * 64, live[tt], a.qneg);
   }
 
   // This wave's share of every block's loads: instructions wave*DPW ..
@@ -617,32 +655,11 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
         sa = Ops::qk(kra[c], qop[tt][c], sa);
         sb = Ops::qk(krb[c], qop[tt][c], sb);
       }
-      float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
-      if constexpr (!kInterior) {
+      const float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+      bool ok[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int key = key0 + (i >> 2) * 16 + 4 * (i & 3) + gq;
-          x[i] = key < lim[tt] ? x[i] : -INFINITY;
-        }
-      }
-      const float mx =
-          fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      const float smax = rows_max(mx) * a.qscale;
-      if (__ballot(smax > m[tt] + kRescaleLog2)) {
-        const float mn = fmaxf(m[tt], smax);
-        const float alpha = fast_exp2(m[tt] - mn);
-        m[tt] = mn;
-        l[tt] *= alpha;
-#pragma unroll
-        for (int t = 0; t < VPL; ++t) acc[tt][t] *= alpha;
-      }
-      const float nm = -m[tt];
-      float p[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], a.qscale, nm));
-      l[tt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      pb[tt] = make_uint4(Ops::pack(p[0], p[1]), Ops::pack(p[2], p[3]), Ops::pack(p[4], p[5]),
-                          Ops::pack(p[6], p[7]));
+      for (int i = 0; i < 8; ++i) ok[i] = key0 + (i >> 2) * 16 + 4 * (i & 3) + gq < lim[tt];
+      pb[tt] = softmax_pair<DT, VPL, kInterior>(x, ok, a.qscale, m[tt], l[tt], acc[tt]);
     }
 #pragma unroll
     for (int t = 0; t < VPL; ++t) {
@@ -656,38 +673,51 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
       for (int tt = 0; tt < kWaveTiles; ++tt) acc[tt][t] = Ops::qk(vt, pb[tt], acc[tt][t]);
     }
   };
-  // One ring step: wait for this wave's loads of the pair in slots (xa, xb),
-  // barrier (every wave's loads of it have landed and every wave has finished
-  // the previous step), refill the previous step's slots (xp, xq) with the
-  // blocks 2*(NP-1) ahead, then compute.
-  auto ring_step = [&](int jp, int xa, int xb, int xp, int xq) {
+  // One ring step over pair p, held in ring pair `sp` (slots 2sp, 2sp+1):
+  // wait for this wave's loads of it, barrier (every wave's loads of it have
+  // landed and every wave has finished the previous step), refill the
+  // previous step's pair with the blocks 2*(NP-1) ahead, then compute.
+  auto ring_step = [&](auto sp, int p, auto interior) {
+    constexpr int xa = 2 * decltype(sp)::value, xp = 2 * ((decltype(sp)::value + NP - 1) % NP);
     wait_vmcnt<(NP - 2) * 2 * DPW>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    load_block(jp + 2 * (NP - 1), xp);
-    load_block(jp + 2 * (NP - 1) + 1, xq);
+    load_block(2 * p + 2 * (NP - 1), xp);
+    load_block(2 * p + 2 * (NP - 1) + 1, xp + 1);
     __builtin_amdgcn_sched_barrier(0);
-    const int key0 = start + jp * BS;
-    if (key0 < end) {
-      if (key0 + 2 * BS <= safe) step(xa, xb, key0, std::true_type{});
-      else step(xa, xb, key0, std::false_type{});
-    }
+    step(xa, xa + 1, start + 2 * p * BS, interior);
   };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
 
+  // Pairs with a key below `end` run, the others are never started (the
+  // step count is the same for every wave, so the barriers match).  Pairs
+  // wholly below this wave's `safe` take the unmasked step, in whole turns of
+  // the ring, so that loop is straight-line code; the rest (the causal edge,
+  // the partition's last pair, a turn's remainder) take the masked one, also
+  // in turns of the ring (a step chosen per pair by its slot would keep the
+  // registers of every slot's variant live: occupancy 1 instead of 2).
+  const int npairs = (nblk + 1) / 2;
+  const int nint = min(npairs, max(0, (safe - start) / (2 * BS)));
 #pragma unroll
   for (int x = 0; x < 2 * (NP - 1); ++x) load_block(x, x);
-  for (int j = 0; j < nblk; j += RB) {
-    if constexpr (NP == 3) {
-      ring_step(j, 0, 1, 4, 5);
-      ring_step(j + 2, 2, 3, 0, 1);
-      ring_step(j + 4, 4, 5, 2, 3);
-    } else {
-      ring_step(j, 0, 1, 6, 7);
-      ring_step(j + 2, 2, 3, 0, 1);
-      ring_step(j + 4, 4, 5, 2, 3);
-      ring_step(j + 6, 6, 7, 4, 5);
-    }
+  int p = 0;
+  for (; p + NP <= nint; p += NP) {
+    ring_step(C0{}, p, std::true_type{});
+    ring_step(C1{}, p + 1, std::true_type{});
+    ring_step(C2{}, p + 2, std::true_type{});
+    if constexpr (NP == 4) ring_step(C3{}, p + 3, std::true_type{});
   }
+  for (; p < npairs; p += NP) {
+    ring_step(C0{}, p, std::false_type{});
+    if (p + 1 < npairs) ring_step(C1{}, p + 1, std::false_type{});
+    if (p + 2 < npairs) ring_step(C2{}, p + 2, std::false_type{});
+    if constexpr (NP == 4)
+      if (p + 3 < npairs) ring_step(C3{}, p + 3, std::false_type{});
+  }
+  wait_vmcnt<0>();  // no load into this workgroup's LDS outlives it
 
 #pragma unroll
   for (int tt = 0; tt < kWaveTiles; ++tt) {
@@ -874,6 +904,14 @@ int prefill_rows(void* out, const void* query, const pa::PoolView& pv, const int
   return pa::launch_status();
 }
 
+// Scores are scaled by |scale| (in log2 units for exp2); a negative scale
+// flips the query's signs instead, so the tiles' running max of the raw
+// scores stays the max of the scaled ones.
+void set_scale(PrefillArgs* a, float scale) {
+  a->qscale = std::fabs(scale) * 1.44269504088896340736f;  // log2(e)
+  a->qneg = scale < 0.f;
+}
+
 void set_pool(PrefillArgs* a, const pa::PoolView& pv, const pa::DecodeShape& s) {
   a->k_pool = pv.k;
   a->v_pool = pv.v;
@@ -969,7 +1007,7 @@ extern "C" int pa_prefill_attention_layout(void* out, const void* query, const v
   a.num_parts = parts;
   a.groups = pg.groups;
   a.tiles = pg.tiles;
-  a.qscale = scale * 1.44269504088896340736f;  // log2(e)
+  set_scale(&a, scale);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * pg.waves), 0, st, a);
   rc = pa::launch_status();
@@ -1050,7 +1088,7 @@ extern "C" int pa_decode_attention_shared_prefix(
   a.part_tokens = pa::kSharedPrefixPartition;
   a.groups = gd.groups;
   a.partial_stride = slots;
-  a.qscale = scale * 1.44269504088896340736f;
+  set_scale(&a, scale);
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   // Prefix pass: one "sequence" per group whose rows are the members' queries
