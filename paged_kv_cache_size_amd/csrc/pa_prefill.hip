@@ -124,25 +124,64 @@ __device__ __forceinline__ uint4 query_chunk(const uint8_t* p, bool live, int qn
   return live ? make_uint4(v.x ^ f, v.y ^ f, v.z ^ f, v.w ^ f) : make_uint4(0, 0, 0, 0);
 }
 
+// Four consecutive output elements from four floats (8 bytes for 16-bit
+// types, 16 for fp32).
+template <int DT>
+__device__ __forceinline__ void store4(uint8_t* dst, const float (&f)[4]) {
+  if constexpr (DT == DT_F32) {
+    *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+  } else {
+    auto bits = [](float x) { return DT == DT_BF16 ? float_to_bf16_bits(x) : float_to_f16_bits(x); };
+    *reinterpret_cast<uint2*>(dst) = make_uint2(bits(f[0]) | (bits(f[1]) << 16), bits(f[2]) | (bits(f[3]) << 16));
+  }
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane 4a + b receives element
+// b of the four 16-bit elements addressed by lanes a, a + 4, a + 8, a + 12.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint8_t* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)((__attribute__((address_space(3))) uint8_t*)p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// XOR swizzle of a V row's 16-byte chunks in LDS for the transposed reads:
+// a 32-lane half of one read touches 8 rows (4 rows of two row groups) at the
+// same pair of chunks; row t's chunks are moved by 2*f(t) with f distinct
+// over those rows, so the 8 pairs land on distinct banks.  (Rows of 8 chunks
+// pair up by parity inside 256 bytes, so f keeps only the row's group.)
+template <int CPR>
+__device__ __forceinline__ int vswz_t(int t) {
+  return 2 * ((((t >> 2) & 3) | ((t & 1) << 2)) & (CPR / 2 - 1));
+}
+
 // The end of one column's work in one partition: lane (gq, col) holds
-// accumulator tile t register r = O[col][dim (D/16)(4gq + r) + t], the
-// column's running max m (log2 units) and denominator lt.
+// accumulator tile t register r = O[col][dim (D/16)(4gq + r) + t] (V rows
+// paired in registers) or O[col][dim 16t + 4gq + r] (kTr: V read transposed
+// from LDS), the column's running max m (log2 units) and denominator lt.
 //  * slot mode (partial_base >= 0): partials into slot partial_base + s,
 //    m = -inf when the column saw no key;
 //  * a column whose keys fit one partition: its output row;
 //  * otherwise: partials for the combine kernel.
-template <int DT, int D>
+template <int DT, int D, bool kTr = false>
 __device__ __forceinline__ void store_column(const PrefillArgs& a, const f32x4* acc, float m, float lt, size_t qrow,
                                              int s, int col_parts, int gq) {
-  constexpr int VPL = D / 16, DPL = 4 * VPL, ROWB = D * 2;
+  constexpr int VPL = D / 16, DPL = 4 * VPL, ROWB = D * 2, EB = DT == DT_F32 ? 4 : 2;
   auto store_partial = [&](size_t idx, float mm) {
-    float* dst = a.ws_acc + idx * D + gq * DPL;
+    if constexpr (kTr) {
+      float* dst = a.ws_acc + idx * D + 4 * gq;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+      for (int t = 0; t < VPL; ++t)
+        *reinterpret_cast<float4*>(dst + 16 * t) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+    } else {
+      float* dst = a.ws_acc + idx * D + gq * DPL;
 #pragma unroll
-      for (int t = 0; t < VPL; t += 4)
-        *reinterpret_cast<float4*>(dst + VPL * r + t) =
-            make_float4(acc[t][r], acc[t + 1][r], acc[t + 2][r], acc[t + 3][r]);
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < VPL; t += 4)
+          *reinterpret_cast<float4*>(dst + VPL * r + t) =
+              make_float4(acc[t][r], acc[t + 1][r], acc[t + 2][r], acc[t + 3][r]);
+    }
     if (gq == 0) a.ws_ml[idx] = make_float2(mm, lt);
   };
   if (a.partial_base >= 0) {
@@ -152,12 +191,21 @@ __device__ __forceinline__ void store_column(const PrefillArgs& a, const f32x4* 
   if (s >= col_parts) return;  // no keys of this column here
   if (col_parts == 1) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    float o[DPL];
+    if constexpr (kTr) {
+      uint8_t* dst = (uint8_t*)a.out + qrow * ROWB + 4 * gq * EB;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+      for (int t = 0; t < VPL; ++t) {
+        const float o[4] = {acc[t][0] * inv, acc[t][1] * inv, acc[t][2] * inv, acc[t][3] * inv};
+        store4<DT>(dst + 16 * t * EB, o);
+      }
+    } else {
+      float o[DPL];
 #pragma unroll
-      for (int t = 0; t < VPL; ++t) o[VPL * r + t] = acc[t][r] * inv;
-    store_row<DT, DPL>((uint8_t*)a.out + qrow * ROWB + gq * DPL * 2, o);
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < VPL; ++t) o[VPL * r + t] = acc[t][r] * inv;
+      store_row<DT, DPL>((uint8_t*)a.out + qrow * ROWB + gq * DPL * 2, o);
+    }
   } else {
     store_partial(qrow * a.num_parts + s, m);
   }
@@ -455,7 +503,6 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
   // more waves than instructions the last waves issue none)
   constexpr int DPW = (2 * KI + kWgWaves - 1) / kWgWaves;
   constexpr int KBYTES = BS * ROWB;
-  using VT = typename VRow<VPL>::T;
   static_assert(BS == 16 && (2 * KI) % DPW == 0, "tile shape");
   static_assert(NP == 3 || NP == 4, "the ring is unrolled for three or four pairs");
 
@@ -550,7 +597,7 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
     const int sl = 64 * idx + lane, t = sl / CPR, q = sl % CPR;
     const int tr = GATHER ? t % pool_bs : t;  // the row inside its pool block
     rblk[i] = GATHER ? t / pool_bs : 0;
-    goff[i] = (uint32_t)tr * row_stride + hoff + (uint32_t)((is_k[i] ? (q ^ kswz_t<CPR>(t)) : q) * 16);
+    goff[i] = (uint32_t)tr * row_stride + hoff + (uint32_t)((q ^ (is_k[i] ? kswz_t<CPR>(t) : vswz_t<CPR>(t))) * 16);
     lds_off[i] = idx * 1024;
   }
   uint32_t kread[NKC];  // QK A operand: token 4*(col%4) + col/4, chunk 4c + gq
@@ -559,7 +606,16 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
 #pragma unroll
     for (int c = 0; c < NKC; ++c) kread[c] = (uint32_t)(t * CPR + ((4 * c + gq) ^ kswz_t<CPR>(t))) * 16;
   }
-  const uint32_t vread = (uint32_t)gq * ROWB + col * VPL * 2;  // row gq (+4i), this lane's dims
+  // P.V A operand of output tile t (dims 16t + col) by transposed reads: this
+  // lane addresses row 4(col / 4) + gq, dims 16t + 4(col % 4) .. + 3, so that
+  // lane (gq, col) receives that dim of rows gq, gq + 4, gq + 8, gq + 12.
+  uint32_t vtr[VPL];
+  {
+    const int r = 4 * (col >> 2) + gq;
+#pragma unroll
+    for (int t = 0; t < VPL; ++t)
+      vtr[t] = (uint32_t)(r * ROWB + ((2 * t + ((col & 3) >> 1)) ^ vswz_t<CPR>(r)) * 16 + (col & 1) * 8);
+  }
 
   constexpr int XB = NP > 3 ? KBYTES : 16;  // slots 6 and 7 exist with four pairs
   __shared__ __attribute__((aligned(1024))) uint8_t ks0[KBYTES], ks1[KBYTES], ks2[KBYTES], ks3[KBYTES],
@@ -628,22 +684,26 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
   auto step = [&](int xa, int xb, int key0, auto interior) {
     constexpr bool kInterior = decltype(interior)::value;
     uint4 kra[NKC], krb[NKC];
-    VT v[8];
+    uint2 va[VPL], vb[VPL];  // keys 4k + gq of block A (B), k = 0..3, at dim 16t + col
 #pragma unroll
     for (int c = 0; c < NKC; ++c) {
       kra[c] = *reinterpret_cast<const uint4*>(kslot(xa) + kread[c]);
       krb[c] = *reinterpret_cast<const uint4*>(kslot(xb) + kread[c]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[i] = *reinterpret_cast<const VT*>(vslot(xa) + vread + 4 * i * ROWB);
-      v[4 + i] = *reinterpret_cast<const VT*>(vslot(xb) + vread + 4 * i * ROWB);
+    for (int t = 0; t < VPL; ++t) {
+      va[t] = lds_read_tr16(vslot(xa) + vtr[t]);
+      vb[t] = lds_read_tr16(vslot(xb) + vtr[t]);
     }
-    if constexpr (!kInterior) {
+    if constexpr (!kInterior) {  // rows past the last key (stale, even NaN) must not reach the MFMA
+      auto keep = [&](int k0) {
+        return (k0 + gq < end ? 0xffffu : 0u) | (k0 + 4 + gq < end ? 0xffff0000u : 0u);
+      };
+      const uint2 ma = make_uint2(keep(key0), keep(key0 + 8)), mb = make_uint2(keep(key0 + 16), keep(key0 + 24));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int key = key0 + (i >> 2) * 16 + 4 * (i & 3) + gq;
-        v[i] = key < end ? v[i] : VT{};  // rows past the last key (stale, even NaN) must not reach the MFMA
+      for (int t = 0; t < VPL; ++t) {
+        va[t] = make_uint2(va[t].x & ma.x, va[t].y & ma.y);
+        vb[t] = make_uint2(vb[t].x & mb.x, vb[t].y & mb.y);
       }
     }
     uint4 pb[kWaveTiles];
@@ -663,12 +723,7 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
     }
 #pragma unroll
     for (int t = 0; t < VPL; ++t) {
-      const int w = t >> 1;
-      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-      const uint4 vt = make_uint4(__builtin_amdgcn_perm(vword<VPL>(v[1], w), vword<VPL>(v[0], w), sel),
-                                  __builtin_amdgcn_perm(vword<VPL>(v[3], w), vword<VPL>(v[2], w), sel),
-                                  __builtin_amdgcn_perm(vword<VPL>(v[5], w), vword<VPL>(v[4], w), sel),
-                                  __builtin_amdgcn_perm(vword<VPL>(v[7], w), vword<VPL>(v[6], w), sel));
+      const uint4 vt = make_uint4(va[t].x, va[t].y, vb[t].x, vb[t].y);
 #pragma unroll
       for (int tt = 0; tt < kWaveTiles; ++tt) acc[tt][t] = Ops::qk(vt, pb[tt], acc[tt][t]);
     }
@@ -722,7 +777,7 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
 #pragma unroll
   for (int tt = 0; tt < kWaveTiles; ++tt) {
     const float lt = rows_sum(l[tt]);
-    if (live[tt]) store_column<DT, D>(a, acc[tt], m[tt], lt, qrow[tt], s, col_parts[tt], gq);
+    if (live[tt]) store_column<DT, D, true>(a, acc[tt], m[tt], lt, qrow[tt], s, col_parts[tt], gq);
   }
 }
 
