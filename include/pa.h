@@ -166,7 +166,8 @@ size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_heads, int32_t
  *   k_pool, v_pool [*, block_size, num_kv_heads, head_dim], dtype
  *   block_tables   int32 [num_seqs, max_blocks_per_seq]
  *   context_lens   int32 [num_seqs], each in [1, max_context_len]
- *   scale          softmax scale, usually head_dim^-1/2 (HB, "分页注意力")
+ *   scale          softmax scale, usually head_dim^-1/2 (HB, "分页注意力"); any finite value,
+ *                  negative and zero included (zero: the plain mean of the visible V rows)
  *   workspace      device buffer of workspace_bytes >=
  *                  pa_decode_workspace_bytes(...), or NULL/0 when
  *                  max_context_len needs a single partition

@@ -9,13 +9,14 @@
 //
 // The tile is the decode MFMA tile with its 16 columns re-purposed: a column
 // is a (new token, query head) pair of one KV head's group instead of one
-// query head of the single new token.  Per 16-token block of the context:
-//   QK:  S^T[key][column]  = K[16 x D] . Q^T[D x 16]   mfma_f32_16x16x32 (D/32)
-//   PV:  O^T[dim][column] += V^T[16 x 16] . P^T          mfma_f32_16x16x16 (D/16)
-// with the same operand layouts as the decode kernel (K through LDS in the
-// swizzled row order, V row-coalesced into registers and paired by v_perm).
-// Causality is a per-column key limit applied to the scores; V rows past the
-// partition's last key are zeroed, so stale slots never reach the MFMA.
+// query head of the single new token.  Per pair of 16-token blocks (32 keys):
+//   QK:  S^T[key][column]  = K[16 x D] . Q^T[D x 16]   mfma_f32_16x16x32 (D/32 per block)
+//   PV:  O^T[dim][column] += V^T[16 x 32] . P^T          mfma_f32_16x16x32 (D/16)
+// K goes through LDS in a swizzled row order.  The per-wave tile pairs V rows
+// (loaded into registers) by v_perm; the cooperative tile reads V transposed
+// from LDS (ds_read_b64_tr_b16).  Causality is a per-column key limit applied
+// to the probabilities; V rows past the partition's last key are zeroed, so
+// stale slots never reach the MFMA.
 // Long contexts split into partitions like decode; the partials are merged per
 // (query row, head) by the combine kernel below.
 #include <hip/hip_runtime.h>
@@ -471,14 +472,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Cooperative form for wide column ranges (long varlen rows, chunked
-// prefill): the waves of a workgroup take 32 consecutive columns each of one
-// (sequence, KV head unit), as two 16-column tiles, and share
-// one copy of each K/V block.  The blocks stream through an LDS ring of
-// 2 * NP blocks, K swizzled as in the per-wave tile and V row-major, filled by
-// direct-to-LDS loads that the waves split between them; one barrier
-// per two-block step publishes a pair and frees the pair read in the step
-// before.  Each wave reads K (the QK A operand) and its V rows (the P.V A
-// operand) from LDS once per step and applies them to both of its tiles.
+// prefill): the waves of a workgroup take 16 * TILES consecutive columns each
+// of one (sequence, KV head unit) and share one copy of each K/V block.  The
+// blocks stream through an LDS ring of 2 * NP blocks, K and V each with its
+// own chunk swizzle, filled by direct-to-LDS loads that the waves split
+// between them; one barrier per two-block step publishes a pair and frees the
+// pair read in the step before.  Each wave reads K (the QK A operand) and V
+// transposed (the P.V A operand) from LDS once per step and applies them to
+// all of its tiles.
 // Arithmetic per tile is that of prefill_mfma_kernel: 32-key steps, P.V on
 // 16x16x32, lazily moved running max, mask-free interior steps.
 // WAVES waves of TILES 16-column tiles each: 128 columns for long runs of new
