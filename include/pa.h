@@ -105,7 +105,8 @@ typedef enum pa_kv_layout {
  * is >= max_blocks_per_seq gets slot -1 (pa_reshape_and_cache skips it).
  * Errors: INVALID_ARG for null pointers, num_seqs/num_tokens/block_size/
  * max_blocks_per_seq <= 0, or num_tokens != num_seqs when query_start_loc is
- * NULL.
+ * NULL.  An empty batch (num_seqs == num_tokens == 0) is allowed and enqueues
+ * nothing; its pointers may be NULL.
  */
 int pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
                     const int32_t* context_lens, const int32_t* query_start_loc,
@@ -182,6 +183,10 @@ size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_heads, int32_t
  * num_heads % num_kv_heads != 0, max_context_len > max_blocks_per_seq *
  * block_size, or a non-finite scale; UNSUPPORTED for other dtype /
  * head_dim / block_size; WORKSPACE if the workspace is too small.
+ * num_seqs == 0 (an empty batch) is allowed and enqueues nothing; the
+ * pointers other than v_pool may then be NULL.  The same holds for
+ * pa_decode_partitions, pa_decode_combine and
+ * pa_decode_attention_shared_prefix.
  */
 int pa_decode_attention(void* out, const void* query, const void* k_pool, const void* v_pool,
                         const int32_t* block_tables, const int32_t* context_lens,
@@ -292,7 +297,8 @@ int32_t pa_decode_plan_partition_size(int32_t num_seqs, int32_t num_heads, int32
  * or a size pa_decode_attention_ex accepts.  The workspace
  * must hold pa_prefill_workspace_bytes(...) for the same partition_size (0 when
  * the context fits one partition).  Rows past query_start_loc[num_seqs] are
- * not written.  Device contents are the caller's contract (n_b <= L_b <=
+ * not written.  num_tokens == 0 is allowed and enqueues nothing (pointers may
+ * then be NULL).  Device contents are the caller's contract (n_b <= L_b <=
  * max_context_len, n_b <= max_query_len, valid block ids).
  */
 int pa_prefill_attention(void* out, const void* query, const void* k_pool, const void* v_pool,

@@ -282,7 +282,7 @@ def pa_decode_attention(query, k_pool, v_pool, block_tables, context_lens, scale
     if block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_tables / context_lens batch mismatch")
     if max_context_len is None:
-        max_context_len = int(context_lens.max().item())
+        max_context_len = int(context_lens.max().item()) if B else 0
     mb = block_tables.shape[1]
     if out is None:
         out = torch.empty_like(query)

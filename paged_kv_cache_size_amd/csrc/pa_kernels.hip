@@ -873,6 +873,7 @@ int resident_per_cu(const void* fn, int threads) {
 extern "C" int pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens,
                                const int32_t* query_start_loc, int32_t num_seqs, int32_t max_blocks_per_seq,
                                int32_t block_size, int64_t num_tokens, void* stream) {
+  if (num_seqs == 0 && num_tokens == 0) return PA_OK;  // an empty batch
   int rc = pa::check_slot_mapping(slot_mapping, block_tables, context_lens, query_start_loc, num_seqs,
                                   max_blocks_per_seq, block_size, num_tokens);
   if (rc != PA_OK) return rc;
@@ -963,6 +964,7 @@ extern "C" int pa_decode_attention_layout(void* out, const void* query, const vo
                                           int32_t max_context_len, float scale, pa_dtype dtype, void* workspace,
                                           size_t workspace_bytes, int32_t partition_size, pa_kv_layout layout,
                                           void* stream) {
+  if (num_seqs == 0) return PA_OK;  // an empty batch
   const pa::DecodeShape shp{num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                             max_context_len, (int)dtype};
   pa::PoolView pv;
@@ -1009,6 +1011,7 @@ extern "C" int pa_decode_partitions(void* out, const void* query, const void* k_
                                     pa_dtype dtype, void* workspace, size_t workspace_bytes,
                                     int32_t partition_size, void* stream) {
   if (partition_size == 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;  // an empty batch
   const pa::DecodeShape shp{num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                             max_context_len, (int)dtype};
   DecodePlan plan;
@@ -1024,6 +1027,7 @@ extern "C" int pa_decode_partitions(void* out, const void* query, const void* k_
 extern "C" int pa_decode_combine(void* out, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                                  int32_t head_dim, int32_t max_context_len, int32_t partition_size, pa_dtype dtype,
                                  const void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs == 0) return PA_OK;  // an empty batch
   int rc = pa::check_combine(out, context_lens, num_seqs, num_heads, head_dim, max_context_len, partition_size,
                              (int)dtype);
   if (rc != PA_OK) return rc;

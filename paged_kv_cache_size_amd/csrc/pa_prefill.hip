@@ -395,9 +395,6 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
   // column col.  P.V runs on mfma_f32_16x16x32 with the contraction index
   // k = 8gq + j <-> key 4(j % 4) + gq of block A (j < 4) or B (j >= 4): the
   // lane's own score registers are its B operand, its own V rows its A operand.
-  // The running max moves only when a score exceeds it by more than 2^8
-  // (probabilities stay <= 256, exact in fp32 sums), so the rescale of the
-  // accumulators is a rare, wave-uniform branch.
   auto step = [&](const uint4* kra, const uint4* krb, const VT* va_rows, const VT* vb_rows, int key0,
                   auto interior) {
     constexpr bool kInterior = decltype(interior)::value;
@@ -1005,6 +1002,7 @@ extern "C" int pa_prefill_attention_layout(void* out, const void* query, const v
                                            int32_t max_context_len, float scale, pa_dtype dtype, void* workspace,
                                            size_t workspace_bytes, int32_t partition_size, pa_kv_layout layout,
                                            void* stream) {
+  if (num_tokens == 0) return PA_OK;  // no new tokens
   const pa::PrefillShape shp{{num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                               max_context_len, (int)dtype},
                              num_tokens,
@@ -1108,6 +1106,7 @@ extern "C" int pa_decode_attention_shared_prefix(
     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
     int32_t max_context_len, int32_t max_prefix_len, float scale, pa_dtype dtype, void* workspace,
     size_t workspace_bytes, void* stream) {
+  if (num_seqs == 0) return PA_OK;  // an empty batch
   const pa::PrefillShape shp{{num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                               max_context_len, (int)dtype},
                              num_seqs,

@@ -55,7 +55,7 @@ def decode(**kw):
     (dict(k=None), B.PA_ERR_INVALID_ARG),
     (dict(bt=None), B.PA_ERR_INVALID_ARG),
     (dict(lens=None), B.PA_ERR_INVALID_ARG),
-    (dict(B=0), B.PA_ERR_INVALID_ARG),
+    (dict(B=-1), B.PA_ERR_INVALID_ARG),
     (dict(H=-1), B.PA_ERR_INVALID_ARG),
     (dict(H=6, Hkv=4), B.PA_ERR_INVALID_ARG),
     (dict(maxlen=129), B.PA_ERR_INVALID_ARG),     # > mb * bs
@@ -79,6 +79,26 @@ def decode(**kw):
 ])
 def test_decode_argument_checks(kw, status):
     assert decode(**kw) == status
+
+
+def test_empty_batches_enqueue_nothing():
+    # no sequence (decode) or no new token (prefill) is a valid call that
+    # touches no pointer, null ones included
+    lib = B.lib()
+    nul = dict(out=None, query=None, k=None, v=FAKE, bt=None, lens=None)
+    assert decode(B=0, ps=0, **nul) == B.PA_OK
+    assert decode(B=0, ps=16, **nul) == B.PA_OK
+    assert lib.pa_decode_partitions(None, None, None, None, None, None, 0, 8, 2, 128, 16, 8, 128, 0.088,
+                                    B.PA_BF16, None, 0, 16, None) == B.PA_OK
+    assert lib.pa_decode_combine(None, None, 0, 8, 128, 128, 16, B.PA_BF16, None, 0, None) == B.PA_OK
+    assert lib.pa_slot_mapping(None, None, None, None, 0, 8, 16, 0, None) == B.PA_OK
+    assert prefill(T=0, B=0, out=None, query=None, k=None, bt=None, lens=None, qsl=None) == B.PA_OK
+    assert lib.pa_decode_attention_shared_prefix(None, None, None, None, None, None, None, None, None, 0, 0, 0, 8,
+                                                 2, 128, 16, 8, 128, 0, 0.088, B.PA_BF16, None, 0,
+                                                 None) == B.PA_OK
+    # sizes are still checked where the call has work
+    assert lib.pa_slot_mapping(None, None, None, None, 0, 8, 16, 5, None) == B.PA_ERR_INVALID_ARG
+    assert decode(B=-1, **nul) == B.PA_ERR_INVALID_ARG
 
 
 def test_workspace_sizes():
@@ -108,7 +128,7 @@ def prefill(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(qsl=None), B.PA_ERR_INVALID_ARG),
     (dict(out=None), B.PA_ERR_INVALID_ARG),
-    (dict(T=0), B.PA_ERR_INVALID_ARG),
+    (dict(T=-1), B.PA_ERR_INVALID_ARG),
     (dict(mq=0), B.PA_ERR_INVALID_ARG),
     (dict(mq=41), B.PA_ERR_INVALID_ARG),          # longer than all rows
     (dict(mq=40, maxlen=32, mb=2), B.PA_ERR_INVALID_ARG),  # more new tokens than context
@@ -185,7 +205,7 @@ def test_slot_mapping_argument_checks():
     f = B.lib().pa_slot_mapping
     assert f(None, FAKE, FAKE, None, 4, 8, 16, 4, None) == B.PA_ERR_INVALID_ARG
     assert f(FAKE, FAKE, FAKE, None, 4, 8, 16, 5, None) == B.PA_ERR_INVALID_ARG  # decode needs num_tokens == num_seqs
-    assert f(FAKE, FAKE, FAKE, None, 0, 8, 16, 0, None) == B.PA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, None, -1, 8, 16, -1, None) == B.PA_ERR_INVALID_ARG
     assert f(FAKE, FAKE, FAKE, FAKE, 4, 8, 0, 9, None) == B.PA_ERR_INVALID_ARG
 
 

@@ -272,6 +272,29 @@ def test_zero_length_context_gives_zeros():
         assert np.max(np.abs(out[[1, 3]].cpu().numpy() - ref)) <= 1e-5
 
 
+@pytest.mark.parametrize("name", ["tiny_f32", "qwen1p5b_bf16"])
+def test_empty_batch_changes_nothing(name):
+    # no sequence: slot mapping, the pool write, decode and prefill all return
+    # empty results and leave the pools bitwise untouched
+    w = W.make_workload(name)
+    say(f"empty batch on the pools of {name}")
+    t = W.make_tensors(w, 0, DEV)
+    kp0, vp0 = t["k_pool"].clone(), t["v_pool"].clone()
+    H, D = t["query"].shape[1:]
+    bt = torch.empty((0, w.block_tables.shape[1]), dtype=torch.int32, device=DEV)
+    lens = torch.empty(0, dtype=torch.int32, device=DEV)
+    slots = PB.pa_slot_mapping(bt, lens, w.block_size)
+    PB.pa_reshape_and_cache(t["key"][:0], t["value"][:0], t["k_pool"], t["v_pool"], slots)
+    q = t["query"][:0]
+    out = PB.pa_decode_attention(q, t["k_pool"], t["v_pool"], bt, lens, w.scale)
+    out16 = PB.pa_decode_attention(q, t["k_pool"], t["v_pool"], bt, lens, w.scale, 64, partition_size=16)
+    qsl = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pre = PB.pa_prefill_attention(q, t["k_pool"], t["v_pool"], bt, lens, qsl, w.scale, 0, 64)
+    torch.cuda.synchronize()
+    assert slots.shape == (0,) and out.shape == (0, H, D) and out16.shape == (0, H, D) and pre.shape == (0, H, D)
+    assert torch.equal(bits(t["k_pool"]), bits(kp0)) and torch.equal(bits(t["v_pool"]), bits(vp0))
+
+
 # ------------------------------------------------------------------ properties
 
 def test_block_permutation_gives_bitwise_identical_output():
