@@ -719,12 +719,18 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
       for (int i = 0; i < 8; ++i) ok[i] = key0 + (i >> 2) * 16 + 4 * (i & 3) + gq < lim[tt];
       pb[tt] = softmax_pair<DT, VPL, kInterior>(x, ok, a.qscale, m[tt], l[tt], acc[tt]);
     }
+    // The P.V MFMAs issue at raised wave priority: the wave's 16 independent
+    // MFMAs go out back to back while the SIMD's other wave (another
+    // workgroup's) runs its softmax beside them.  Measured 3% faster on
+    // chunked prefill; the same around the QK MFMAs gained nothing.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < VPL; ++t) {
       const uint4 vt = make_uint4(va[t].x, va[t].y, vb[t].x, vb[t].y);
 #pragma unroll
       for (int tt = 0; tt < kWaveTiles; ++tt) acc[tt][t] = Ops::qk(vt, pb[tt], acc[tt][t]);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   // One ring step over pair p, held in ring pair `sp` (slots 2sp, 2sp+1):
   // wait for this wave's loads of it, barrier (every wave's loads of it have
