@@ -83,16 +83,19 @@ __device__ __forceinline__ float rows_maximum(float x) {  // over the 4 row grou
 // The online-softmax update of one column tile for a pair of 16-key blocks.
 // x[i]: the lane's raw score (scale not applied) of key 4(i%4) + gq of block
 // i/4; ok[i] (boundary steps only): that key is visible to the lane's column.
+// l (kMfmaSum false) or lacc (true): the running denominator.
 // Moves the running max m (log2 units) when a score exceeds it by more than
 // 2^8 (probabilities stay <= 256, exact in fp32 sums) and then rescales l and
 // the accumulators - a rare, wave-uniform branch; adds the probabilities to l
-// and returns them packed as the P.V B operand.  Absent keys get p = 0 by a
+// (kMfmaSum: the caller sums them on the matrix core instead, into *lacc,
+// which the rescale then scales) and returns them packed as the P.V B
+// operand.  Absent keys get p = 0 by a
 // select after the exponential (not a -inf score, which times a zero scale
 // would be NaN).  qscale >= 0, so the max of the raw scores scales to the max
 // of the scaled ones.
-template <int DT, int VPL, bool kInterior>
+template <int DT, int VPL, bool kInterior, bool kMfmaSum = false>
 __device__ __forceinline__ uint4 softmax_pair(const float (&x)[8], const bool (&ok)[8], float qscale, float& m,
-                                              float& l, f32x4* acc) {
+                                              float* l, f32x4* acc, f32x4* lacc) {
   using Ops = MfmaOps<DT>;
   float xm[8];
 #pragma unroll
@@ -102,7 +105,10 @@ __device__ __forceinline__ uint4 softmax_pair(const float (&x)[8], const bool (&
     const float mn = fmaxf(m, smax);
     const float alpha = fast_exp2(m - mn);
     m = mn;
-    l *= alpha;
+    if constexpr (kMfmaSum)
+      *lacc *= alpha;
+    else
+      *l *= alpha;
 #pragma unroll
     for (int t = 0; t < VPL; ++t) acc[t] *= alpha;
   }
@@ -113,7 +119,7 @@ __device__ __forceinline__ uint4 softmax_pair(const float (&x)[8], const bool (&
     const float e = fast_exp2(fmaf(x[i], qscale, nm));
     p[i] = kInterior || ok[i] ? e : 0.f;
   }
-  l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  if constexpr (!kMfmaSum) *l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   return make_uint4(Ops::pack(p[0], p[1]), Ops::pack(p[2], p[3]), Ops::pack(p[4], p[5]), Ops::pack(p[6], p[7]));
 }
 
@@ -414,7 +420,7 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
       if constexpr (!kInterior)
         v[i] = key < end ? v[i] : VT{};  // rows past the last key (stale, even NaN) must not reach the MFMA
     }
-    const uint4 pb = softmax_pair<DT, VPL, kInterior>(x, ok, a.qscale, m, l, acc);
+    const uint4 pb = softmax_pair<DT, VPL, kInterior>(x, ok, a.qscale, m, &l, acc, nullptr);
 #pragma unroll
     for (int t = 0; t < VPL; ++t) {
       const int w = t >> 1;
@@ -632,11 +638,12 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
   for (int tt = 0; tt < kWaveTiles; ++tt)
 #pragma unroll
     for (int t = 0; t < VPL; ++t) acc[tt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[kWaveTiles], l[kWaveTiles];
+  float m[kWaveTiles];
+  f32x4 lacc[kWaveTiles];  // every register: the column's denominator
 #pragma unroll
   for (int tt = 0; tt < kWaveTiles; ++tt) {
     m[tt] = kMaxFloor;
-    l[tt] = 0.f;
+    lacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // Loads past the partition go through an empty descriptor (zeros, no
@@ -717,7 +724,7 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
       bool ok[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) ok[i] = key0 + (i >> 2) * 16 + 4 * (i & 3) + gq < lim[tt];
-      pb[tt] = softmax_pair<DT, VPL, kInterior>(x, ok, a.qscale, m[tt], l[tt], acc[tt]);
+      pb[tt] = softmax_pair<DT, VPL, kInterior, true>(x, ok, a.qscale, m[tt], nullptr, acc[tt], &lacc[tt]);
     }
     // The P.V MFMAs issue at raised wave priority: the wave's 16 independent
     // MFMAs go out back to back while the SIMD's other wave (another
@@ -729,6 +736,14 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
       const uint4 vt = make_uint4(va[t].x, va[t].y, vb[t].x, vb[t].y);
 #pragma unroll
       for (int tt = 0; tt < kWaveTiles; ++tt) acc[tt][t] = Ops::qk(vt, pb[tt], acc[tt][t]);
+    }
+    {  // the softmax denominators: a 16 x 32 block of ones times P^T gives every
+       // row of lacc the column's sum of the same rounded probabilities P.V
+       // weighs, one MFMA per tile instead of 8 VALU adds
+      constexpr uint32_t one2 = DT == DT_BF16 ? 0x3f803f80u : 0x3c003c00u;  // two 16-bit 1.0
+      const uint4 ones = make_uint4(one2, one2, one2, one2);
+#pragma unroll
+      for (int tt = 0; tt < kWaveTiles; ++tt) lacc[tt] = Ops::qk(ones, pb[tt], lacc[tt]);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -780,7 +795,7 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
 
 #pragma unroll
   for (int tt = 0; tt < kWaveTiles; ++tt) {
-    const float lt = rows_sum(l[tt]);
+    const float lt = lacc[tt][0];
     if (live[tt]) store_column<DT, D, true>(a, acc[tt], m[tt], lt, qrow[tt], s, col_parts[tt], gq);
   }
 }
