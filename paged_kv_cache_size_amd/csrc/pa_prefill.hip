@@ -80,22 +80,20 @@ __device__ __forceinline__ float rows_maximum(float x) {  // over the 4 row grou
   return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// The online-softmax update of one column tile for a pair of 16-key blocks.
-// x[i]: the lane's raw score (scale not applied) of key 4(i%4) + gq of block
+// The online-softmax update of one column tile for a pair of 16-key blocks
+// (the per-wave tile; the cooperative tile runs the same update phased over
+// its tiles, with one branch for all their rescales).  x[i]: the lane's raw score (scale not applied) of key 4(i%4) + gq of block
 // i/4; ok[i] (boundary steps only): that key is visible to the lane's column.
-// l (kMfmaSum false) or lacc (true): the running denominator.
 // Moves the running max m (log2 units) when a score exceeds it by more than
 // 2^8 (probabilities stay <= 256, exact in fp32 sums) and then rescales l and
 // the accumulators - a rare, wave-uniform branch; adds the probabilities to l
-// (kMfmaSum: the caller sums them on the matrix core instead, into *lacc,
-// which the rescale then scales) and returns them packed as the P.V B
-// operand.  Absent keys get p = 0 by a
+// and returns them packed as the P.V B operand.  Absent keys get p = 0 by a
 // select after the exponential (not a -inf score, which times a zero scale
 // would be NaN).  qscale >= 0, so the max of the raw scores scales to the max
 // of the scaled ones.
-template <int DT, int VPL, bool kInterior, bool kMfmaSum = false>
+template <int DT, int VPL, bool kInterior>
 __device__ __forceinline__ uint4 softmax_pair(const float (&x)[8], const bool (&ok)[8], float qscale, float& m,
-                                              float* l, f32x4* acc, f32x4* lacc) {
+                                              float& l, f32x4* acc) {
   using Ops = MfmaOps<DT>;
   float xm[8];
 #pragma unroll
@@ -105,10 +103,7 @@ __device__ __forceinline__ uint4 softmax_pair(const float (&x)[8], const bool (&
     const float mn = fmaxf(m, smax);
     const float alpha = fast_exp2(m - mn);
     m = mn;
-    if constexpr (kMfmaSum)
-      *lacc *= alpha;
-    else
-      *l *= alpha;
+    l *= alpha;
 #pragma unroll
     for (int t = 0; t < VPL; ++t) acc[t] *= alpha;
   }
@@ -119,7 +114,7 @@ __device__ __forceinline__ uint4 softmax_pair(const float (&x)[8], const bool (&
     const float e = fast_exp2(fmaf(x[i], qscale, nm));
     p[i] = kInterior || ok[i] ? e : 0.f;
   }
-  if constexpr (!kMfmaSum) *l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   return make_uint4(Ops::pack(p[0], p[1]), Ops::pack(p[2], p[3]), Ops::pack(p[4], p[5]), Ops::pack(p[6], p[7]));
 }
 
@@ -420,7 +415,7 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
       if constexpr (!kInterior)
         v[i] = key < end ? v[i] : VT{};  // rows past the last key (stale, even NaN) must not reach the MFMA
     }
-    const uint4 pb = softmax_pair<DT, VPL, kInterior>(x, ok, a.qscale, m, &l, acc, nullptr);
+    const uint4 pb = softmax_pair<DT, VPL, kInterior>(x, ok, a.qscale, m, l, acc);
 #pragma unroll
     for (int t = 0; t < VPL; ++t) {
       const int w = t >> 1;
@@ -711,7 +706,11 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
         vb[t] = make_uint2(vb[t].x & mb.x, vb[t].y & mb.y);
       }
     }
-    uint4 pb[kWaveTiles];
+    // Scores of every tile first, so the second tile's QK MFMAs overlap the
+    // first tile's max; then one wave-uniform branch for all tiles' rare
+    // rescales; then each tile's probabilities and its P.V MFMAs, so the next
+    // tile's exponentials overlap this tile's matrix work.
+    float x[kWaveTiles][8];
 #pragma unroll
     for (int tt = 0; tt < kWaveTiles; ++tt) {
       f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
@@ -720,30 +719,61 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
         sa = Ops::qk(kra[c], qop[tt][c], sa);
         sb = Ops::qk(krb[c], qop[tt][c], sb);
       }
-      const float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
-      bool ok[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ok[i] = key0 + (i >> 2) * 16 + 4 * (i & 3) + gq < lim[tt];
-      pb[tt] = softmax_pair<DT, VPL, kInterior, true>(x, ok, a.qscale, m[tt], nullptr, acc[tt], &lacc[tt]);
+      for (int i = 0; i < 4; ++i) {
+        x[tt][i] = sa[i];
+        x[tt][4 + i] = sb[i];
+      }
     }
-    // The P.V MFMAs issue at raised wave priority: the wave's 16 independent
+    auto visible = [&](int tt, int i) {
+      return kInterior || key0 + (i >> 2) * 16 + 4 * (i & 3) + gq < lim[tt];
+    };
+    float smax[kWaveTiles];
+    bool move = false;
+#pragma unroll
+    for (int tt = 0; tt < kWaveTiles; ++tt) {
+      float xm[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xm[i] = visible(tt, i) ? x[tt][i] : -INFINITY;
+      smax[tt] = rows_maximum(max8(xm)) * a.qscale;
+      move = move || smax[tt] > m[tt] + kRescaleLog2;
+    }
+    if (__ballot(move)) {  // rare: some column's max moved by more than 2^8
+#pragma unroll
+      for (int tt = 0; tt < kWaveTiles; ++tt) {
+        const float mn = fmaxf(m[tt], smax[tt]);
+        const float alpha = fast_exp2(m[tt] - mn);
+        m[tt] = mn;
+        lacc[tt] *= alpha;
+#pragma unroll
+        for (int t = 0; t < VPL; ++t) acc[tt][t] *= alpha;
+      }
+    }
+    // The P.V MFMAs issue at raised wave priority: the wave's independent
     // MFMAs go out back to back while the SIMD's other wave (another
     // workgroup's) runs its softmax beside them.  Measured 3% faster on
     // chunked prefill; the same around the QK MFMAs gained nothing.
+    // The softmax denominators come from the matrix core too: a 16 x 32 block
+    // of ones times P^T gives every row of lacc the column's sum of the same
+    // rounded probabilities P.V weighs, one MFMA per tile instead of 8 adds.
+    constexpr uint32_t one2 = DT == DT_BF16 ? 0x3f803f80u : 0x3c003c00u;  // two 16-bit 1.0
+    const uint4 ones = make_uint4(one2, one2, one2, one2);
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int t = 0; t < VPL; ++t) {
-      const uint4 vt = make_uint4(va[t].x, va[t].y, vb[t].x, vb[t].y);
+    for (int tt = 0; tt < kWaveTiles; ++tt) {
+      const float nm = -m[tt];
+      float p[8];
 #pragma unroll
-      for (int tt = 0; tt < kWaveTiles; ++tt) acc[tt][t] = Ops::qk(vt, pb[tt], acc[tt][t]);
-    }
-    {  // the softmax denominators: a 16 x 32 block of ones times P^T gives every
-       // row of lacc the column's sum of the same rounded probabilities P.V
-       // weighs, one MFMA per tile instead of 8 VALU adds
-      constexpr uint32_t one2 = DT == DT_BF16 ? 0x3f803f80u : 0x3c003c00u;  // two 16-bit 1.0
-      const uint4 ones = make_uint4(one2, one2, one2, one2);
+      for (int i = 0; i < 8; ++i) {
+        const float e = fast_exp2(fmaf(x[tt][i], a.qscale, nm));
+        p[i] = visible(tt, i) ? e : 0.f;  // absent keys: a select, not -inf * scale
+      }
+      const uint4 pb = make_uint4(Ops::pack(p[0], p[1]), Ops::pack(p[2], p[3]), Ops::pack(p[4], p[5]),
+                                  Ops::pack(p[6], p[7]));
 #pragma unroll
-      for (int tt = 0; tt < kWaveTiles; ++tt) lacc[tt] = Ops::qk(ones, pb[tt], lacc[tt]);
+      for (int t = 0; t < VPL; ++t)
+        acc[tt][t] = Ops::qk(make_uint4(va[t].x, va[t].y, vb[t].x, vb[t].y), pb, acc[tt][t]);
+      lacc[tt] = Ops::qk(ones, pb, lacc[tt]);
     }
     __builtin_amdgcn_s_setprio(0);
   };
