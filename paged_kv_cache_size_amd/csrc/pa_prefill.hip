@@ -364,7 +364,7 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
       for (int i = 0; i < NLI; ++i)
         __builtin_amdgcn_global_load_lds(
             (const __attribute__((address_space(1))) void*)(a.k_pool + kbase[i] + kin[i]),
-            (__attribute__((address_space(3))) void*)(slot_base(slot) + i * 1024), 16, 0, 0);
+            (__attribute__((address_space(3))) void*)(slot_base(slot) + i * 1024), 16, 0, kKCpol);
 #pragma unroll
       for (int i = 0; i < 4; ++i) vr[i] = *reinterpret_cast<const VT*>(a.v_pool + vbase[i] + vin[i]);
       return;
@@ -378,7 +378,8 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
 #pragma unroll
     for (int i = 0; i < NLI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (__attribute__((address_space(3))) void*)(slot_base(slot) + i * 1024), 16, (int)kdma[i], 0, 0, 0);
+          rk, (__attribute__((address_space(3))) void*)(slot_base(slot) + i * 1024), 16, (int)kdma[i], 0, 0,
+          kKCpol);
 #pragma unroll
     for (int i = 0; i < 4; ++i) vr[i] = buffer_load_v<VT>(rv, voff + (uint32_t)(4 * i) * row_stride);
   };
@@ -489,6 +490,11 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
   constexpr int kWaveCols = 16 * kWaveTiles;      // columns per wave
   constexpr int kWgWaves = WAVES;                 // waves per workgroup
   constexpr int kWgCols = kWaveCols * kWgWaves;   // columns per workgroup
+  // The 2-wave shapes cover every column of a (sequence, unit) in one
+  // workgroup, so each K block is read once: K streams non-temporal as in
+  // decode.  The 4-wave shape's column groups re-read a sequence's blocks
+  // through L2, so its loads keep the default policy.
+  constexpr int kKPol = WAVES == 2 ? kKCpol : 0;
   constexpr bool SUB = MODE == kBlocksLarge;
   constexpr bool GATHER = MODE == kBlocksSmall;
   using Ops = MfmaOps<DT>;
@@ -655,10 +661,11 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
       for (int i = 0; i < DPW; ++i) {
         if (!has[i]) continue;
         const uint8_t* src = (is_k[i] ? a.k_pool : a.v_pool) + base[i] + goff[i];
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                         (__attribute__((address_space(3))) void*)((is_k[i] ? kslot(x) : vslot(x)) +
-                                                                                   lds_off[i]),
-                                         16, 0, 0);
+        auto* dst = (__attribute__((address_space(3))) void*)((is_k[i] ? kslot(x) : vslot(x)) + lds_off[i]);
+        if (is_k[i])  // wave-uniform
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src, dst, 16, 0, kKPol);
+        else
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src, dst, 16, 0, 0);
       }
       return;
     }
@@ -673,7 +680,7 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
       if (!has[i]) continue;
       if (is_k[i])
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kslot(x) + lds_off[i]),
-                                                 16, (int)goff[i], 0, 0, 0);
+                                                 16, (int)goff[i], 0, 0, kKPol);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vslot(x) + lds_off[i]),
                                                  16, (int)goff[i], 0, 0, 0);
