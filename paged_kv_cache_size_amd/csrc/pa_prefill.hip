@@ -1208,6 +1208,10 @@ extern "C" int pa_decode_attention_shared_prefix(
   // and whose keys are the shared prefix, read through the first member's
   // table; no causal limit inside the prefix (every member's position lies
   // past it).
+  // A group whose members bring more than 16 (member, query head) columns
+  // per KV head runs the cooperative tile, whose waves share one read of
+  // each prefix block - when that still gives two workgroups per compute
+  // unit; fewer, larger groups keep the per-wave tile's parallelism.
   a.context_lens = prefix_lens;
   a.query_start_loc = group_start;
   a.table_rows = group_start;
@@ -1215,10 +1219,24 @@ extern "C" int pa_decode_attention_shared_prefix(
   a.causal = 0;
   a.num_parts = p1;
   a.partial_base = 0;
-  a.tiles = (int)(((int64_t)max_group_size * gd.repc + 15) / 16);
-  int64_t grid = (int64_t)num_groups * a.tiles * p1 * gd.groups;
+  pa::PrefillShape pre = shp;
+  pre.d.num_seqs = num_groups;
+  pre.max_query_len = max_group_size;
+  pa::PrefillGrid pg = pa::prefill_grid(pre);
+  if (pg.wide && pg.items * p1 < 2 * (int64_t)std::max(1, pa::device_cu_count())) {
+    pg.wide = false;
+    pg.tiles = (int)(((int64_t)max_group_size * gd.repc + 15) / 16);
+    pg.groups = gd.groups;
+    pg.waves = gd.wpw;
+    pg.items = (int64_t)num_groups * pg.tiles * pg.groups;
+  }
+  PrefillFn pfn = pg.wide ? pick_prefill_wide(shp.d.dtype, shp.d.head_dim, pg, block_size) : fn;
+  if (!pfn) return PA_ERR_UNSUPPORTED;
+  a.groups = pg.groups;
+  a.tiles = pg.tiles;
+  int64_t grid = pg.items * p1;
   if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * gd.wpw), 0, st, a);
+  hipLaunchKernelGGL(pfn, dim3((unsigned)grid), dim3(64 * pg.waves), 0, st, a);
   rc = pa::launch_status();
   if (rc != PA_OK) return rc;
 
@@ -1230,6 +1248,7 @@ extern "C" int pa_decode_attention_shared_prefix(
   a.causal = 1;
   a.num_parts = p2;
   a.partial_base = p1;
+  a.groups = gd.groups;
   a.tiles = 1;
   grid = (int64_t)num_seqs * p2 * gd.groups;
   if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
