@@ -479,8 +479,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // pair read in the step before.  Each wave reads K (the QK A operand) and V
 // transposed (the P.V A operand) from LDS once per step and applies them to
 // all of its tiles.
-// Arithmetic per tile is that of prefill_mfma_kernel: 32-key steps, P.V on
-// 16x16x32, lazily moved running max, mask-free interior steps.
+// Arithmetic per tile follows prefill_mfma_kernel (32-key steps, P.V on
+// 16x16x32, lazily moved running max, mask-free interior steps), ordered by
+// phase over the wave's tiles, with the softmax denominators summed by an
+// extra MFMA per tile.
 // WAVES waves of TILES 16-column tiles each: 128 columns for long runs of new
 // tokens (4 x 2; 8 waves measured 6% slower), 64 or 32 for short ones (2 x 2,
 // 2 x 1).
