@@ -126,6 +126,21 @@ def test_mixed_groups_block_sizes(bs):
     check(w, g, seed=2)
 
 
+@pytest.mark.parametrize("bs", [1, 4, 16, 64])
+def test_many_wide_groups_block_sizes(bs):
+    # 64 groups of 6 with 32/8 heads: 24 (member, head) columns per KV head
+    # and 512 workgroups, so the prefix pass runs the cooperative tile, with
+    # small blocks gathered row by row and large ones walked in windows
+    rng = np.random.default_rng(bs + 100)
+    prompts = [int(x) for x in rng.integers(max(20, 2 * bs), 200 + 2 * bs, 64)]  # at least one whole block
+    forks = [6] * 64
+    gens = [[int(x) for x in rng.integers(1, 40, 6)] for _ in range(64)]
+    w = forked_batch(prompts, forks, gens, 32, 8, 128, "bf16", seed=bs, bs=bs)
+    g = PB.pa_shared_prefix_groups(w.block_tables, w.context_lens, bs)
+    assert g.num_groups == 64 and g.max_group_size == 6
+    check(w, g, seed=3)
+
+
 def test_no_shared_prefix_degenerates_to_plain_decode():
     w = W.make_workload("qwen1p5b_bf16")
     g = PB.pa_shared_prefix_groups(w.block_tables, w.context_lens, w.block_size)
