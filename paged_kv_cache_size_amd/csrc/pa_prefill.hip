@@ -914,13 +914,20 @@ PrefillFn pick_prefill_bs(int wpw, int block_size) {
 #ifndef PA_PREFILL_PAIRS
 #define PA_PREFILL_PAIRS 3
 #endif
-constexpr int kPrefillPairs = PA_PREFILL_PAIRS;  // ring pairs of the cooperative tile
+// Ring pairs of the cooperative tile: the 4-wave shape (compute bound) keeps
+// three (48 KiB of LDS; a fourth measured the same), the 2-wave shapes
+// (bandwidth bound, several new tokens per sequence) take four, one more
+// pair of loads in flight per workgroup (8 and 16 new tokens per sequence:
+// 5% and 3% faster).
+constexpr int kPrefillPairs = PA_PREFILL_PAIRS;
+constexpr int kPrefillPairsNarrow = 4;
 
 template <int DT, int D, int WAVES, int TILES>
 PrefillFn pick_prefill_wide_bs(int block_size) {
-  if (block_size == pa::kBlockSize) return prefill_wg_kernel<DT, D, kPrefillPairs, kBlocks16, WAVES, TILES>;
-  if (block_size > pa::kBlockSize) return prefill_wg_kernel<DT, D, kPrefillPairs, kBlocksLarge, WAVES, TILES>;
-  return prefill_wg_kernel<DT, D, kPrefillPairs, kBlocksSmall, WAVES, TILES>;
+  constexpr int NP = WAVES == 2 ? kPrefillPairsNarrow : kPrefillPairs;
+  if (block_size == pa::kBlockSize) return prefill_wg_kernel<DT, D, NP, kBlocks16, WAVES, TILES>;
+  if (block_size > pa::kBlockSize) return prefill_wg_kernel<DT, D, NP, kBlocksLarge, WAVES, TILES>;
+  return prefill_wg_kernel<DT, D, NP, kBlocksSmall, WAVES, TILES>;
 }
 
 template <int DT, int D>
