@@ -915,38 +915,43 @@ PrefillFn pick_prefill_bs(int wpw, int block_size) {
 #define PA_PREFILL_PAIRS 3
 #endif
 // Ring pairs of the cooperative tile: the 4-wave shape (compute bound) keeps
-// three (48 KiB of LDS; a fourth measured the same), the 2-wave shapes
-// (bandwidth bound, several new tokens per sequence) take four, one more
-// pair of loads in flight per workgroup (8 and 16 new tokens per sequence:
-// 5% and 3% faster).
+// three (48 KiB of LDS; a fourth measured the same).  The 2-wave shapes of
+// pa_prefill_attention (bandwidth bound: several new tokens per sequence,
+// grids of many workgroups per compute unit) take four, one more pair of
+// loads in flight (8 and 16 new tokens per sequence: 5% and 3% faster); the
+// cascade's prefix pass keeps three, so that three workgroups fit a compute
+// unit (2400-token prompts: 86 us with three, 104 us with four).
 constexpr int kPrefillPairs = PA_PREFILL_PAIRS;
-constexpr int kPrefillPairsNarrow = 4;
+constexpr int kPrefillPairsDeep = 4;
 
-template <int DT, int D, int WAVES, int TILES>
+template <int DT, int D, int WAVES, int TILES, bool DEEP>
 PrefillFn pick_prefill_wide_bs(int block_size) {
-  constexpr int NP = WAVES == 2 ? kPrefillPairsNarrow : kPrefillPairs;
+  constexpr int NP = WAVES == 2 && DEEP ? kPrefillPairsDeep : kPrefillPairs;
   if (block_size == pa::kBlockSize) return prefill_wg_kernel<DT, D, NP, kBlocks16, WAVES, TILES>;
   if (block_size > pa::kBlockSize) return prefill_wg_kernel<DT, D, NP, kBlocksLarge, WAVES, TILES>;
   return prefill_wg_kernel<DT, D, NP, kBlocksSmall, WAVES, TILES>;
 }
 
 template <int DT, int D>
-PrefillFn pick_prefill_wide_shape(const pa::PrefillGrid& g, int block_size) {
-  if (g.waves == 2 && g.wave_tiles == 1) return pick_prefill_wide_bs<DT, D, 2, 1>(block_size);
-  if (g.waves == 2 && g.wave_tiles == 2) return pick_prefill_wide_bs<DT, D, 2, 2>(block_size);
+PrefillFn pick_prefill_wide_shape(const pa::PrefillGrid& g, int block_size, bool deep) {
+  if (g.waves == 2 && g.wave_tiles == 1)
+    return deep ? pick_prefill_wide_bs<DT, D, 2, 1, true>(block_size) : pick_prefill_wide_bs<DT, D, 2, 1, false>(block_size);
+  if (g.waves == 2 && g.wave_tiles == 2)
+    return deep ? pick_prefill_wide_bs<DT, D, 2, 2, true>(block_size) : pick_prefill_wide_bs<DT, D, 2, 2, false>(block_size);
   if (g.waves == pa::kPrefillWgWaves && g.wave_tiles == pa::kPrefillWaveTiles)
-    return pick_prefill_wide_bs<DT, D, pa::kPrefillWgWaves, pa::kPrefillWaveTiles>(block_size);
+    return pick_prefill_wide_bs<DT, D, pa::kPrefillWgWaves, pa::kPrefillWaveTiles, false>(block_size);
   return nullptr;
 }
 
-PrefillFn pick_prefill_wide(int dtype, int d, const pa::PrefillGrid& g, int block_size) {
+// deep: the 2-wave shapes with four ring pairs (see kPrefillPairsDeep).
+PrefillFn pick_prefill_wide(int dtype, int d, const pa::PrefillGrid& g, int block_size, bool deep) {
   switch (dtype) {
     case PA_F16:
-      return d == 64 ? pick_prefill_wide_shape<DT_F16, 64>(g, block_size)
-                     : pick_prefill_wide_shape<DT_F16, 128>(g, block_size);
+      return d == 64 ? pick_prefill_wide_shape<DT_F16, 64>(g, block_size, deep)
+                     : pick_prefill_wide_shape<DT_F16, 128>(g, block_size, deep);
     case PA_BF16:
-      return d == 64 ? pick_prefill_wide_shape<DT_BF16, 64>(g, block_size)
-                     : pick_prefill_wide_shape<DT_BF16, 128>(g, block_size);
+      return d == 64 ? pick_prefill_wide_shape<DT_BF16, 64>(g, block_size, deep)
+                     : pick_prefill_wide_shape<DT_BF16, 128>(g, block_size, deep);
     default: return nullptr;
   }
 }
@@ -1085,7 +1090,7 @@ extern "C" int pa_prefill_attention_layout(void* out, const void* query, const v
                         workspace_bytes, partition_size, stream);
   const pa::DecodeGrid gd = pa::decode_grid(shp.d);
   const pa::PrefillGrid pg = pa::prefill_grid(shp);
-  PrefillFn fn = pg.wide ? pick_prefill_wide(shp.d.dtype, shp.d.head_dim, pg, block_size)
+  PrefillFn fn = pg.wide ? pick_prefill_wide(shp.d.dtype, shp.d.head_dim, pg, block_size, true)
                          : pick_prefill(shp.d.dtype, shp.d.head_dim, gd.wpw, block_size);
   if (!fn) return PA_ERR_UNSUPPORTED;
   int cus = 256, per_cu = 1;
@@ -1239,7 +1244,7 @@ extern "C" int pa_decode_attention_shared_prefix(
     pg.waves = gd.wpw;
     pg.items = (int64_t)num_groups * pg.tiles * pg.groups;
   }
-  PrefillFn pfn = pg.wide ? pick_prefill_wide(shp.d.dtype, shp.d.head_dim, pg, block_size) : fn;
+  PrefillFn pfn = pg.wide ? pick_prefill_wide(shp.d.dtype, shp.d.head_dim, pg, block_size, false) : fn;
   if (!pfn) return PA_ERR_UNSUPPORTED;
   a.groups = pg.groups;
   a.tiles = pg.tiles;
