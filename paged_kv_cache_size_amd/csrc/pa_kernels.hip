@@ -216,7 +216,11 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
     const size_t off = (size_t)(uint32_t)pb * block_stride;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      kr[i] = *reinterpret_cast<const uint4*>(kbase + off + (size_t)i * RPI * row_stride);
+      // K streams non-temporal, as in the matrix-core tile (fp32 256 x 4096:
+      // 1425 -> 1298 us)
+      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+      kr[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+                                            kbase + off + (size_t)i * RPI * row_stride)));
       vr[i] = *reinterpret_cast<const uint4*>(vbase + off + (size_t)i * RPI * row_stride);
     }
   };
