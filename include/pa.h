@@ -174,8 +174,8 @@ size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_heads, int32_t
  *                  max_context_len needs a single partition
  *
  * Supported: dtype F32/F16/BF16, head_dim 64 or 128, num_heads a multiple
- * of num_kv_heads; block_size a power of two from 1 to 256 for F16/BF16 (the
- * handbook's block-size trade-off, section "块大小怎么选"), 16 for F32.
+ * of num_kv_heads; block_size a power of two from 1 to 256 (the handbook's
+ * block-size trade-off, section "块大小怎么选").
  * Device contents: block ids must address blocks of the pools and
  * context_lens must lie in [0, max_context_len]; anything else is undefined
  * (reads outside the pools).  A context length of 0 yields zeros.
@@ -291,7 +291,7 @@ int32_t pa_decode_plan_partition_size(int32_t num_seqs, int32_t num_heads, int32
  *   other arguments  as pa_decode_attention (pools, tables, scale, dtype, stream).
  * fp16 and bf16 run matrix-core tiles shared by the rows of a sequence; fp32
  * runs every row as a decode query with its own causal context (the VALU
- * tile; block_size 16).  Block sizes as pa_decode_attention.
+ * tile).  Block sizes as pa_decode_attention.
  * partition_size: 0 lets the library choose (it may split long contexts into
  * partitions merged by a second kernel, keeping the partials within 256 MiB),
  * or a size pa_decode_attention_ex accepts.  The workspace

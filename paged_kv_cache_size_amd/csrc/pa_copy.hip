@@ -48,13 +48,14 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const V* k_src, const 
 // `planes` = 2: a K and a V pool; 1: one pool (the fused layout; the v
 // pointers are not used).
 template <typename V>
-void launch(const void* k_src, const void* v_src, void* k_dst, void* v_dst, const int64_t* src, const int64_t* dst,
+int launch(const void* k_src, const void* v_src, void* k_dst, void* v_dst, const int64_t* src, const int64_t* dst,
             int64_t pairs, int planes, int64_t block_bytes, int64_t src_blocks, int64_t dst_blocks, hipStream_t st) {
   const int64_t vecs = block_bytes / (int64_t)sizeof(V);
   const int64_t per_wg = 256 * 4;
   const unsigned slices = (unsigned)std::min<int64_t>((vecs + per_wg - 1) / per_wg, 65535);
-  hipLaunchKernelGGL(copy_blocks_kernel<V>, dim3((unsigned)pairs, (unsigned)planes, slices), dim3(256), 0, st,
-                     (const V*)k_src, (const V*)v_src, (V*)k_dst, (V*)v_dst, src, dst, vecs, src_blocks, dst_blocks);
+  return pa::launch_kernel(copy_blocks_kernel<V>, dim3((unsigned)pairs, (unsigned)planes, slices), dim3(256), st,
+                           (const V*)k_src, (const V*)v_src, (V*)k_dst, (V*)v_dst, src, dst, vecs, src_blocks,
+                           dst_blocks);
 }
 
 int copy_between(const void* k_src, const void* v_src, int64_t src_blocks, void* k_dst, void* v_dst,
@@ -65,12 +66,13 @@ int copy_between(const void* k_src, const void* v_src, int64_t src_blocks, void*
   if (planes == 2) align |= (uintptr_t)v_src | (uintptr_t)v_dst;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (block_bytes % 16 == 0 && align % 16 == 0)
-    launch<uint4>(k_src, v_src, k_dst, v_dst, src, dst, pairs, planes, block_bytes, src_blocks, dst_blocks, st);
-  else if (block_bytes % 4 == 0 && align % 4 == 0)
-    launch<uint32_t>(k_src, v_src, k_dst, v_dst, src, dst, pairs, planes, block_bytes, src_blocks, dst_blocks, st);
-  else
-    launch<uint16_t>(k_src, v_src, k_dst, v_dst, src, dst, pairs, planes, block_bytes, src_blocks, dst_blocks, st);
-  return pa::launch_status();
+    return launch<uint4>(k_src, v_src, k_dst, v_dst, src, dst, pairs, planes, block_bytes, src_blocks, dst_blocks,
+                         st);
+  if (block_bytes % 4 == 0 && align % 4 == 0)
+    return launch<uint32_t>(k_src, v_src, k_dst, v_dst, src, dst, pairs, planes, block_bytes, src_blocks,
+                            dst_blocks, st);
+  return launch<uint16_t>(k_src, v_src, k_dst, v_dst, src, dst, pairs, planes, block_bytes, src_blocks, dst_blocks,
+                          st);
 }
 
 // Pool geometry in vectors of the copy width.
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(256) void convert_blocks_kernel(const V* k_src, con
 }
 
 template <typename V>
-void launch_convert(const pa::PoolView& s, const pa::PoolView& d, const int64_t* src, const int64_t* dst,
+int launch_convert(const pa::PoolView& s, const pa::PoolView& d, const int64_t* src, const int64_t* dst,
                     int64_t pairs, int64_t src_blocks, int64_t dst_blocks, int block_size, int num_kv_heads,
                     int head_bytes, hipStream_t st) {
   constexpr int64_t W = sizeof(V);
@@ -109,9 +111,9 @@ void launch_convert(const pa::PoolView& s, const pa::PoolView& d, const int64_t*
   const int64_t vecs = (int64_t)block_size * num_kv_heads * head_bytes / W;  // per plane
   const int64_t per_wg = 256 * 4;
   const unsigned slices = (unsigned)std::min<int64_t>((vecs + per_wg - 1) / per_wg, 65535);
-  hipLaunchKernelGGL(convert_blocks_kernel<V>, dim3((unsigned)pairs, 2, slices), dim3(256), 0, st, (const V*)s.k,
-                     (const V*)s.v, (V*)const_cast<uint8_t*>(d.k), (V*)const_cast<uint8_t*>(d.v), gs, gd, src, dst,
-                     src_blocks, dst_blocks, num_kv_heads, (int)(head_bytes / W), vecs);
+  return pa::launch_kernel(convert_blocks_kernel<V>, dim3((unsigned)pairs, 2, slices), dim3(256), st, (const V*)s.k,
+                           (const V*)s.v, (V*)const_cast<uint8_t*>(d.k), (V*)const_cast<uint8_t*>(d.v), gs, gd, src,
+                           dst, src_blocks, dst_blocks, num_kv_heads, (int)(head_bytes / W), vecs);
 }
 
 }  // namespace
@@ -163,13 +165,11 @@ extern "C" int pa_convert_blocks(void* dst_k_pool, void* dst_v_pool, pa_kv_layou
   const uintptr_t align = (uintptr_t)s.k | (uintptr_t)s.v | (uintptr_t)d.k | (uintptr_t)d.v | (uintptr_t)head_bytes;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (align % 16 == 0)
-    launch_convert<uint4>(s, d, src_blocks, dst_blocks, num_pairs, src_num_blocks, dst_num_blocks, block_size,
-                          num_kv_heads, head_bytes, st);
-  else if (align % 4 == 0)
-    launch_convert<uint32_t>(s, d, src_blocks, dst_blocks, num_pairs, src_num_blocks, dst_num_blocks, block_size,
-                             num_kv_heads, head_bytes, st);
-  else
-    launch_convert<uint16_t>(s, d, src_blocks, dst_blocks, num_pairs, src_num_blocks, dst_num_blocks, block_size,
-                             num_kv_heads, head_bytes, st);
-  return pa::launch_status();
+    return launch_convert<uint4>(s, d, src_blocks, dst_blocks, num_pairs, src_num_blocks, dst_num_blocks, block_size,
+                                 num_kv_heads, head_bytes, st);
+  if (align % 4 == 0)
+    return launch_convert<uint32_t>(s, d, src_blocks, dst_blocks, num_pairs, src_num_blocks, dst_num_blocks,
+                                    block_size, num_kv_heads, head_bytes, st);
+  return launch_convert<uint16_t>(s, d, src_blocks, dst_blocks, num_pairs, src_num_blocks, dst_num_blocks,
+                                  block_size, num_kv_heads, head_bytes, st);
 }

@@ -20,10 +20,9 @@ constexpr int kMaxAutoPartitionBlocks = 64;  // automatic choice without the con
 
 int elem_bytes(int dtype);  // 0 for an unknown dtype
 
-// Pool block sizes the 16-bit paths run (powers of two, 1..256): the MFMA
-// tiles take 16-token steps, so a larger block holds several steps and a
-// smaller one contributes a few rows to a step; fp32 (VALU tile) reads whole
-// 16-row blocks only.
+// Pool block sizes every path runs (powers of two, 1..256): the tiles take
+// 16-token steps, so a larger block holds several steps and a smaller one
+// contributes a few rows to a step.
 constexpr int kMinDecodeBlock = 1;
 constexpr int kMaxDecodeBlock = 256;
 bool decode_block_size_ok(int block_size, int dtype);

@@ -128,14 +128,22 @@ struct DecodeTile {
 };
 
 // One wave = one (sequence b, partition s, KV head g, chunk of REPC query heads).
-// Lane l reads, for every block, rows i*RPI + l/LPR (i < NLD), bytes
-// (l % LPR)*16 .. +16 of the row.  Each lane runs its own online softmax over
-// the tokens it holds (all LPR lanes of a row group hold the same tokens and
-// compute identical values); the RPI row-group streams merge at the end.
-template <int DT, int D, int REPC>
+// The wave walks the partition in steps of 16 tokens.  Lane l reads, for
+// every step, rows i*RPI + l/LPR (i < NLD), bytes (l % LPR)*16 .. +16 of the
+// row.  Each lane runs its own online softmax over the tokens it holds (all
+// LPR lanes of a row group hold the same tokens and compute identical
+// values); the RPI row-group streams merge at the end.
+// Pool block sizes (MODE, as in the matrix-core tile below): a 16-token block
+// is one step; a larger block is walked in 16-row windows (table entry
+// step >> shift); for a smaller one every row's block comes from the
+// partition's table staged in LDS (step j, row t: entry (j << shift) +
+// t / block_size, row t % block_size of that block).
+template <int DT, int D, int REPC, int MODE>
 __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs a) {
   using T = DecodeTile<DT, D, REPC>;
   constexpr int BS = T::BS, ROWB = T::ROWB, LPR = T::LPR, RPI = T::RPI, NLD = T::NLD, EPL = T::EPL;
+  constexpr bool SUB = MODE == kBlocksLarge;
+  constexpr bool GATHER = MODE == kBlocksSmall;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -176,13 +184,24 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
   }
   const int end = min(L, start + a.part_tokens);
   const int seq_parts = (L + a.part_tokens - 1) / a.part_tokens;
-  const int blk0 = start / BS;
-  const int nblk = (end - start + BS - 1) / BS;  // <= kMaxPartitionBlocks
+  const int pshift = MODE != kBlocks16 ? a.block_shift : 0;
+  const int pool_bs = SUB ? BS << pshift : GATHER ? BS >> pshift : BS;  // tokens per pool block
+  const int blk0 = start / pool_bs;  // partitions start on a pool block
+  const int nblk = (end - start + BS - 1) / BS;  // 16-token steps
+  const int nent = (end - start + pool_bs - 1) / pool_bs;  // table entries of the partition
 
-  // This partition's block-table slice, fetched per block by readlane.
+  // This partition's block-table slice: in VGPR lanes, fetched per step by
+  // readlane (blocks of 16 tokens or more, <= kMaxPartitionBlocks entries),
+  // or staged in LDS for the workgroup and read per row (smaller blocks,
+  // <= kMaxSmallBlockPartition entries; every wave of the workgroup serves
+  // the same row and partition).
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk0;
   TableSlice tab;
-  tab.load(bt, nblk, lane);
+  __shared__ int32_t stab[GATHER ? pa::kMaxSmallBlockPartition : 1];
+  if constexpr (GATHER)
+    stage_table(stab, bt, nent);
+  else
+    tab.load(bt, nent, lane);
 
   // Query rows of the REPC heads, scaled into log2 units.
   float q[REPC][EPL];
@@ -201,6 +220,18 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
   const size_t lane_off = (size_t)r * row_stride + (size_t)g * a.head_stride + (size_t)c * 16;
   const uint8_t* kbase = a.k_pool + lane_off;
   const uint8_t* vbase = a.v_pool + lane_off;
+  // Small blocks: row i*RPI + r of a step lies in the step's block blk[i],
+  // at byte offset in[i] of that block.
+  int sblk[GATHER ? NLD : 1];
+  size_t sin[GATHER ? NLD : 1];
+  if constexpr (GATHER) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int t = i * RPI + r;
+      sblk[i] = t / pool_bs;
+      sin[i] = (size_t)(t % pool_bs) * row_stride + (size_t)g * a.head_stride + (size_t)c * 16;
+    }
+  }
 
   float m[REPC], l[REPC], acc[REPC][EPL];
 #pragma unroll
@@ -211,14 +242,26 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
 
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   auto load_block = [&](int j, uint4* kr, uint4* vr) {
-    const int pb = tab.get(j);
-    const size_t off = (size_t)(uint32_t)pb * block_stride;
+    if constexpr (GATHER) {  // per-row blocks; rows past the partition re-read its last block (masked)
+      size_t base[NLD];
+      step_block_bases<NLD>(stab, j, pshift, nent, block_stride, sblk, base);
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        kr[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                              reinterpret_cast<const u32x4_t*>(a.k_pool + base[i] + sin[i])));
+        vr[i] = *reinterpret_cast<const uint4*>(a.v_pool + base[i] + sin[i]);
+      }
+      return;
+    }
+    const size_t off = SUB ? (size_t)(uint32_t)tab.get(j >> pshift) * block_stride +
+                                 (size_t)(j & ((1 << pshift) - 1)) * BS * row_stride
+                           : (size_t)(uint32_t)tab.get(j) * block_stride;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       // K streams non-temporal, as in the matrix-core tile (fp32 256 x 4096:
       // 1425 -> 1298 us)
-      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
       kr[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
                                             kbase + off + (size_t)i * RPI * row_stride)));
       vr[i] = *reinterpret_cast<const uint4*>(vbase + off + (size_t)i * RPI * row_stride);
@@ -283,14 +326,13 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
   // Two register buffers: the next block's loads are in flight while the
   // current block is computed.
   uint4 ka[NLD], va[NLD], kb[NLD], vb[NLD];
-  const int first_tok = blk0 * BS;
   load_block(0, ka, va);
   for (int j = 0; j < nblk; j += 2) {
     if (j + 1 < nblk) load_block(j + 1, kb, vb);
-    process(ka, va, min(BS, end - (first_tok + j * BS)));
+    process(ka, va, min(BS, end - (start + j * BS)));
     if (j + 1 >= nblk) break;
     if (j + 2 < nblk) load_block(j + 2, ka, va);
-    process(kb, vb, min(BS, end - (first_tok + (j + 1) * BS)));
+    process(kb, vb, min(BS, end - (start + (j + 1) * BS)));
   }
 
   // Merge the RPI row-group streams.
@@ -640,19 +682,26 @@ using DecodeFn = void (*)(const DecodeArgs);
 #endif
 constexpr int kRing = PA_MFMA_RING;  // ring depth (blocks) of the MFMA decode kernel
 
-template <int DT, int D>
+template <int DT, int D, int MODE>
 DecodeFn pick_rep(int repc) {
   switch (repc) {
-    case 1: return decode_partition_kernel<DT, D, 1>;
-    case 2: return decode_partition_kernel<DT, D, 2>;
-    case 3: return decode_partition_kernel<DT, D, 3>;
-    case 4: return decode_partition_kernel<DT, D, 4>;
-    case 5: return decode_partition_kernel<DT, D, 5>;
-    case 6: return decode_partition_kernel<DT, D, 6>;
-    case 7: return decode_partition_kernel<DT, D, 7>;
-    case 8: return decode_partition_kernel<DT, D, 8>;
+    case 1: return decode_partition_kernel<DT, D, 1, MODE>;
+    case 2: return decode_partition_kernel<DT, D, 2, MODE>;
+    case 3: return decode_partition_kernel<DT, D, 3, MODE>;
+    case 4: return decode_partition_kernel<DT, D, 4, MODE>;
+    case 5: return decode_partition_kernel<DT, D, 5, MODE>;
+    case 6: return decode_partition_kernel<DT, D, 6, MODE>;
+    case 7: return decode_partition_kernel<DT, D, 7, MODE>;
+    case 8: return decode_partition_kernel<DT, D, 8, MODE>;
     default: return nullptr;
   }
+}
+
+template <int DT, int D>
+DecodeFn pick_rep_bs(int repc, int block_size) {
+  if (block_size == pa::kBlockSize) return pick_rep<DT, D, kBlocks16>(repc);
+  if (block_size > pa::kBlockSize) return pick_rep<DT, D, kBlocksLarge>(repc);
+  return pick_rep<DT, D, kBlocksSmall>(repc);
 }
 
 template <int DT, int D, int MODE>
@@ -676,7 +725,8 @@ DecodeFn pick_mfma_bs(int wpw, int block_size) {
 // kernel (one per waves-per-workgroup).
 DecodeFn pick_decode(int dtype, int d, const pa::DecodeGrid& g, int block_size) {
   switch (dtype) {
-    case PA_F32: return d == 64 ? pick_rep<DT_F32, 64>(g.repc) : pick_rep<DT_F32, 128>(g.repc);
+    case PA_F32:
+      return d == 64 ? pick_rep_bs<DT_F32, 64>(g.repc, block_size) : pick_rep_bs<DT_F32, 128>(g.repc, block_size);
     case PA_F16:
       return d == 64 ? pick_mfma_bs<DT_F16, 64>(g.wpw, block_size) : pick_mfma_bs<DT_F16, 128>(g.wpw, block_size);
     case PA_BF16:
@@ -702,10 +752,11 @@ struct DecodePlan {
   size_t need = 0;
 };
 
-// Host checks and the partition count; no HIP call unless partition_req == 0.
+// Host checks, the partition count and the partial bytes it needs; no HIP
+// call unless partition_req == 0.
 int plan_decode(const void* out, const void* query, const void* k_pool, const void* v_pool,
                 const int32_t* block_tables, const int32_t* context_lens, const pa::DecodeShape& shp,
-                float scale, void* workspace, size_t workspace_bytes, int32_t partition_req, DecodePlan* plan) {
+                float scale, int32_t partition_req, DecodePlan* plan) {
   int rc = pa::check_decode(out, query, k_pool, v_pool, block_tables, context_lens, shp, scale);
   if (rc != PA_OK) return rc;
   if (partition_req != 0 && pa::partition_size(shp, partition_req, 256, 1) < 0) return PA_ERR_INVALID_ARG;
@@ -723,8 +774,12 @@ int plan_decode(const void* out, const void* query, const void* k_pool, const vo
   plan->ps = ps;
   plan->parts = pa::num_partitions(shp.max_context_len, ps);
   plan->need = pa::workspace_bytes(shp.num_seqs, shp.num_heads, shp.head_dim, plan->parts);
-  if (plan->need > 0 && (workspace == nullptr || workspace_bytes < plan->need)) return PA_ERR_WORKSPACE;
   return PA_OK;
+}
+
+// PA_ERR_WORKSPACE unless `bytes` at `workspace` hold the plan's partials.
+int check_workspace(const DecodePlan& plan, const void* workspace, size_t bytes) {
+  return plan.need > 0 && (workspace == nullptr || bytes < plan.need) ? PA_ERR_WORKSPACE : PA_OK;
 }
 
 float2* ml_region(void* workspace, const pa::DecodeShape& shp, int parts) {
@@ -767,8 +822,7 @@ int launch_partitions(void* out, const void* query, const pa::PoolView& pv, cons
   a.num_parts = plan.parts;
   a.groups = gd.groups;
   a.qscale = scale * 1.44269504088896340736f;  // log2(e)
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * gd.wpw), 0, static_cast<hipStream_t>(stream), a);
-  return pa::launch_status();
+  return pa::launch_kernel(fn, dim3((unsigned)grid), dim3(64 * gd.wpw), static_cast<hipStream_t>(stream), a);
 }
 
 int launch_combine(void* out, const int32_t* context_lens, const pa::DecodeShape& shp, void* workspace,
@@ -777,10 +831,9 @@ int launch_combine(void* out, const int32_t* context_lens, const pa::DecodeShape
   CombineFn cf = pick_combine(shp.dtype, shp.head_dim);
   if (!cf) return PA_ERR_UNSUPPORTED;
   const int64_t waves = (int64_t)shp.num_seqs * shp.num_heads;
-  hipLaunchKernelGGL(cf, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, static_cast<hipStream_t>(stream), out,
-                     static_cast<const float*>(workspace), ml_region(workspace, shp, plan.parts), context_lens,
-                     shp.num_seqs, shp.num_heads, plan.ps, plan.parts);
-  return pa::launch_status();
+  return pa::launch_kernel(cf, dim3((unsigned)((waves + 3) / 4)), dim3(256), static_cast<hipStream_t>(stream), out,
+                           static_cast<const float*>(workspace), ml_region(workspace, shp, plan.parts),
+                           context_lens, shp.num_seqs, shp.num_heads, plan.ps, plan.parts);
 }
 
 }  // namespace
@@ -801,8 +854,6 @@ int device_cu_count() {
   if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
-
-int launch_status() { return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
 const void* decode_rows_kernel(const DecodeShape& s, int* threads) {
   const DecodeGrid g = decode_grid(s);
@@ -844,8 +895,7 @@ int launch_decode_rows(void* out, const void* query, const PoolView& pv, const i
   a.num_parts = num_parts;
   a.groups = gd.groups;
   a.qscale = scale * 1.44269504088896340736f;  // log2(e)
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * gd.wpw), 0, static_cast<hipStream_t>(stream), a);
-  return launch_status();
+  return launch_kernel(fn, dim3((unsigned)grid), dim3(64 * gd.wpw), static_cast<hipStream_t>(stream), a);
 }
 
 // Workgroups of `fn` (with `threads` threads) resident per compute unit, cached
@@ -882,27 +932,24 @@ extern "C" int pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_table
                                   max_blocks_per_seq, block_size, num_tokens);
   if (rc != PA_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (!query_start_loc) {
-    hipLaunchKernelGGL(slot_mapping_decode_kernel, dim3((num_seqs + 255) / 256), dim3(256), 0, st, slot_mapping,
-                       block_tables, context_lens, num_seqs, max_blocks_per_seq, block_size);
-  } else {
-    hipLaunchKernelGGL(slot_mapping_varlen_kernel, dim3(num_seqs), dim3(64), 0, st, slot_mapping, block_tables,
-                       context_lens, query_start_loc, max_blocks_per_seq, block_size, num_tokens);
-  }
-  return pa::launch_status();
+  if (!query_start_loc)
+    return pa::launch_kernel(slot_mapping_decode_kernel, dim3((num_seqs + 255) / 256), dim3(256), st, slot_mapping,
+                             block_tables, context_lens, num_seqs, max_blocks_per_seq, block_size);
+  return pa::launch_kernel(slot_mapping_varlen_kernel, dim3(num_seqs), dim3(64), st, slot_mapping, block_tables,
+                           context_lens, query_start_loc, max_blocks_per_seq, block_size, num_tokens);
 }
 
 namespace {
 
 template <typename V>
-void launch_reshape(const void* key, const void* value, const pa::PoolView& pv, const int64_t* slots,
-                    int64_t num_tokens, int num_kv_heads, int head_bytes, int block_size, int64_t num_slots,
-                    int threads, hipStream_t st) {
+int launch_reshape(const void* key, const void* value, const pa::PoolView& pv, const int64_t* slots,
+                   int64_t num_tokens, int num_kv_heads, int head_bytes, int block_size, int64_t num_slots,
+                   int threads, hipStream_t st) {
   constexpr int64_t W = sizeof(V);
-  hipLaunchKernelGGL(reshape_and_cache_kernel<V>, dim3((unsigned)num_tokens, 2), dim3(threads), 0, st,
-                     (const V*)key, (const V*)value, (V*)const_cast<uint8_t*>(pv.k), (V*)const_cast<uint8_t*>(pv.v),
-                     slots, (int)(head_bytes / W), num_kv_heads, block_size, pv.block_stride / W, pv.row_stride / W,
-                     pv.head_stride / W, num_slots);
+  return pa::launch_kernel(reshape_and_cache_kernel<V>, dim3((unsigned)num_tokens, 2), dim3(threads), st,
+                           (const V*)key, (const V*)value, (V*)const_cast<uint8_t*>(pv.k),
+                           (V*)const_cast<uint8_t*>(pv.v), slots, (int)(head_bytes / W), num_kv_heads, block_size,
+                           pv.block_stride / W, pv.row_stride / W, pv.head_stride / W, num_slots);
 }
 
 }  // namespace
@@ -927,29 +974,18 @@ extern "C" int pa_reshape_and_cache_layout(const void* key, const void* value, v
   const int64_t row_vecs = row_bytes / vec;
   const int threads = row_vecs >= 256 ? 256 : (row_vecs > 64 ? 128 : 64);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const auto run = [&](auto vec_type) {
+    using V = decltype(vec_type);
+    return launch_reshape<V>(key, value, pv, slot_mapping, num_tokens, num_kv_heads, head_bytes, block_size,
+                             num_slots, threads, st);
+  };
   switch (vec) {
-    case 16:
-      launch_reshape<uint4>(key, value, pv, slot_mapping, num_tokens, num_kv_heads, head_bytes, block_size,
-                            num_slots, threads, st);
-      break;
-    case 8:
-      launch_reshape<uint2>(key, value, pv, slot_mapping, num_tokens, num_kv_heads, head_bytes, block_size,
-                            num_slots, threads, st);
-      break;
-    case 4:
-      launch_reshape<uint32_t>(key, value, pv, slot_mapping, num_tokens, num_kv_heads, head_bytes, block_size,
-                               num_slots, threads, st);
-      break;
-    case 2:
-      launch_reshape<uint16_t>(key, value, pv, slot_mapping, num_tokens, num_kv_heads, head_bytes, block_size,
-                               num_slots, threads, st);
-      break;
-    default:
-      launch_reshape<uint8_t>(key, value, pv, slot_mapping, num_tokens, num_kv_heads, head_bytes, block_size,
-                              num_slots, threads, st);
-      break;
+    case 16: return run(uint4{});
+    case 8: return run(uint2{});
+    case 4: return run(uint32_t{});
+    case 2: return run(uint16_t{});
+    default: return run(uint8_t{});
   }
-  return pa::launch_status();
 }
 
 extern "C" int pa_reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
@@ -978,8 +1014,8 @@ extern "C" int pa_decode_attention_layout(void* out, const void* query, const vo
   rc = pa::pool_view(k_pool, v_pool, (int)layout, block_size, num_kv_heads, head_dim, (int)dtype, &pv);
   if (rc != PA_OK) return rc;
   DecodePlan plan;
-  rc = plan_decode(out, query, pv.k, pv.v, block_tables, context_lens, shp, scale, workspace, workspace_bytes,
-                   partition_size, &plan);
+  rc = plan_decode(out, query, pv.k, pv.v, block_tables, context_lens, shp, scale, partition_size, &plan);
+  if (rc == PA_OK) rc = check_workspace(plan, workspace, workspace_bytes);
   if (rc != PA_OK) return rc;
   rc = launch_partitions(out, query, pv, block_tables, context_lens, shp, scale, workspace, plan, stream);
   if (rc != PA_OK) return rc;
@@ -1019,8 +1055,8 @@ extern "C" int pa_decode_partitions(void* out, const void* query, const void* k_
   const pa::DecodeShape shp{num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                             max_context_len, (int)dtype};
   DecodePlan plan;
-  int rc = plan_decode(out, query, k_pool, v_pool, block_tables, context_lens, shp, scale, workspace,
-                       workspace_bytes, partition_size, &plan);
+  int rc = plan_decode(out, query, k_pool, v_pool, block_tables, context_lens, shp, scale, partition_size, &plan);
+  if (rc == PA_OK) rc = check_workspace(plan, workspace, workspace_bytes);
   if (rc != PA_OK) return rc;
   pa::PoolView pv;
   rc = pa::pool_view(k_pool, v_pool, PA_KV_SPLIT, block_size, num_kv_heads, head_dim, (int)dtype, &pv);
@@ -1040,7 +1076,8 @@ extern "C" int pa_decode_combine(void* out, const int32_t* context_lens, int32_t
   plan.ps = partition_size;
   plan.parts = pa::num_partitions(max_context_len, partition_size);
   plan.need = pa::workspace_bytes(num_seqs, num_heads, head_dim, plan.parts);
-  if (plan.need > 0 && (workspace == nullptr || workspace_bytes < plan.need)) return PA_ERR_WORKSPACE;
+  rc = check_workspace(plan, workspace, workspace_bytes);
+  if (rc != PA_OK) return rc;
   return launch_combine(out, context_lens, shp, const_cast<void*>(workspace), plan, stream);
 }
 

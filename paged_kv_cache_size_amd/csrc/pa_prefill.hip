@@ -1023,10 +1023,9 @@ int prefill_rows(void* out, const void* query, const pa::PoolView& pv, const int
   PrefillCombineFn cf = pick_prefill_combine(d.dtype, d.head_dim);
   if (!cf) return PA_ERR_UNSUPPORTED;
   const int64_t waves = (int64_t)shp.num_tokens * d.num_heads;
-  hipLaunchKernelGGL(cf, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, static_cast<hipStream_t>(stream), out,
-                     ws_acc, ws_ml, context_lens, query_start_loc, d.num_seqs, shp.num_tokens, d.num_heads, ps,
-                     parts);
-  return pa::launch_status();
+  return pa::launch_kernel(cf, dim3((unsigned)((waves + 3) / 4)), dim3(256), static_cast<hipStream_t>(stream), out,
+                           ws_acc, ws_ml, context_lens, query_start_loc, d.num_seqs, shp.num_tokens, d.num_heads, ps,
+                           parts);
 }
 
 // Scores are scaled by |scale| (in log2 units for exp2); a negative scale
@@ -1135,15 +1134,13 @@ extern "C" int pa_prefill_attention_layout(void* out, const void* query, const v
   a.tiles = pg.tiles;
   set_scale(&a, scale);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * pg.waves), 0, st, a);
-  rc = pa::launch_status();
+  rc = pa::launch_kernel(fn, dim3((unsigned)grid), dim3(64 * pg.waves), st, a);
   if (rc != PA_OK || parts <= 1) return rc;
   PrefillCombineFn cf = pick_prefill_combine(shp.d.dtype, shp.d.head_dim);
   if (!cf) return PA_ERR_UNSUPPORTED;
   const int64_t waves = (int64_t)num_tokens * num_heads;
-  hipLaunchKernelGGL(cf, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, out, a.ws_acc, a.ws_ml, context_lens,
-                     query_start_loc, num_seqs, num_tokens, num_heads, ps, parts);
-  return pa::launch_status();
+  return pa::launch_kernel(cf, dim3((unsigned)((waves + 3) / 4)), dim3(256), st, out, a.ws_acc, a.ws_ml,
+                           context_lens, query_start_loc, num_seqs, num_tokens, num_heads, ps, parts);
 }
 
 extern "C" int pa_prefill_attention(void* out, const void* query, const void* k_pool, const void* v_pool,
@@ -1250,8 +1247,7 @@ extern "C" int pa_decode_attention_shared_prefix(
   a.tiles = pg.tiles;
   int64_t grid = pg.items * p1;
   if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-  hipLaunchKernelGGL(pfn, dim3((unsigned)grid), dim3(64 * pg.waves), 0, st, a);
-  rc = pa::launch_status();
+  rc = pa::launch_kernel(pfn, dim3((unsigned)grid), dim3(64 * pg.waves), st, a);
   if (rc != PA_OK) return rc;
 
   // Suffix pass: every sequence's own keys past its group's prefix.
@@ -1266,12 +1262,10 @@ extern "C" int pa_decode_attention_shared_prefix(
   a.tiles = 1;
   grid = (int64_t)num_seqs * p2 * gd.groups;
   if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * gd.wpw), 0, st, a);
-  rc = pa::launch_status();
+  rc = pa::launch_kernel(fn, dim3((unsigned)grid), dim3(64 * gd.wpw), st, a);
   if (rc != PA_OK) return rc;
 
   const int64_t waves = (int64_t)num_seqs * num_heads;
-  hipLaunchKernelGGL(mf, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, out, a.ws_acc, a.ws_ml, (int)waves,
-                     slots);
-  return pa::launch_status();
+  return pa::launch_kernel(mf, dim3((unsigned)((waves + 3) / 4)), dim3(256), st, out, a.ws_acc, a.ws_ml,
+                           (int)waves, slots);
 }

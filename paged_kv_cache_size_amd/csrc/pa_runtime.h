@@ -1,9 +1,17 @@
 // Host-side runtime queries shared by the libpa launchers (HIP calls, cached
-// per device where they cost a driver round trip), and the one launcher one
-// source file lends another.
+// per device where they cost a driver round trip), the checked kernel launch
+// every launcher goes through, and the one launcher one source file lends
+// another.
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <tuple>
+#include <type_traits>
+#include <utility>
+
+#include "pa.h"
 
 namespace pa {
 
@@ -12,8 +20,35 @@ int device_cu_count();
 // Workgroups of kernel `fn` with `threads` threads that fit one compute unit
 // at once (cached per device and kernel), or 0 on failure.
 int resident_per_cu(const void* fn, int threads);
-// PA_OK, or PA_ERR_HIP if the last launch failed.
-int launch_status();
+
+// A launch the hardware can address: every grid dimension at least 1 and its
+// work-items (workgroups x threads) within 32 bits, which is how the dispatch
+// counts them.  Pure host arithmetic.
+inline bool grid_fits(dim3 grid, dim3 block) {
+  const uint64_t lim = 0xffffffffull;
+  return grid.x > 0 && grid.y > 0 && grid.z > 0 && (uint64_t)grid.x * block.x <= lim &&
+         (uint64_t)grid.y * block.y <= lim && (uint64_t)grid.z * block.z <= lim;
+}
+
+// Launch `fn` with `args` converted to its parameter types: PA_ERR_INVALID_ARG
+// (nothing enqueued) for a grid outside grid_fits, PA_ERR_HIP when the runtime
+// refuses the launch, else PA_OK.  The status is the launch call's own return
+// value, so an error some earlier call left pending in the runtime neither
+// fails this launch nor gets consumed by it.
+template <typename... P, typename... A>
+int launch_kernel(void (*fn)(P...), dim3 grid, dim3 block, hipStream_t stream, A&&... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "argument count");
+  if (!grid_fits(grid, block)) return PA_ERR_INVALID_ARG;
+  std::tuple<std::decay_t<P>...> vals(std::forward<A>(args)...);
+  void* ptrs[sizeof...(P) > 0 ? sizeof...(P) : 1] = {};
+  std::apply([&ptrs](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&v)), ...);
+  }, vals);
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, block, ptrs, 0, stream) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
 
 struct DecodeShape;
 struct PoolView;

@@ -58,10 +58,8 @@ extern "C" int pa_stream_read(const void* src, size_t bytes, void* sink, int non
   const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(want, 16384));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (nontemporal)
-    hipLaunchKernelGGL(stream_read_kernel<true>, dim3(grid), dim3(kThreads), 0, st, (const u32x4*)src, n_vec,
-                       (uint32_t*)sink);
-  else
-    hipLaunchKernelGGL(stream_read_kernel<false>, dim3(grid), dim3(kThreads), 0, st, (const u32x4*)src, n_vec,
-                       (uint32_t*)sink);
-  return pa::launch_status();
+    return pa::launch_kernel(stream_read_kernel<true>, dim3(grid), dim3(kThreads), st, (const u32x4*)src, n_vec,
+                             (uint32_t*)sink);
+  return pa::launch_kernel(stream_read_kernel<false>, dim3(grid), dim3(kThreads), st, (const u32x4*)src, n_vec,
+                           (uint32_t*)sink);
 }

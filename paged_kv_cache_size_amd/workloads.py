@@ -437,6 +437,37 @@ def mixed_varlen_bf16(seed: int = 0) -> PrefillBatch:
     return pb
 
 
+def handbook_verification_batch():
+    """The handbook's paged-attention verification run ("分页 KV Cache",
+    section "分页注意力"): three requests at different stages - one decode
+    token on a 37-token context, a whole 5-token prompt, the last 8 tokens of a
+    20-token chunked prefill - with 8 query / 2 KV heads, head_dim 64, fp32,
+    block size 4, in a 32-block pool whose blocks are handed out one per
+    request in turn, so the requests' blocks interleave.
+
+    Returns (tables, seq_lens, query_lens, ks, vs, qs): ks[i] / vs[i] are the
+    request's whole-context K/V [L_i, 2, 64] and qs[i] its new tokens' queries
+    [n_i, 8, 64], float32 tensors on the CPU drawn from torch's CPU generator
+    seeded with 0 in the page's order (all K, then all V, then all queries)."""
+    import torch
+
+    num_heads, num_kv_heads, head_dim, block_size = 8, 2, 64, 4
+    seq_lens, query_lens = [37, 5, 20], [1, 5, 8]
+    pool = BlockPool(32)
+    tables = [[] for _ in seq_lens]
+    while True:
+        short = [i for i, L in enumerate(seq_lens) if len(tables[i]) * block_size < L]
+        if not short:
+            break
+        for i in short:
+            tables[i] += pool.allocate(1)
+    gen = torch.Generator().manual_seed(0)
+    ks = [torch.randn(L, num_kv_heads, head_dim, generator=gen) for L in seq_lens]
+    vs = [torch.randn(L, num_kv_heads, head_dim, generator=gen) for L in seq_lens]
+    qs = [torch.randn(n, num_heads, head_dim, generator=gen) for n in query_lens]
+    return tables, seq_lens, query_lens, ks, vs, qs
+
+
 PREFILL_BUILDERS = {
     "chunked_prefill_llama_bf16": chunked_prefill_llama_bf16,
     "mixed_varlen_bf16": mixed_varlen_bf16,

@@ -66,7 +66,8 @@ def decode(**kw):
     (dict(D=96), B.PA_ERR_UNSUPPORTED),
     (dict(bs=24, mb=6), B.PA_ERR_UNSUPPORTED),    # not a power of two
     (dict(bs=512, mb=1), B.PA_ERR_UNSUPPORTED),
-    (dict(dtype=B.PA_F32, bs=32, mb=4), B.PA_ERR_UNSUPPORTED),
+    (dict(dtype=B.PA_F32, bs=512, mb=1), B.PA_ERR_UNSUPPORTED),
+    (dict(dtype=B.PA_F32, bs=32, mb=4), B.PA_ERR_INVALID_ARG),  # fp32 too: partitions hold whole blocks
     (dict(bs=32, mb=4, ps=16), B.PA_ERR_INVALID_ARG),  # partitions hold whole blocks
     (dict(bs=4, mb=32, ps=8), B.PA_ERR_INVALID_ARG),   # and whole 16-token steps
     (dict(bs=1, mb=2048, maxlen=2048, ps=1040), B.PA_ERR_INVALID_ARG),  # small blocks: above 1024 blocks
@@ -135,7 +136,8 @@ def prefill(**kw):
     (dict(H=6, Hkv=4), B.PA_ERR_INVALID_ARG),
     (dict(maxlen=129), B.PA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), B.PA_ERR_INVALID_ARG),
-    (dict(dtype=B.PA_F32, bs=32, mb=4), B.PA_ERR_UNSUPPORTED),  # fp32 rows run the 16-row VALU tile
+    (dict(dtype=B.PA_F32, bs=32, mb=4, ps=16), B.PA_ERR_INVALID_ARG),  # fp32 rows: whole blocks per partition
+    (dict(dtype=B.PA_F32, bs=512, mb=1), B.PA_ERR_UNSUPPORTED),
     (dict(dtype=B.PA_F32, ps=16), B.PA_ERR_WORKSPACE),  # fp32 is accepted: 8 partitions need a workspace
     (dict(dtype=B.PA_F32, ps=24), B.PA_ERR_INVALID_ARG),
     (dict(D=96), B.PA_ERR_UNSUPPORTED),
@@ -273,3 +275,12 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         B.lib()
+
+
+def test_oversized_grid_is_an_argument_error():
+    # 2^25 new tokens of 8 KV heads x 128 bf16 dims: one workgroup of 128
+    # threads per token row is 2^32 work-items in the grid's x dimension, one
+    # more than the dispatch can count; refused on the host, nothing launched
+    n = 1 << 25
+    rc = B.lib().pa_reshape_and_cache(FAKE, FAKE, FAKE, FAKE, FAKE, n, 8, 128, 16, 1 << 22, B.PA_BF16, None)
+    assert rc == B.PA_ERR_INVALID_ARG

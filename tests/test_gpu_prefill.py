@@ -154,6 +154,71 @@ def test_fp32_rows(h, hkv):
     check_prefill(pb, seed=5, partition_size=64, poisoned=True)
 
 
+@pytest.mark.parametrize("bs", [1, 2, 4, 8, 32, 64, 256])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp32_rows_block_sizes(bs, d):
+    # the fp32 tile over every pool block size: rows gathered through a table
+    # staged in LDS (blocks under 16 tokens) or 16-row windows of larger blocks
+    lens = [1, 2, 15, 16, 17, 64, 129, 700]
+    qlens = [1, 2, 15, 3, 17, 40, 1, 300]
+    pb = W.prefill_batch(lens, qlens, 8, 2, d, "f32", seed=bs + d, extra_cols=1, block_size=bs)
+    check_prefill(pb, seed=bs, partition_size=0, poisoned=True)
+    check_prefill(pb, seed=bs, partition_size=max(16, bs) * 2, poisoned=True)
+
+
+@pytest.mark.parametrize("ps", [0, 16])
+def test_handbook_verification_run(ps):
+    # The handbook's own check ("分页 KV Cache", section "分页注意力"): fp32,
+    # 8 query / 2 KV heads, head_dim 64, block size 4, a decode token on 37
+    # tokens, a whole 5-token prompt and the last 8 tokens of a 20-token
+    # chunk, the requests' blocks interleaved; every context token written
+    # through the slot mapping, then paged attention against the unpaged
+    # (contiguous) attention, each request within 1e-5.
+    tables, seq_lens, query_lens, ks, vs, qs = W.handbook_verification_batch()
+    bs, nb, hkv, d = 4, 32, 2, 64
+    pad = nb - 1  # a block no request owns, NaN-filled like every unowned block
+    width = max(len(t) for t in tables)
+    bt_np = np.full((len(tables), width), pad, np.int32)
+    for i, t in enumerate(tables):
+        bt_np[i, :len(t)] = t
+    owned = {b for t in tables for b in t}
+    k_pool = torch.zeros((nb, bs, hkv, d), dtype=torch.float32, device=DEV)
+    v_pool = torch.zeros_like(k_pool)
+    unowned = torch.tensor(sorted(set(range(nb)) - owned), device=DEV)
+    k_pool[unowned] = float("nan")
+    v_pool[unowned] = float("nan")
+    kp0, vp0 = k_pool.cpu().numpy(), v_pool.cpu().numpy()
+    bt = torch.from_numpy(bt_np).to(DEV)
+    lens = torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
+    # write every context position (the page writes whole requests)
+    qsl_all = torch.tensor(np.concatenate([[0], np.cumsum(seq_lens)]), dtype=torch.int32, device=DEV)
+    key, value = torch.cat(ks).to(DEV), torch.cat(vs).to(DEV)
+    slots = PB.pa_slot_mapping(bt, lens, bs, query_start_loc=qsl_all, num_tokens=sum(seq_lens))
+    PB.pa_reshape_and_cache(key, value, k_pool, v_pool, slots)
+    qsl_np = np.concatenate([[0], np.cumsum(query_lens)]).astype(np.int32)
+    q = torch.cat(qs).to(DEV)
+    out = PB.pa_prefill_attention(q, k_pool, v_pool, bt, lens, torch.from_numpy(qsl_np).to(DEV), d ** -0.5,
+                                  max(query_lens), max(seq_lens), partition_size=ps)
+    torch.cuda.synchronize()
+
+    ref_slots = O.slot_mapping(bt_np, seq_lens, bs, query_lens=seq_lens)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    O.reshape_and_cache(kp0, torch.cat(ks).numpy(), ref_slots)
+    O.reshape_and_cache(vp0, torch.cat(vs).numpy(), ref_slots)
+    assert np.array_equal(k_pool.cpu().numpy().view(np.uint32), kp0.view(np.uint32))
+    assert np.array_equal(v_pool.cpu().numpy().view(np.uint32), vp0.view(np.uint32))
+    got = out.cpu().numpy().astype(np.float64)
+    ref = O.paged_attention(q.cpu().numpy(), kp0, vp0, bt_np, seq_lens, qsl_np, d ** -0.5, "f32")
+    for i, (L, n) in enumerate(zip(seq_lens, query_lens)):
+        rows = slice(int(qsl_np[i]), int(qsl_np[i + 1]))
+        contiguous = O.contiguous_attention(qs[i].numpy(), ks[i].numpy(), vs[i].numpy(), d ** -0.5, "f32")
+        err = float(np.max(np.abs(got[rows] - contiguous)))
+        err_paged = float(np.max(np.abs(got[rows] - ref[rows])))
+        say(f"  request {i}: context {L}, new tokens {n}: max abs err {err:.1e} vs contiguous, "
+            f"{err_paged:.1e} vs the paged oracle")
+        assert err < 1e-5 and err_paged < 1e-5, (i, err, err_paged)
+
+
 @pytest.mark.parametrize("bs,ps", [(1, 1024), (2, 2048), (4, 2048)])
 def test_small_blocks_long_partitions(bs, ps):
     # blocks under 16 tokens: the partition's table (up to 1024 entries) is

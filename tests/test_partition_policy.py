@@ -113,9 +113,6 @@ def test_block_size_support():
     lib = B.lib()
     f = lambda bs, dt: lib.pa_decode_plan_partition_size(4, 8, 2, 128, 256, bs, dt, None, 256, 2)  # noqa: E731
     for bs in (1, 2, 4, 8, 16, 32, 64, 128, 256):
-        assert f(bs, B.PA_BF16) > 0 and f(bs, B.PA_F16) > 0
+        assert f(bs, B.PA_BF16) > 0 and f(bs, B.PA_F16) > 0 and f(bs, B.PA_F32) > 0
     for bs in (3, 12, 24, 512):
-        assert f(bs, B.PA_BF16) == -B.PA_ERR_UNSUPPORTED
-    assert f(16, B.PA_F32) > 0
-    for bs in (8, 32):
-        assert f(bs, B.PA_F32) == -B.PA_ERR_UNSUPPORTED  # the fp32 tile reads whole 16-row blocks
+        assert f(bs, B.PA_BF16) == -B.PA_ERR_UNSUPPORTED and f(bs, B.PA_F32) == -B.PA_ERR_UNSUPPORTED

@@ -101,3 +101,12 @@ def test_aux_bytes_tiny_and_llama():
     # the Llama layer: 2 MiB of queries, 2 MiB of outputs, 256 KiB of table entries, full blocks
     a = W.make_workload("llama_gqa4k_bf16").aux_bytes()
     assert a == {"query": 2 << 20, "out": 2 << 20, "block_table_entries": 256 << 10, "tail_slots": 0}
+
+
+def test_handbook_verification_batch_reproduces_the_printed_tables():
+    # "分页 KV Cache", section "分页注意力": the run prints the block tables its
+    # turn-by-turn allocation produced
+    tables, seq_lens, query_lens, ks, vs, qs = W.handbook_verification_batch()
+    assert tables == [[0, 3, 6, 8, 10, 12, 13, 14, 15, 16], [1, 4], [2, 5, 7, 9, 11]]
+    assert [k.shape for k in ks] == [(37, 2, 64), (5, 2, 64), (20, 2, 64)]
+    assert [q.shape for q in qs] == [(1, 8, 64), (5, 8, 64), (8, 8, 64)]
