@@ -14,8 +14,9 @@
  *    HIP device, allocated and owned by the caller.  The library allocates
  *    nothing, keeps no state beyond per-device caches of the compute-unit
  *    count and of how many workgroups of each decode kernel fit one compute
- *    unit (both filled on first use, guarded for concurrent callers), and may
- *    be called from several threads.
+ *    unit (both filled on first use, guarded for concurrent callers) and the
+ *    static partial buffer of pa_decode_attention_noalloc (one per GPU, the
+ *    only call that uses it), and may be called from several threads.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
  *    enqueues work on it and returns; nothing synchronises the device.  Two
  *    calls on one stream run in call order, which is how a pool write is
@@ -238,6 +239,33 @@ int pa_decode_combine(void* out, const int32_t* context_lens, int32_t num_seqs,
                       int32_t num_heads, int32_t head_dim, int32_t max_context_len,
                       int32_t partition_size, pa_dtype dtype, const void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_attention_noalloc - pa_decode_attention_ex for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments without the workspace; the
+ * call allocates nothing (no hipMalloc / hipFree, no allocating library
+ * routine).  The split-context partials go to a device buffer of
+ * PA_DECODE_SCRATCH_BYTES that the library holds, one per GPU, from the first
+ * call on that GPU until the process ends.
+ *   partition_size  as pa_decode_attention_ex (0: the library's own choice).
+ * Errors: as pa_decode_attention_ex, and PA_ERR_WORKSPACE, with nothing
+ * enqueued, when the partition size needs more partial bytes than
+ * PA_DECODE_SCRATCH_BYTES (pa_decode_workspace_bytes_ex gives the count for
+ * an explicit size); PA_ERR_HIP if the buffer's address cannot be obtained.
+ * Sharing: every call on one GPU uses that GPU's one buffer, which keeps the
+ * last call's partials (each partial a call reads, the same call writes
+ * first, so nothing needs clearing).  Calls ordered on one stream are safe;
+ * calls whose work may overlap on the device (several streams, or several
+ * threads enqueueing at once) race on the buffer and may return wrong results.
+ */
+#define PA_DECODE_SCRATCH_BYTES ((size_t)64 << 20)
+int pa_decode_attention_noalloc(void* out, const void* query, const void* k_pool, const void* v_pool,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t max_context_len, float scale, pa_dtype dtype,
+                                int32_t partition_size, void* stream);
 
 /*
  * Partition size (tokens) for the decode kernels on the current device, or a

@@ -32,6 +32,8 @@ SIGNATURES = {
                                            _F32, ctypes.c_int, _P, _SZ, _P]),
     "pa_decode_attention_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                               _F32, ctypes.c_int, _P, _SZ, _I32, _P]),
+    "pa_decode_attention_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                   _I32, _F32, ctypes.c_int, _I32, _P]),
     "pa_decode_partitions": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                             _F32, ctypes.c_int, _P, _SZ, _I32, _P]),
     "pa_decode_combine": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _SZ, _P]),

@@ -1096,3 +1096,64 @@ extern "C" int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads,
   if (cus <= 0 || per_cu <= 0) return -PA_ERR_HIP;
   return pa::partition_size(shp, 0, cus, per_cu, host_context_lens);
 }
+
+// ------------------------------------------------------------------ decode without a workspace argument
+//
+// For callers that cannot allocate device memory: the split-context partials
+// live in `scratch`, one copy per GPU, held until the process ends.  In host
+// code the name `scratch` only stands in for the symbol; its device address
+// comes from hipGetSymbolAddress, once per device, with that device current.
+
+static __device__ __align__(256) uint8_t scratch[PA_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+
+// Device address of the current device's `scratch`, or nullptr on a HIP error.
+void* scratch_on_current_device() {
+  static std::atomic<void*> addr[kScratchDevices] = {};
+  static std::mutex mu;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(mu);
+  p = addr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" int pa_decode_attention_noalloc(void* out, const void* query, const void* k_pool, const void* v_pool,
+                                           const int32_t* block_tables, const int32_t* context_lens,
+                                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                           int32_t max_context_len, float scale, pa_dtype dtype,
+                                           int32_t partition_size, void* stream) {
+  if (num_seqs == 0) return PA_OK;  // an empty batch
+  if (!v_pool) return PA_ERR_INVALID_ARG;
+  const pa::DecodeShape shp{num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                            max_context_len, (int)dtype};
+  pa::PoolView pv;
+  int rc = pa::check_decode(out, query, k_pool, v_pool, block_tables, context_lens, shp, scale);
+  if (rc != PA_OK) return rc;
+  rc = pa::pool_view(k_pool, v_pool, PA_KV_SPLIT, block_size, num_kv_heads, head_dim, (int)dtype, &pv);
+  if (rc != PA_OK) return rc;
+  DecodePlan plan;
+  rc = plan_decode(out, query, pv.k, pv.v, block_tables, context_lens, shp, scale, partition_size, &plan);
+  if (rc != PA_OK) return rc;
+  if (plan.need > PA_DECODE_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (plan.need > 0) {
+    ws = scratch_on_current_device();
+    if (!ws) return PA_ERR_HIP;
+  }
+  rc = launch_partitions(out, query, pv, block_tables, context_lens, shp, scale, ws, plan, stream);
+  if (rc != PA_OK) return rc;
+  return launch_combine(out, context_lens, shp, ws, plan, stream);
+}

@@ -277,6 +277,44 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         B.lib()
 
 
+def noalloc(**kw):
+    args = dict(out=FAKE, query=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, B=4, H=8, Hkv=2, D=128, bs=16,
+                mb=8, maxlen=128, scale=0.088, dtype=B.PA_BF16, ps=16)
+    args.update(kw)
+    a = args
+    return B.lib().pa_decode_attention_noalloc(a["out"], a["query"], a["k"], a["v"], a["bt"], a["lens"], a["B"],
+                                               a["H"], a["Hkv"], a["D"], a["bs"], a["mb"], a["maxlen"], a["scale"],
+                                               a["dtype"], a["ps"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), B.PA_ERR_INVALID_ARG),
+    (dict(v=None), B.PA_ERR_INVALID_ARG),
+    (dict(H=6, Hkv=4), B.PA_ERR_INVALID_ARG),
+    (dict(maxlen=129), B.PA_ERR_INVALID_ARG),
+    (dict(ps=24), B.PA_ERR_INVALID_ARG),
+    (dict(D=96), B.PA_ERR_UNSUPPORTED),
+    # 4096 x 64 heads x 256 partitions of partials: far beyond the static buffer
+    (dict(B=4096, H=64, Hkv=8, mb=256, maxlen=4096, ps=16), B.PA_ERR_WORKSPACE),
+])
+def test_noalloc_argument_checks(kw, status):
+    # every case fails on the host, before the buffer's address is looked up
+    assert noalloc(**kw) == status
+
+
+def test_noalloc_scratch_limit_is_the_header_constant():
+    text = HEADER.read_text()
+    m = re.search(r"#define PA_DECODE_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    limit = int(m.group(1)) << int(m.group(2))
+    # the largest batch whose partials fit the static buffer, by the workspace
+    # query; one sequence more is refused on the host as WORKSPACE
+    per_seq = B.lib().pa_decode_workspace_bytes_ex(1, 64, 128, 4096, 16, 16)
+    fit = limit // per_seq
+    assert B.lib().pa_decode_workspace_bytes_ex(fit, 64, 128, 4096, 16, 16) <= limit
+    assert B.lib().pa_decode_workspace_bytes_ex(fit + 1, 64, 128, 4096, 16, 16) > limit
+    assert noalloc(B=fit + 1, H=64, Hkv=8, mb=256, maxlen=4096, ps=16) == B.PA_ERR_WORKSPACE
+
+
 def test_oversized_grid_is_an_argument_error():
     # 2^25 new tokens of 8 KV heads x 128 bf16 dims: one workgroup of 128
     # threads per token row is 2^32 work-items in the grid's x dimension, one
