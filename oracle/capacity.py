@@ -11,15 +11,19 @@ from .paged_attention import num_blocks
 def kv_bytes(layers, kv_heads, head_dim, tokens, element_bytes, requests=1):
     """Bytes of K and V for ``requests`` requests of ``tokens`` tokens each.
 
-    Two tensors (K and V) per layer, each KV head holding head_dim elements
-    per token: M = 2 * L * H_kv * T * d * b (KC, section "从张量元素数推导容量"
-    (capacity from element counts)).  Non-positive or non-integer sizes are
-    rejected, as the page's helper does.
+    Each layer keeps a K tensor and a V tensor, each with head_dim elements
+    per KV head and token, so M = 2 * L * H_kv * T * d * b (KC, section
+    "从张量元素数推导容量" (capacity from element counts)).  Every size must be
+    a positive int (bool is not accepted as one); anything else raises
+    ValueError.
     """
-    values = (layers, kv_heads, head_dim, tokens, element_bytes, requests)
-    if any(not isinstance(x, int) or isinstance(x, bool) or x <= 0 for x in values):
-        raise ValueError("all size arguments must be positive integers")
-    return 2 * layers * kv_heads * head_dim * tokens * element_bytes * requests
+    sizes = {"layers": layers, "kv_heads": kv_heads, "head_dim": head_dim, "tokens": tokens,
+             "element_bytes": element_bytes, "requests": requests}
+    for name, value in sizes.items():
+        if type(value) is not int or value < 1:
+            raise ValueError(f"{name} must be a positive integer, got {value!r}")
+    one_tensor = layers * kv_heads * head_dim * tokens * element_bytes  # K alone (or V alone), one request
+    return 2 * one_tensor * requests
 
 
 def kv_bytes_per_token(layers, kv_heads, head_dim, element_bytes):

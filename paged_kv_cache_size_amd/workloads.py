@@ -36,40 +36,57 @@ ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 
 
 class BlockPool:
-    """Fixed set of physical blocks: FIFO free queue plus reference counts.
+    """The physical blocks of one pool, for building inputs.
 
-    Behaves like the handbook's BlockPool: ``allocate(n)`` takes n blocks from
-    the head of the free queue or returns None when short, ``free`` drops one
-    reference per block and re-queues a block at the tail when its count
-    reaches zero.  ``retain`` adds a reference (a fork sharing the block).
+    Blocks not in use wait in line, first in first out; a block in use
+    carries the number of sequences holding it.  The behaviour is the
+    handbook's pool ("分页 KV Cache", sections "实现" and "块表与 slot
+    mapping"): a request for more blocks than are waiting gets None and
+    changes nothing, blocks are handed out from the front of the line, and a
+    block whose last holder lets go rejoins the line at the back.  A fork
+    takes one more hold on every block it shares (``retain``).
     """
 
     def __init__(self, num_blocks: int, order=None):
         self.num_blocks = int(num_blocks)
-        self.ref_cnt = [0] * self.num_blocks
-        ids = range(self.num_blocks) if order is None else [int(x) for x in order]
-        self.free_queue = deque(ids)
+        initial = range(self.num_blocks) if order is None else order
+        self._waiting = deque(int(x) for x in initial)
+        self._holds = {}  # block id -> sequences holding it (absent when free)
 
-    def num_free(self) -> int:
-        return len(self.free_queue)
+    def free_count(self) -> int:
+        """Blocks waiting to be handed out."""
+        return len(self._waiting)
+
+    def holds(self, block) -> int:
+        """Sequences holding ``block`` (0 when it is free)."""
+        return self._holds.get(int(block), 0)
+
+    def held(self) -> dict:
+        """Every block in use and its hold count."""
+        return dict(self._holds)
 
     def allocate(self, n: int):
-        if n > len(self.free_queue):
+        n = int(n)
+        if n > len(self._waiting):
             return None
-        blocks = [self.free_queue.popleft() for _ in range(n)]
-        for b in blocks:
-            self.ref_cnt[b] = 1
-        return blocks
+        out = []
+        while len(out) < n:
+            block = self._waiting.popleft()
+            self._holds[block] = 1
+            out.append(block)
+        return out
 
     def retain(self, blocks) -> None:
-        for b in blocks:
-            self.ref_cnt[b] += 1
+        for block in blocks:
+            self._holds[block] += 1
 
     def free(self, blocks) -> None:
-        for b in blocks:
-            self.ref_cnt[b] -= 1
-            if self.ref_cnt[b] == 0:
-                self.free_queue.append(b)
+        for block in blocks:
+            remaining = self._holds.pop(block) - 1
+            if remaining > 0:
+                self._holds[block] = remaining
+            else:
+                self._waiting.append(block)
 
 
 @dataclass
@@ -96,7 +113,7 @@ class SeqBlocks:
                 if got is None:
                     raise MemoryError("block pool exhausted")
                 self.blocks.append(got[0])
-            elif pool.ref_cnt[self.blocks[-1]] > 1:
+            elif pool.holds(self.blocks[-1]) > 1:
                 got = pool.allocate(1)
                 if got is None:
                     raise MemoryError("block pool exhausted")
@@ -207,7 +224,7 @@ def _alloc_plain(lens, bs):
         s = SeqBlocks(bs)
         s.append(int(n), pool, copies)
         seqs.append(s)
-    used = pool.num_blocks - pool.num_free()
+    used = pool.num_blocks - pool.free_count()
     return seqs, used, copies
 
 

@@ -170,10 +170,10 @@ def test_random_traces_match_the_python_pool(seed):
             cow = m.append(native[i], n)
             python[i].append(n, pool, copies)
             assert cow == (None if not copies else copies[0][:2])
-        assert m.num_free() == pool.num_free()
+        assert m.num_free() == pool.free_count()
     for s, p in zip(native, python):
         assert m.block_table(s) == p.blocks and m.length(s) == p.length
-    assert all(m.ref_count(b) == pool.ref_cnt[b] for b in range(nb))
+    assert all(m.ref_count(b) == pool.holds(b) for b in range(nb))
 
 
 # ------------------------------------------------------------------ the oracle's block copy

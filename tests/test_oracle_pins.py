@@ -74,7 +74,7 @@ def test_fifo_pool_doctest():
     d = load("allocator_examples.json")["fifo_doctest"]
     pool = BlockPool(d["num_blocks"])
     table = pool.allocate(d["first_allocate"])
-    assert (table, pool.num_free()) == (d["first_table"], d["free_after_first"])
+    assert (table, pool.free_count()) == (d["first_table"], d["free_after_first"])
     pool.allocate(d["second_allocate"])
     pool.free(table)
     assert pool.allocate(d["third_allocate"]) == d["third_table"]
@@ -97,7 +97,7 @@ def test_round_robin_tables_from_page():
 
 
 def _refs(pool):
-    return {str(i): c for i, c in enumerate(pool.ref_cnt) if c > 0}
+    return {str(b): c for b, c in sorted(pool.held().items())}
 
 
 def test_fork_copy_on_write_snapshots():
