@@ -493,6 +493,64 @@ def time_stages(stages, steps, warmup):
     return ms_per_step, per, wall
 
 
+def time_plain_entry(t, bt, lens, w, steps, warmup, sched_ps):
+    """pa_decode_attention called as a C user calls it: no host lengths, so
+    the library picks the partition size itself (taking every sequence at
+    max_context_len), workspace sized by pa_decode_workspace_bytes.  Time per
+    call from events around back-to-back calls on the current stream, beside
+    pa_decode_attention_ex at the scheduler's size `sched_ps` timed the same
+    way."""
+    import ctypes
+
+    import torch
+
+    from paged_kv_cache_size_amd import binding as PB
+
+    lib = PB.lib()
+    q = t["query"]
+    B, H, D = q.shape
+    need = int(lib.pa_decode_workspace_bytes(B, H, D, w.max_context_len, w.block_size))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+    ptr = lambda x: ctypes.c_void_p(x.data_ptr())  # noqa: E731
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    args = (ptr(out), ptr(q), ptr(t["k_pool"]), ptr(t["v_pool"]), ptr(bt), ptr(lens), B, H, w.num_kv_heads, D,
+            w.block_size, w.max_blocks_per_seq, w.max_context_len, w.scale, PB.pa_dtype(q), ptr(ws), need, stream)
+
+    sched_need = PB.pa_decode_workspace_bytes(B, H, D, w.max_context_len, w.block_size, sched_ps)
+    sched_ws = torch.empty(max(sched_need, 1), dtype=torch.uint8, device=q.device)
+    sched_args = args[:15] + (ptr(sched_ws), sched_need, int(sched_ps), stream)
+
+    def plain():
+        rc = lib.pa_decode_attention(*args)
+        if rc != PB.PA_OK:
+            raise PB.PAError(rc, "pa_decode_attention")
+
+    def sched():
+        rc = lib.pa_decode_attention_ex(*sched_args)
+        if rc != PB.PA_OK:
+            raise PB.PAError(rc, "pa_decode_attention_ex")
+
+    def per_call_us(call):
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3
+
+    us, us_sched = per_call_us(plain), per_call_us(sched)
+    ps = PB.pa_decode_partition_size(B, H, w.num_kv_heads, D, w.max_context_len, w.block_size, q.dtype)
+    gbps = w.kv_unique_read_bytes() / (us * 1e-6) / 1e9
+    return {"partition_size": ps, "us_per_call": us, "kv_GBps": gbps, "frac": gbps / HBM_PEAK_GBPS,
+            "scheduler_partition_size": int(sched_ps), "scheduler_us_per_call": us_sched,
+            "plain_over_scheduler": us / us_sched}
+
+
 def time_graph(stages, steps, warmup):
     """The step captured once as a HIP graph and replayed: time per replay
     (events around all replays on the current stream)."""
@@ -707,6 +765,12 @@ def main_decode(args, oracle_pool):
         ms_per_step = time_graph(stages, args.steps, args.warmup)
     part_pct = percentiles_us(time_stages.samples[2])
     step_pct = percentiles_us([sum(x) for x in zip(*time_stages.samples)])
+    # the merge stage launches a kernel only when some context spans several partitions
+    merged = ps > 0 and args.layout == "split" and not args.shared_prefix and \
+        PB.pa_decode_workspace_bytes(B, H, D, w.max_context_len, w.block_size, ps) > 0
+    plain = None
+    if not args.shared_prefix and args.layout == "split" and len(pools) == 1:
+        plain = time_plain_entry(t, bt, lens, w, args.steps, args.warmup, ps)
     ceiling = stream_ceiling(stream_buffers)
 
     kv_bytes = w.kv_read_bytes()
@@ -744,7 +808,9 @@ def main_decode(args, oracle_pool):
         "kv_GBps_step": kv_bytes / (ms_per_step * 1e-3) / 1e9,
         "context_tokens_per_s": float(w.context_lens.sum()) / (ms_per_step * 1e-3),
         "kernel_us": {"slot_mapping": per_kernel_ms[0] * 1e3, "reshape_and_cache": per_kernel_ms[1] * 1e3,
-                      "decode_partition": per_kernel_ms[2] * 1e3, "combine": per_kernel_ms[3] * 1e3},
+                      "decode_partition": per_kernel_ms[2] * 1e3,
+                      "combine": per_kernel_ms[3] * 1e3 if merged else None},
+        "plain_entry_point": plain,
         "decode_partition_us_percentiles": part_pct,
         "step_us_percentiles": step_pct,
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,

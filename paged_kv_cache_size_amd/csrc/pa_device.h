@@ -238,6 +238,8 @@ struct MfmaOps<DT_BF16> {
     const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};  // v_cvt_pk_bf16_f32, nearest even
     return __builtin_bit_cast(uint32_t, v);
   }
+  // the sum of the two values a pack() word holds, as the matrix core reads them
+  static __device__ __forceinline__ float sum_pair(uint32_t w) { return bf16_lo(w) + bf16_hi(w); }
 };
 
 template <>
@@ -252,6 +254,9 @@ struct MfmaOps<DT_F16> {
   }
   static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
     return float_to_f16_bits(lo) | (float_to_f16_bits(hi) << 16);
+  }
+  static __device__ __forceinline__ float sum_pair(uint32_t w) {
+    return f16_bits_to_float(w & 0xffffu) + f16_bits_to_float(w >> 16);
   }
 };
 

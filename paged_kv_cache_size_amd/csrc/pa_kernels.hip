@@ -598,8 +598,9 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - mn);
-    l = fmaf(l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
     const uint2 pb = make_uint2(Ops::pack(p[0], p[1]), Ops::pack(p[2], p[3]));
+    // the denominator sums the same dtype-rounded weights that P.V multiplies
+    l = fmaf(l, alpha, Ops::sum_pair(pb.x) + Ops::sum_pair(pb.y));
 #pragma unroll
     for (int t = 0; t < VPL; ++t) {
       const int w = t >> 1;

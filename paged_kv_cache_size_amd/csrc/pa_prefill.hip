@@ -86,8 +86,9 @@ __device__ __forceinline__ float rows_maximum(float x) {  // over the 4 row grou
 // i/4; ok[i] (boundary steps only): that key is visible to the lane's column.
 // Moves the running max m (log2 units) when a score exceeds it by more than
 // 2^8 (probabilities stay <= 256, exact in fp32 sums) and then rescales l and
-// the accumulators - a rare, wave-uniform branch; adds the probabilities to l
-// and returns them packed as the P.V B operand.  Absent keys get p = 0 by a
+// the accumulators - a rare, wave-uniform branch; adds the probabilities, as
+// rounded to the 16-bit type, to l and returns them packed as the P.V B
+// operand.  Absent keys get p = 0 by a
 // select after the exponential (not a -inf score, which times a zero scale
 // would be NaN).  qscale >= 0, so the max of the raw scores scales to the max
 // of the scaled ones.
@@ -114,8 +115,11 @@ __device__ __forceinline__ uint4 softmax_pair(const float (&x)[8], const bool (&
     const float e = fast_exp2(fmaf(x[i], qscale, nm));
     p[i] = kInterior || ok[i] ? e : 0.f;
   }
-  l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-  return make_uint4(Ops::pack(p[0], p[1]), Ops::pack(p[2], p[3]), Ops::pack(p[4], p[5]), Ops::pack(p[6], p[7]));
+  const uint4 pk =
+      make_uint4(Ops::pack(p[0], p[1]), Ops::pack(p[2], p[3]), Ops::pack(p[4], p[5]), Ops::pack(p[6], p[7]));
+  // the denominator sums the same dtype-rounded weights that P.V multiplies
+  l += (Ops::sum_pair(pk.x) + Ops::sum_pair(pk.y)) + (Ops::sum_pair(pk.z) + Ops::sum_pair(pk.w));
+  return pk;
 }
 
 // A query operand chunk (8 16-bit values) as loaded, with every sign flipped
