@@ -39,6 +39,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_size_amd", "csrc", "pa_kernels.hip")
 METRIC = "paged decode attention tokens/s and KV-read GB/s (% of MI355X HBM peak)"
 PREFILL_METRIC = "chunked-prefill paged attention new tokens/s and TFLOP/s (% of MI355X dense MFMA peak)"
+MULTI_TOKEN_METRIC = "multi-token paged attention new tokens/s and KV-read GB/s (% of MI355X HBM peak)"
 COPY_METRIC = "copy-on-write block copies/s and copy GB/s (% of MI355X HBM peak)"
 SWAP_METRIC = "block swap-out + swap-in GB/s between HBM and pinned host memory (% of a PCIe Gen5 x16 link)"
 HOST_LINK_GBPS = 64.0  # PCIe Gen5 x16, one direction, published
@@ -313,15 +314,23 @@ def main_prefill(args):
     ms_per_step, per_kernel_ms, wall = time_stages(stages, args.steps, args.warmup)
     flops = pb.attention_flops()
     attn_ms = per_kernel_ms[2]
-    # the library runs the cooperative tile once a sequence brings more than
-    # 16 (token, query head) columns per KV head
-    rep = H // w.num_kv_heads
-    repc = max(c for c in range(1, 17) if rep % c == 0)
-    kernel = "prefill_wg_kernel" if pb.max_query_len * repc > 16 else "prefill_mfma_kernel"
-    achieved = flops / (attn_ms * 1e-3) / 1e12
-    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    if w.dtype == "f32":
+        # fp32: the VALU tile in column mode, bound by HBM (every context
+        # token's K and V read once per step)
+        kernel = "decode_partition_kernel (column mode)"
+        achieved = pb.kv_read_bytes() / (attn_ms * 1e-3) / 1e9
+        bound, peak, unit = "hbm", HBM_PEAK_GBPS, "GB/s"
+    else:
+        # the library runs the cooperative tile once a sequence brings more
+        # than 16 (token, query head) columns per KV head
+        rep = H // w.num_kv_heads
+        repc = max(c for c in range(1, 17) if rep % c == 0)
+        kernel = "prefill_wg_kernel" if pb.max_query_len * repc > 16 else "prefill_mfma_kernel"
+        achieved = flops / (attn_ms * 1e-3) / 1e12
+        bound, peak, unit = "mfma", MFMA_PEAK_TFLOPS[w.dtype], "TFLOP/s"
     rec = {
-        "metric": PREFILL_METRIC, "value": T / (ms_per_step * 1e-3), "unit": "new tokens/s", "n_gpus": 1,
+        "metric": MULTI_TOKEN_METRIC if bound == "hbm" else PREFILL_METRIC, "value": T / (ms_per_step * 1e-3),
+        "unit": "new tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "accumulate": "f32", "data": "synthetic",
         "config": {"workload": pb.name, "num_seqs": w.num_seqs, "new_tokens": T, "max_query_len": pb.max_query_len,
@@ -332,9 +341,10 @@ def main_prefill(args):
         "attention_flops_per_step": flops,
         "kernel_us": {"slot_mapping": per_kernel_ms[0] * 1e3, "reshape_and_cache": per_kernel_ms[1] * 1e3,
                       "prefill_attention": attn_ms * 1e3},
-        "roofline": {"bound": "mfma", "kernel": kernel, "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": load_traffic(pb.name, "prefill_attention") if args.layout == "split" else None},
+        "roofline": {"bound": bound, "kernel": kernel, "achieved": achieved, "peak": peak,
+                     "unit": unit, "frac": achieved / peak,
+                     "traffic": (load_traffic(pb.name, "decode_partition" if w.dtype == "f32" else "prefill_attention")
+                                 if args.layout == "split" else None)},
         "kv_read_bytes_per_step": pb.kv_read_bytes(),
         "cpu_baseline": base,
         "wall_s_timed": wall,

@@ -59,7 +59,10 @@ DecodeGrid decode_grid(const DecodeShape& s) {
   g.repc = rep_per_wave(g.rep, max_rep_per_wave(s.dtype));
   g.chunks = g.rep / g.repc;
   g.units = s.num_kv_heads * g.chunks;
-  g.wpw = g.units % 4 == 0 ? 4 : (g.units % 2 == 0 ? 2 : 1);
+  g.wpw = (kDecodeMaxWpw >= 8 && s.dtype != PA_F32 && g.units % 8 == 0) ? 8
+          : g.units % 4 == 0                                                ? 4
+          : g.units % 2 == 0                                                ? 2
+                                                                            : 1;
   g.groups = g.units / g.wpw;
   return g;
 }
@@ -376,14 +379,32 @@ int prefill_partition_bounds(const PrefillShape& s, int* min_parts, int* max_par
   return PA_OK;
 }
 
+int cols_per_wave(int head_dim) { return head_dim == 64 ? kMaxRepPerWaveValu : kMaxRepPerWaveValu / 2; }
+
+ColumnGrid column_grid(const PrefillShape& s) {
+  const int64_t rep = s.d.num_heads / s.d.num_kv_heads;
+  ColumnGrid g;
+  g.cols = cols_per_wave(s.d.head_dim);
+  const int64_t chunks = ((int64_t)s.max_query_len * rep + g.cols - 1) / g.cols;
+  g.wpw = chunks >= 4 ? 4 : (chunks >= 2 ? 2 : 1);
+  g.ctiles = (int)((chunks + g.wpw - 1) / g.wpw);
+  g.items = (int64_t)s.d.num_seqs * s.d.num_kv_heads * g.ctiles;
+  return g;
+}
+
 int prefill_partition_size(const PrefillShape& s, int requested, int num_cus, int wg_per_cu) {
+  const PrefillGrid pg = prefill_grid(s);
+  return prefill_partition_size_for(s, pg.items, pg.waves, requested, num_cus, wg_per_cu);
+}
+
+int prefill_partition_size_for(const PrefillShape& s, int64_t items_per_part, int waves, int requested,
+                               int num_cus, int wg_per_cu) {
   const int bs = s.d.block_size;
   if (requested != 0) return validate_prefill_partition(requested, bs);
   // Partitions are whole granules (max(16, block size) tokens); costs count
   // 16-token steps.
   const int64_t gran = partition_granule(bs);
   const int64_t steps_per_gran = gran / kBlockSize;
-  const PrefillGrid pg = prefill_grid(s);
   const int64_t slots = total_slots(num_cus, wg_per_cu);
   const int64_t ng = (s.d.max_context_len + gran - 1) / gran;
   int lo = 1, hi = 1;
@@ -396,13 +417,13 @@ int prefill_partition_size(const PrefillShape& s, int requested, int num_cus, in
     prev_pg = pgr;
     const int64_t p = (ng + pgr - 1) / pgr;
     if (p > hi || pgr * gran > max_prefill_partition_tokens(bs)) continue;
-    const int64_t items = pg.items * p;
+    const int64_t items = items_per_part * p;
     const double item = (double)(pgr * steps_per_gran) + kItemSetup;
     const int64_t tail = items % slots;
     double cost = (double)(items / slots) * item;
     if (tail > 0) cost += item / std::min(kMaxSpeedup, (double)slots / (double)tail);
     if (p > 1) {  // merge: every partial read once
-      const double wg_step_bytes = (double)pg.waves * 2.0 * kBlockSize * s.d.head_dim * elem_bytes(s.d.dtype);
+      const double wg_step_bytes = (double)waves * 2.0 * kBlockSize * s.d.head_dim * elem_bytes(s.d.dtype);
       cost += kMergeLaunch + 2.0 * (double)s.num_tokens * s.d.num_heads * p * (s.d.head_dim + 2) * 4.0 /
                                  ((double)slots * wg_step_bytes);
     }

@@ -80,6 +80,13 @@ int check_decode(const void* out, const void* query, const void* k_pool, const v
                  const int32_t* block_tables, const int32_t* context_lens, const DecodeShape& s,
                  float scale);
 
+#ifndef PA_DECODE_MAX_WPW
+#define PA_DECODE_MAX_WPW 4
+#endif
+// Most waves per workgroup of the 16-bit decode kernel (4, or 8 when the
+// build sets PA_DECODE_MAX_WPW=8).
+constexpr int kDecodeMaxWpw = PA_DECODE_MAX_WPW;
+
 // Launch geometry of the decode partition kernel: one wave per (sequence,
 // partition, KV head, chunk of `repc` query heads); `wpw` waves per workgroup
 // share (sequence, partition); `groups` workgroups per (sequence, partition).
@@ -158,6 +165,21 @@ struct PrefillGrid {
 };
 PrefillGrid prefill_grid(const PrefillShape& s);
 
+// Column mode of the VALU tile (fp32 prefill): the columns of a (sequence,
+// KV head) are its (new token, query head) pairs, `cols` per wave, the waves
+// of a workgroup on consecutive columns so they read each K/V block at the
+// same time; ctiles workgroups per (sequence, KV head, partition).  Eight
+// columns per wave at head_dim 64, four at 128 (eight would need more than
+// 256 registers: one wave per SIMD instead of two).
+int cols_per_wave(int head_dim);
+struct ColumnGrid {
+  int cols;       // columns per wave
+  int wpw;        // waves per workgroup
+  int ctiles;     // workgroups per (sequence, KV head, partition)
+  int64_t items;  // workgroups per partition
+};
+ColumnGrid column_grid(const PrefillShape& s);
+
 // Partitions the automatic prefill split may use: at least enough for the
 // 256-block table slice, at most one per 128 tokens, and partials within
 // kPrefillWorkspaceCap.
@@ -167,6 +189,9 @@ int prefill_partition_bounds(const PrefillShape& s, int* min_parts, int* max_par
 // to pick the candidate of least cost (every item taken at max_context_len,
 // whole waves of `slots` workgroups, plus the merge).  Negated pa_status on error.
 int prefill_partition_size(const PrefillShape& s, int requested, int num_cus, int wg_per_cu);
+// The same choice for a launch of `items` workgroups of `waves` waves per partition.
+int prefill_partition_size_for(const PrefillShape& s, int64_t items, int waves, int requested, int num_cus,
+                               int wg_per_cu);
 
 // Shared-prefix (cascade) decode: partitions of both passes, and the partial
 // slots per (row, head): the prefix's partitions, then the suffix's.

@@ -107,12 +107,14 @@ struct DecodeArgs {
   // span = what one 16-token step of a block may touch from its first byte
   int64_t block_stride;
   uint32_t row_stride, head_stride, span;
-  // Row mode (VALU kernel only): non-null query_start_loc [num_seqs + 1]
-  // makes each work row one query row of a varlen batch - row r of sequence b
-  // at position L_b - n_b + i sees keys [0, L_b - n_b + i] - instead of one
-  // decode query per sequence.
+  // Column mode (VALU kernel only): non-null query_start_loc [num_seqs + 1]
+  // makes the columns of a (sequence, KV head) its (new token, query head)
+  // pairs - new token i of sequence b at position L_b - n_b + i sees keys
+  // [0, L_b - n_b + i] - instead of the query heads of one decode query;
+  // ctiles workgroups of wpw waves per (sequence, KV head, partition) cover
+  // them, REPC columns per wave.
   const int32_t* query_start_loc;
-  int num_seqs;
+  int num_seqs, ctiles;
 };
 
 template <int DT, int D, int REPC>
@@ -127,7 +129,10 @@ struct DecodeTile {
   static_assert(LPR >= 8 && LPR <= 32 && BS % RPI == 0, "tile shape");
 };
 
-// One wave = one (sequence b, partition s, KV head g, chunk of REPC query heads).
+// One wave = REPC columns of one (sequence b, partition s, KV head g): in
+// decode, a chunk of the query heads g serves; in column mode, consecutive
+// (new token, query head) pairs of a varlen batch, each with its own causal
+// key limit, so the rows of a sequence share every K/V read of the wave.
 // The wave walks the partition in steps of 16 tokens.  Lane l reads, for
 // every step, rows i*RPI + l/LPR (i < NLD), bytes (l % LPR)*16 .. +16 of the
 // row.  Each lane runs its own online softmax over the tokens it holds (all
@@ -149,52 +154,78 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
   const int wave = threadIdx.x >> 6;
   const int wpw = blockDim.x >> 6;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int grp = logical % a.groups;
-  const int seq_part = logical / a.groups;
-  const int s = seq_part % a.num_parts;
-  const int row = seq_part / a.num_parts;  // sequence (decode) or query row (row mode)
-  const int unit = grp * wpw + wave;
-  const int g = unit / a.chunks;
-  const int h0 = g * a.rep + (unit % a.chunks) * REPC;
   const int r = lane / LPR, c = lane % LPR;
 
-  int b = row, L;
-  if (a.query_start_loc) {  // the sequence owning this row: largest b with qsl[b] <= row
-    int lo = 0, hi = a.num_seqs;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.query_start_loc[mid] <= row) lo = mid;
-      else hi = mid;
+  // This wave's columns: the output row (query row * H + query head) and the
+  // number of context keys each sees; wg_lim bounds the keys of every wave
+  // of the workgroup (they share b and s, and so the block-table range).
+  int b, g, s, wg_lim;
+  size_t qrow[REPC];
+  int lim[REPC];
+  bool live[REPC];
+  if (!a.query_start_loc) {  // decode: the query heads of KV head g, one query row
+    const int grp = logical % a.groups;
+    const int seq_part = logical / a.groups;
+    s = seq_part % a.num_parts;
+    b = seq_part / a.num_parts;
+    const int unit = grp * wpw + wave;
+    g = unit / a.chunks;
+    const int h0 = g * a.rep + (unit % a.chunks) * REPC;
+    wg_lim = a.context_lens[b];
+#pragma unroll
+    for (int h = 0; h < REPC; ++h) {
+      qrow[h] = (size_t)b * a.num_heads + h0 + h;
+      lim[h] = wg_lim;
+      live[h] = true;
     }
-    b = lo;
+  } else {  // column mode: (new token, query head) pairs, ctile fastest so they share K/V in L2
+    const int ct = logical % a.ctiles;
+    int rest = logical / a.ctiles;
+    s = rest % a.num_parts;
+    rest /= a.num_parts;
+    g = rest % a.num_kv_heads;
+    b = rest / a.num_kv_heads;
     const int q0 = a.query_start_loc[b], n = a.query_start_loc[b + 1] - q0;
-    if (row >= q0 + n) return;  // a row no sequence owns
-    L = a.context_lens[b] - n + (row - q0) + 1;
-  } else {
-    L = a.context_lens[b];
+    const int L = a.context_lens[b];
+    const int cols = n * a.rep;
+    if (ct * wpw * REPC >= cols) return;  // workgroup-uniform: no column of this sequence here
+    const int c0 = (ct * wpw + wave) * REPC;
+    wg_lim = L - n + (min(cols, (ct + 1) * wpw * REPC) - 1) / a.rep + 1;
+#pragma unroll
+    for (int h = 0; h < REPC; ++h) {
+      const int cc = c0 + h, ti = cc / a.rep;
+      live[h] = cc < cols;
+      qrow[h] = (size_t)(q0 + (live[h] ? ti : 0)) * a.num_heads + g * a.rep + cc % a.rep;
+      lim[h] = live[h] ? L - n + ti + 1 : 0;
+    }
   }
+  int wlim = 0, lim_min = 1 << 30;  // this wave's key range, and where its masks start
+#pragma unroll
+  for (int h = 0; h < REPC; ++h)
+    if (live[h]) {
+      wlim = max(wlim, lim[h]);
+      lim_min = min(lim_min, lim[h]);
+    }
+
   const int start = s * a.part_tokens;
-  if (start >= L) {
-    if (s == 0 && r == 0) {  // empty context: zeros
+  const int wg_end = min(wg_lim, start + a.part_tokens);
+  if (start >= wg_end) {  // workgroup-uniform
+    if (!a.query_start_loc && s == 0 && r == 0) {  // decode, empty context: zeros
       float z[EPL] = {};
-      for (int h = 0; h < REPC; ++h)
-        store_row<DT, EPL>((uint8_t*)a.out + ((size_t)row * a.num_heads + h0 + h) * ROWB + c * 16, z);
+      for (int h = 0; h < REPC; ++h) store_row<DT, EPL>((uint8_t*)a.out + qrow[h] * ROWB + c * 16, z);
     }
     return;
   }
-  const int end = min(L, start + a.part_tokens);
-  const int seq_parts = (L + a.part_tokens - 1) / a.part_tokens;
   const int pshift = MODE != kBlocks16 ? a.block_shift : 0;
   const int pool_bs = SUB ? BS << pshift : GATHER ? BS >> pshift : BS;  // tokens per pool block
   const int blk0 = start / pool_bs;  // partitions start on a pool block
-  const int nblk = (end - start + BS - 1) / BS;  // 16-token steps
-  const int nent = (end - start + pool_bs - 1) / pool_bs;  // table entries of the partition
+  const int nent = (wg_end - start + pool_bs - 1) / pool_bs;  // table entries the workgroup reads
 
   // This partition's block-table slice: in VGPR lanes, fetched per step by
   // readlane (blocks of 16 tokens or more, <= kMaxPartitionBlocks entries),
   // or staged in LDS for the workgroup and read per row (smaller blocks,
   // <= kMaxSmallBlockPartition entries; every wave of the workgroup serves
-  // the same row and partition).
+  // the same sequence and partition).
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk0;
   TableSlice tab;
   __shared__ int32_t stab[GATHER ? pa::kMaxSmallBlockPartition : 1];
@@ -203,16 +234,17 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
   else
     tab.load(bt, nent, lane);
 
-  // Query rows of the REPC heads, scaled into log2 units.
+  const int end = min(wlim, start + a.part_tokens);  // this wave's keys
+  if (start >= end) return;  // no key of this wave's columns here (no barrier follows)
+  const int nblk = (end - start + BS - 1) / BS;  // 16-token steps
+
+  // Query rows of the REPC columns, scaled into log2 units.
   float q[REPC][EPL];
-  {
-    const uint8_t* qp = (const uint8_t*)a.query + ((size_t)row * a.num_heads + h0) * ROWB + c * 16;
 #pragma unroll
-    for (int h = 0; h < REPC; ++h) {
-      unpack16<DT>(*reinterpret_cast<const uint4*>(qp + h * ROWB), q[h]);
+  for (int h = 0; h < REPC; ++h) {
+    unpack16<DT>(*reinterpret_cast<const uint4*>((const uint8_t*)a.query + qrow[h] * ROWB + c * 16), q[h]);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) q[h][e] *= a.qscale;
-    }
+    for (int e = 0; e < EPL; ++e) q[h][e] *= a.qscale;
   }
 
   const size_t row_stride = a.row_stride;
@@ -242,15 +274,23 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
 
+  // K streams non-temporal in decode, as in the matrix-core tile (fp32
+  // 256 x 4096: 1425 -> 1298 us): each K row is read by one wave.  In column
+  // mode the waves of a workgroup read the same rows together, so K keeps the
+  // default policy and the later waves find it in the caches.
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const bool k_once = a.query_start_loc == nullptr;
+  auto load_k = [&](const uint8_t* p) -> uint4 {
+    if (k_once) return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+    return *reinterpret_cast<const uint4*>(p);
+  };
   auto load_block = [&](int j, uint4* kr, uint4* vr) {
     if constexpr (GATHER) {  // per-row blocks; rows past the partition re-read its last block (masked)
       size_t base[NLD];
       step_block_bases<NLD>(stab, j, pshift, nent, block_stride, sblk, base);
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        kr[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
-                                              reinterpret_cast<const u32x4_t*>(a.k_pool + base[i] + sin[i])));
+        kr[i] = load_k(a.k_pool + base[i] + sin[i]);
         vr[i] = *reinterpret_cast<const uint4*>(a.v_pool + base[i] + sin[i]);
       }
       return;
@@ -260,15 +300,16 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
                            : (size_t)(uint32_t)tab.get(j) * block_stride;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      // K streams non-temporal, as in the matrix-core tile (fp32 256 x 4096:
-      // 1425 -> 1298 us)
-      kr[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
-                                            kbase + off + (size_t)i * RPI * row_stride)));
+      kr[i] = load_k(kbase + off + (size_t)i * RPI * row_stride);
       vr[i] = *reinterpret_cast<const uint4*>(vbase + off + (size_t)i * RPI * row_stride);
     }
   };
 
-  auto process = [&](const uint4* kr, const uint4* vr, int valid) {
+  // One step whose first key is tok0: keys at or past a column's limit get
+  // score -inf and weight 0 (rows past the wave's last key, stale or NaN,
+  // are zeroed before they reach the sums); steps below every limit skip the
+  // masks.
+  auto process = [&](const uint4* kr, const uint4* vr, int tok0) {
     float sc[NLD][REPC];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
@@ -282,13 +323,13 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
         sc[i][h] = group_sum<LPR>(part);
       }
     }
-    const bool partial = valid < BS;
+    const bool partial = tok0 + BS > lim_min;
     if (partial) {
 #pragma unroll
       for (int i = 0; i < NLD; ++i)
-        if (i * RPI + r >= valid)
 #pragma unroll
-          for (int h = 0; h < REPC; ++h) sc[i][h] = -INFINITY;
+        for (int h = 0; h < REPC; ++h)
+          if (tok0 + i * RPI + r >= lim[h]) sc[i][h] = -INFINITY;
     }
 #pragma unroll
     for (int h = 0; h < REPC; ++h) {
@@ -306,15 +347,16 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
     }
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const bool ok = !partial || (i * RPI + r < valid);
+      const int key = tok0 + i * RPI + r;
       float vf[EPL];
       unpack16<DT>(vr[i], vf);
-      if (!ok) {
+      if (partial && key >= end) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) vf[e] = 0.f;
       }
 #pragma unroll
       for (int h = 0; h < REPC; ++h) {
+        const bool ok = !partial || key < lim[h];
         const float p = ok ? fast_exp2(sc[i][h] - m[h]) : 0.f;
         l[h] += p;
 #pragma unroll
@@ -329,10 +371,10 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
   load_block(0, ka, va);
   for (int j = 0; j < nblk; j += 2) {
     if (j + 1 < nblk) load_block(j + 1, kb, vb);
-    process(ka, va, min(BS, end - (start + j * BS)));
+    process(ka, va, start + j * BS);
     if (j + 1 >= nblk) break;
     if (j + 2 < nblk) load_block(j + 2, ka, va);
-    process(kb, vb, min(BS, end - (start + (j + 1) * BS)));
+    process(kb, vb, start + (j + 1) * BS);
   }
 
   // Merge the RPI row-group streams.
@@ -347,19 +389,20 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
   }
   if (r != 0) return;
 
-  if (seq_parts == 1) {
+  // A column whose keys fit one partition writes its output row; the others
+  // leave partials for the merge (none in a partition past their keys).
 #pragma unroll
-    for (int h = 0; h < REPC; ++h) {
+  for (int h = 0; h < REPC; ++h) {
+    const int col_parts = (lim[h] + a.part_tokens - 1) / a.part_tokens;
+    if (!live[h] || s >= col_parts) continue;
+    if (col_parts == 1) {
       const float inv = l[h] > 0.f ? 1.f / l[h] : 0.f;
       float o[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[e] = acc[h][e] * inv;
-      store_row<DT, EPL>((uint8_t*)a.out + ((size_t)row * a.num_heads + h0 + h) * ROWB + c * 16, o);
-    }
-  } else {
-#pragma unroll
-    for (int h = 0; h < REPC; ++h) {
-      const size_t idx = ((size_t)row * a.num_heads + h0 + h) * a.num_parts + s;
+      store_row<DT, EPL>((uint8_t*)a.out + qrow[h] * ROWB + c * 16, o);
+    } else {
+      const size_t idx = qrow[h] * a.num_parts + s;
       float* dst = a.ws_acc + idx * D + c * EPL;
 #pragma unroll
       for (int e = 0; e < EPL; e += 4)
@@ -711,6 +754,9 @@ DecodeFn pick_mfma(int wpw) {
     case 1: return decode_mfma_kernel<DT, D, kRing, 1, MODE>;
     case 2: return decode_mfma_kernel<DT, D, kRing, 2, MODE>;
     case 4: return decode_mfma_kernel<DT, D, kRing, 4, MODE>;
+#if PA_DECODE_MAX_WPW >= 8
+    case 8: return decode_mfma_kernel<DT, D, kRing, 8, MODE>;
+#endif
     default: return nullptr;
   }
 }
@@ -722,9 +768,18 @@ DecodeFn pick_mfma_bs(int wpw, int block_size) {
   return pick_mfma<DT, D, kBlocksSmall>(wpw);
 }
 
+#ifndef PA_MHA_VALU
+#define PA_MHA_VALU 0
+#endif
+
 // fp32: VALU kernel (one instantiation per heads-per-wave); fp16/bf16: MFMA
-// kernel (one per waves-per-workgroup).
+// kernel (one per waves-per-workgroup).  A build with PA_MHA_VALU=1 runs
+// 16-bit batches without query-head groups (MHA) on the VALU kernel too.
 DecodeFn pick_decode(int dtype, int d, const pa::DecodeGrid& g, int block_size) {
+  if (PA_MHA_VALU && dtype != PA_F32 && g.rep == 1) {
+    if (dtype == PA_F16) return d == 64 ? pick_rep_bs<DT_F16, 64>(1, block_size) : pick_rep_bs<DT_F16, 128>(1, block_size);
+    return d == 64 ? pick_rep_bs<DT_BF16, 64>(1, block_size) : pick_rep_bs<DT_BF16, 128>(1, block_size);
+  }
   switch (dtype) {
     case PA_F32:
       return d == 64 ? pick_rep_bs<DT_F32, 64>(g.repc, block_size) : pick_rep_bs<DT_F32, 128>(g.repc, block_size);
@@ -811,6 +866,7 @@ int launch_partitions(void* out, const void* query, const pa::PoolView& pv, cons
   a.context_lens = context_lens;
   a.query_start_loc = nullptr;
   a.num_seqs = shp.num_seqs;
+  a.ctiles = 0;  // column mode only
   a.ws_acc = static_cast<float*>(workspace);
   a.ws_ml = ml_region(workspace, shp, plan.parts);
   a.num_heads = shp.num_heads;
@@ -856,21 +912,28 @@ int device_cu_count() {
   return cus;
 }
 
-const void* decode_rows_kernel(const DecodeShape& s, int* threads) {
-  const DecodeGrid g = decode_grid(s);
-  *threads = 64 * g.wpw;
-  return reinterpret_cast<const void*>(pick_decode(s.dtype, s.head_dim, g, s.block_size));
+// fp32 column mode: cols_per_wave(head_dim) columns per wave whatever the group size.
+DecodeFn pick_columns(const PrefillShape& s) {
+  if (s.d.dtype != PA_F32) return nullptr;
+  const int cols = cols_per_wave(s.d.head_dim);
+  return s.d.head_dim == 64 ? pick_rep_bs<DT_F32, 64>(cols, s.d.block_size)
+                            : pick_rep_bs<DT_F32, 128>(cols, s.d.block_size);
 }
 
-int launch_decode_rows(void* out, const void* query, const PoolView& pv, const int32_t* block_tables,
-                       const int32_t* context_lens, const int32_t* query_start_loc, const DecodeShape& s,
-                       int num_rows, float scale, void* ws_acc, void* ws_ml, int part_tokens, int num_parts,
-                       void* stream) {
-  const DecodeGrid gd = decode_grid(s);
-  const int64_t grid = (int64_t)num_rows * num_parts * gd.groups;
+const void* columns_kernel(const PrefillShape& s, int* threads) {
+  *threads = 64 * column_grid(s).wpw;
+  return reinterpret_cast<const void*>(pick_columns(s));
+}
+
+int launch_columns(void* out, const void* query, const PoolView& pv, const int32_t* block_tables,
+                   const int32_t* context_lens, const int32_t* query_start_loc, const PrefillShape& s, float scale,
+                   void* ws_acc, void* ws_ml, int part_tokens, int num_parts, void* stream) {
+  const ColumnGrid cg = column_grid(s);
+  const int64_t grid = cg.items * num_parts;
   if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-  DecodeFn fn = pick_decode(s.dtype, s.head_dim, gd, s.block_size);
+  DecodeFn fn = pick_columns(s);
   if (!fn) return PA_ERR_UNSUPPORTED;
+  const DecodeShape& d = s.d;
   DecodeArgs a;
   a.out = out;
   a.query = query;
@@ -879,24 +942,25 @@ int launch_decode_rows(void* out, const void* query, const PoolView& pv, const i
   a.block_stride = pv.block_stride;
   a.row_stride = (uint32_t)pv.row_stride;
   a.head_stride = (uint32_t)pv.head_stride;
-  a.span = (uint32_t)pv.step_span(s.head_dim * elem_bytes(s.dtype), s.num_kv_heads);
+  a.span = (uint32_t)pv.step_span(d.head_dim * elem_bytes(d.dtype), d.num_kv_heads);
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.query_start_loc = query_start_loc;
-  a.num_seqs = s.num_seqs;
+  a.num_seqs = d.num_seqs;
+  a.ctiles = cg.ctiles;
   a.ws_acc = static_cast<float*>(ws_acc);
   a.ws_ml = static_cast<float2*>(ws_ml);
-  a.num_heads = s.num_heads;
-  a.num_kv_heads = s.num_kv_heads;
-  a.rep = gd.rep;
-  a.chunks = gd.chunks;
-  a.max_blocks_per_seq = s.max_blocks_per_seq;
-  a.block_shift = block_shift(s.block_size);
+  a.num_heads = d.num_heads;
+  a.num_kv_heads = d.num_kv_heads;
+  a.rep = d.num_heads / d.num_kv_heads;
+  a.chunks = 0;  // decode mode only
+  a.groups = 0;
+  a.max_blocks_per_seq = d.max_blocks_per_seq;
+  a.block_shift = block_shift(d.block_size);
   a.part_tokens = part_tokens;
   a.num_parts = num_parts;
-  a.groups = gd.groups;
   a.qscale = scale * 1.44269504088896340736f;  // log2(e)
-  return launch_kernel(fn, dim3((unsigned)grid), dim3(64 * gd.wpw), static_cast<hipStream_t>(stream), a);
+  return launch_kernel(fn, dim3((unsigned)grid), dim3(64 * cg.wpw), static_cast<hipStream_t>(stream), a);
 }
 
 // Workgroups of `fn` (with `threads` threads) resident per compute unit, cached

@@ -983,37 +983,27 @@ size_t prefill_workspace(const pa::PrefillShape& s, int parts) {
   return pa::workspace_bytes(s.num_tokens, s.d.num_heads, s.d.head_dim, parts);
 }
 
-// fp32: every query row runs the VALU decode tile with its own causal
-// context (row i of sequence b sees keys 0 .. L_b - n_b + i), partials merged
-// as for the 16-bit tiles.  Rows share no K/V reads inside a workgroup: a
-// correctness path for fp32 pools, not a matrix-core one.
+// fp32: the VALU tile in column mode - the columns of a (sequence, KV head)
+// are its (new token, query head) pairs, eight per wave, each with its own
+// causal key limit; the waves of a workgroup take consecutive columns, so a
+// sequence's rows share each K/V read of a wave and its workgroup's waves
+// read the same blocks together.  Partials merged as for the 16-bit tiles.
 int prefill_rows(void* out, const void* query, const pa::PoolView& pv, const int32_t* block_tables,
                  const int32_t* context_lens, const int32_t* query_start_loc, const pa::PrefillShape& shp,
                  float scale, void* workspace, size_t workspace_bytes, int32_t partition_size, void* stream) {
   const pa::DecodeShape& d = shp.d;
-  int ps;
-  if (partition_size != 0) {
-    ps = pa::validate_partition(partition_size, d.block_size);
-    if (ps < 0) return -ps;
-  } else {
+  const pa::ColumnGrid cg = pa::column_grid(shp);
+  int cus = 256, per_cu = 1;
+  if (partition_size == 0) {
     int threads = 0;
-    const void* fn = pa::decode_rows_kernel(d, &threads);
+    const void* fn = pa::columns_kernel(shp, &threads);
     if (!fn) return PA_ERR_UNSUPPORTED;
-    const int cus = pa::device_cu_count();
-    const int per_cu = pa::resident_per_cu(fn, threads);
+    cus = pa::device_cu_count();
+    per_cu = pa::resident_per_cu(fn, threads);
     if (cus <= 0 || per_cu <= 0) return PA_ERR_HIP;
-    pa::DecodeShape rows = d;
-    rows.num_seqs = shp.num_tokens;  // every row taken at max_context_len
-    ps = pa::partition_size(rows, 0, cus, per_cu);
-    if (ps <= 0) return -ps;
-    int lo = 1, hi = 1;  // stay within the workspace pa_prefill_workspace_bytes sizes
-    pa::prefill_partition_bounds(shp, &lo, &hi);
-    if (pa::num_partitions(d.max_context_len, ps) > hi) {
-      const int gran = pa::partition_granule(d.block_size);
-      ps = (d.max_context_len + hi - 1) / hi;
-      ps = (ps + gran - 1) / gran * gran;
-    }
   }
+  const int ps = pa::prefill_partition_size_for(shp, cg.items, cg.wpw, partition_size, cus, per_cu);
+  if (ps <= 0) return -ps;
   const int parts = pa::num_partitions(d.max_context_len, ps);
   const size_t need = prefill_workspace(shp, parts);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
@@ -1021,8 +1011,8 @@ int prefill_rows(void* out, const void* query, const pa::PoolView& pv, const int
   float2* ws_ml = parts > 1 ? reinterpret_cast<float2*>(static_cast<float*>(workspace) +
                                                         (size_t)shp.num_tokens * d.num_heads * parts * d.head_dim)
                             : nullptr;
-  int rc = pa::launch_decode_rows(out, query, pv, block_tables, context_lens, query_start_loc, d, shp.num_tokens,
-                                  scale, ws_acc, ws_ml, ps, parts, stream);
+  int rc = pa::launch_columns(out, query, pv, block_tables, context_lens, query_start_loc, shp, scale, ws_acc,
+                              ws_ml, ps, parts, stream);
   if (rc != PA_OK || parts <= 1) return rc;
   PrefillCombineFn cf = pick_prefill_combine(d.dtype, d.head_dim);
   if (!cf) return PA_ERR_UNSUPPORTED;

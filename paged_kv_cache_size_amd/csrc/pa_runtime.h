@@ -50,17 +50,16 @@ int launch_kernel(void (*fn)(P...), dim3 grid, dim3 block, hipStream_t stream, A
              : PA_ERR_HIP;
 }
 
-struct DecodeShape;
+struct PrefillShape;
 struct PoolView;
-// The VALU decode kernel run over the query rows of a varlen batch (fp32
-// prefill): the kernel for shape `s` (num_seqs = sequences) and its
-// workgroup size, then the launch over `num_rows` rows (query_start_loc [num_seqs + 1]),
-// partials into ws_acc [rows, H, parts, D] / ws_ml [rows, H, parts] when a
-// row's keys span several partitions.
-const void* decode_rows_kernel(const DecodeShape& s, int* threads);
-int launch_decode_rows(void* out, const void* query, const PoolView& pv, const int32_t* block_tables,
-                       const int32_t* context_lens, const int32_t* query_start_loc, const DecodeShape& s,
-                       int num_rows, float scale, void* ws_acc, void* ws_ml, int part_tokens, int num_parts,
-                       void* stream);
+// The VALU decode kernel in column mode over the new tokens of a varlen batch
+// (fp32 prefill): the kernel for shape `s` and its workgroup size, then the
+// launch (query_start_loc [num_seqs + 1]), partials into
+// ws_acc [rows, H, parts, D] / ws_ml [rows, H, parts] for rows whose keys span
+// several partitions.
+const void* columns_kernel(const PrefillShape& s, int* threads);
+int launch_columns(void* out, const void* query, const PoolView& pv, const int32_t* block_tables,
+                   const int32_t* context_lens, const int32_t* query_start_loc, const PrefillShape& s, float scale,
+                   void* ws_acc, void* ws_ml, int part_tokens, int num_parts, void* stream);
 
 }  // namespace pa

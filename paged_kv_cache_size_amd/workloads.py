@@ -485,9 +485,24 @@ def handbook_verification_batch():
     return tables, seq_lens, query_lens, ks, vs, qs
 
 
+def multi_token_llama_f32(seed: int = 0, num_seqs: int = 256, context: int = 4096, new_tokens: int = 4,
+                          block_size: int = 16) -> PrefillBatch:
+    """Several new tokens per sequence on the Llama-style GQA layer in fp32: 256
+    sequences of 4096 tokens each add 4 tokens (a verification step of
+    speculative decoding, or a short chunk); 32 query / 8 KV heads, D 128, fp32
+    (8.6 GB of K/V); physical ids shuffled in a pool with 10% slack.  Each
+    (sequence, KV head) has 4 x 4 = 16 (token, query head) columns."""
+    pb = prefill_batch([context] * num_seqs, [new_tokens] * num_seqs, 32, 8, 128, "f32", seed=seed,
+                       name="multi_token_llama_f32", block_size=block_size)
+    pb.description = (f"{num_seqs} seqs x {new_tokens} new tokens on {context - new_tokens} cached tokens, "
+                      f"H 32 / Hkv 8, D 128, fp32")
+    return pb
+
+
 PREFILL_BUILDERS = {
     "chunked_prefill_llama_bf16": chunked_prefill_llama_bf16,
     "mixed_varlen_bf16": mixed_varlen_bf16,
+    "multi_token_llama_f32": multi_token_llama_f32,
 }
 
 

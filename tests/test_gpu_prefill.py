@@ -144,9 +144,11 @@ def test_block_sizes(bs, wide):
     check_prefill(pb, seed=bs, partition_size=max(16, bs), poisoned=True)
 
 
-@pytest.mark.parametrize("h,hkv", [(8, 2), (32, 8), (12, 12), (9, 1)])
+@pytest.mark.parametrize("h,hkv", [(8, 2), (32, 8), (12, 12), (9, 1), (12, 2), (6, 1)])
 def test_fp32_rows(h, hkv):
-    # fp32: each query row runs the VALU tile with its own causal context
+    # fp32: the VALU tile over (new token, query head) columns, each with its
+    # own causal key limit; groups of 6 and 9 make a wave's columns straddle
+    # two new tokens
     lens = [1, 2, 15, 16, 17, 64, 129, 700]
     qlens = [1, 2, 15, 3, 17, 40, 1, 300]
     pb = W.prefill_batch(lens, qlens, h, hkv, 64, "f32", seed=h + hkv, extra_cols=1)
@@ -164,6 +166,24 @@ def test_fp32_rows_block_sizes(bs, d):
     pb = W.prefill_batch(lens, qlens, 8, 2, d, "f32", seed=bs + d, extra_cols=1, block_size=bs)
     check_prefill(pb, seed=bs, partition_size=0, poisoned=True)
     check_prefill(pb, seed=bs, partition_size=max(16, bs) * 2, poisoned=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp32_whole_prompts_and_decode_rows(d):
+    # whole prompts (n = L: the full causal triangle) beside decode rows and
+    # chunks, fp32, every column with its own limit
+    lens = [1, 2, 15, 16, 17, 64, 129, 300, 1000]
+    qlens = [1, 2, 15, 16, 1, 64, 100, 300, 8]
+    pb = W.prefill_batch(lens, qlens, 8, 2, d, "f32", seed=d, extra_cols=1)
+    check_prefill(pb, seed=3, partition_size=0, poisoned=True)
+    check_prefill(pb, seed=3, partition_size=128, poisoned=True)
+
+
+def test_fp32_multi_token_llama_subset():
+    # the fp32 multi-token batch of the benchmark (4 new tokens on 4096-token
+    # contexts, 32/8 heads, D 128) on 8 sequences, at the automatic partition
+    pb = W.multi_token_llama_f32(num_seqs=8)
+    check_prefill(pb, seed=0, partition_size=0)
 
 
 @pytest.mark.parametrize("ps", [0, 16])
