@@ -432,10 +432,16 @@ int pa_seq_block_table(const pa_block_pool* pool, int32_t seq, int32_t* table, i
  * parallel sampling: "KV cache: capacity derivation, paging and reclamation",
  * section on shared prefixes; xxqk.cn PagedAttention article, parallel
  * sampling).  seq_prefix_lens[b] repeats its group's prefix length.
- * A prefix pass reads each group's prefix blocks once and scores them against
- * every member's query; a suffix pass reads each sequence's blocks past the
- * prefix; a merge combines the two softmax partials per (sequence, head).
- * The result equals pa_decode_attention's within rounding.
+ * With 16-token blocks and fp16/bf16 one launch does it all: a workgroup per
+ * (group, KV head, set of members whose query heads fill the 16 matrix-core
+ * columns) reads the shared blocks once for the set, then each member's own
+ * blocks, its waves splitting those steps and merging their softmax states
+ * in LDS.  Otherwise (other block sizes, or more steps per set than four
+ * waves' table slices hold) a prefix pass reads each group's prefix blocks
+ * once and scores them against every member's query, a suffix pass reads
+ * each sequence's blocks past the prefix, and a merge combines the two
+ * softmax partials per (sequence, head).  Either way the result equals
+ * pa_decode_attention's within rounding.
  *   group_start int32 [num_groups + 1], prefix_lens int32 [num_groups],
  *   seq_prefix_lens int32 [num_seqs]: device memory (pa_shared_prefix_groups
  *   computes them on the host from the tables).
@@ -472,7 +478,8 @@ int pa_shared_prefix_groups(const int32_t* block_tables, const int32_t* context_
                             int32_t* num_groups, int32_t* max_group_size, int32_t* max_prefix_len);
 
 /*
- * Entry points over either pool layout (pa_kv_layout).  Each behaves exactly
+ * Entry points over either pool layout (pa_kv_layout), the shared-prefix
+ * decode's among them (declared above with the others).  Each behaves exactly
  * as the entry point of the same name without "_layout" - same arguments,
  * device-content rules and errors - with the pool given by `layout`:
  *   PA_KV_SPLIT  k_pool and v_pool as everywhere else;
@@ -486,6 +493,15 @@ int pa_reshape_and_cache_layout(const void* key, const void* value, void* k_pool
                                 const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype dtype,
                                 pa_kv_layout layout, void* stream);
+int pa_decode_attention_shared_prefix_layout(void* out, const void* query, const void* k_pool, const void* v_pool,
+                                             const int32_t* block_tables, const int32_t* context_lens,
+                                             const int32_t* group_start, const int32_t* prefix_lens,
+                                             const int32_t* seq_prefix_lens, int32_t num_seqs, int32_t num_groups,
+                                             int32_t max_group_size, int32_t num_heads, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                             int32_t max_context_len, int32_t max_prefix_len, float scale,
+                                             pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                                             pa_kv_layout layout, void* stream);
 int pa_decode_attention_layout(void* out, const void* query, const void* k_pool, const void* v_pool,
                                const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,

@@ -59,6 +59,9 @@ SIGNATURES = {
     "pa_decode_attention_shared_prefix": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                                          _I32, _I32, _I32, _I32, _I32, _I32, _F32, ctypes.c_int,
                                                          _P, _SZ, _P]),
+    "pa_decode_attention_shared_prefix_layout": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32,
+                                                                _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                                _F32, ctypes.c_int, _P, _SZ, ctypes.c_int, _P]),
     "pa_shared_prefix_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "pa_shared_prefix_groups": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "pa_reshape_and_cache_layout": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I64, ctypes.c_int,
@@ -452,14 +455,16 @@ def pa_shared_prefix_groups(block_tables, context_lens, block_size: int, min_pre
 
 
 def pa_decode_attention_shared_prefix(query, k_pool, v_pool, block_tables, context_lens, groups, scale: float,
-                                      max_context_len: int, out=None, workspace=None, device_groups=None):
+                                      max_context_len: int, out=None, workspace=None, device_groups=None,
+                                      layout: int = PA_KV_SPLIT):
     """Cascade decode: shared prefixes read once per group.  ``groups`` is a
     SharedPrefixGroups; ``device_groups`` optionally its three arrays already
-    on the device (group_start, prefix_lens, seq_prefix_lens)."""
+    on the device (group_start, prefix_lens, seq_prefix_lens).  ``layout``
+    PA_KV_FUSED: ``k_pool`` is the fused pool and ``v_pool`` None."""
     torch = _torch()
     B, H, D = query.shape
-    nb, bs, hkv, d2 = k_pool.shape
-    if d2 != D or k_pool.shape != v_pool.shape or block_tables.shape[0] != B or context_lens.shape != (B,):
+    (nb, bs, hkv, d2), kp, vp = _pool(k_pool, v_pool, layout)
+    if d2 != D or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("shapes do not match")
     if device_groups is None:
         device_groups = tuple(torch.from_numpy(x).to(query.device)
@@ -470,14 +475,16 @@ def pa_decode_attention_shared_prefix(query, k_pool, v_pool, block_tables, conte
     need = int(lib().pa_shared_prefix_workspace_bytes(B, H, D, int(max_context_len), groups.max_prefix_len))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=query.device)
-    rc = lib().pa_decode_attention_shared_prefix(
-        _dev(out, "out", query.dtype, 3), _dev(query, "query", ndim=3), _dev(k_pool, "k_pool", ndim=4),
-        _dev(v_pool, "v_pool", ndim=4), _dev(block_tables, "block_tables", torch.int32, 2),
-        _dev(context_lens, "context_lens", torch.int32, 1), _dev(gs, "group_start", torch.int32, 1),
-        _dev(pl, "prefix_lens", torch.int32, 1), _dev(spl, "seq_prefix_lens", torch.int32, 1), B, groups.num_groups,
-        groups.max_group_size, H, hkv, D, bs, block_tables.shape[1], int(max_context_len), groups.max_prefix_len,
-        float(scale), pa_dtype(query), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-        _stream(query))
+    args = (_dev(out, "out", query.dtype, 3), _dev(query, "query", ndim=3), kp, vp,
+            _dev(block_tables, "block_tables", torch.int32, 2), _dev(context_lens, "context_lens", torch.int32, 1),
+            _dev(gs, "group_start", torch.int32, 1), _dev(pl, "prefix_lens", torch.int32, 1),
+            _dev(spl, "seq_prefix_lens", torch.int32, 1), B, groups.num_groups, groups.max_group_size, H, hkv, D, bs,
+            block_tables.shape[1], int(max_context_len), groups.max_prefix_len, float(scale), pa_dtype(query),
+            _dev(workspace, "workspace"), workspace.numel() * workspace.element_size())
+    if layout == PA_KV_SPLIT:
+        rc = lib().pa_decode_attention_shared_prefix(*args, _stream(query))
+    else:
+        rc = lib().pa_decode_attention_shared_prefix_layout(*args, int(layout), _stream(query))
     _check(rc, "pa_decode_attention_shared_prefix")
     return out
 

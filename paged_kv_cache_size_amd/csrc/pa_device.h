@@ -168,6 +168,14 @@ __device__ __forceinline__ void step_block_bases(const int32_t* stab, int jj, in
   for (int i = 0; i < N; ++i) base[i] = (size_t)(uint32_t)stab[min(e0 + blk[i], nent - 1)] * block_stride;
 }
 
+// s_waitcnt vmcnt(N), the other counters left free (gfx9 field layout:
+// vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Workgroup id -> logical id such that each XCD (workgroups are dealt to the
 // 8 XCDs round-robin) receives one contiguous range of logical ids; a bijection
 // whatever the hardware order.

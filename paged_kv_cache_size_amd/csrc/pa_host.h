@@ -193,6 +193,19 @@ int prefill_partition_size(const PrefillShape& s, int requested, int num_cus, in
 int prefill_partition_size_for(const PrefillShape& s, int64_t items, int waves, int requested, int num_cus,
                                int wg_per_cu);
 
+// Shared-prefix decode in one launch: a workgroup per (group, KV head, chunk
+// of query heads, set of members), the set's members x query heads filling
+// the 16 columns of the matrix-core tile; `waves` waves split the set's key
+// steps (its shared blocks, then each member's own) and merge in LDS.
+// waves == 0: the batch does not fit this form (block size other than 16,
+// fp32, or more than 4 x 256 steps per set) and takes the three-launch
+// cascade.
+struct SharedPrefixGrid {
+  int members_per_set, sets, waves;
+  int64_t items;  // workgroups
+};
+SharedPrefixGrid shared_prefix_grid(const DecodeShape& s, int num_groups, int max_group_size, int num_cus);
+
 // Shared-prefix (cascade) decode: partitions of both passes, and the partial
 // slots per (row, head): the prefix's partitions, then the suffix's.
 constexpr int kSharedPrefixPartition = 1024;

@@ -466,13 +466,6 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
   if (live) store_column<DT, D>(a, acc, m, lt, qrow, s, col_parts, gq);
 }
 
-// s_waitcnt vmcnt(N), the other counters left free (gfx9 field layout:
-// vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // Cooperative form for wide column ranges (long varlen rows, chunked
 // prefill): the waves of a workgroup take 16 * TILES consecutive columns each
@@ -1162,20 +1155,21 @@ extern "C" size_t pa_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num
   return (size_t)num_seqs * num_heads * slots * ((size_t)head_dim + 2) * sizeof(float);
 }
 
-extern "C" int pa_decode_attention_shared_prefix(
+extern "C" int pa_decode_attention_shared_prefix_layout(
     void* out, const void* query, const void* k_pool, const void* v_pool, const int32_t* block_tables,
     const int32_t* context_lens, const int32_t* group_start, const int32_t* prefix_lens,
     const int32_t* seq_prefix_lens, int32_t num_seqs, int32_t num_groups, int32_t max_group_size,
     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
     int32_t max_context_len, int32_t max_prefix_len, float scale, pa_dtype dtype, void* workspace,
-    size_t workspace_bytes, void* stream) {
+    size_t workspace_bytes, pa_kv_layout layout, void* stream) {
   if (num_seqs == 0) return PA_OK;  // an empty batch
   const pa::PrefillShape shp{{num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                               max_context_len, (int)dtype},
                              num_seqs,
                              1};
-  int rc = pa::check_shared_prefix(out, query, k_pool, v_pool, block_tables, context_lens, group_start, prefix_lens,
-                                   seq_prefix_lens, shp, num_groups, max_group_size, max_prefix_len, scale);
+  int rc = pa::check_shared_prefix(out, query, k_pool, layout == PA_KV_FUSED ? k_pool : v_pool, block_tables,
+                                   context_lens, group_start, prefix_lens, seq_prefix_lens, shp, num_groups,
+                                   max_group_size, max_prefix_len, scale);
   if (rc != PA_OK) return rc;
   const int p1 = pa::num_partitions(std::max(max_prefix_len, 1), pa::kSharedPrefixPartition);
   const int slots = pa::shared_prefix_slots(max_context_len, max_prefix_len);
@@ -1188,8 +1182,16 @@ extern "C" int pa_decode_attention_shared_prefix(
   if (!fn || !mf) return PA_ERR_UNSUPPORTED;
 
   pa::PoolView pv;
-  rc = pa::pool_view(k_pool, v_pool, PA_KV_SPLIT, block_size, num_kv_heads, head_dim, (int)dtype, &pv);
+  rc = pa::pool_view(k_pool, v_pool, (int)layout, block_size, num_kv_heads, head_dim, (int)dtype, &pv);
   if (rc != PA_OK) return rc;
+#ifndef PA_SHARED_PREFIX_SINGLE
+#define PA_SHARED_PREFIX_SINGLE 1
+#endif
+  if (PA_SHARED_PREFIX_SINGLE) {  // one launch when the batch fits it, else the passes below
+    rc = pa::launch_shared_prefix_single(out, query, pv, block_tables, context_lens, group_start, prefix_lens, shp.d,
+                                         num_groups, max_group_size, scale, stream);
+    if (rc != PA_ERR_UNSUPPORTED) return rc;
+  }
   PrefillArgs a;
   set_pool(&a, pv, shp.d);
   a.out = out;
@@ -1262,4 +1264,20 @@ extern "C" int pa_decode_attention_shared_prefix(
   const int64_t waves = (int64_t)num_seqs * num_heads;
   return pa::launch_kernel(mf, dim3((unsigned)((waves + 3) / 4)), dim3(256), st, out, a.ws_acc, a.ws_ml,
                            (int)waves, slots);
+}
+
+extern "C" int pa_decode_attention_shared_prefix(
+    void* out, const void* query, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+    const int32_t* context_lens, const int32_t* group_start, const int32_t* prefix_lens,
+    const int32_t* seq_prefix_lens, int32_t num_seqs, int32_t num_groups, int32_t max_group_size,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t max_context_len, int32_t max_prefix_len, float scale, pa_dtype dtype, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  if (num_seqs == 0) return PA_OK;  // an empty batch: every pointer may be NULL
+  if (!v_pool) return PA_ERR_INVALID_ARG;
+  return pa_decode_attention_shared_prefix_layout(out, query, k_pool, v_pool, block_tables, context_lens, group_start,
+                                                  prefix_lens, seq_prefix_lens, num_seqs, num_groups, max_group_size,
+                                                  num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                                  max_context_len, max_prefix_len, scale, dtype, workspace,
+                                                  workspace_bytes, PA_KV_SPLIT, stream);
 }

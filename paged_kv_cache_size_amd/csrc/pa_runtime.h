@@ -62,4 +62,12 @@ int launch_columns(void* out, const void* query, const PoolView& pv, const int32
                    const int32_t* context_lens, const int32_t* query_start_loc, const PrefillShape& s, float scale,
                    void* ws_acc, void* ws_ml, int part_tokens, int num_parts, void* stream);
 
+struct DecodeShape;
+// Shared-prefix decode in one launch (shared_prefix_grid); PA_ERR_UNSUPPORTED,
+// with nothing enqueued, when the batch does not fit that form.
+int launch_shared_prefix_single(void* out, const void* query, const PoolView& pv, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* group_start, const int32_t* prefix_lens,
+                                const DecodeShape& s, int num_groups, int max_group_size, float scale,
+                                void* stream);
+
 }  // namespace pa

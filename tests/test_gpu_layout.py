@@ -213,3 +213,35 @@ def test_fused_prefill_matches_split(ps):
     err = float(np.max(np.abs(O.widen(W.raw_numpy(fused_out), w.dtype) - ref)))
     say(f"  max abs err {err:.3e}")
     assert err <= TOL["bf16"], err
+
+
+# ------------------------------------------------------------------ shared-prefix decode
+
+@pytest.mark.parametrize("bs", [16, 4, 32])
+def test_shared_prefix_decode_fused_equals_split(bs):
+    # the cascade over a fused pool reads the same rows in the same order as
+    # over the split pools: bitwise equal outputs, within 2e-2 of the oracle;
+    # block 16 takes the one-launch form, 4 and 32 the three passes
+    from test_gpu_shared_prefix import forked_batch
+    rng = np.random.default_rng(bs + 40)
+    prompts = [int(x) for x in rng.integers(2 * bs, 300, 24)]
+    forks = [int(x) for x in rng.integers(1, 9, 24)]
+    gens = [[int(x) for x in rng.integers(1, 50, f)] for f in forks]
+    w = forked_batch(prompts, forks, gens, 32, 8, 128, "bf16", seed=bs, bs=bs)
+    say(f"shared prefix fused vs split bs={bs} B={w.num_seqs}")
+    g = PB.pa_shared_prefix_groups(w.block_tables, w.context_lens, bs)
+    t = W.make_tensors(w, 2, DEV)
+    fused = to_torch(O.fuse_kv(W.raw_numpy(t["k_pool"]), W.raw_numpy(t["v_pool"])), w.dtype)
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    lens = torch.from_numpy(w.context_lens).to(DEV)
+    split_out = PB.pa_decode_attention_shared_prefix(t["query"], t["k_pool"], t["v_pool"], bt, lens, g, w.scale,
+                                                     w.max_context_len)
+    fused_out = PB.pa_decode_attention_shared_prefix(t["query"], fused, None, bt, lens, g, w.scale,
+                                                     w.max_context_len, layout=FUSED)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(split_out), bits(fused_out))
+    ref = O.decode_attention(W.raw_numpy(t["query"]), W.raw_numpy(t["k_pool"]), W.raw_numpy(t["v_pool"]),
+                             w.block_tables, w.context_lens, w.scale, w.dtype)
+    err = float(np.max(np.abs(O.widen(W.raw_numpy(fused_out), w.dtype) - ref)))
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]

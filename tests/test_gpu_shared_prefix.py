@@ -72,7 +72,8 @@ def forked_batch(prompts, forks, gens, h, hkv, d, dtype, seed, bs=16):
     the library's block pool (copy-on-write pairs replayed by the tensor
     builder, which copies the prompt rows)."""
     rng = np.random.default_rng(seed)
-    nb = 4096 * max(1, 16 // bs)  # room for every token at any block size
+    need = sum(-(-p // bs) + f * (-(-max(gl) // bs) + 1) for p, f, gl in zip(prompts, forks, gens)) + 64
+    nb = max(4096 * max(1, 16 // bs), need)  # room for every token at any block size
     m = PB.BlockManager(nb, bs, free_order=rng.permutation(nb))
     seqs, copies = [], []
     for p, f, gl in zip(prompts, forks, gens):
@@ -146,3 +147,40 @@ def test_no_shared_prefix_degenerates_to_plain_decode():
     g = PB.pa_shared_prefix_groups(w.block_tables, w.context_lens, w.block_size)
     assert g.max_prefix_len == 0
     check(w, g)
+
+
+@pytest.mark.parametrize("h,hkv", [(8, 4), (32, 4), (16, 1), (64, 2), (32, 8)])
+def test_group_sizes_and_head_groupings(h, hkv):
+    # query heads per KV head 2, 8, 16, 32 (two head chunks) and 4: one to
+    # eight members share the 16 columns of a wave, and a group of 16 samples
+    # spans several member sets; members of one group end at different lengths
+    rng = np.random.default_rng(h + hkv)
+    prompts = [300, 77, 1000, 16]
+    forks = [16, 5, 3, 9]
+    gens = [[int(x) for x in rng.integers(1, 90, f)] for f in forks]
+    w = forked_batch(prompts, forks, gens, h, hkv, 128, "bf16", seed=h * 3 + hkv)
+    g = PB.pa_shared_prefix_groups(w.block_tables, w.context_lens, 16)
+    assert g.num_groups == 4 and g.max_group_size == 16
+    check(w, g, seed=4)
+
+
+def test_many_small_groups():
+    # 300 prompts forked in two: more (group, KV head, member set) units than
+    # the machine holds two waves of, so each unit runs on one wave
+    rng = np.random.default_rng(11)
+    prompts = [int(x) for x in rng.integers(17, 400, 300)]
+    forks = [2] * 300
+    gens = [[int(x) for x in rng.integers(1, 30, 2)] for _ in range(300)]
+    w = forked_batch(prompts, forks, gens, 32, 8, 128, "bf16", seed=11)
+    g = PB.pa_shared_prefix_groups(w.block_tables, w.context_lens, 16)
+    assert g.num_groups == 300
+    check(w, g, seed=5, rows=list(range(0, 600, 5)))
+
+
+def test_long_shared_prompts():
+    # 32 prompts of 3600 tokens, 8 samples each: the set's 237 steps are split
+    # over four waves whose partial softmax states are merged in LDS
+    w = W.make_workload("shared_prefix_long_bf16")
+    g = PB.pa_shared_prefix_groups(w.block_tables, w.context_lens, w.block_size)
+    assert g.num_groups == 32
+    check(w, g, rows=list(range(0, 256, 9)))
