@@ -406,7 +406,10 @@ int prefill_partition_bounds(const PrefillShape& s, int* min_parts, int* max_par
   return PA_OK;
 }
 
-int cols_per_wave(int head_dim) { return head_dim == 64 ? kMaxRepPerWaveValu : kMaxRepPerWaveValu / 2; }
+int cols_per_wave(int head_dim) {
+  if (kColumnsMfma) return 16;
+  return head_dim == 64 ? kMaxRepPerWaveValu : kMaxRepPerWaveValu / 2;
+}
 
 ColumnGrid column_grid(const PrefillShape& s) {
   const int64_t rep = s.d.num_heads / s.d.num_kv_heads;

@@ -168,9 +168,14 @@ PrefillGrid prefill_grid(const PrefillShape& s);
 // Column mode of the VALU tile (fp32 prefill): the columns of a (sequence,
 // KV head) are its (new token, query head) pairs, `cols` per wave, the waves
 // of a workgroup on consecutive columns so they read each K/V block at the
-// same time; ctiles workgroups per (sequence, KV head, partition).  Eight
-// columns per wave at head_dim 64, four at 128 (eight would need more than
-// 256 registers: one wave per SIMD instead of two).
+// same time; ctiles workgroups per (sequence, KV head, partition).  The
+// matrix-core tile (fp32 MFMA) takes 16 columns per wave; the VALU tile
+// (a build with PA_F32_COLUMNS_MFMA=0) eight at head_dim 64 and four at 128
+// (eight would need more than 256 registers: one wave per SIMD, not two).
+#ifndef PA_F32_COLUMNS_MFMA
+#define PA_F32_COLUMNS_MFMA 1
+#endif
+constexpr bool kColumnsMfma = PA_F32_COLUMNS_MFMA != 0;
 int cols_per_wave(int head_dim);
 struct ColumnGrid {
   int cols;       // columns per wave

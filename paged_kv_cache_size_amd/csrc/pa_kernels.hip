@@ -412,6 +412,199 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
   }
 }
 
+// ------------------------------------------------------------------ fp32 matrix-core column tile
+//
+// Column mode in fp32 on the matrix cores (mfma_f32_16x16x4_f32): a wave
+// takes 16 columns - (new token, query head) pairs of one (sequence, KV head),
+// each with its own causal key limit - so that each fp32 K/V element it loads
+// serves 16 columns through the matrix core instead of the VALU.  Per 16-token
+// step, lane l = 16 gq + c (c = l % 16):
+//  * QK: S[key][column] over D/4 MFMAs.  Lane l holds K row c and the query
+//    of column c at dims 16i + 4gq .. +4 (load i), so MFMA 4i + j contracts
+//    dim 16i + 4gq + j: a permutation of the dims, the same on both sides.
+//    The scores come back as lane l = (gq, c): keys 4gq + r (r = 0..3) of
+//    column c.
+//  * P.V: O^T[dim][column] over 4 x D/16 MFMAs.  MFMA (r, t) contracts keys
+//    4k + r (k = 0..3, the lane group), so the lane's own weight r is its B
+//    operand; lane l holds V rows 4gq + r at dims (D/16) c .. +D/16 as the A
+//    operand of tiles t = 0..D/16-1.  Tile t, register i of lane (gq, c) is
+//    dim (D/16)(4gq + i) + t of column c: a lane owns D/4 consecutive dims.
+// Softmax as the 16-bit decode tile: the running max uniform over the four
+// lane groups of a column, partial denominators summed at the end.
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void columns_f32_mfma_kernel(const DecodeArgs a) {
+  constexpr int BS = pa::kBlockSize;
+  constexpr int ROWB = D * 4;
+  constexpr int NKL = D / 16;  // K loads (float4) per lane and step; QK MFMAs = 4 NKL
+  constexpr int DV = D / 16;   // dims per lane of one V row (V floats), P.V tiles
+  constexpr int NVL = DV / 4;  // float4 loads per V row
+  constexpr int DPL = D / 4;   // output dims per lane
+  constexpr bool SUB = MODE == kBlocksLarge;
+  constexpr bool GATHER = MODE == kBlocksSmall;
+  using f4 = f32x4;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wpw = blockDim.x >> 6;
+  const int gq = lane >> 4, c = lane & 15;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int ct = logical % a.ctiles;
+  int rest = logical / a.ctiles;
+  const int s = rest % a.num_parts;
+  rest /= a.num_parts;
+  const int g = rest % a.num_kv_heads;
+  const int b = rest / a.num_kv_heads;
+  const int q0 = a.query_start_loc[b], n = a.query_start_loc[b + 1] - q0;
+  const int L = a.context_lens[b];
+  const int cols = n * a.rep;
+  if (ct * wpw * 16 >= cols) return;  // workgroup-uniform: no column of this sequence here
+  const int wg_lim = L - n + (min(cols, (ct + 1) * wpw * 16) - 1) / a.rep + 1;
+  const int c0 = (ct * wpw + wave) * 16;
+  // this lane's column (c) and the wave's last live column
+  const int cc = c0 + c, ti = cc / a.rep;
+  const bool live = cc < cols;
+  const size_t qrow = (size_t)(q0 + (live ? ti : 0)) * a.num_heads + g * a.rep + cc % a.rep;
+  const int lim = live ? L - n + ti + 1 : 0;
+  const int last_col = min(cols, c0 + 16) - 1;
+  const int wlim = c0 < cols ? L - n + last_col / a.rep + 1 : 0;  // limits grow with the column
+  const int lim_min = c0 < cols ? L - n + c0 / a.rep + 1 : 0;
+
+  const int start = s * a.part_tokens;
+  const int wg_end = min(wg_lim, start + a.part_tokens);
+  if (start >= wg_end) return;  // workgroup-uniform
+  const int pshift = MODE != kBlocks16 ? a.block_shift : 0;
+  const int pool_bs = SUB ? BS << pshift : GATHER ? BS >> pshift : BS;
+  const int blk0 = start / pool_bs;
+  const int nent = (wg_end - start + pool_bs - 1) / pool_bs;
+  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk0;
+  TableSlice tab;
+  __shared__ int32_t stab[GATHER ? pa::kMaxSmallBlockPartition : 1];
+  if constexpr (GATHER)
+    stage_table(stab, bt, nent);
+  else
+    tab.load(bt, nent, lane);
+  const int end = min(wlim, start + a.part_tokens);  // this wave's keys
+  if (start >= end) return;  // no barrier follows
+  const int nblk = (end - start + BS - 1) / BS;
+
+  // The query of column c at dims 16i + 4gq .. +4, scaled into log2 units.
+  f4 qv[NKL];
+  {
+    const float* qp = (const float*)a.query + qrow * D + 4 * gq;
+#pragma unroll
+    for (int i = 0; i < NKL; ++i) {
+      const float4 v = *reinterpret_cast<const float4*>(qp + 16 * i);
+      qv[i] = live ? f4{v.x * a.qscale, v.y * a.qscale, v.z * a.qscale, v.w * a.qscale} : f4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // Byte offsets inside a block: K row c, V rows 4gq + r.
+  const size_t row_stride = a.row_stride, block_stride = (size_t)a.block_stride;
+  const size_t hoff = (size_t)g * a.head_stride;
+  const size_t kin = hoff + (size_t)4 * gq * 4;
+  const size_t vin = hoff + (size_t)DV * c * 4;
+  // where a row of step j lies: (table entry, row inside its block)
+  auto row_addr = [&](int j, int t) -> size_t {
+    if constexpr (GATHER) {
+      const int e = min((j << pshift) + t / pool_bs, nent - 1);
+      return (size_t)(uint32_t)stab[e] * block_stride + (size_t)(t % pool_bs) * row_stride;
+    } else if constexpr (SUB) {
+      return (size_t)(uint32_t)tab.get(j >> pshift) * block_stride +
+             ((size_t)(j & ((1 << pshift) - 1)) * BS + t) * row_stride;
+    } else {
+      return (size_t)(uint32_t)tab.get(j) * block_stride + (size_t)t * row_stride;
+    }
+  };
+  auto load_step = [&](int j, f4* kr, f4* vr) {
+    const uint8_t* kp = a.k_pool + row_addr(j, c) + kin;
+#pragma unroll
+    for (int i = 0; i < NKL; ++i) kr[i] = *reinterpret_cast<const f4*>(kp + 64 * i);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint8_t* vp = a.v_pool + row_addr(j, 4 * gq + r) + vin;
+#pragma unroll
+      for (int h = 0; h < NVL; ++h) vr[r * NVL + h] = *reinterpret_cast<const f4*>(vp + 16 * h);
+    }
+  };
+
+  f4 acc[DV];
+#pragma unroll
+  for (int t = 0; t < DV; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  auto process = [&](const f4* kr, const f4* vr, int tok0) {
+    // Four independent accumulation chains (dims 16i + 4gq + j, one chain per
+    // j) summed in pairs at the end: the MFMAs need not wait on each other,
+    // and each fp32 sum runs over a quarter of the products.
+    f4 sp[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int i = 0; i < NKL; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sp[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[i][j], qv[i][j], sp[j], 0, 0, 0);
+    const f4 sacc = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+    const bool partial = tok0 + BS > lim_min;
+    float sc[4];
+    bool ok[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      ok[r] = !partial || tok0 + 4 * gq + r < lim;
+      sc[r] = ok[r] ? sacc[r] : -INFINITY;
+    }
+    const float mn = fmaxf(m, rows_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]))));
+    const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m - mn);
+    m = mn;
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = ok[r] ? fast_exp2(sc[r] - mn) : 0.f;
+    l = fmaf(l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+#pragma unroll
+    for (int t = 0; t < DV; ++t) acc[t] *= alpha;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      // rows past the wave's last key (stale, even NaN) must not reach the MFMA
+      const bool vok = !partial || tok0 + 4 * gq + r < end;
+#pragma unroll
+      for (int t = 0; t < DV; ++t) {
+        const float v = vok ? vr[r * NVL + t / 4][t % 4] : 0.f;
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, p[r], acc[t], 0, 0, 0);
+      }
+    }
+  };
+
+  f4 ka[NKL], va[4 * NVL], kb[NKL], vb[4 * NVL];
+  load_step(0, ka, va);
+  for (int j = 0; j < nblk; j += 2) {
+    if (j + 1 < nblk) load_step(j + 1, kb, vb);
+    process(ka, va, start + j * BS);
+    if (j + 1 >= nblk) break;
+    if (j + 2 < nblk) load_step(j + 2, ka, va);
+    process(kb, vb, start + (j + 1) * BS);
+  }
+
+  const float lt = rows_sum(l);
+  if (!live) return;
+  // lane (gq, c) holds dims (D/16)(4gq + i) + t, i.e. D/4 consecutive dims from 4 (D/16) gq
+  float o[DPL];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < DV; ++t) o[DV * i + t] = acc[t][i];
+  const int col_parts = (lim + a.part_tokens - 1) / a.part_tokens;
+  if (s >= col_parts) return;
+  if (col_parts == 1) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] *= inv;
+    store_row<DT_F32, DPL>((uint8_t*)a.out + qrow * ROWB + (size_t)DPL * gq * 4, o);
+  } else {
+    const size_t idx = qrow * a.num_parts + s;
+    float* dst = a.ws_acc + idx * D + DPL * gq;
+#pragma unroll
+    for (int e = 0; e < DPL; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+    if (gq == 0) a.ws_ml[idx] = make_float2(m, lt);
+  }
+}
+
 // ------------------------------------------------------------------ MFMA decode (16-bit K/V)
 //
 // The query-head group of one KV head against a 16-token block is a small
@@ -912,10 +1105,19 @@ int device_cu_count() {
   return cus;
 }
 
-// fp32 column mode: cols_per_wave(head_dim) columns per wave whatever the group size.
+template <int D>
+DecodeFn pick_columns_mfma(int block_size) {
+  if (block_size == kBlockSize) return columns_f32_mfma_kernel<D, kBlocks16>;
+  if (block_size > kBlockSize) return columns_f32_mfma_kernel<D, kBlocksLarge>;
+  return columns_f32_mfma_kernel<D, kBlocksSmall>;
+}
+
+// fp32 column mode: the matrix-core tile (16 columns per wave), or with
+// PA_F32_COLUMNS_MFMA=0 the VALU tile (cols_per_wave(head_dim) columns).
 DecodeFn pick_columns(const PrefillShape& s) {
   if (s.d.dtype != PA_F32) return nullptr;
   const int cols = cols_per_wave(s.d.head_dim);
+  if (kColumnsMfma) return s.d.head_dim == 64 ? pick_columns_mfma<64>(s.d.block_size) : pick_columns_mfma<128>(s.d.block_size);
   return s.d.head_dim == 64 ? pick_rep_bs<DT_F32, 64>(cols, s.d.block_size)
                             : pick_rep_bs<DT_F32, 128>(cols, s.d.block_size);
 }
