@@ -139,6 +139,31 @@ struct TableSlice {
   }
 };
 
+// A forward-moving view of a TableSlice for callers that ask for entries in
+// non-decreasing order: it keeps the register holding the 64 entries around
+// the last one asked for, so an entry costs one readlane; moving on to the
+// next register is a rare wave-uniform branch.
+struct TableWindow {
+  int w = 0;     // entries base .. base + 63
+  int base = 0;  // a multiple of 64, wave-uniform
+  __device__ __forceinline__ void init(const TableSlice& t) {
+    w = t.r[0];
+    base = 0;
+  }
+  // entry j (wave-uniform, base <= j < 64 * kTabRegs)
+  __device__ __forceinline__ int get(const TableSlice& t, int j) {
+    if (j - base >= 64) {
+      const int k = j >> 6;
+      int v = t.r[0];
+#pragma unroll
+      for (int i = 1; i < kTabRegs; ++i) v = (k == i) ? t.r[i] : v;
+      w = v;
+      base = k << 6;
+    }
+    return __builtin_amdgcn_readlane(w, j - base);
+  }
+};
+
 // Pool block sizes against the 16-token steps of the MFMA tiles:
 //  * kBlocks16: blocks and steps coincide;
 //  * kBlocksLarge: blocks of 16 << shift tokens; a step is a window of 16

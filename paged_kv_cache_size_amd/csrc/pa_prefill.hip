@@ -567,11 +567,14 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
 
   const int32_t* bt = a.block_tables + (size_t)trow * a.max_blocks_per_seq + blk0;
   TableSlice tab;  // blocks of 16 tokens or more: the slice in VGPR lanes
+  TableWindow twin;  // read forward only: the steps' blocks come in order
   __shared__ int32_t stab[GATHER ? pa::kMaxSmallBlockPartition : 1];  // small blocks: in LDS
-  if constexpr (GATHER)
+  if constexpr (GATHER) {
     stage_table(stab, bt, nent);
-  else
+  } else {
     tab.load(bt, nent, lane);
+    twin.init(tab);
+  }
 
   uint4 qop[kWaveTiles][NKC];
 #pragma unroll
@@ -638,11 +641,12 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
   for (int tt = 0; tt < kWaveTiles; ++tt)
 #pragma unroll
     for (int t = 0; t < VPL; ++t) acc[tt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[kWaveTiles];
+  float m[kWaveTiles], mth[kWaveTiles];  // running max (log2 units), and m + kRescaleLog2
   f32x4 lacc[kWaveTiles];  // every register: the column's denominator
 #pragma unroll
   for (int tt = 0; tt < kWaveTiles; ++tt) {
     m[tt] = kMaxFloor;
+    mth[tt] = kMaxFloor + kRescaleLog2;
     lacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
@@ -668,9 +672,9 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
       }
       return;
     }
-    const size_t off = SUB ? (size_t)(uint32_t)tab.get(jj >> pshift) * block_stride +
+    const size_t off = SUB ? (size_t)(uint32_t)twin.get(tab, jj >> pshift) * block_stride +
                                  (size_t)(jj & ((1 << pshift) - 1)) * step_stride
-                           : (size_t)(uint32_t)tab.get(jj) * block_stride;
+                           : (size_t)(uint32_t)twin.get(tab, jj) * block_stride;
     const uint32_t span = real ? a.span : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_block_rsrc(a.k_pool + off, span);
     const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, span);
@@ -734,22 +738,27 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
     auto visible = [&](int tt, int i) {
       return kInterior || key0 + (i >> 2) * 16 + 4 * (i & 3) + gq < lim[tt];
     };
-    float smax[kWaveTiles];
+    // The test for a move looks at the lane's own 8 scores: some lane's max
+    // passes the threshold exactly when its column's max does (scaling by
+    // qscale >= 0 and rounding keep the order), so the column max across the
+    // four lane groups is taken only inside the rare branch.
+    float lmax[kWaveTiles];
     bool move = false;
 #pragma unroll
     for (int tt = 0; tt < kWaveTiles; ++tt) {
       float xm[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) xm[i] = visible(tt, i) ? x[tt][i] : -INFINITY;
-      smax[tt] = rows_maximum(max8(xm)) * a.qscale;
-      move = move || smax[tt] > m[tt] + kRescaleLog2;
+      lmax[tt] = max8(xm);
+      move = move || lmax[tt] * a.qscale > mth[tt];
     }
     if (__ballot(move)) {  // rare: some column's max moved by more than 2^8
 #pragma unroll
       for (int tt = 0; tt < kWaveTiles; ++tt) {
-        const float mn = fmaxf(m[tt], smax[tt]);
+        const float mn = fmaxf(m[tt], rows_maximum(lmax[tt]) * a.qscale);
         const float alpha = fast_exp2(m[tt] - mn);
         m[tt] = mn;
+        mth[tt] = mn + kRescaleLog2;
         lacc[tt] *= alpha;
 #pragma unroll
         for (int t = 0; t < VPL; ++t) acc[tt][t] *= alpha;
