@@ -156,7 +156,11 @@ struct TableWindow {
       const int k = j >> 6;
       int v = t.r[0];
 #pragma unroll
-      for (int i = 1; i < kTabRegs; ++i) v = (k == i) ? t.r[i] : v;
+      for (int i = 1; i < kTabRegs; ++i) {
+        int c = t.r[i];
+        asm("" : "+v"(c));  // a plain select per register, not an indexed (scratch) array access
+        v = (k == i) ? c : v;
+      }
       w = v;
       base = k << 6;
     }

@@ -124,6 +124,16 @@ def test_dtypes_and_head_dims(dtype, d, ps):
     check_prefill(pb, seed=1, partition_size=ps, poisoned=True)
 
 
+@pytest.mark.parametrize("dtype,d", [("f16", 64), ("f16", 128), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("ps", [0, 64])
+def test_dtypes_and_head_dims_long_runs(dtype, d, ps):
+    # runs of 64 and more new tokens (256 and more columns per KV head) take
+    # the cooperative tile in its widest shape over several column groups,
+    # beside short rows and decode steps, at both head sizes and 16-bit types
+    pb = W.prefill_batch([1, 7, 100, 700, 1500], [1, 7, 64, 300, 520], 8, 2, d, dtype, seed=13, extra_cols=1)
+    check_prefill(pb, seed=1, partition_size=ps, poisoned=True)
+
+
 @pytest.mark.parametrize("h,hkv", [(8, 8), (8, 4), (32, 8), (12, 2), (32, 1), (9, 1), (22, 2), (40, 40)])
 def test_head_groupings(h, hkv):
     pb = W.prefill_batch(SMALL_LENS, SMALL_QLENS, h, hkv, 128, "bf16", seed=h * 10 + hkv)

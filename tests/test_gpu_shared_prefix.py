@@ -142,6 +142,21 @@ def test_many_wide_groups_block_sizes(bs):
     check(w, g, seed=3)
 
 
+@pytest.mark.parametrize("bs,dtype,d", [(4, "bf16", 128), (32, "f16", 64)])
+def test_wide_group_prefix_pass(bs, dtype, d):
+    # a group of 70 samples with 32/8 heads: 280 (member, head) columns per
+    # KV head, so the prefix pass (block sizes other than 16 take the passes)
+    # runs the cooperative tile over several column groups with its partials
+    # in slots
+    rng = np.random.default_rng(bs + 300)
+    prompts, forks = [300, 90], [70, 3]
+    gens = [[int(x) for x in rng.integers(1, 50, f)] for f in forks]
+    w = forked_batch(prompts, forks, gens, 32, 8, d, dtype, seed=bs, bs=bs)
+    g = PB.pa_shared_prefix_groups(w.block_tables, w.context_lens, bs)
+    assert g.max_group_size == 70
+    check(w, g, seed=4)
+
+
 def test_no_shared_prefix_degenerates_to_plain_decode():
     w = W.make_workload("qwen1p5b_bf16")
     g = PB.pa_shared_prefix_groups(w.block_tables, w.context_lens, w.block_size)
