@@ -317,7 +317,7 @@ def main_prefill(args):
     if w.dtype == "f32":
         # fp32: the VALU tile in column mode, bound by HBM (every context
         # token's K and V read once per step)
-        kernel = "decode_partition_kernel (column mode)"
+        kernel = "columns_f32_mfma_kernel (fp32 column tile)"
         achieved = pb.kv_read_bytes() / (attn_ms * 1e-3) / 1e9
         bound, peak, unit = "hbm", HBM_PEAK_GBPS, "GB/s"
     else:
