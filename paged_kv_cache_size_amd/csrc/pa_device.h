@@ -249,13 +249,17 @@ __device__ __forceinline__ VT buffer_load_v(__amdgpu_buffer_rsrc_t r, uint32_t o
     return __builtin_bit_cast(VT, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kVCpol));
 }
 
-// XOR swizzle of a K row's 16-byte chunks in LDS: token t's chunk k sits at
-// position k ^ kswz(t), so the 16 rows read by one 16-lane group at a fixed
-// chunk land in 16 distinct bank groups.  (Rows of 16 chunks: kswz = t;
-// rows of 8 chunks: two rows share 16 positions, kswz = t / 2.)
+// XOR swizzle of a K row's 16-byte chunks in LDS for the matrix-core tiles,
+// whose lane in MFMA column col reads token t = 4 (col % 4) + col / 4 at
+// chunk 4c + gq: token t's chunk k sits at position k ^ kswz(t).  Rows of 16
+// chunks: kswz(t) = col(t) = 4 (t % 4) + t / 4, so a lane reads chunk
+// (4c + gq) ^ col - measured on gfx950 with four waves reading two blocks
+// each, 71 clocks per wave and block pair, against 98 for k ^ t, which the
+// 16-byte reads' lane grouping turns into two-way bank conflicts.  Rows of 8
+// chunks: two rows share 16 positions, kswz(t) = t / 2.
 template <int CPR>
 __device__ __forceinline__ int kswz_t(int t) {
-  return CPR == 16 ? t : (t >> 1) & (CPR - 1);
+  return CPR == 16 ? ((t & 3) << 2) | (t >> 2) : (t >> 1) & (CPR - 1);
 }
 
 template <int DT>
