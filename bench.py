@@ -651,7 +651,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the hot path has no multi-GPU form in this build", file=sys.stderr)
+              "the library runs one GPU per process and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import torch
