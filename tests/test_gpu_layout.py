@@ -215,6 +215,31 @@ def test_fused_prefill_matches_split(ps):
     assert err <= TOL["bf16"], err
 
 
+@pytest.mark.parametrize("bs,d", [(16, 128), (4, 64), (64, 128)])
+def test_fused_prefill_f32_matches_split(bs, d):
+    # the fp32 column tile over a fused pool: the same rows in the same order
+    # as over the split pools (bitwise), at pool blocks of 16, 4 and 64 tokens
+    pb = W.prefill_batch([1, 7, 100, 700, 1500], [1, 7, 64, 300, 520], 8, 2, d, "f32", seed=bs + d,
+                         extra_cols=1, block_size=bs)
+    w = pb.workload
+    say(f"fused fp32 prefill bs={bs} d={d}")
+    t = W.make_prefill_tensors(pb, 0, DEV)
+    kr, vr = W.raw_numpy(t["k_pool"]), W.raw_numpy(t["v_pool"])
+    fused = to_torch(O.fuse_kv(kr, vr), "f32")
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    lens = torch.from_numpy(w.context_lens).to(DEV)
+    args = (bt, lens, t["query_start_loc"], w.scale, pb.max_query_len, w.max_context_len)
+    split_out = PB.pa_prefill_attention(t["query"], t["k_pool"], t["v_pool"], *args)
+    fused_out = PB.pa_prefill_attention(t["query"], fused, None, *args, layout=FUSED)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(split_out), bits(fused_out))
+    ref = O.paged_attention(W.raw_numpy(t["query"]), kr, vr, w.block_tables, w.context_lens, pb.query_start_loc,
+                            w.scale, w.dtype)
+    err = float(np.max(np.abs(O.widen(W.raw_numpy(fused_out), w.dtype) - ref)))
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL["f32"], err
+
+
 # ------------------------------------------------------------------ shared-prefix decode
 
 @pytest.mark.parametrize("bs", [16, 4, 32])
