@@ -52,7 +52,16 @@
 extern "C" {
 #endif
 
-typedef enum pa_status {
+/* The enums below are int-sized in C and in C++ (where they get int as a
+ * fixed underlying type), so a caller may pass any int: a value outside the
+ * listed ones is rejected with an error status, never read as undefined. */
+#ifdef __cplusplus
+#define PA_ENUM_BASE : int
+#else
+#define PA_ENUM_BASE
+#endif
+
+typedef enum pa_status PA_ENUM_BASE {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, inconsistent shape */
   PA_ERR_UNSUPPORTED = 2, /* dtype / head_dim / block_size outside the compiled set */
@@ -61,7 +70,7 @@ typedef enum pa_status {
   PA_ERR_NO_BLOCKS = 5    /* the block pool has too few free blocks; nothing changed */
 } pa_status;
 
-typedef enum pa_dtype {
+typedef enum pa_dtype PA_ENUM_BASE {
   PA_F32 = 0,  /* IEEE binary32 */
   PA_F16 = 1,  /* IEEE binary16 */
   PA_BF16 = 2  /* bfloat16 (upper 16 bits of a binary32) */
@@ -80,7 +89,7 @@ typedef enum pa_dtype {
  * Both hold the same logical K[slot][h][:], V[slot][h][:]; only addresses
  * differ, so every result is the same in both layouts.
  */
-typedef enum pa_kv_layout {
+typedef enum pa_kv_layout PA_ENUM_BASE {
   PA_KV_SPLIT = 0,
   PA_KV_FUSED = 1
 } pa_kv_layout;
