@@ -327,8 +327,10 @@ int32_t pa_decode_plan_partition_size(int32_t num_seqs, int32_t num_heads, int32
  *   max_query_len    host bound of n_b; 1 <= max_query_len <= num_tokens.
  *   other arguments  as pa_decode_attention (pools, tables, scale, dtype, stream).
  * fp16 and bf16 run matrix-core tiles shared by the rows of a sequence; fp32
- * runs every row as a decode query with its own causal context (the VALU
- * tile).  Block sizes as pa_decode_attention.
+ * runs the fp32 matrix-core column tile, whose columns are the (new token,
+ * query head) pairs of one sequence and KV head, each with its own causal
+ * key limit, so the rows of a sequence share every K/V read.  Block sizes as
+ * pa_decode_attention.
  * partition_size: 0 lets the library choose (it may split long contexts into
  * partitions merged by a second kernel, keeping the partials within 256 MiB),
  * or a size pa_decode_attention_ex accepts.  The workspace
