@@ -315,7 +315,7 @@ def main_prefill(args):
     flops = pb.attention_flops()
     attn_ms = per_kernel_ms[2]
     if w.dtype == "f32":
-        # fp32: the VALU tile in column mode, bound by HBM (every context
+        # fp32: the matrix-core column tile, bound by HBM (every context
         # token's K and V read once per step)
         kernel = "columns_f32_mfma_kernel (fp32 column tile)"
         achieved = pb.kv_read_bytes() / (attn_ms * 1e-3) / 1e9

@@ -165,13 +165,14 @@ struct PrefillGrid {
 };
 PrefillGrid prefill_grid(const PrefillShape& s);
 
-// Column mode of the VALU tile (fp32 prefill): the columns of a (sequence,
+// Column mode of the fp32 tiles (fp32 prefill): the columns of a (sequence,
 // KV head) are its (new token, query head) pairs, `cols` per wave, the waves
 // of a workgroup on consecutive columns so they read each K/V block at the
 // same time; ctiles workgroups per (sequence, KV head, partition).  The
-// matrix-core tile (fp32 MFMA) takes 16 columns per wave; the VALU tile
-// (a build with PA_F32_COLUMNS_MFMA=0) eight at head_dim 64 and four at 128
-// (eight would need more than 256 registers: one wave per SIMD, not two).
+// matrix-core tile (fp32 MFMA, the default) takes 16 columns per wave; the
+// VALU tile (a build with PA_F32_COLUMNS_MFMA=0) eight at head_dim 64 and
+// four at 128 (eight would need more than 256 registers: one wave per SIMD,
+// not two).
 #ifndef PA_F32_COLUMNS_MFMA
 #define PA_F32_COLUMNS_MFMA 1
 #endif

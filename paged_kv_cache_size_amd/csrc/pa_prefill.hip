@@ -985,11 +985,12 @@ size_t prefill_workspace(const pa::PrefillShape& s, int parts) {
   return pa::workspace_bytes(s.num_tokens, s.d.num_heads, s.d.head_dim, parts);
 }
 
-// fp32: the VALU tile in column mode - the columns of a (sequence, KV head)
-// are its (new token, query head) pairs, eight per wave, each with its own
-// causal key limit; the waves of a workgroup take consecutive columns, so a
-// sequence's rows share each K/V read of a wave and its workgroup's waves
-// read the same blocks together.  Partials merged as for the 16-bit tiles.
+// fp32: the column tile - the columns of a (sequence, KV head) are its (new
+// token, query head) pairs, 16 per wave on the matrix cores, each with its
+// own causal key limit; the waves of a workgroup take consecutive columns,
+// so a sequence's rows share each K/V read of a wave and its workgroup's
+// waves read the same blocks together.  Partials merged as for the 16-bit
+// tiles.
 int prefill_rows(void* out, const void* query, const pa::PoolView& pv, const int32_t* block_tables,
                  const int32_t* context_lens, const int32_t* query_start_loc, const pa::PrefillShape& shp,
                  float scale, void* workspace, size_t workspace_bytes, int32_t partition_size, void* stream) {

@@ -52,8 +52,8 @@ int launch_kernel(void (*fn)(P...), dim3 grid, dim3 block, hipStream_t stream, A
 
 struct PrefillShape;
 struct PoolView;
-// The VALU decode kernel in column mode over the new tokens of a varlen batch
-// (fp32 prefill): the kernel for shape `s` and its workgroup size, then the
+// The fp32 column tile over the new tokens of a varlen batch (fp32
+// prefill): the kernel for shape `s` and its workgroup size, then the
 // launch (query_start_loc [num_seqs + 1]), partials into
 // ws_acc [rows, H, parts, D] / ws_ml [rows, H, parts] for rows whose keys span
 // several partitions.

@@ -156,9 +156,9 @@ def test_block_sizes(bs, wide):
 
 @pytest.mark.parametrize("h,hkv", [(8, 2), (32, 8), (12, 12), (9, 1), (12, 2), (6, 1)])
 def test_fp32_rows(h, hkv):
-    # fp32: the VALU tile over (new token, query head) columns, each with its
-    # own causal key limit; groups of 6 and 9 make a wave's columns straddle
-    # two new tokens
+    # fp32: the column tile over (new token, query head) columns, each with
+    # its own causal key limit; groups of 6 and 9 make a 16-column tile
+    # straddle new tokens
     lens = [1, 2, 15, 16, 17, 64, 129, 700]
     qlens = [1, 2, 15, 3, 17, 40, 1, 300]
     pb = W.prefill_batch(lens, qlens, h, hkv, 64, "f32", seed=h + hkv, extra_cols=1)
