@@ -6,6 +6,7 @@ Always recompiles.  The shared library lands next to this file, where the
 binding loads it from.
 """
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -50,18 +51,22 @@ def _run(cmd, verbose):
 def build(verbose: bool = True) -> str:
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="pa_build_") as tmp:
-        host_objs = []
+        host_objs, dev_objs, steps = [], [], []
         for src in sorted(f for f in os.listdir(CSRC) if f.endswith(".cpp")):
             obj = os.path.join(tmp, src[:-4] + ".o")
-            _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
-                  os.path.join(CSRC, src), "-o", obj], verbose)
+            steps.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
+                          os.path.join(CSRC, src), "-o", obj])
             host_objs.append(obj)
-        dev_objs = []
         for src in sorted(f for f in os.listdir(CSRC) if f.endswith(".hip")):
             obj = os.path.join(tmp, src[:-4] + ".o")
-            _run([hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", *DEVICE_FLAGS,
-                  "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+            steps.append([hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", *DEVICE_FLAGS,
+                          "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
             dev_objs.append(obj)
+        # the translation units compile independently: one process each, a few at a time
+        workers = max(1, min(len(steps), os.cpu_count() or 1, 8))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as pool:
+            for fut in [pool.submit(_run, cmd, verbose) for cmd in steps]:
+                fut.result()
         out_tmp = LIB + ".tmp"
         _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *host_objs, *dev_objs, "-o", out_tmp], verbose)
         os.replace(out_tmp, LIB)

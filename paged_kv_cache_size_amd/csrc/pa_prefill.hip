@@ -373,9 +373,9 @@ __global__ __launch_bounds__(64 * WPW) void prefill_mfma_kernel(const PrefillArg
       for (int i = 0; i < 4; ++i) vr[i] = *reinterpret_cast<const VT*>(a.v_pool + vbase[i] + vin[i]);
       return;
     }
-    const size_t off = SUB ? (size_t)(uint32_t)tab.get(jj >> pshift) * block_stride +
+    const size_t off = SUB ? (size_t)(uint32_t)tab.get(jj >> pshift) * (uint32_t)block_stride +
                                  (size_t)(jj & ((1 << pshift) - 1)) * step_stride
-                           : (size_t)(uint32_t)tab.get(jj) * block_stride;
+                           : (size_t)(uint32_t)tab.get(jj) * (uint32_t)block_stride;  // stride <= 2^31 (host check)
     const uint32_t span = real ? a.span : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_block_rsrc(a.k_pool + off, span);
     const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, span);
@@ -654,6 +654,12 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
   // memory access), so every wait count is exact; with small blocks
   // (per-lane addresses) they re-read the last step's rows instead, which
   // the step past `end` never uses.
+  // A wave's loads are all of K or all of V (its DPW instructions never
+  // straddle the K | V boundary), so one pool base and descriptor serve it.
+  static_assert(KI % DPW == 0, "a wave's share of a block's loads is of one kind");
+  const bool wave_k = is_k[0];
+  const uint8_t* const wave_pool = wave_k ? a.k_pool : a.v_pool;
+  const uint32_t bstride32 = (uint32_t)a.block_stride;  // <= 2^31 (checked on the host)
   auto load_block = [&](int j, int x) {
     const bool real = j <= last;
     const int jj = real ? j : last;
@@ -672,20 +678,19 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_wg_kernel(const PrefillArg
       }
       return;
     }
-    const size_t off = SUB ? (size_t)(uint32_t)twin.get(tab, jj >> pshift) * block_stride +
+    const size_t off = SUB ? (size_t)(uint32_t)twin.get(tab, jj >> pshift) * bstride32 +
                                  (size_t)(jj & ((1 << pshift) - 1)) * step_stride
-                           : (size_t)(uint32_t)twin.get(tab, jj) * block_stride;
+                           : (size_t)(uint32_t)twin.get(tab, jj) * bstride32;
     const uint32_t span = real ? a.span : 0u;
-    const __amdgpu_buffer_rsrc_t rk = make_block_rsrc(a.k_pool + off, span);
-    const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, span);
+    const __amdgpu_buffer_rsrc_t r = make_block_rsrc(wave_pool + off, span);
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       if (!has[i]) continue;
-      if (is_k[i])
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kslot(x) + lds_off[i]),
+      if (wave_k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(kslot(x) + lds_off[i]),
                                                  16, (int)goff[i], 0, 0, kKPol);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vslot(x) + lds_off[i]),
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(vslot(x) + lds_off[i]),
                                                  16, (int)goff[i], 0, 0, 0);
     }
   };
