@@ -792,10 +792,9 @@ __global__ __launch_bounds__(64 * WPW) void decode_mfma_kernel(const DecodeArgs 
       for (int i = 0; i < 4; ++i) vr[i] = *reinterpret_cast<const VT*>(a.v_pool + vb[i] + vin[i]);
       return;
     }
-    const uint32_t bstride = (uint32_t)a.block_stride;  // <= 2^31 (checked on the host)
-    const size_t off = SUB ? (size_t)(uint32_t)tab.get(jj >> pshift) * bstride +
+    const size_t off = SUB ? (size_t)(uint32_t)tab.get(jj >> pshift) * (size_t)a.block_stride +
                                  (size_t)(jj & ((1 << pshift) - 1)) * step_stride
-                           : (size_t)(uint32_t)tab.get(jj) * bstride;
+                           : (size_t)(uint32_t)tab.get(jj) * (size_t)a.block_stride;
     const uint32_t span = real ? a.span : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_block_rsrc(a.k_pool + off, span);
     const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, span);

@@ -187,7 +187,7 @@ __global__ __launch_bounds__(64 * NW) void shared_prefix_kernel(const GroupArgs 
   auto load_block = [&](int j, int slot, VT* vr) {
     const bool real = j <= last;
     const int jj = real ? j : max(last, 0);
-    const size_t off = (size_t)(uint32_t)tab.get(jj) * (uint32_t)a.block_stride;  // stride <= 2^31 (host check)
+    const size_t off = (size_t)(uint32_t)tab.get(jj) * (size_t)a.block_stride;
     const uint32_t span = real ? a.span : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_block_rsrc(a.k_pool + off, span);
     const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, span);
