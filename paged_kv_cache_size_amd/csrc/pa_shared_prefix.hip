@@ -95,6 +95,18 @@ __global__ __launch_bounds__(64 * NW) void shared_prefix_kernel(const GroupArgs 
   const int head = g * a.rep + chunk * a.repc + col % a.repc;
   uint8_t* const out_row = (uint8_t*)a.out + ((size_t)row * a.num_heads + head) * ROWB + gq * DPL * 2;
 
+  // Q^T as the QK B operand: column col = (member mi, head), k-chunk c =
+  // dims 32c + 8gq .. +8 (loaded first: it needs only the group's rows).
+  uint4 qop[NKC];
+  {
+    const uint8_t* qp = (const uint8_t*)a.query + ((size_t)row * a.num_heads + head) * ROWB + gq * 16;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qp + c * 64);
+      qop[c] = live ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
+
   // The set's steps: the P shared blocks, then each member's blocks past
   // them.  Member k's context length sits in lane k (one load for all).
   const int len_lane = lane < nm ? a.context_lens[row0 + m0 + lane] : 0;
@@ -116,39 +128,30 @@ __global__ __launch_bounds__(64 * NW) void shared_prefix_kernel(const GroupArgs 
     const int e = 64 * k + lane;
     int blk = 0, t = 0;
     if (e < nsteps) {
+      // the step's table row and entry first (lengths only), then one load
       const int j = j0 + e;
-      if (j < P) {
-        blk = a.block_tables[(size_t)row0 * a.max_blocks_per_seq + j];
-        t = (kAllMembers << 8) | BS;
-      } else {
+      int trow = row0, bi = j;
+      t = (kAllMembers << 8) | BS;
+      if (j >= P) {
         int left = j - P;
         for (int kk = 0; kk < nm; ++kk) {
           const int L = len_of(kk);
           const int own = own_steps(L);
           if (left < own) {
-            const int bi = P + left;
-            blk = a.block_tables[(size_t)(row0 + m0 + kk) * a.max_blocks_per_seq + bi];
+            trow = row0 + m0 + kk;
+            bi = P + left;
             t = (kk << 8) | min(BS, L - bi * BS);
             break;
           }
           left -= own;
         }
       }
+      blk = a.block_tables[(size_t)trow * a.max_blocks_per_seq + bi];
     }
     tab.r[k] = blk;
     tag.r[k] = t;
   }
 
-  // Q^T as the QK B operand: column col = (member mi, head), k-chunk c = dims 32c + 8gq .. +8.
-  uint4 qop[NKC];
-  {
-    const uint8_t* qp = (const uint8_t*)a.query + ((size_t)row * a.num_heads + head) * ROWB + gq * 16;
-#pragma unroll
-    for (int c = 0; c < NKC; ++c) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qp + c * 64);
-      qop[c] = live ? v : make_uint4(0, 0, 0, 0);
-    }
-  }
 
   // K: direct-to-LDS loads of whole rows, chunk q of token t at position
   // q ^ kswz(t) (the decode tile's layout); V: rows gq + 4i into registers.
@@ -261,51 +264,70 @@ __global__ __launch_bounds__(64 * NW) void shared_prefix_kernel(const GroupArgs 
   wait_vmcnt<0>();  // the ring's last loads have landed: its slots are free for the merge
 
   if constexpr (NW > 1) {
-    // Every wave but the first leaves its state in its own ring slots:
-    // accumulators of lanes 0-31 in slot 0, 32-63 in slot 1, (max,
-    // denominator) of each column in slot 2.  The first wave merges them
-    // with the softmax rescaling by 2^(m_w - max_w m_w).
-    auto acc_at = [&](int w) {
-      uint8_t* base = lane < 32 ? &ks0[w][0] : &ks1[w][0];
+    // Every wave leaves its state in its own ring slots (accumulators of
+    // lanes 0-31 in slot 0, 32-63 in slot 1, register r of all eight tiles
+    // together; (max, denominator) of each column in slot 2); then wave w
+    // merges register r = w of every wave (dims 32 gq + 8w .. +8 of column
+    // col) with the softmax rescaling and stores that quarter of the rows.
+    static_assert(NW == 4 || NW == 2, "merge split");
+    auto acc_at = [&](int v) {
+      uint8_t* base = lane < 32 ? &ks0[v][0] : &ks1[v][0];
       return reinterpret_cast<float4*>(base + (lane & 31) * DPL * 4);
     };
-    auto ml_at = [&](int w) { return reinterpret_cast<float2*>(&ks2[w][0]); };
-    if (wave > 0) {
+    auto ml_at = [&](int v) { return reinterpret_cast<float2*>(&ks2[v][0]); };
+    {
       float4* dst = acc_at(wave);
 #pragma unroll
-      for (int tt = 0; tt < VPL; ++tt) dst[tt] = make_float4(acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]);
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int tt = 0; tt < VPL; tt += 4)
+          dst[(r * VPL + tt) / 4] = make_float4(acc[tt][r], acc[tt + 1][r], acc[tt + 2][r], acc[tt + 3][r]);
       if (gq == 0) ml_at(wave)[col] = make_float2(m, lt);
     }
     __syncthreads();
-    if (wave > 0) return;
-    float M = m;
+    if (!live) return;
+    float mv[NW], fv[NW];
+    float M = -INFINITY;
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, ml_at(w)[col].x);
-    const float f0 = m == -INFINITY ? 0.f : fast_exp2(m - M);
-    lt *= f0;
+    for (int v = 0; v < NW; ++v) {
+      const float2 ml = ml_at(v)[col];
+      mv[v] = ml.x;
+      fv[v] = ml.y;
+      M = fmaxf(M, ml.x);
+    }
+    float den = 0.f;
+    constexpr int RPW = 4 / NW;  // accumulator registers each wave merges
+    float o[RPW * VPL];
 #pragma unroll
-    for (int tt = 0; tt < VPL; ++tt) acc[tt] *= f0;
+    for (int i = 0; i < RPW * VPL; ++i) o[i] = 0.f;
 #pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      const float2 ml = ml_at(w)[col];
-      const float f = ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - M);
-      lt = fmaf(f, ml.y, lt);
-      const float4* src = acc_at(w);
+    for (int v = 0; v < NW; ++v) {
+      const float f = mv[v] == -INFINITY ? 0.f : fast_exp2(mv[v] - M);
+      den = fmaf(f, fv[v], den);
+      const float4* src = acc_at(v);
 #pragma unroll
-      for (int tt = 0; tt < VPL; ++tt) {
-        const float4 v = src[tt];
-        acc[tt] += f32x4{f * v.x, f * v.y, f * v.z, f * v.w};
+      for (int i = 0; i < RPW * VPL; i += 4) {
+        const float4 x = src[(wave * RPW * VPL + i) / 4];
+        o[i] = fmaf(f, x.x, o[i]);
+        o[i + 1] = fmaf(f, x.y, o[i + 1]);
+        o[i + 2] = fmaf(f, x.z, o[i + 2]);
+        o[i + 3] = fmaf(f, x.w, o[i + 3]);
       }
     }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+    for (int i = 0; i < RPW * VPL; ++i) o[i] *= inv;
+    store_row<DT, RPW * VPL>(out_row + wave * RPW * VPL * 2, o);
+  } else {
+    if (!live) return;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float o[DPL];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int tt = 0; tt < VPL; ++tt) o[VPL * r + tt] = acc[tt][r] * inv;
+    store_row<DT, DPL>(out_row, o);
   }
-  if (!live) return;
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  float o[DPL];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int tt = 0; tt < VPL; ++tt) o[VPL * r + tt] = acc[tt][r] * inv;
-  store_row<DT, DPL>(out_row, o);
 }
 
 using GroupFn = void (*)(const GroupArgs);

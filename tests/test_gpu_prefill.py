@@ -314,9 +314,11 @@ def bench_partition_size(pb):
     return 0  # the automatic choice, as the benchmark launches it
 
 
-def check_sampled_rows(pb, partition_size, n_seqs=3):
-    """Whole step on the device; the oracle on a few rows of a few sequences,
-    each row the decode of its context cut at its own position."""
+def check_sampled_rows(pb, partition_size, n_seqs=3, rows=4):
+    """Whole step on the device; the oracle on rows of a few sequences (all of
+    them when n_seqs is None), each row the decode of its context cut at its
+    own position: the first two rows, the last, and rows - 3 more spread
+    evenly over the chunk."""
     w = pb.workload
     t = W.make_prefill_tensors(pb, 0, DEV)
     slots, out = prefill_step(pb, t, partition_size)
@@ -326,26 +328,31 @@ def check_sampled_rows(pb, partition_size, n_seqs=3):
     rng = np.random.default_rng(5)
     qsl = pb.query_start_loc
     worst = 0.0
-    for b in sorted(rng.choice(w.num_seqs, min(n_seqs, w.num_seqs), replace=False).tolist()):
+    seqs = range(w.num_seqs) if n_seqs is None else rng.choice(w.num_seqs, min(n_seqs, w.num_seqs), replace=False)
+    n_rows = 0
+    for b in sorted(int(x) for x in seqs):
         L, n = int(w.context_lens[b]), int(pb.query_lens[b])
         nb = O.num_blocks(L, w.block_size)
         ids = torch.tensor(w.block_tables[b, :nb].astype(np.int64), device=DEV)
         kp, vp = W.raw_numpy(t["k_pool"][ids]), W.raw_numpy(t["v_pool"][ids])
         table = list(range(nb))
-        for i in sorted({x for x in (0, 1, n // 2, n - 1) if x < n}):
+        picks = {0, 1, n - 1} | {int(x) for x in np.linspace(0, n - 1, max(rows - 3, 1) + 2)[1:-1].round()}
+        for i in sorted(x for x in picks if 0 <= x < n):
+            n_rows += 1
             row = int(qsl[b]) + i
             ref = O.decode_attention(W.raw_numpy(t["query"][row:row + 1]), kp, vp, [table], [L - n + i + 1],
                                      w.scale, w.dtype)
             got = O.widen(W.raw_numpy(out[row:row + 1]), w.dtype)
             worst = max(worst, float(np.max(np.abs(got - ref))))
-    say(f"  sampled rows: max abs err {worst:.3e}")
+    say(f"  {n_rows} sampled rows, every head: max abs err {worst:.3e}")
     assert worst <= TOLS[w.dtype], worst
 
 
 def test_chunked_prefill_llama_full_size_sampled():
+    # every sequence of the benchmark's batch, 20 rows each (about 15 s of oracle)
     pb = W.chunked_prefill_llama_bf16()
-    say(f"{pb.name} full size, sampled rows")
-    check_sampled_rows(pb, bench_partition_size(pb))
+    say(f"{pb.name} full size, sampled rows of every sequence")
+    check_sampled_rows(pb, bench_partition_size(pb), n_seqs=None, rows=20)
 
 
 @pytest.mark.parametrize("ps", [0, 4096])
