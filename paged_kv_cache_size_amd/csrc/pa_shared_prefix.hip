@@ -187,10 +187,14 @@ __global__ __launch_bounds__(64 * NW) void shared_prefix_kernel(const GroupArgs 
   // Step j: K into ring slot `slot`, V into registers.  Past the wave's
   // last step the loads go through an empty descriptor (zeros, no memory
   // access), so every wait stays an exact count.
+  // both read forward only: the loads' entries and the steps' tags come in order
+  TableWindow twin, tagw;
+  twin.init(tab);
+  tagw.init(tag);
   auto load_block = [&](int j, int slot, VT* vr) {
     const bool real = j <= last;
     const int jj = real ? j : max(last, 0);
-    const size_t off = (size_t)(uint32_t)tab.get(jj) * (size_t)a.block_stride;
+    const size_t off = (size_t)(uint32_t)twin.get(tab, jj) * (uint32_t)a.block_stride;  // stride <= 2^31 (host check)
     const uint32_t span = real ? a.span : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_block_rsrc(a.k_pool + off, span);
     const __amdgpu_buffer_rsrc_t rv = make_block_rsrc(a.v_pool + off, span);
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(64 * NW) void shared_prefix_kernel(const GroupArgs 
       read_k(u, kr);
       load_block(jj + NBUF - 1, (u + NBUF - 1) % NBUF, vr[(u + NBUF - 1) % NBUF]);
       __builtin_amdgcn_sched_barrier(0);
-      process(kr, vr[u], jj <= last ? tag.get(jj) : 0);
+      process(kr, vr[u], jj <= last ? tagw.get(tag, jj) : 0);
     }
   }
   float lt = rows_sum(l);
