@@ -321,7 +321,19 @@ __global__ __launch_bounds__(64 * NW) void shared_prefix_kernel(const GroupArgs 
     const float inv = den > 0.f ? 1.f / den : 0.f;
 #pragma unroll
     for (int i = 0; i < RPW * VPL; ++i) o[i] *= inv;
-    store_row<DT, RPW * VPL>(out_row + wave * RPW * VPL * 2, o);
+    // this wave's NO consecutive dims of the lane's row segment in the query
+    // dtype (nearest even): 8-byte or 16-byte stores
+    constexpr int NO = RPW * VPL;
+    static_assert(NO == 4 || NO % 8 == 0, "a wave stores 8 bytes or whole 16-byte chunks of each row");
+    uint8_t* const dst = out_row + wave * NO * 2;
+    if constexpr (NO == 4) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(Ops::pack(o[0], o[1]), Ops::pack(o[2], o[3]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < NO; i += 8)
+        *reinterpret_cast<uint4*>(dst + 2 * i) = make_uint4(Ops::pack(o[i], o[i + 1]), Ops::pack(o[i + 2], o[i + 3]),
+                                                            Ops::pack(o[i + 4], o[i + 5]), Ops::pack(o[i + 6], o[i + 7]));
+    }
   } else {
     if (!live) return;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;

@@ -192,16 +192,18 @@ def test_many_small_groups():
     check(w, g, seed=5, rows=list(range(0, 600, 5)))
 
 
-@pytest.mark.parametrize("prompts,samples", [(40, 3), (160, 3), (48, 6)])
-def test_merge_across_wave_counts(prompts, samples):
+@pytest.mark.parametrize("prompts,samples,d,dtype", [(40, 3, 128, "bf16"), (160, 3, 128, "bf16"), (48, 6, 128, "bf16"),
+                                                     (40, 3, 64, "f16"), (160, 3, 64, "bf16"), (48, 6, 64, "f16")])
+def test_merge_across_wave_counts(prompts, samples, d, dtype):
     # 32/8 heads, one (group, KV head) unit per member set: 320 units run four
     # waves per set, 1280 two, and 48 x 6 (two sets of 3) four again with a
     # shared prefix of 1-7 blocks; every wave's partial state is merged in LDS
-    # by the waves together (each writes a quarter or a half of every row)
+    # by the waves together, each storing a quarter or a half of every row's
+    # dims (8 or 4 bytes per lane at head_dim 64)
     rng = np.random.default_rng(prompts + samples)
     plens = [int(x) for x in rng.integers(17, 120, prompts)]
     gens = [[int(x) for x in rng.integers(1, 40, samples)] for _ in range(prompts)]
-    w = forked_batch(plens, [samples] * prompts, gens, 32, 8, 128, "bf16", seed=prompts)
+    w = forked_batch(plens, [samples] * prompts, gens, 32, 8, d, dtype, seed=prompts)
     g = PB.pa_shared_prefix_groups(w.block_tables, w.context_lens, 16)
     assert g.num_groups == prompts
     check(w, g, seed=3)
