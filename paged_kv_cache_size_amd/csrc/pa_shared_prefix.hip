@@ -182,7 +182,10 @@ __global__ __launch_bounds__(64 * NW) void shared_prefix_kernel(const GroupArgs 
   f32x4 acc[VPL];
 #pragma unroll
   for (int t = 0; t < VPL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;  // running max (log2 units) and partial denominator of this lane's column
+  // running max (log2 units; a finite floor until the first key), the
+  // threshold that moves it, and the partial denominator of this lane's column
+  constexpr float kFloor = -3.0e38f, kLazyLog2 = 8.f;
+  float m = kFloor, mth = kFloor + kLazyLog2, l = 0.f;
 
   // Step j: K into ring slot `slot`, V into registers.  Past the wave's
   // last step the loads go through an empty descriptor (zeros, no memory
@@ -221,31 +224,46 @@ __global__ __launch_bounds__(64 * NW) void shared_prefix_kernel(const GroupArgs 
 #pragma unroll
     for (int c = 0; c < NKC; ++c) sacc = Ops::qk(kr[c], qop[c], sacc);
     float sc[4];
-    bool ok[4];
-    VT vm[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool row_ok = 4 * i + gq < valid;
-      ok[i] = act && row_ok;
-      sc[i] = ok[i] ? sacc[i] * a.qscale : -INFINITY;
-      vm[i] = row_ok ? vr[i] : VT{};  // stale rows (even NaN) must not reach the MFMA
+    for (int i = 0; i < 4; ++i) sc[i] = act && 4 * i + gq < valid ? sacc[i] * a.qscale : -INFINITY;
+    // rows past the block's valid count (stale, even NaN) must not reach the
+    // MFMA: only a member's last block has any (a wave-uniform test)
+    VT vm[4];
+    if (valid < BS) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vm[i] = 4 * i + gq < valid ? vr[i] : VT{};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vm[i] = vr[i];
     }
-    const float mn = fmaxf(m, rows_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]))));
-    const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m - mn);  // a column with no key yet stays at 0
-    m = mn;
+    // The running max moves only when a score passes it by more than 2^8
+    // (log2 units), so weights stay <= 256 and the rescale of the
+    // accumulators is a rare wave-uniform branch; each lane tests its own
+    // four scores, and the column max across the lane groups is taken only
+    // inside the branch.  The max is finite from the start (a floor), so an
+    // absent key's score of -inf gives weight exp2(-inf) = 0 with no select.
+    const float smax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    if (__ballot(smax > mth)) {
+      const float mn = fmaxf(m, rows_max(smax));
+      const float alpha = fast_exp2(m - mn);  // 0 while m is the floor
+      m = mn;
+      mth = mn + kLazyLog2;
+      l *= alpha;
+#pragma unroll
+      for (int tt = 0; tt < VPL; ++tt) acc[tt] *= alpha;
+    }
     float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = ok[i] ? fast_exp2(sc[i] - mn) : 0.f;
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - m);
     const uint2 pb = make_uint2(Ops::pack(p[0], p[1]), Ops::pack(p[2], p[3]));
     // the denominator sums the same dtype-rounded weights that P.V multiplies
-    l = fmaf(l, alpha, Ops::sum_pair(pb.x) + Ops::sum_pair(pb.y));
+    l += Ops::sum_pair(pb.x) + Ops::sum_pair(pb.y);
 #pragma unroll
     for (int tt = 0; tt < VPL; ++tt) {
       const int w = tt >> 1;
       const uint32_t sel = (tt & 1) ? 0x07060302u : 0x05040100u;  // high or low 16-bit halves
       const uint2 va = make_uint2(__builtin_amdgcn_perm(vword<VPL>(vm[1], w), vword<VPL>(vm[0], w), sel),
                                   __builtin_amdgcn_perm(vword<VPL>(vm[3], w), vword<VPL>(vm[2], w), sel));
-      acc[tt] *= alpha;
       acc[tt] = Ops::pv(va, pb, acc[tt]);
     }
   };
