@@ -15,9 +15,11 @@
 // The NW waves of the workgroup split that list of steps evenly, each with
 // its own online softmax over its part, and merge their partial states
 // through LDS at the end, so no partial leaves the workgroup and no second
-// launch merges them.  Per step the arithmetic is the decode tile's: QK on
+// launch merges them.  Per step the operands are the decode tile's: QK on
 // mfma_f32_16x16x32, P.V on mfma_f32_16x16x16, K through an LDS ring filled
-// by direct-to-LDS loads, V in registers, masks applied as selects.
+// by direct-to-LDS loads, V in registers; the running max moves lazily (by
+// more than 2^8 only, as in the prefill tiles) and masks are selects on the
+// scores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
