@@ -121,6 +121,7 @@ def test_decode_past_4gib(dtype, h, hkv, d, lens, ps):
     # the oracle's pools: the seeded small pools with the oracle's own write
     kp, vp = W.raw_numpy(t["k_pool"]), W.raw_numpy(t["v_pool"])
     small_slots = O.slot_mapping(w.block_tables, w.context_lens, w.block_size)
+    assert np.array_equal(slots_small.cpu().numpy(), small_slots)
     O.reshape_and_cache(kp, W.raw_numpy(t["key"]), small_slots)
     O.reshape_and_cache(vp, W.raw_numpy(t["value"]), small_slots)
     # the rows written past 4 GiB, and every other block moved there
