@@ -549,6 +549,54 @@ int pa_convert_blocks(void* dst_k_pool, void* dst_v_pool, pa_kv_layout dst_layou
                       pa_dtype dtype, void* stream);
 
 /*
+ * pa_write_new_tokens - the slot mapping and the pool write of one decode
+ * step in one launch.
+ *
+ * Sequence b's new token is the last position of its context, p =
+ * context_lens[b] - 1 (HB, "分页注意力"); its slot is
+ * block_tables[b][p / block_size] * block_size + p % block_size (HB, "块表与
+ * slot mapping"), and its K and V rows key[b], value[b] are copied bit for bit
+ * into that slot of the pools (HB, "实现", PagedKVCache.write): the result of
+ * pa_slot_mapping (query_start_loc NULL) followed by pa_reshape_and_cache_layout.
+ *
+ *   key, value      [num_seqs, num_kv_heads, head_dim], dtype
+ *   k_pool, v_pool  pools of `layout` with num_blocks blocks (v_pool NULL
+ *                   for PA_KV_FUSED)
+ *   block_tables    int32 [num_seqs, max_blocks_per_seq]
+ *   context_lens    int32 [num_seqs], each including the new token
+ *   slot_mapping    out, int64 [num_seqs], or NULL when the caller does not
+ *                   need the slots
+ *
+ * Device contents: as pa_slot_mapping and pa_reshape_and_cache - a context
+ * of 0 tokens or a logical block >= max_blocks_per_seq gives slot -1, and a
+ * slot outside the pool writes nothing; each new token's slot must be its
+ * sequence's own.  Errors: INVALID_ARG for null pointers or non-positive
+ * sizes, UNSUPPORTED for an unknown dtype, HIP.  num_seqs == 0 enqueues
+ * nothing.
+ */
+int pa_write_new_tokens(const void* key, const void* value, void* k_pool, void* v_pool,
+                        const int32_t* block_tables, const int32_t* context_lens, int64_t* slot_mapping,
+                        int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t max_blocks_per_seq, int64_t num_blocks, pa_dtype dtype,
+                        pa_kv_layout layout, void* stream);
+
+/*
+ * pa_decode_step - a whole decode step: pa_write_new_tokens, then
+ * pa_decode_attention_layout over the contexts that now include the new
+ * tokens (two launches, three when a context is split into partitions).
+ * Arguments as those two calls take them; workspace >=
+ * pa_decode_workspace_bytes_ex(..., partition_size) (with partition_size 0,
+ * pa_decode_workspace_bytes).  Every argument check of both calls runs
+ * before anything is enqueued, so a rejected step writes nothing.
+ */
+int pa_decode_step(void* out, const void* query, const void* key, const void* value, void* k_pool,
+                   void* v_pool, const int32_t* block_tables, const int32_t* context_lens,
+                   int64_t* slot_mapping, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                   int32_t max_context_len, float scale, pa_dtype dtype, void* workspace,
+                   size_t workspace_bytes, int32_t partition_size, pa_kv_layout layout, void* stream);
+
+/*
  * Measurement: a streaming read of `bytes` bytes of device memory at `src`
  * (16-byte aligned, bytes a multiple of 16), each byte loaded once in 16-byte
  * vector loads spread over the whole device, non-temporal if `nontemporal` is

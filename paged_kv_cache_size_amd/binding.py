@@ -73,6 +73,10 @@ SIGNATURES = {
                                                    ctypes.c_int, _P]),
     "pa_convert_blocks": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _P, _P, ctypes.c_int, _I64, _P, _P, _I64, _I32,
                                          _I32, _I32, ctypes.c_int, _P]),
+    "pa_write_new_tokens": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I64,
+                                           ctypes.c_int, ctypes.c_int, _P]),
+    "pa_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I64,
+                                      _I32, _F32, ctypes.c_int, _P, _SZ, _I32, ctypes.c_int, _P]),
     "pa_stream_read": (ctypes.c_int, [_P, _SZ, _P, ctypes.c_int, _P]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
@@ -218,6 +222,62 @@ def pa_reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, layout: int =
     else:
         rc = lib().pa_reshape_and_cache_layout(*args, int(layout), _stream(key))
     _check(rc, "pa_reshape_and_cache")
+
+
+def pa_write_new_tokens(key, value, k_pool, v_pool, block_tables, context_lens, slot_out=None,
+                        layout: int = PA_KV_SPLIT):
+    """Slot mapping and pool write of a decode step in one launch: each
+    sequence's new token (its last context position) into its slot; the
+    slots go to ``slot_out`` (int64 [B]) when given (see pa.h)."""
+    torch = _torch()
+    (nb, bs, hkv, d), kp, vp = _pool(k_pool, v_pool, layout)
+    B = block_tables.shape[0]
+    if key.shape != (B, hkv, d) or value.shape != key.shape:
+        raise ValueError(f"key/value must be [num_seqs, num_kv_heads, head_dim] = {(B, hkv, d)}")
+    if not (key.dtype == value.dtype == k_pool.dtype):
+        raise TypeError("key, value and pools must share a dtype")
+    if context_lens.shape != (B,):
+        raise ValueError("context_lens must be [num_seqs]")
+    rc = lib().pa_write_new_tokens(
+        _dev(key, "key", ndim=3), _dev(value, "value", ndim=3), kp, vp,
+        _dev(block_tables, "block_tables", torch.int32, 2), _dev(context_lens, "context_lens", torch.int32, 1),
+        None if slot_out is None else _dev(slot_out, "slot_out", torch.int64, 1), B, hkv, d, bs,
+        block_tables.shape[1], nb, pa_dtype(key), int(layout), _stream(key))
+    _check(rc, "pa_write_new_tokens")
+    return slot_out
+
+
+def pa_decode_step(query, key, value, k_pool, v_pool, block_tables, context_lens, scale: float,
+                   max_context_len: int, out=None, workspace=None, slot_out=None, partition_size: int = 0,
+                   layout: int = PA_KV_SPLIT):
+    """A whole decode step in one library call: the new tokens' slots and
+    K/V rows (one launch), then paged attention over the contexts that
+    include them; returns ``out`` [B, H, D] (see pa.h)."""
+    torch = _torch()
+    B, H, D = query.shape
+    (nb, bs, hkv, d2), kp, vp = _pool(k_pool, v_pool, layout)
+    if d2 != D or key.shape != (B, hkv, D) or value.shape != key.shape:
+        raise ValueError("query / key / value / pool shapes do not match")
+    if not (query.dtype == key.dtype == value.dtype == k_pool.dtype):
+        raise TypeError("query, key, value and pools must share a dtype")
+    if block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables / context_lens batch mismatch")
+    if out is None:
+        out = torch.empty_like(query)
+    need = pa_decode_workspace_bytes(B, H, D, max_context_len, bs, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = None if workspace is None else _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().pa_decode_step(
+        _dev(out, "out", query.dtype, 3), _dev(query, "query", ndim=3), _dev(key, "key", ndim=3),
+        _dev(value, "value", ndim=3), kp, vp, _dev(block_tables, "block_tables", torch.int32, 2),
+        _dev(context_lens, "context_lens", torch.int32, 1),
+        None if slot_out is None else _dev(slot_out, "slot_out", torch.int64, 1), B, H, hkv, D, bs,
+        block_tables.shape[1], nb, int(max_context_len), float(scale), pa_dtype(query), ws_ptr, ws_bytes,
+        int(partition_size), int(layout), _stream(query))
+    _check(rc, "pa_decode_step")
+    return out
 
 
 def pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, block_size,
@@ -619,9 +679,6 @@ def pa_decode_combine(out, context_lens, max_context_len: int, partition_size: i
 def decode_step(query, key, value, k_pool, v_pool, block_tables, context_lens, scale: float,
                 max_context_len: int, out=None, workspace=None, slot_out=None, partition_size: int = 0):
     """The whole decode hot path on one stream: slots of the new tokens,
-    their K/V written into the pools, then paged attention."""
-    bs = k_pool.shape[1]
-    slots = pa_slot_mapping(block_tables, context_lens, bs, out=slot_out)
-    pa_reshape_and_cache(key, value, k_pool, v_pool, slots)
-    return pa_decode_attention(query, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
-                               out=out, workspace=workspace, partition_size=partition_size)
+    their K/V written into the pools, then paged attention (pa_decode_step)."""
+    return pa_decode_step(query, key, value, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
+                          out=out, workspace=workspace, slot_out=slot_out, partition_size=partition_size)

@@ -322,3 +322,68 @@ def test_oversized_grid_is_an_argument_error():
     n = 1 << 25
     rc = B.lib().pa_reshape_and_cache(FAKE, FAKE, FAKE, FAKE, FAKE, n, 8, 128, 16, 1 << 22, B.PA_BF16, None)
     assert rc == B.PA_ERR_INVALID_ARG
+
+
+def write_new(**kw):
+    args = dict(key=FAKE, value=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, slots=None, B=4, Hkv=2, D=128, bs=16,
+                mb=8, nb=64, dtype=B.PA_BF16, layout=B.PA_KV_SPLIT)
+    args.update(kw)
+    a = args
+    return B.lib().pa_write_new_tokens(a["key"], a["value"], a["k"], a["v"], a["bt"], a["lens"], a["slots"], a["B"],
+                                       a["Hkv"], a["D"], a["bs"], a["mb"], a["nb"], a["dtype"], a["layout"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(key=None), B.PA_ERR_INVALID_ARG),
+    (dict(value=None), B.PA_ERR_INVALID_ARG),
+    (dict(k=None), B.PA_ERR_INVALID_ARG),
+    (dict(v=None), B.PA_ERR_INVALID_ARG),
+    (dict(bt=None), B.PA_ERR_INVALID_ARG),
+    (dict(lens=None), B.PA_ERR_INVALID_ARG),
+    (dict(B=-1), B.PA_ERR_INVALID_ARG),
+    (dict(Hkv=0), B.PA_ERR_INVALID_ARG),
+    (dict(D=0), B.PA_ERR_INVALID_ARG),
+    (dict(bs=0), B.PA_ERR_INVALID_ARG),
+    (dict(mb=0), B.PA_ERR_INVALID_ARG),
+    (dict(nb=0), B.PA_ERR_INVALID_ARG),
+    (dict(dtype=7), B.PA_ERR_UNSUPPORTED),
+    (dict(layout=5), B.PA_ERR_INVALID_ARG),
+    (dict(B=0, key=None, value=None, k=None, v=None, bt=None, lens=None), B.PA_OK),  # an empty batch
+])
+def test_write_new_tokens_argument_checks(kw, status):
+    assert write_new(**kw) == status
+
+
+def step(**kw):
+    args = dict(out=FAKE, query=FAKE, key=FAKE, value=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, slots=None, B=4, H=8,
+                Hkv=2, D=128, bs=16, mb=8, nb=64, maxlen=128, scale=0.088, dtype=B.PA_BF16, ws=None, wsb=0, ps=16,
+                layout=B.PA_KV_SPLIT)
+    args.update(kw)
+    a = args
+    return B.lib().pa_decode_step(a["out"], a["query"], a["key"], a["value"], a["k"], a["v"], a["bt"], a["lens"],
+                                  a["slots"], a["B"], a["H"], a["Hkv"], a["D"], a["bs"], a["mb"], a["nb"],
+                                  a["maxlen"], a["scale"], a["dtype"], a["ws"], a["wsb"], a["ps"], a["layout"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), B.PA_ERR_INVALID_ARG),
+    (dict(query=None), B.PA_ERR_INVALID_ARG),
+    (dict(key=None), B.PA_ERR_INVALID_ARG),
+    (dict(value=None), B.PA_ERR_INVALID_ARG),
+    (dict(k=None), B.PA_ERR_INVALID_ARG),
+    (dict(v=None), B.PA_ERR_INVALID_ARG),
+    (dict(nb=0), B.PA_ERR_INVALID_ARG),
+    (dict(H=6, Hkv=4), B.PA_ERR_INVALID_ARG),
+    (dict(maxlen=129), B.PA_ERR_INVALID_ARG),           # beyond max_blocks_per_seq * block_size
+    (dict(scale=float("nan")), B.PA_ERR_INVALID_ARG),
+    (dict(D=96), B.PA_ERR_UNSUPPORTED),
+    (dict(dtype=7), B.PA_ERR_UNSUPPORTED),
+    (dict(layout=5), B.PA_ERR_INVALID_ARG),
+    (dict(ps=24), B.PA_ERR_INVALID_ARG),                # not a whole number of 16-token steps
+    (dict(ps=64, maxlen=128), B.PA_ERR_WORKSPACE),      # two partitions and no workspace
+    (dict(ps=0, maxlen=128 * 8, mb=64), B.PA_ERR_WORKSPACE),  # the library's choice needs the documented bound
+    (dict(B=0, out=None, query=None, key=None, value=None, k=None, v=None, bt=None, lens=None), B.PA_OK),
+])
+def test_decode_step_argument_checks(kw, status):
+    """Every check runs before anything is enqueued (no HIP call is reached)."""
+    assert step(**kw) == status
