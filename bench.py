@@ -2,8 +2,10 @@
 """Benchmark of the paged-decode hot path on one MI355X.
 
 One step = the whole decode hot path over one batch: slot mapping of the new
-tokens, their K/V written into the paged pools, paged attention over every
-sequence's context (partition kernel + merge kernel).  Default workload: the
+tokens and their K/V written into the paged pools (one launch,
+pa_write_new_tokens, as pa_decode_step runs it; ``--separate-write`` for the
+two launches pa_slot_mapping + pa_reshape_and_cache), paged attention over
+every sequence's context (partition kernel + merge kernel).  Default workload: the
 Llama-style GQA layer, 256 sequences x 4096 tokens, 32 query / 8 KV heads,
 head_dim 128, bf16, block 16 (4 GiB of K/V read per step).
 
@@ -61,6 +63,9 @@ def parse():
                    help="pool layout: split K and V pools, or one fused [NB, H_kv, BS, 2D] pool")
     p.add_argument("--shared-prefix", action="store_true",
                    help="decode with shared prompt prefixes read once per group (cascade)")
+    p.add_argument("--separate-write", action="store_true",
+                   help="slot mapping and pool write as two launches (pa_slot_mapping, pa_reshape_and_cache) "
+                        "instead of one (pa_write_new_tokens, as pa_decode_step runs them)")
     p.add_argument("--graph", action="store_true",
                    help="time the step as one captured HIP graph (launch costs gone; per-kernel times stay eager)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -723,6 +728,15 @@ def main_decode(args, oracle_pool):
         turn[0] += 1
         PB.pa_reshape_and_cache(t["key"], t["value"], *pool(), slots)
 
+    def k_write_new():  # slots and rows in one launch
+        turn[0] += 1
+        PB.pa_write_new_tokens(t["key"], t["value"], *pool(), bt, lens, slot_out=slots)
+
+    # the step's first two stages: the slot mapping and the pool write, or
+    # both in one launch and an empty second stage
+    def write_stages(sep, fused_new):
+        return [k_slot, sep] if args.separate_write else [fused_new, lambda: None]
+
     def k_part():
         PB.pa_decode_partitions(t["query"], *pool(), bt, lens, w.scale, w.max_context_len, ps,
                                 workspace=ws, out=out)
@@ -730,7 +744,7 @@ def main_decode(args, oracle_pool):
     def k_comb():
         PB.pa_decode_combine(out, lens, w.max_context_len, ps, workspace=ws)
 
-    stages = [k_slot, k_write, k_part, k_comb]
+    stages = write_stages(k_write, k_write_new) + [k_part, k_comb]
     kernel = "decode_partition_kernel" if w.dtype == "f32" else "decode_mfma_kernel"
     stream_buffers = [t["k_pool"], t["v_pool"]]
     if args.layout == "fused":
@@ -745,11 +759,15 @@ def main_decode(args, oracle_pool):
         def k_write():
             PB.pa_reshape_and_cache(t["key"], t["value"], fused, None, slots, layout=PB.PA_KV_FUSED)
 
+        def k_write_new_fused():
+            PB.pa_write_new_tokens(t["key"], t["value"], fused, None, bt, lens, slot_out=slots,
+                                   layout=PB.PA_KV_FUSED)
+
         def k_part():  # the merge kernel runs inside when a sequence spans several partitions
             PB.pa_decode_attention(t["query"], fused, None, bt, lens, w.scale, w.max_context_len, out=out,
                                    workspace=ws, partition_size=ps, layout=PB.PA_KV_FUSED)
 
-        stages = [k_slot, k_write, k_part, lambda: None]
+        stages = write_stages(k_write, k_write_new_fused) + [k_part, lambda: None]
         stream_buffers = [fused]
     if args.shared_prefix:
         # groups found on the host from the tables (scheduler work, untimed)
@@ -764,7 +782,7 @@ def main_decode(args, oracle_pool):
             PB.pa_decode_attention_shared_prefix(t["query"], *pool(), bt, lens, groups, w.scale,
                                                  w.max_context_len, out=out, workspace=cws, device_groups=dgroups)
 
-        stages = [k_slot, k_write, k_cascade, lambda: None]
+        stages = write_stages(k_write, k_write_new) + [k_cascade, lambda: None]
         kernel = "prefill_mfma_kernel prefix + suffix passes and merge_slots_kernel (one stage)"
         ps = 0
     ms_per_step, per_kernel_ms, wall = time_stages(stages, args.steps, args.warmup)
@@ -809,6 +827,7 @@ def main_decode(args, oracle_pool):
                    "head_dim": D, "block_size": w.block_size, "num_blocks": w.num_blocks,
                    "partition_size": ps, "shared_prefix_cascade": bool(args.shared_prefix),
                    "pool_layout": args.layout, "hip_graph": bool(args.graph),
+                   "new_token_write": "two launches" if args.separate_write else "one launch",
                    "pool_replicas": len(pools),
                    "description": w.description},
         "kv_read_bytes_per_step": kv_bytes,
@@ -817,9 +836,10 @@ def main_decode(args, oracle_pool):
         "ms_per_step_eager": eager_ms,
         "kv_GBps_step": kv_bytes / (ms_per_step * 1e-3) / 1e9,
         "context_tokens_per_s": float(w.context_lens.sum()) / (ms_per_step * 1e-3),
-        "kernel_us": {"slot_mapping": per_kernel_ms[0] * 1e3, "reshape_and_cache": per_kernel_ms[1] * 1e3,
-                      "decode_partition": per_kernel_ms[2] * 1e3,
-                      "combine": per_kernel_ms[3] * 1e3 if merged else None},
+        "kernel_us": dict(({"slot_mapping": per_kernel_ms[0] * 1e3, "reshape_and_cache": per_kernel_ms[1] * 1e3}
+                           if args.separate_write else {"write_new_tokens": per_kernel_ms[0] * 1e3}),
+                          decode_partition=per_kernel_ms[2] * 1e3,
+                          combine=per_kernel_ms[3] * 1e3 if merged else None),
         "plain_entry_point": plain,
         "decode_partition_us_percentiles": part_pct,
         "step_us_percentiles": step_pct,
