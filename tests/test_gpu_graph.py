@@ -96,6 +96,47 @@ def test_decode_step_graph(name):
     replay_and_check(g, out, ws, eager)
 
 
+@pytest.mark.parametrize("name", ["qwen1p5b_bf16", "shared_prefix_bf16"])
+def test_one_call_decode_step_graph(name):
+    """pa_decode_step (slots and new rows in one launch, then attention)
+    captured whole: every replay bitwise equal to the eager step, which
+    matches the oracle, and the slots and pools left as the oracle writes
+    them (rewriting the same rows is idempotent)."""
+    w = W.make_workload(name)
+    say(f"graph one-call decode step {name}")
+    t = W.make_tensors(w, 0, DEV)
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    lens = torch.from_numpy(w.context_lens).to(DEV)
+    B, H, D = t["query"].shape
+    ps = PB.pa_decode_partition_size(B, H, w.num_kv_heads, D, w.max_context_len, w.block_size, torch.bfloat16,
+                                     context_lens=w.context_lens)
+    ws = torch.empty(max(1, PB.pa_decode_workspace_bytes(B, H, D, w.max_context_len, w.block_size, ps)),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(t["query"])
+    slots = torch.empty(B, dtype=torch.int64, device=DEV)
+    kp_raw, vp_raw = W.raw_numpy(t["k_pool"]), W.raw_numpy(t["v_pool"])
+
+    def step():
+        PB.pa_decode_step(t["query"], t["key"], t["value"], t["k_pool"], t["v_pool"], bt, lens, w.scale,
+                          w.max_context_len, out=out, workspace=ws, slot_out=slots, partition_size=ps)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    ref_slots = O.slot_mapping(w.block_tables, w.context_lens, w.block_size)
+    O.reshape_and_cache(kp_raw, W.raw_numpy(t["key"]), ref_slots)
+    O.reshape_and_cache(vp_raw, W.raw_numpy(t["value"]), ref_slots)
+    ref = O.decode_attention(W.raw_numpy(t["query"]), kp_raw, vp_raw, w.block_tables, w.context_lens, w.scale,
+                             w.dtype)
+    assert float(np.max(np.abs(O.widen(W.raw_numpy(eager), w.dtype) - ref))) <= TOL
+    g = capture(step)
+    slots.fill_(-5)
+    replay_and_check(g, out, ws, eager)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    assert np.array_equal(W.raw_numpy(t["k_pool"]).view(np.uint8), kp_raw.view(np.uint8))
+    assert np.array_equal(W.raw_numpy(t["v_pool"]).view(np.uint8), vp_raw.view(np.uint8))
+
+
 def test_prefill_step_graph():
     pb = W.mixed_varlen_bf16(seed=1)
     w = pb.workload
