@@ -747,6 +747,7 @@ def main_decode(args, oracle_pool):
     stages = write_stages(k_write, k_write_new) + [k_part, k_comb]
     kernel = "decode_partition_kernel" if w.dtype == "f32" else "decode_mfma_kernel"
     stream_buffers = [t["k_pool"], t["v_pool"]]
+    fused = None
     if args.layout == "fused":
         if args.shared_prefix or len(pools) > 1:
             raise SystemExit("--layout fused runs without --shared-prefix and --replicas")
@@ -786,13 +787,30 @@ def main_decode(args, oracle_pool):
         kernel = "prefill_mfma_kernel prefix + suffix passes and merge_slots_kernel (one stage)"
         ps = 0
     ms_per_step, per_kernel_ms, wall = time_stages(stages, args.steps, args.warmup)
+    stage_samples = time_stages.samples
+    staged_ms = ms_per_step
+    step_call = "one library call per stage"
+    if not args.shared_prefix and not args.separate_write:
+        # The step as a caller makes it: one library call, pa_decode_step (the
+        # same launches as the stages above, bitwise the same results); the
+        # stages above give the per-kernel times.
+        layout = PB.PA_KV_FUSED if args.layout == "fused" else PB.PA_KV_SPLIT
+
+        def one_call():
+            turn[0] += 1
+            k, v = (fused, None) if args.layout == "fused" else pool()
+            PB.pa_decode_step(t["query"], t["key"], t["value"], k, v, bt, lens, w.scale, w.max_context_len,
+                              out=out, workspace=ws, slot_out=slots, partition_size=ps, layout=layout)
+
+        ms_per_step, _, wall = time_stages([one_call], args.steps, args.warmup)
+        step_call = "pa_decode_step (one call)"
     eager_ms = ms_per_step
     if args.graph:
         if len(pools) > 1:
             raise SystemExit("--graph captures one pool; it runs without --replicas")
         ms_per_step = time_graph(stages, args.steps, args.warmup)
-    part_pct = percentiles_us(time_stages.samples[2])
-    step_pct = percentiles_us([sum(x) for x in zip(*time_stages.samples)])
+    part_pct = percentiles_us(stage_samples[2])
+    step_pct = percentiles_us([sum(x) for x in zip(*stage_samples)])
     # the merge stage launches a kernel only when some context spans several partitions
     merged = ps > 0 and args.layout == "split" and not args.shared_prefix and \
         PB.pa_decode_workspace_bytes(B, H, D, w.max_context_len, w.block_size, ps) > 0
@@ -834,6 +852,8 @@ def main_decode(args, oracle_pool):
         "kv_unique_read_bytes_per_step": kv_unique,
         "aux_bytes_per_step": w.aux_bytes(),
         "ms_per_step_eager": eager_ms,
+        "step_call": step_call,
+        "ms_per_step_separate_calls": staged_ms,
         "kv_GBps_step": kv_bytes / (ms_per_step * 1e-3) / 1e9,
         "context_tokens_per_s": float(w.context_lens.sum()) / (ms_per_step * 1e-3),
         "kernel_us": dict(({"slot_mapping": per_kernel_ms[0] * 1e3, "reshape_and_cache": per_kernel_ms[1] * 1e3}
